@@ -1,0 +1,29 @@
+"""CPU oracle (TEST INFRASTRUCTURE ONLY).
+
+A plain float64 definition of block-sparse top-p attention with a cached-residual epilogue,
+written from the pages' description of the method. Only `tests/`, the package smoke check
+(`__graft_entry__.smoke`) and the benchmark's `cpu_baseline` leg may import it. It shares no
+code with the HIP library and never imports it.
+
+Parity status per function (pins live in tests/test_oracle_pins.py):
+  block_partition, block_mean_pool, block_scores, softmax_rows, topp_select, kept_lists,
+  mask_from_lists, masked_attention, dense_attention, residual_epilogue, dense_with_capture:
+  pinned (closed forms, invariants, library special cases, brute force, planted mutants).
+  The conventions the pages leave open (scale of the pooled logits, no log-block-size term,
+  tie order, inclusive threshold) are readings; the pins fix the oracle to those readings.
+"""
+from .oracle import (  # noqa: F401
+    block_mean_pool,
+    block_partition,
+    block_scores,
+    block_sparsity,
+    dense_attention,
+    dense_with_capture,
+    kept_flops,
+    kept_lists,
+    mask_from_lists,
+    masked_attention,
+    residual_epilogue,
+    softmax_rows,
+    topp_select,
+)

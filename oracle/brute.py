@@ -1,0 +1,93 @@
+"""Scalar pure-Python brute force for tiny inputs (test infrastructure, like the rest of the oracle).
+
+Every quantity is computed element by element with Python floats and `math`, without numpy
+vectorisation, so that the vectorised oracle can be checked against an independent spelling
+of the same definitions. The top-p check here does not sort at all: it enumerates every subset
+of key blocks, which characterises the top-p set without reference to an ordering.
+"""
+from __future__ import annotations
+
+import itertools
+import math
+
+
+def pool(x, n_tokens, block, dim):
+    """x: nested list [N][D] -> [M][D] block means over valid tokens."""
+    m = -(-n_tokens // block)
+    out = []
+    for j in range(m):
+        lo, hi = j * block, min(n_tokens, (j + 1) * block)
+        row = []
+        for d in range(dim):
+            acc = 0.0
+            for t in range(lo, hi):
+                acc += x[t][d]
+            row.append(acc / (hi - lo))
+        out.append(row)
+    return out
+
+
+def scores(q, k, n_tokens, block, dim, sm_scale):
+    """[M][M] block-pair softmax of s * (mean q_i . mean k_j)."""
+    qb = pool(q, n_tokens, block, dim)
+    kb = pool(k, n_tokens, block, dim)
+    m = len(qb)
+    out = []
+    for i in range(m):
+        logits = []
+        for j in range(m):
+            dot = 0.0
+            for d in range(dim):
+                dot += qb[i][d] * kb[j][d]
+            logits.append(sm_scale * dot)
+        mx = max(logits)
+        ex = [math.exp(v - mx) for v in logits]
+        tot = sum(ex)
+        out.append([e / tot for e in ex])
+    return out
+
+
+def min_cardinality_subsets(prob_row, p):
+    """Exhaustive search: (k*, best mass) where k* is the fewest blocks reaching mass >= p and
+    best mass is the largest mass over all subsets of that size. p >= 1 -> all blocks."""
+    m = len(prob_row)
+    if p >= 1.0:
+        return m, sum(prob_row)
+    for size in range(1, m + 1):
+        best = None
+        for sub in itertools.combinations(range(m), size):
+            mass = sum(prob_row[j] for j in sub)
+            if best is None or mass > best:
+                best = mass
+        if best >= p:
+            return size, best
+    return m, sum(prob_row)
+
+
+def attention_row(qt, keys, values, sm_scale):
+    """One query against a list of keys/values: softmax(s q.k) weighted sum, scalar loops."""
+    logits = []
+    for kr in keys:
+        dot = 0.0
+        for a, b in zip(qt, kr):
+            dot += a * b
+        logits.append(sm_scale * dot)
+    mx = max(logits)
+    w = [math.exp(v - mx) for v in logits]
+    tot = sum(w)
+    dim = len(values[0])
+    out = [0.0] * dim
+    for wi, vr in zip(w, values):
+        for d in range(dim):
+            out[d] += wi / tot * vr[d]
+    return out
+
+
+def masked_attention(q, k, v, n_tokens, block, sm_scale, mask_rows):
+    """q, k, v: [N][D] lists; mask_rows[i] = set of kept key blocks for query block i."""
+    out = []
+    for t in range(n_tokens):
+        i = t // block
+        toks = [u for u in range(n_tokens) if (u // block) in mask_rows[i]]
+        out.append(attention_row(q[t], [k[u] for u in toks], [v[u] for u in toks], sm_scale))
+    return out

@@ -1,0 +1,221 @@
+"""Plain float64 CPU oracle for block-sparse top-p attention with a cached-residual epilogue.
+
+TEST INFRASTRUCTURE. Only the tests, the package smoke check and the benchmark's CPU-baseline
+leg may import this module; the HIP library never does, and this module imports nothing from
+it. Every array is upcast to float64 before any arithmetic (bf16 -> fp64 is exact).
+
+Sources (page title, then section / figure):
+  [RECAP]   "RECAP: Reciprocal Sparse Attention and Hierarchical Caching for Efficient Video
+            Diffusion", paperpeel.com/paper/2610.26244.
+  [HEAD]    head-wise adaptive top-p abstract on thelatestinai.com/papers/2610.26244 (page titled
+            RECAP), first abstract.
+  [GSRS]    Growing Sparsity and Reduced Search abstract, same page, third abstract.
+  [CALIB]   CalibAtt, thelatestinai.com/papers/2603.05503.
+  [DFS]     "Ride the Wave: Precision-Allocated Sparse Attention for Smooth Video Generation",
+            thelatestinai.com/papers/2604.12219 (DFSAttn abstract).
+
+The method reaches plain masked softmax attention exactly (up to rounding) once the kept set
+is known, so attention here is that definition written out. Mask prediction is a heuristic,
+so it follows the steps in order: block partition, block means, block-pair softmax, top-p.
+Readings where the pages are silent (all listed in the design notes):
+  * the pooled logits use the attention scale s (default 1/sqrt(D)) and no log-block-size term;
+  * the last block may be short; pooling averages its valid tokens only, padded keys carry
+    no weight and padded query rows do not exist;
+  * equal block probabilities are ordered by lower key-block index first;
+  * the threshold is inclusive (the crossing block is kept, so kept mass >= p); p >= 1 keeps
+    every block; p = 0 keeps exactly the top block;
+  * the residual epilogue adds c_h * R to the sparse output, R = O_dense - O_sparse captured
+    at a dense refresh on the same kept set.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def block_partition(n_tokens: int, block: int):
+    """Block j holds tokens [j*b, min(N, (j+1)*b)); M = ceil(N / b); queries and keys alike.
+
+    Blocks of b tokens over the flattened sequence: [CALIB] Table S6 (query x key block
+    sizes) and Fig. S14; [DFS] abstract (block sparse attention over token blocks).
+    Returns (starts, ends) as int arrays of length M.
+    """
+    if n_tokens < 1 or block < 1:
+        raise ValueError("need n_tokens >= 1 and block >= 1")
+    m = -(-n_tokens // block)
+    starts = np.arange(m, dtype=np.int64) * block
+    ends = np.minimum(starts + block, n_tokens)
+    return starts, ends
+
+
+def block_mean_pool(x: np.ndarray, block: int) -> np.ndarray:
+    """Mean of each token block: X̄_j = (1/n_j) * sum_{t in block j} X_t.
+
+    [RECAP] §3.2: block means give the initial estimates used to score omitted interactions.
+    x: [B, H, N, D] -> [B, H, M, D] float64.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    starts, ends = block_partition(x.shape[2], block)
+    out = np.empty(x.shape[:2] + (len(starts), x.shape[3]), dtype=np.float64)
+    for j, (s, e) in enumerate(zip(starts, ends)):
+        out[:, :, j, :] = x[:, :, s:e, :].sum(axis=2) / float(e - s)
+    return out
+
+
+def softmax_rows(logits: np.ndarray) -> np.ndarray:
+    """exp(L - max_j L) / sum_j exp(L - max_j L) along the last axis (two-pass, stable)."""
+    shifted = logits - logits.max(axis=-1, keepdims=True)
+    e = np.exp(shifted)
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def block_scores(q: np.ndarray, k: np.ndarray, block: int, sm_scale: float) -> np.ndarray:
+    """Block-pair probabilities P̄[b,h,i,j] = softmax_j(s * Q̄_i . K̄_j).
+
+    Mask prediction scores block pairs from mean-pooled queries and keys and normalises each
+    query-block row with a softmax ([RECAP] §3.2 block means; [HEAD] online top-p mask
+    prediction; [GSRS] top-p over block weights). q, k: [B, H, N, D] -> [B, H, M, M].
+    """
+    qb = block_mean_pool(q, block)
+    kb = block_mean_pool(k, block)
+    logits = float(sm_scale) * np.matmul(qb, np.swapaxes(kb, -1, -2))
+    return softmax_rows(logits)
+
+
+def topp_select(probs: np.ndarray, top_p) -> dict:
+    """Per query-block row, keep the fewest key blocks whose probability mass reaches p_h.
+
+    [HEAD] (per-head top-p thresholds, online top-p), [GSRS] (top-p selection for adaptive
+    sparsity), [CALIB] Fig. 5 (threshold the top key blocks per query block):
+      1. order key blocks by probability, descending; equal values by lower index first;
+      2. C_k = running sum of the first k ordered probabilities (fp64, in that order);
+      3. k* = M if p >= 1, else the smallest k with C_k >= p (M if none);
+      4. keep the first k* ordered blocks; kept mass = C_{k*}.
+    probs: [B, H, M_q, M]; top_p: scalar or per-head array of length H.
+    Returns dict(mask bool [B,H,M,M], count int64 [B,H,M], mass float64 [B,H,M],
+                 order int64 [B,H,M,M]).
+    """
+    probs = np.asarray(probs, dtype=np.float64)
+    B, H, _, M = probs.shape  # rows are query blocks, columns key blocks
+    p = np.broadcast_to(np.asarray(top_p, dtype=np.float64), (H,))
+    idx = np.broadcast_to(np.arange(M, dtype=np.int64), probs.shape)
+    # lexsort: last key is primary -> (-prob) ascending == prob descending, then index ascending
+    order = np.lexsort((idx, -probs), axis=-1)
+    sorted_p = np.take_along_axis(probs, order, axis=-1)
+    csum = np.cumsum(sorted_p, axis=-1)  # sequential accumulation along each row
+    p_b = p[None, :, None, None]
+    reached = csum >= p_b
+    first = np.where(reached.any(axis=-1), reached.argmax(axis=-1) + 1, M)
+    count = np.where(p[None, :, None] >= 1.0, M, first).astype(np.int64)
+    rank = np.empty_like(order)
+    np.put_along_axis(rank, order, np.broadcast_to(np.arange(M), order.shape), axis=-1)
+    mask = rank < count[..., None]
+    mass = np.take_along_axis(csum, (count - 1)[..., None], axis=-1)[..., 0]
+    return {"mask": mask, "count": count, "mass": mass, "order": order}
+
+
+def kept_lists(mask: np.ndarray):
+    """Ascending kept key-block indices per row: (count [B,H,M], idx [B,H,M,M] padded -1)."""
+    B, H, M, _ = mask.shape
+    count = mask.sum(axis=-1).astype(np.int64)
+    idx = np.full((B, H, M, M), -1, dtype=np.int64)
+    for b in range(B):
+        for h in range(H):
+            for i in range(M):
+                js = np.nonzero(mask[b, h, i])[0]
+                idx[b, h, i, : len(js)] = js
+    return count, idx
+
+
+def mask_from_lists(count: np.ndarray, idx: np.ndarray, m: int) -> np.ndarray:
+    """Boolean block mask [B,H,M,M] from kept lists (entries past `count` are ignored)."""
+    count = np.asarray(count)
+    idx = np.asarray(idx)
+    B, H, M = count.shape
+    mask = np.zeros((B, H, M, m), dtype=bool)
+    for b in range(B):
+        for h in range(H):
+            for i in range(M):
+                c = int(count[b, h, i])
+                mask[b, h, i, idx[b, h, i, :c]] = True
+    return mask
+
+
+def _attend(qt: np.ndarray, kt: np.ndarray, vt: np.ndarray, sm_scale: float) -> np.ndarray:
+    """softmax(s * q k^T) v for one set of queries over one key set, two-pass in fp64."""
+    s = float(sm_scale) * (qt @ kt.T)
+    s -= s.max(axis=-1, keepdims=True)
+    w = np.exp(s)
+    w /= w.sum(axis=-1, keepdims=True)
+    return w @ vt
+
+
+def masked_attention(q, k, v, block: int, sm_scale: float, mask: np.ndarray,
+                     rows=None) -> np.ndarray:
+    """Block-sparse attention: each query attends only to the valid tokens of its kept blocks.
+
+    For a query t in block i with kept key blocks J_i, O_t = softmax_u(s * Q_t . K_u) V_u over
+    u in the union of the blocks in J_i. This is the computation that block-sparse kernels
+    perform on "selected interactions" ([RECAP] §4.1 implementation details; [DFS] abstract).
+    q, k, v: [B, H, N, D]; mask: bool [B, H, M, M]; rows: optional iterable of (b, h, i)
+    query blocks to compute (others are left NaN). Returns float64 [B, H, N, D].
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, H, N, D = q.shape
+    starts, ends = block_partition(N, block)
+    M = len(starts)
+    out = np.full((B, H, N, D), np.nan, dtype=np.float64)
+    if rows is None:
+        rows = [(b, h, i) for b in range(B) for h in range(H) for i in range(M)]
+    for b, h, i in rows:
+        js = np.nonzero(mask[b, h, i])[0]
+        if len(js) == 0:
+            raise ValueError("a query block must keep at least one key block")
+        toks = np.concatenate([np.arange(starts[j], ends[j]) for j in js])
+        qs = slice(starts[i], ends[i])
+        out[b, h, qs] = _attend(q[b, h, qs], k[b, h, toks], v[b, h, toks], sm_scale)
+    return out
+
+
+def dense_attention(q, k, v, sm_scale: float, rows=None, block: int = 64) -> np.ndarray:
+    """Full softmax attention over all N keys: the dense refresh ([RECAP] §4.1, §3.2)."""
+    q = np.asarray(q, dtype=np.float64)
+    B, H, N, D = q.shape
+    M = -(-N // block)
+    return masked_attention(q, k, v, block, sm_scale, np.ones((B, H, M, M), dtype=bool),
+                            rows=rows)
+
+
+def residual_epilogue(o_sparse: np.ndarray, residual: np.ndarray, res_scale) -> np.ndarray:
+    """O' = O_sparse + c_h * R per head: the cached dense refinement added to the fresh sparse
+    estimate ([RECAP] §3.2: with y_t = ȳ_t + d_t the reconstruction ŷ_t = ȳ_t + d_h has error
+    d_h - d_t, zero at the refresh step; §1 and §5: fresh statistics set how strongly the aging
+    refinement is applied, here the per-head scale c_h)."""
+    o_sparse = np.asarray(o_sparse, dtype=np.float64)
+    c = np.asarray(res_scale, dtype=np.float64).reshape(1, -1, 1, 1)
+    return o_sparse + c * np.asarray(residual, dtype=np.float64)
+
+
+def dense_with_capture(q, k, v, block: int, sm_scale: float, mask: np.ndarray, rows=None):
+    """Dense refresh that also captures the dense-minus-sparse residual on the same inputs.
+
+    R = O_dense - O_sparse(J) ([RECAP] §3.2 discrepancy d_h cached at the refresh step; §2:
+    dense-minus-window attention residuals shared across steps). Returns (O_dense, R).
+    """
+    o_d = dense_attention(q, k, v, sm_scale, rows=rows, block=block)
+    o_s = masked_attention(q, k, v, block, sm_scale, mask, rows=rows)
+    return o_d, o_d - o_s
+
+
+def block_sparsity(count: np.ndarray, m: int) -> float:
+    """Fraction of skipped block pairs: 1 - mean(k*) / M."""
+    return 1.0 - float(np.mean(count)) / float(m)
+
+
+def kept_flops(count_or_mask, n_tokens: int, block: int, head_dim: int) -> float:
+    """Attention FLOPs on kept pairs: 4 * D * sum over kept (i, j) of n_i * n_j."""
+    starts, ends = block_partition(n_tokens, block)
+    n = (ends - starts).astype(np.float64)
+    mask = np.asarray(count_or_mask)
+    return float(4.0 * head_dim * np.einsum("bhij,i,j->", mask.astype(np.float64), n, n))

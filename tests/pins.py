@@ -1,0 +1,324 @@
+"""Checks that pin the CPU oracle to facts outside itself.
+
+Each `check_*` function raises AssertionError when the oracle (the module `oracle.oracle`,
+looked up at call time so that a test can plant a mistake in it) disagrees with a closed form,
+an invariant, a library routine or the scalar brute force. `test_oracle_pins.py` runs every
+check on the real oracle; `test_oracle_mutants.py` plants plausible mistakes in the oracle and
+requires that at least one check fails for each.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+from oracle import brute
+from oracle import oracle as O
+
+
+def _rand(shape, seed, scale=1.0):
+    return np.random.default_rng(seed).normal(0.0, scale, size=shape)
+
+
+# ----------------------------------------------------------------------------- pooling
+def check_pool_block_constant():
+    """A block-constant input pools to that constant, including the short last block."""
+    n, b, d = 200, 64, 3  # blocks of 64, 64, 64, 8
+    x = np.zeros((1, 1, n, d))
+    vals = [1.5, -2.25, 7.0, 0.125]
+    for j, v in enumerate(vals):
+        x[0, 0, j * b:(j + 1) * b, :] = v
+    pooled = O.block_mean_pool(x, b)
+    assert pooled.shape == (1, 1, 4, d)
+    assert np.array_equal(pooled[0, 0, :, 0], np.array(vals)), pooled[0, 0, :, 0]
+
+
+def check_pool_closed_form_ragged():
+    """X_t[d] = t + 10 d: block mean over [s, e) is (s + e - 1)/2 + 10 d (arithmetic series)."""
+    n, b, d = 150, 32, 4  # last block has 22 tokens
+    t = np.arange(n, dtype=np.float64)[:, None]
+    x = (t + 10.0 * np.arange(d)[None, :])[None, None]
+    pooled = O.block_mean_pool(x, b)[0, 0]
+    for j in range(pooled.shape[0]):
+        s, e = j * b, min(n, (j + 1) * b)
+        want = (s + e - 1) / 2.0 + 10.0 * np.arange(d)
+        assert np.allclose(pooled[j], want, rtol=0, atol=1e-12), (j, pooled[j], want)
+
+
+def check_pool_mass_invariant():
+    """sum_j n_j * X̄_j equals sum_t X_t (pooling preserves the total)."""
+    n, b = 333, 64
+    x = _rand((2, 3, n, 5), 7)
+    pooled = O.block_mean_pool(x, b)
+    s, e = O.block_partition(n, b)
+    nj = (e - s).astype(np.float64)
+    lhs = np.einsum("bhjd,j->bhd", pooled, nj)
+    assert np.allclose(lhs, x.sum(axis=2), rtol=1e-12, atol=1e-10)
+
+
+# ----------------------------------------------------------------------------- scores
+def _two_block_case(a0, a1, x0, x1, b=8):
+    """D = 1; query blocks are constant a0, a1; key blocks are constant x0, x1."""
+    q = np.zeros((1, 1, 2 * b, 1))
+    k = np.zeros((1, 1, 2 * b, 1))
+    q[0, 0, :b, 0], q[0, 0, b:, 0] = a0, a1
+    k[0, 0, :b, 0], k[0, 0, b:, 0] = x0, x1
+    return q, k
+
+
+def check_scores_closed_form():
+    """Two blocks: P̄[i,0] = 1 / (1 + exp(s * a_i * (x1 - x0))) (logistic of the logit gap)."""
+    a0, a1, x0, x1, s = 0.7, -1.9, 0.4, 2.3, 0.5
+    q, k = _two_block_case(a0, a1, x0, x1)
+    p = O.block_scores(q, k, 8, s)[0, 0]
+    for i, a in enumerate((a0, a1)):
+        p0 = 1.0 / (1.0 + math.exp(s * a * (x1 - x0)))
+        assert abs(p[i, 0] - p0) < 1e-14 and abs(p[i, 1] - (1.0 - p0)) < 1e-14, (i, p[i], p0)
+
+
+def check_scores_rows_and_degenerate():
+    """Rows sum to 1; a single block gives 1; identical key blocks give uniform 1/M."""
+    q = _rand((1, 2, 300, 16), 3)
+    k = _rand((1, 2, 300, 16), 4)
+    p = O.block_scores(q, k, 64, 0.25)
+    assert np.allclose(p.sum(-1), 1.0, atol=1e-14)
+    one = O.block_scores(q[:, :, :40], k[:, :, :40], 64, 0.25)
+    assert one.shape == (1, 2, 1, 1) and np.all(one == 1.0)
+    kc = np.tile(_rand((1, 2, 64, 16), 5), (1, 1, 5, 1))  # every key block is the same block
+    pu = O.block_scores(q[:, :, :320], kc, 64, 0.25)
+    assert np.allclose(pu, 0.2, atol=1e-15)
+
+
+def check_scores_scale_and_shift():
+    """softmax(2L) = P^2 / sum P^2 (the scale multiplies the logits); adding one vector to
+    every key leaves each row unchanged (a per-row constant logit shift)."""
+    q = _rand((1, 1, 256, 8), 11)
+    k = _rand((1, 1, 256, 8), 12)
+    p1 = O.block_scores(q, k, 32, 0.3)
+    p2 = O.block_scores(q, k, 32, 0.6)
+    sq = p1 ** 2
+    assert np.allclose(p2, sq / sq.sum(-1, keepdims=True), rtol=1e-12, atol=1e-15)
+    shift = _rand((1, 1, 1, 8), 13) * 3.0
+    p3 = O.block_scores(q, k + shift, 32, 0.3)
+    assert np.allclose(p3, p1, rtol=1e-11, atol=1e-15)
+    p0 = O.block_scores(q, k, 32, 0.0)
+    assert np.allclose(p0, 1.0 / 8.0, atol=1e-15)
+
+
+def check_scores_vs_brute():
+    """Vectorised scores equal the scalar loop spelling on a tiny ragged input."""
+    n, b, d, s = 45, 8, 5, 0.37
+    q = _rand((1, 1, n, d), 21)
+    k = _rand((1, 1, n, d), 22)
+    got = O.block_scores(q, k, b, s)[0, 0]
+    want = np.array(brute.scores(q[0, 0].tolist(), k[0, 0].tolist(), n, b, d, s))
+    assert np.allclose(got, want, rtol=0, atol=1e-13), np.abs(got - want).max()
+
+
+# ----------------------------------------------------------------------------- top-p
+def check_topp_inclusive_dyadic():
+    """Dyadic probabilities: p = 0.75 is reached exactly by {0, 1}; the crossing block is kept."""
+    probs = np.array([0.5, 0.25, 0.125, 0.125])[None, None, None, :]
+    probs = np.repeat(probs, 4, axis=2)
+    r = O.topp_select(probs, 0.75)
+    assert np.all(r["count"] == 2) and np.all(r["mask"][0, 0, :, :2]) and not r["mask"][..., 2:].any()
+    assert np.all(r["mass"] == 0.75)
+    r = O.topp_select(probs, 0.7500001)
+    assert np.all(r["count"] == 3)
+
+
+def check_topp_ties_lower_index():
+    """Equal probabilities are taken in ascending key-block order; p = 0 keeps the argmax."""
+    probs = np.full((1, 1, 1, 4), 0.25)
+    r = O.topp_select(probs, 0.5)
+    assert r["mask"][0, 0, 0].tolist() == [True, True, False, False]
+    probs2 = np.array([0.1, 0.4, 0.1, 0.4])[None, None, None, :]
+    r = O.topp_select(probs2, 0.0)
+    assert r["mask"][0, 0, 0].tolist() == [False, True, False, False]
+    r = O.topp_select(probs2, 0.45)
+    assert r["mask"][0, 0, 0].tolist() == [False, True, False, True]
+    r = O.topp_select(probs2, 0.85)
+    assert r["mask"][0, 0, 0].tolist() == [True, True, False, True]
+
+
+def _random_prob_rows(m, rows, seed, temp=1.5):
+    g = np.random.default_rng(seed)
+    logits = g.normal(0.0, temp, size=(1, 1, rows, m))
+    return O.softmax_rows(logits)
+
+
+def check_topp_invariants():
+    """Kept mass >= p; dropping the smallest kept block falls below p (minimality); sets nest
+    in p; p >= 1 keeps every block; p = 0 keeps exactly one block."""
+    probs = _random_prob_rows(37, 50, 31)
+    prev = None
+    for p in (0.0, 0.3, 0.6, 0.9, 0.97, 1.0):
+        r = O.topp_select(probs, p)
+        mask = r["mask"]
+        mass = (probs * mask).sum(-1)
+        assert np.all(mass >= p - 1e-12)
+        assert np.allclose(mass, r["mass"], atol=1e-12)
+        assert np.array_equal(mask.sum(-1), r["count"])
+        if p < 1.0:
+            smallest = np.where(mask, probs, np.inf).min(-1)
+            assert np.all((r["count"] == 1) | (mass - smallest < p)), p
+        if prev is not None:
+            assert np.all(~prev | mask), "kept sets must grow with p"
+        prev = mask
+    assert np.all(O.topp_select(probs, 1.0)["count"] == 37)
+    assert np.all(O.topp_select(probs, 0.0)["count"] == 1)
+    am = O.topp_select(probs, 0.0)["mask"].argmax(-1)
+    assert np.array_equal(am, probs.argmax(-1))
+
+
+def check_topp_vs_subset_search():
+    """For M <= 9: k* is the fewest blocks of any subset reaching p, and the kept set has the
+    largest mass among subsets of that size (exhaustive enumeration, no sorting)."""
+    probs = _random_prob_rows(9, 12, 41, temp=1.0)
+    for p in (0.35, 0.8, 0.95):
+        r = O.topp_select(probs, p)
+        for i in range(probs.shape[2]):
+            row = probs[0, 0, i].tolist()
+            kstar, best = brute.min_cardinality_subsets(row, p)
+            assert r["count"][0, 0, i] == kstar, (p, i, r["count"][0, 0, i], kstar)
+            assert abs(r["mass"][0, 0, i] - best) < 1e-12
+
+
+def check_topp_per_head_threshold():
+    """Thresholds apply per head: head h uses p[h]."""
+    probs = np.repeat(_random_prob_rows(20, 6, 51), 2, axis=1)
+    r = O.topp_select(probs, np.array([0.0, 1.0]))
+    assert np.all(r["count"][:, 0] == 1) and np.all(r["count"][:, 1] == 20)
+
+
+# ----------------------------------------------------------------------------- attention
+def _sdpa64(q, k, v, scale, mask=None):
+    tq, tk, tv = (torch.from_numpy(np.ascontiguousarray(a)) for a in (q, k, v))
+    am = None if mask is None else torch.from_numpy(mask)
+    o = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=am, scale=scale)
+    return o.numpy()
+
+
+def _token_mask(block_mask, n, b):
+    tb = np.arange(n) // b
+    return block_mask[:, :, tb][:, :, :, tb]
+
+
+def check_dense_vs_sdpa():
+    """All blocks kept == dense == torch SDPA in float64 (library routine)."""
+    n, b, d, s = 150, 32, 16, 0.2
+    q, k, v = (_rand((2, 2, n, d), 60 + i) for i in range(3))
+    m = -(-n // b)
+    dense = O.dense_attention(q, k, v, s, block=b)
+    allkept = O.masked_attention(q, k, v, b, s, np.ones((2, 2, m, m), bool))
+    ref = _sdpa64(q, k, v, s)
+    assert np.allclose(dense, ref, rtol=0, atol=1e-12), np.abs(dense - ref).max()
+    assert np.array_equal(dense, allkept)
+
+
+def check_masked_vs_sdpa():
+    """Block mask expanded to tokens == torch SDPA with that boolean mask (float64)."""
+    n, b, d, s = 173, 32, 8, 0.35
+    q, k, v = (_rand((1, 3, n, d), 70 + i) for i in range(3))
+    m = -(-n // b)
+    g = np.random.default_rng(77)
+    mask = g.random((1, 3, m, m)) < 0.4
+    mask[..., np.arange(m), (np.arange(m) * 3) % m] = True  # at least one block per row
+    got = O.masked_attention(q, k, v, b, s, mask)
+    ref = _sdpa64(q, k, v, s, _token_mask(mask, n, b))
+    assert np.allclose(got, ref, rtol=0, atol=1e-12), np.abs(got - ref).max()
+
+
+def check_masked_vs_brute():
+    """Vectorised masked attention equals the scalar loops on a tiny ragged input."""
+    n, b, d, s = 21, 4, 3, 0.8
+    q, k, v = (_rand((1, 1, n, d), 80 + i) for i in range(3))
+    m = -(-n // b)
+    rows = [{0}, {0, 1}, {2, 5}, {1, 3}, {4}, {0, 5}]
+    mask = np.zeros((1, 1, m, m), bool)
+    for i, js in enumerate(rows):
+        mask[0, 0, i, list(js)] = True
+    got = O.masked_attention(q, k, v, b, s, mask)[0, 0]
+    want = np.array(brute.masked_attention(q[0, 0].tolist(), k[0, 0].tolist(),
+                                           v[0, 0].tolist(), n, b, s, rows))
+    assert np.allclose(got, want, rtol=0, atol=1e-12), np.abs(got - want).max()
+
+
+def check_attention_hull_and_single_token():
+    """Each output lies in the box of its kept value rows; a row whose only kept block holds
+    one valid token returns that value row exactly; kept-list order does not matter."""
+    n, b, d, s = 129, 64, 6, 0.5  # last block holds one token (index 128)
+    q, k, v = (_rand((1, 1, n, d), 90 + i) for i in range(3))
+    mask = np.zeros((1, 1, 3, 3), bool)
+    mask[0, 0, 0, [0, 1]] = True
+    mask[0, 0, 1, 2] = True
+    mask[0, 0, 2, [1, 2]] = True
+    o = O.masked_attention(q, k, v, b, s, mask)[0, 0]
+    assert np.array_equal(o[64:128], np.repeat(v[0, 0, 128:129], 64, axis=0))
+    lo, hi = v[0, 0, :128].min(0), v[0, 0, :128].max(0)
+    assert np.all(o[:64] >= lo - 1e-12) and np.all(o[:64] <= hi + 1e-12)
+    count, idx = O.kept_lists(mask)
+    rev = idx.copy()
+    rev[0, 0, 0, :2] = rev[0, 0, 0, :2][::-1]
+    assert np.array_equal(O.mask_from_lists(count, rev, 3), mask)
+
+
+# ----------------------------------------------------------------------------- epilogue
+def check_epilogue_identities():
+    """c = 0 gives the sparse output; c = 1 with R captured on the same inputs gives the dense
+    output (refresh-step identity); the output is linear in c and c acts per head."""
+    n, b, d, s = 200, 32, 8, 0.3
+    q, k, v = (_rand((1, 2, n, d), 100 + i) for i in range(3))
+    m = -(-n // b)
+    probs = O.block_scores(q, k, b, s)
+    mask = O.topp_select(probs, 0.6)["mask"]
+    assert mask.sum() < mask.size
+    o_s = O.masked_attention(q, k, v, b, s, mask)
+    o_d, r = O.dense_with_capture(q, k, v, b, s, mask)
+    assert np.array_equal(O.residual_epilogue(o_s, r, [0.0, 0.0]), o_s)
+    assert np.allclose(O.residual_epilogue(o_s, r, [1.0, 1.0]), o_d, rtol=0, atol=1e-12)
+    mixed = O.residual_epilogue(o_s, r, [0.0, 1.0])
+    assert np.array_equal(mixed[:, 0], o_s[:, 0])
+    assert np.allclose(mixed[:, 1], o_d[:, 1], rtol=0, atol=1e-12)
+    half = O.residual_epilogue(o_s, r, [0.5, 0.5])
+    assert np.allclose(half, 0.5 * (o_s + o_d), rtol=0, atol=1e-12)
+    ref = _sdpa64(q, k, v, s)
+    assert np.allclose(o_d, ref, rtol=0, atol=1e-12)
+    _, r_all = O.dense_with_capture(q, k, v, b, s, np.ones((1, 2, m, m), bool))
+    assert np.all(r_all == 0.0)
+
+
+ALL_CHECKS = [
+    check_pool_block_constant,
+    check_pool_closed_form_ragged,
+    check_pool_mass_invariant,
+    check_scores_closed_form,
+    check_scores_rows_and_degenerate,
+    check_scores_scale_and_shift,
+    check_scores_vs_brute,
+    check_topp_inclusive_dyadic,
+    check_topp_ties_lower_index,
+    check_topp_invariants,
+    check_topp_vs_subset_search,
+    check_topp_per_head_threshold,
+    check_dense_vs_sdpa,
+    check_masked_vs_sdpa,
+    check_masked_vs_brute,
+    check_attention_hull_and_single_token,
+    check_epilogue_identities,
+]
+
+
+def failing_checks():
+    """Names of the checks that fail against the oracle as it currently stands."""
+    bad = []
+    for chk in ALL_CHECKS:
+        try:
+            chk()
+        except (AssertionError, ValueError, IndexError) as exc:  # noqa: PERF203
+            bad.append((chk.__name__, repr(exc)[:120]))
+    return bad
+
+
+__all__ = ["ALL_CHECKS", "failing_checks"] + [c.__name__ for c in ALL_CHECKS]

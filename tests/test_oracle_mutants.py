@@ -1,0 +1,147 @@
+"""Plant plausible mistakes in the CPU oracle and require that the pins catch every one.
+
+Each mutant replaces one function of `oracle.oracle` (on the CPU, for the duration of one
+test) with a version carrying a single typical slip: a dropped term, a wrong sign or index, a
+transposed operand, a wrong axis, an off-by-one or a different tie rule. The pins in
+`pins.py` must fail for each, which shows they constrain the oracle beyond its own spelling.
+"""
+import numpy as np
+import pytest
+
+import pins
+from oracle import oracle as O
+
+_REAL = {name: getattr(O, name) for name in dir(O) if not name.startswith("__")}
+
+
+def _pool_divides_by_block(x, block):
+    x = np.asarray(x, dtype=np.float64)
+    s, e = O.block_partition(x.shape[2], block)
+    out = np.empty(x.shape[:2] + (len(s), x.shape[3]))
+    for j, (a, b) in enumerate(zip(s, e)):
+        out[:, :, j] = x[:, :, a:b].sum(axis=2) / float(block)
+    return out
+
+
+def _pool_first_token(x, block):
+    x = np.asarray(x, dtype=np.float64)
+    s, _ = O.block_partition(x.shape[2], block)
+    return x[:, :, s, :]
+
+
+def _scores_with(transform):
+    def f(q, k, block, sm_scale):
+        qb = O.block_mean_pool(q, block)
+        kb = O.block_mean_pool(k, block)
+        return transform(qb, kb, block, sm_scale, q.shape[2])
+    return f
+
+
+def _transposed(qb, kb, block, s, n):
+    return O.softmax_rows(s * np.matmul(kb, np.swapaxes(qb, -1, -2)))
+
+
+def _no_scale(qb, kb, block, s, n):
+    return O.softmax_rows(np.matmul(qb, np.swapaxes(kb, -1, -2)))
+
+
+def _column_softmax(qb, kb, block, s, n):
+    lg = s * np.matmul(qb, np.swapaxes(kb, -1, -2))
+    return np.swapaxes(O.softmax_rows(np.swapaxes(lg, -1, -2)), -1, -2)
+
+
+def _log_block_size(qb, kb, block, s, n):
+    st, en = O.block_partition(n, block)
+    lg = s * np.matmul(qb, np.swapaxes(kb, -1, -2)) + np.log((en - st).astype(float))
+    return O.softmax_rows(lg)
+
+
+def _topp_variant(strict=False, ties_high=False, ascending=False, off_by_one=False,
+                  head0=False):
+    def f(probs, top_p):
+        probs = np.asarray(probs, dtype=np.float64)
+        B, H, _, M = probs.shape
+        p = np.broadcast_to(np.asarray(top_p, dtype=np.float64), (H,)).copy()
+        if head0:
+            p[:] = p[0]
+        idx = np.broadcast_to(np.arange(M), probs.shape)
+        tie = -idx if ties_high else idx
+        order = np.lexsort((tie, probs if ascending else -probs), axis=-1)
+        csum = np.cumsum(np.take_along_axis(probs, order, axis=-1), axis=-1)
+        reached = csum > p[None, :, None, None] if strict else csum >= p[None, :, None, None]
+        first = np.where(reached.any(-1), reached.argmax(-1) + (0 if off_by_one else 1), M)
+        first = np.maximum(first, 1)
+        count = np.where(p[None, :, None] >= 1.0, M, first)
+        rank = np.empty_like(order)
+        np.put_along_axis(rank, order, np.broadcast_to(np.arange(M), order.shape), axis=-1)
+        mask = rank < count[..., None]
+        mass = np.take_along_axis(csum, (count - 1)[..., None], axis=-1)[..., 0]
+        return {"mask": mask, "count": count, "mass": mass, "order": order}
+    return f
+
+
+def _attend_no_scale(qt, kt, vt, s):
+    return _REAL["_attend"](qt, kt, vt, 1.0)
+
+
+def _attend_keys_as_values(qt, kt, vt, s):
+    return _REAL["_attend"](qt, kt, kt[:, : vt.shape[1]] if kt.shape[1] >= vt.shape[1] else vt, s)
+
+
+def _attend_wrong_axis(qt, kt, vt, s):
+    lg = s * (qt @ kt.T)
+    lg -= lg.max(axis=0, keepdims=True)
+    w = np.exp(lg)
+    w /= w.sum(axis=0, keepdims=True)
+    return w @ vt
+
+
+def _masked_ignores_mask(q, k, v, block, sm_scale, mask, rows=None):
+    return _REAL["masked_attention"](q, k, v, block, sm_scale, np.ones_like(mask), rows=rows)
+
+
+def _epilogue_minus(o, r, c):
+    return _REAL["residual_epilogue"](o, -np.asarray(r), c)
+
+
+def _epilogue_heads_reversed(o, r, c):
+    return _REAL["residual_epilogue"](o, r, np.asarray(c, dtype=float)[::-1])
+
+
+def _capture_sign(q, k, v, block, sm_scale, mask, rows=None):
+    o_d, r = _REAL["dense_with_capture"](q, k, v, block, sm_scale, mask, rows=rows)
+    return o_d, -r
+
+
+MUTANTS = {
+    "pool divides by the full block size": ("block_mean_pool", _pool_divides_by_block),
+    "pool takes the first token": ("block_mean_pool", _pool_first_token),
+    "scores transposed (keys x queries)": ("block_scores", _scores_with(_transposed)),
+    "scores drop the scale": ("block_scores", _scores_with(_no_scale)),
+    "softmax over query blocks": ("block_scores", _scores_with(_column_softmax)),
+    "log block size added to logits": ("block_scores", _scores_with(_log_block_size)),
+    "strict threshold": ("topp_select", _topp_variant(strict=True)),
+    "ties prefer higher index": ("topp_select", _topp_variant(ties_high=True)),
+    "keeps the smallest blocks": ("topp_select", _topp_variant(ascending=True)),
+    "count off by one": ("topp_select", _topp_variant(off_by_one=True)),
+    "head 0 threshold for all heads": ("topp_select", _topp_variant(head0=True)),
+    "attention drops the scale": ("_attend", _attend_no_scale),
+    "attention uses keys as values": ("_attend", _attend_keys_as_values),
+    "attention softmax over queries": ("_attend", _attend_wrong_axis),
+    "attention ignores the mask": ("masked_attention", _masked_ignores_mask),
+    "epilogue subtracts the residual": ("residual_epilogue", _epilogue_minus),
+    "epilogue scales reversed across heads": ("residual_epilogue", _epilogue_heads_reversed),
+    "captured residual has the wrong sign": ("dense_with_capture", _capture_sign),
+}
+
+
+@pytest.mark.parametrize("name", list(MUTANTS))
+def test_pins_catch_mutant(name, monkeypatch):
+    attr, repl = MUTANTS[name]
+    monkeypatch.setattr(O, attr, repl)
+    failed = pins.failing_checks()
+    assert failed, f"no pin caught the planted mistake: {name}"
+
+
+def test_real_oracle_passes_every_pin():
+    assert pins.failing_checks() == []
