@@ -1,0 +1,69 @@
+// Internal declarations shared by the HIP kernels and the C-ABI host layer (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace recap {
+
+typedef __bf16 bf16_t;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+constexpr int kMaxHeads = 128;
+constexpr int kKeyTile = 64;  // keys per attention inner-loop tile
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct HeadScalars {
+  float v[kMaxHeads];
+};
+
+// Strided bf16 tensor [B,H,N,D] view (element strides, D contiguous).
+struct Strides {
+  int64_t b, h, n;
+};
+
+// Work-group index remap so that each XCD (8 per MI355X, work-groups dispatched round-robin
+// across them) receives one contiguous range of logical tiles: neighbouring query blocks of
+// one head then share key/value lines in that XCD's L2. A bijection on [0, n) whatever the
+// dispatch order, so correctness does not depend on it.
+__device__ __forceinline__ int xcd_remap(int wg, int n) {
+  const int q = n >> 3, r = n & 7;
+  const int xcd = wg & 7, k = wg >> 3;
+  return (xcd < r) ? xcd * (q + 1) + k : r * (q + 1) + (xcd - r) * q + k;
+}
+
+// ---- launchers (defined in the kernel sources; all asynchronous on `stream`) ----
+hipError_t launch_pool(const bf16_t* q, const bf16_t* k, Strides st, int B, int H, int N, int D,
+                       int block, float* qbar, float* kbar, hipStream_t stream);
+hipError_t launch_scores(const float* qbar, const float* kbar, int BH, int M, int D,
+                         float scale_log2, float* probs, hipStream_t stream);
+hipError_t launch_topp(const float* probs, int B, int H, int M, const HeadScalars& top_p,
+                       int32_t* count, int32_t* idx, uint8_t* mask, float* mass,
+                       hipStream_t stream);
+hipError_t launch_pack_vt(const bf16_t* v, Strides st, int B, int H, int N, int D, int npad,
+                          bf16_t* vt, hipStream_t stream);
+
+enum AttnMode { kSparse = 0, kDense = 1, kCapture = 2 };
+
+struct AttnParams {
+  const bf16_t* q;
+  const bf16_t* k;
+  const bf16_t* vt;  // packed V^T [B*H][D][npad]
+  Strides st;
+  int H, N, M, block, npad;
+  float scale_log2;
+  const int32_t* count;  // [B*H*M]
+  const int32_t* idx;    // [B*H*M*M]
+  const bf16_t* res;     // optional residual (sparse mode)
+  bf16_t* out;
+  bf16_t* res_out;  // capture mode
+  float* os_ws;     // capture mode: fp32 sparse snapshot [B*H][npad][D]
+  HeadScalars res_scale;
+};
+
+hipError_t launch_attention(const AttnParams& p, int B, int D, AttnMode mode, hipStream_t stream);
+
+}  // namespace recap

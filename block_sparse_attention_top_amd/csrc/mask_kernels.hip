@@ -1,0 +1,359 @@
+// Mask prediction on gfx950: block mean pooling, block-pair softmax scores, top-p selection.
+//
+// RECAP (paperpeel.com/paper/2610.26244) Sec. 3.2 uses block means as coarse estimates of
+// the attention each block receives; the first abstract on the RECAP page at
+// thelatestinai.com describes online top-p mask prediction with per-head thresholds, and
+// CalibAtt (thelatestinai.com/papers/2603.05503) Fig. 5 thresholds the top key blocks of
+// every query block. Pooling and top-p are bound by HBM bandwidth and latency; the scores are
+// a small fp32 contraction done on the fp32 matrix cores.
+#include "common.h"
+
+namespace recap {
+
+// ------------------------------------------------------------------------------------------
+// Pooling: one wavefront per (tensor, b, h, block). Lanes stride over the block's rows with
+// 16-byte loads (CH lanes cover one row, G rows in flight per load), accumulate in fp32,
+// reduce across the row groups with lane shuffles and write the fp32 mean row.
+// ------------------------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void pool_kernel(const bf16_t* __restrict__ q,
+                                                   const bf16_t* __restrict__ k, Strides st,
+                                                   int H, int N, int block, int M, int rows,
+                                                   float* __restrict__ qbar,
+                                                   float* __restrict__ kbar) {
+  constexpr int CH = D / 8;   // 16-byte chunks per row
+  constexpr int G = 64 / CH;  // rows loaded per wavefront instruction
+  const int lane = threadIdx.x & 63;
+  const int task = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (task >= 2 * rows) return;
+  const int which = task >= rows;
+  const int row = task - which * rows;
+  const int j = row % M;
+  const int bh = row / M;
+  const int b = bh / H, h = bh - b * H;
+  const bf16_t* src = (which ? k : q) + b * st.b + h * st.h;
+  const int t0 = j * block;
+  const int t1 = min(N, t0 + block);
+  const int c = lane % CH, g = lane / CH;
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+#pragma unroll 4
+  for (int t = t0 + g; t < t1; t += G) {
+    const bf16x8 x = *reinterpret_cast<const bf16x8*>(src + (int64_t)t * st.n + c * 8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] += (float)x[e];
+  }
+#pragma unroll
+  for (int off = CH; off < 64; off <<= 1) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], off);
+  }
+  if (g == 0) {
+    const float n = (float)(t1 - t0);
+    float* dst = (which ? kbar : qbar) + (int64_t)row * D + c * 8;
+    f32x4 lo, hi;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      lo[e] = acc[e] / n;
+      hi[e] = acc[e + 4] / n;
+    }
+    *reinterpret_cast<f32x4*>(dst) = lo;
+    *reinterpret_cast<f32x4*>(dst + 4) = hi;
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// Scores: work-group = (b*h, tile of 32 query blocks); its 4 wavefronts split the key-block
+// tiles. Each 32x32 tile is computed transposed, S^T = K̄ Q̄^T, with the fp32 MFMA 32x32x2:
+// lane (n, half) then owns query block n and 16 key blocks of the tile, so the row softmax
+// runs in-lane. Pass 1 gathers the per-row max and sum (online, combined across halves and
+// wavefronts); pass 2 recomputes the identical tiles and writes exp2(x - m) / l.
+// The contraction over D is split as D index = half * D/2 + s, s = 0..D/2-1, identically
+// for both operands.
+// ------------------------------------------------------------------------------------------
+template <int D>
+__device__ __forceinline__ f32x16 score_tile(const float* __restrict__ kb, int key0, int M,
+                                             const float (&qv)[D / 2], int m_lane, int half) {
+  const int key = min(key0 + m_lane, M - 1);
+  const float* src = kb + (int64_t)key * D + half * (D / 2);
+  float kv[D / 2];
+#pragma unroll
+  for (int s = 0; s < D / 2; s += 4) {
+    const f32x4 x = *reinterpret_cast<const f32x4*>(src + s);
+    kv[s] = x[0];
+    kv[s + 1] = x[1];
+    kv[s + 2] = x[2];
+    kv[s + 3] = x[3];
+  }
+  f32x16 a0 = {}, a1 = {};
+#pragma unroll
+  for (int s = 0; s < D / 2; s += 2) {
+    a0 = __builtin_amdgcn_mfma_f32_32x32x2f32(kv[s], qv[s], a0, 0, 0, 0);
+    a1 = __builtin_amdgcn_mfma_f32_32x32x2f32(kv[s + 1], qv[s + 1], a1, 0, 0, 0);
+  }
+  return a0 + a1;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void score_kernel(const float* __restrict__ qbar,
+                                                    const float* __restrict__ kbar, int M,
+                                                    float scale_log2, float* __restrict__ probs) {
+  __shared__ float red_m[4][32];
+  __shared__ float red_l[4][32];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 31, half = lane >> 5;
+  const int nqt = (M + 31) >> 5;
+  const int bh = blockIdx.x / nqt, qt = blockIdx.x - bh * nqt;
+  const float* qb = qbar + (int64_t)bh * M * D;
+  const float* kb = kbar + (int64_t)bh * M * D;
+  const int qrow = qt * 32 + n;
+  float qv[D / 2];
+  {
+    const float* src = qb + (int64_t)min(qrow, M - 1) * D + half * (D / 2);
+#pragma unroll
+    for (int s = 0; s < D / 2; s += 4) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(src + s);
+      qv[s] = x[0];
+      qv[s + 1] = x[1];
+      qv[s + 2] = x[2];
+      qv[s + 3] = x[3];
+    }
+  }
+  const int nkt = (M + 31) >> 5;
+  float m = -INFINITY, l = 0.f;
+  for (int kt = wave; kt < nkt; kt += 4) {
+    const f32x16 acc = score_tile<D>(kb, kt * 32, M, qv, n, half);
+    float x[16];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = kt * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
+      x[r] = key < M ? acc[r] * scale_log2 : -INFINITY;
+      mx = fmaxf(mx, x[r]);
+    }
+    const float mn = fmaxf(m, mx);
+    float add = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) add += __builtin_amdgcn_exp2f(x[r] - mn);
+    l = l * __builtin_amdgcn_exp2f(m - mn) + add;
+    m = mn;
+  }
+  // combine the two halves of the wavefront, then the four wavefronts
+  {
+    const float mo = __shfl_xor(m, 32), lo = __shfl_xor(l, 32);
+    const float mn = fmaxf(m, mo);
+    l = (m == -INFINITY ? 0.f : l * __builtin_amdgcn_exp2f(m - mn)) +
+        (mo == -INFINITY ? 0.f : lo * __builtin_amdgcn_exp2f(mo - mn));
+    m = mn;
+  }
+  if (half == 0) {
+    red_m[wave][n] = m;
+    red_l[wave][n] = l;
+  }
+  __syncthreads();
+  float mrow = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) mrow = fmaxf(mrow, red_m[w][n]);
+  float lrow = 0.f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const float mw = red_m[w][n];
+    if (mw != -INFINITY) lrow += red_l[w][n] * __builtin_amdgcn_exp2f(mw - mrow);
+  }
+  const float inv = 1.0f / lrow;
+  if (qrow >= M) return;
+  float* prow = probs + ((int64_t)bh * M + qrow) * M;
+  for (int kt = wave; kt < nkt; kt += 4) {
+    const f32x16 acc = score_tile<D>(kb, kt * 32, M, qv, n, half);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = kt * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
+      if (key < M) prow[key] = __builtin_amdgcn_exp2f(acc[r] * scale_log2 - mrow) * inv;
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// Top-p: one work-group of 256 threads per query-block row. Keys (orderable probability bits
+// << 32 | ~index) are bitonic-sorted descending in LDS, which orders probabilities descending
+// and equal values by lower index first. Running mass: fp64 block scan over the sorted
+// values; k* = first prefix reaching p (inclusive), M when p >= 1 or none reaches it. Kept
+// blocks are flagged by index, then compacted in ascending index order with a second scan.
+// ------------------------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t orderable(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float from_orderable(uint32_t u) {
+  return __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
+}
+
+// Inclusive block scan of one value per thread (256 threads); returns the exclusive prefix.
+template <typename T>
+__device__ __forceinline__ T block_exclusive_scan(T v, T* wave_tot, T& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  T x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const T y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) wave_tot[wave] = x;
+  __syncthreads();
+  T base = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const T t = wave_tot[w];
+    if (w < wave) base += t;
+    all += t;
+  }
+  total = all;
+  __syncthreads();
+  return base + x - v;
+}
+
+__global__ __launch_bounds__(256) void topp_kernel(const float* __restrict__ probs, int H, int M,
+                                                   int P, HeadScalars top_p,
+                                                   int32_t* __restrict__ count,
+                                                   int32_t* __restrict__ idx,
+                                                   uint8_t* __restrict__ mask,
+                                                   float* __restrict__ mass) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  uint64_t* keys = reinterpret_cast<uint64_t*>(smem);  // P entries
+  uint8_t* flag = smem + (size_t)P * 8;                 // P entries
+  __shared__ double wtot_d[4];
+  __shared__ int wtot_i[4];
+  __shared__ int kstar_s;
+  __shared__ double mass_s;
+
+  const int tid = threadIdx.x;
+  const int64_t row = blockIdx.x;
+  const int h = (int)((row / M) % H);
+  const float p = top_p.v[h];
+  const float* pr = probs + row * M;
+
+  for (int t = tid; t < P; t += 256) {
+    keys[t] = t < M ? ((uint64_t)orderable(pr[t]) << 32) | (uint64_t)(0xffffffffu - (uint32_t)t)
+                    : 0ull;
+    flag[t] = 0;
+  }
+  if (tid == 0) kstar_s = M;
+  __syncthreads();
+
+  for (int kk = 2; kk <= P; kk <<= 1) {
+    for (int j = kk >> 1; j > 0; j >>= 1) {
+      for (int i = tid; i < (P >> 1); i += 256) {
+        const int a = ((i & ~(j - 1)) << 1) | (i & (j - 1));
+        const int bb = a + j;
+        const uint64_t x = keys[a], y = keys[bb];
+        const bool desc = (a & kk) == 0;
+        if ((x < y) == desc) {
+          keys[a] = y;
+          keys[bb] = x;
+        }
+      }
+      __syncthreads();
+    }
+  }
+
+  // fp64 running mass over the sorted values: each thread owns E consecutive positions.
+  const int E = (P + 255) / 256;
+  const int lo = tid * E;
+  double local = 0.0;
+  for (int e = 0; e < E; ++e) {
+    const int pos = lo + e;
+    if (pos < M) local += (double)from_orderable((uint32_t)(keys[pos] >> 32));
+  }
+  double total;
+  const double base = block_exclusive_scan<double>(local, wtot_d, total);
+  if (p < 1.0f) {
+    double c = base;
+    for (int e = 0; e < E; ++e) {
+      const int pos = lo + e;
+      if (pos >= M) break;
+      c += (double)from_orderable((uint32_t)(keys[pos] >> 32));
+      if (c >= (double)p) {
+        atomicMin(&kstar_s, pos + 1);
+        break;
+      }
+    }
+  }
+  __syncthreads();
+  const int kstar = kstar_s;  // M when p >= 1 or when no prefix reaches p
+  if (kstar == M) {
+    if (tid == 0) mass_s = total;
+  } else if (kstar - 1 >= lo && kstar - 1 < lo + E) {
+    // the owner of position k*-1 recomputes the prefix it crossed p with
+    double c = base;
+    for (int pos = lo; pos < kstar; ++pos) c += (double)from_orderable((uint32_t)(keys[pos] >> 32));
+    mass_s = c;
+  }
+  for (int pos = tid; pos < kstar; pos += 256) {
+    const uint32_t j = 0xffffffffu - (uint32_t)(keys[pos] & 0xffffffffull);
+    flag[j] = 1;
+  }
+  __syncthreads();
+
+  // ascending compaction of the flagged indices
+  int cnt = 0;
+  for (int e = 0; e < E; ++e) {
+    const int jj = lo + e;
+    if (jj < M) cnt += flag[jj];
+  }
+  int tot_i;
+  int off = block_exclusive_scan<int>(cnt, wtot_i, tot_i);
+  int32_t* out_idx = idx + row * M;
+  for (int e = 0; e < E; ++e) {
+    const int jj = lo + e;
+    if (jj < M && flag[jj]) out_idx[off++] = jj;
+  }
+  if (mask != nullptr) {
+    uint8_t* mrow = mask + row * M;
+    for (int jj = tid; jj < M; jj += 256) mrow[jj] = flag[jj];
+  }
+  if (tid == 0) {
+    count[row] = kstar;
+    if (mass != nullptr) mass[row] = (float)mass_s;
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+hipError_t launch_pool(const bf16_t* q, const bf16_t* k, Strides st, int B, int H, int N, int D,
+                       int block, float* qbar, float* kbar, hipStream_t stream) {
+  const int M = (N + block - 1) / block;
+  const int rows = B * H * M;
+  const int grid = (2 * rows + 3) / 4;
+  if (D == 128)
+    pool_kernel<128><<<grid, 256, 0, stream>>>(q, k, st, H, N, block, M, rows, qbar, kbar);
+  else
+    pool_kernel<64><<<grid, 256, 0, stream>>>(q, k, st, H, N, block, M, rows, qbar, kbar);
+  return hipGetLastError();
+}
+
+hipError_t launch_scores(const float* qbar, const float* kbar, int BH, int M, int D,
+                         float scale_log2, float* probs, hipStream_t stream) {
+  const int grid = BH * ((M + 31) / 32);
+  if (D == 128)
+    score_kernel<128><<<grid, 256, 0, stream>>>(qbar, kbar, M, scale_log2, probs);
+  else
+    score_kernel<64><<<grid, 256, 0, stream>>>(qbar, kbar, M, scale_log2, probs);
+  return hipGetLastError();
+}
+
+hipError_t launch_topp(const float* probs, int B, int H, int M, const HeadScalars& top_p,
+                       int32_t* count, int32_t* idx, uint8_t* mask, float* mass,
+                       hipStream_t stream) {
+  int P = 64;
+  while (P < M) P <<= 1;
+  const size_t lds = (size_t)P * 9;
+  if (lds > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute((const void*)topp_kernel,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  topp_kernel<<<B * H * M, 256, lds, stream>>>(probs, H, M, P, top_p, count, idx, mask, mass);
+  return hipGetLastError();
+}
+
+}  // namespace recap

@@ -1,0 +1,299 @@
+// C-ABI entry points: argument validation (before any HIP call), workspace carving and
+// kernel launches. The operations themselves are documented in include/recap.h.
+#include <math.h>
+#include <string.h>
+
+#include <atomic>
+#include <mutex>
+
+#include "../../include/recap.h"
+#include "common.h"
+
+using namespace recap;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+int validate_desc(const recap_desc* d) {
+  if (d == nullptr) return RECAP_E_NULL;
+  if (d->batch < 1 || d->heads < 1 || d->heads > RECAP_MAX_HEADS || d->seq < 1) return RECAP_E_SHAPE;
+  if (d->head_dim != 64 && d->head_dim != 128) return RECAP_E_SHAPE;
+  if (d->block != 64 && d->block != 128) return RECAP_E_SHAPE;
+  if (d->reserved != 0) return RECAP_E_SHAPE;
+  const int64_t m = ((int64_t)d->seq + d->block - 1) / d->block;
+  if (m > RECAP_MAX_BLOCKS) return RECAP_E_SHAPE;
+  // products used in 32-bit grid arithmetic
+  if ((int64_t)d->batch * d->heads * m > (int64_t)1 << 30) return RECAP_E_SHAPE;
+  const int64_t s[3] = {d->stride_b, d->stride_h, d->stride_n};
+  for (int i = 0; i < 3; ++i)
+    if (s[i] <= 0 || (s[i] % 8) != 0) return RECAP_E_STRIDE;
+  // no two (b, h, n) index triples may address the same row: sort the three dimensions by
+  // stride and require each stride to clear the full extent of the next-smaller one
+  int64_t ext[3] = {d->batch, d->heads, d->seq};
+  int64_t st[3] = {d->stride_b, d->stride_h, d->stride_n};
+  for (int i = 0; i < 3; ++i)
+    for (int j = i + 1; j < 3; ++j)
+      if (st[j] < st[i]) {
+        int64_t t = st[i]; st[i] = st[j]; st[j] = t;
+        t = ext[i]; ext[i] = ext[j]; ext[j] = t;
+      }
+  int64_t span = d->head_dim;  // elements covered by the dimensions below
+  for (int i = 0; i < 3; ++i) {
+    if (ext[i] > 1 && st[i] < span) return RECAP_E_STRIDE;
+    span = st[i] * (ext[i] - 1) + span;
+  }
+  return RECAP_OK;
+}
+
+inline int num_blocks(const recap_desc* d) { return (d->seq + d->block - 1) / d->block; }
+
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+size_t pooled_bytes(const recap_desc* d) {
+  return align_up((size_t)d->batch * d->heads * num_blocks(d) * d->head_dim * sizeof(float));
+}
+size_t vt_bytes(const recap_desc* d) {
+  const size_t npad = (size_t)num_blocks(d) * d->block;
+  return align_up((size_t)d->batch * d->heads * d->head_dim * npad * 2);
+}
+size_t snapshot_bytes(const recap_desc* d) {
+  const size_t npad = (size_t)num_blocks(d) * d->block;
+  return align_up((size_t)d->batch * d->heads * npad * d->head_dim * sizeof(float));
+}
+
+size_t workspace_for(int op, const recap_desc* d) {
+  switch (op) {
+    case RECAP_OP_BLOCK_SCORES: return 2 * pooled_bytes(d);
+    case RECAP_OP_TOPP: return 0;
+    case RECAP_OP_SPARSE:
+    case RECAP_OP_DENSE: return vt_bytes(d);
+    case RECAP_OP_DENSE_CAPTURE: return vt_bytes(d) + snapshot_bytes(d);
+    default: return 0;
+  }
+}
+
+int check_workspace(int op, const recap_desc* d, const void* ws, size_t ws_bytes) {
+  const size_t need = workspace_for(op, d);
+  if (need == 0) return RECAP_OK;
+  if (ws == nullptr || ws_bytes < need) return RECAP_E_WORKSPACE;
+  if (((uintptr_t)ws & (kAlign - 1)) != 0) return RECAP_E_ALIGN;
+  return RECAP_OK;
+}
+
+// Per-device "is gfx950" cache, filled once per device.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_dev_ok[kMaxDevices];  // 0 unknown, 1 ok, -1 unsupported
+std::mutex g_dev_mu;
+
+int check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return RECAP_E_DEVICE;
+  }
+  int state = g_dev_ok[dev].load(std::memory_order_acquire);
+  if (state == 0) {
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    state = g_dev_ok[dev].load(std::memory_order_relaxed);
+    if (state == 0) {
+      hipDeviceProp_t prop;
+      if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return RECAP_E_DEVICE;
+      }
+      state = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+      g_dev_ok[dev].store(state, std::memory_order_release);
+    }
+  }
+  return state == 1 ? RECAP_OK : RECAP_E_DEVICE;
+}
+
+inline Strides strides_of(const recap_desc* d) { return Strides{d->stride_b, d->stride_h, d->stride_n}; }
+
+int launched(hipError_t e) {
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return RECAP_E_LAUNCH;
+  }
+  return RECAP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int recap_abi_version(void) { return RECAP_ABI_VERSION; }
+
+const char* recap_status_string(int status) {
+  switch (status) {
+    case RECAP_OK: return "ok";
+    case RECAP_E_NULL: return "a required pointer is NULL";
+    case RECAP_E_SHAPE: return "unsupported shape (batch, heads, seq, head_dim or block)";
+    case RECAP_E_STRIDE: return "invalid strides (positive multiples of 8, non-overlapping)";
+    case RECAP_E_ALIGN: return "a base pointer is not 16-byte aligned (workspace: 256-byte)";
+    case RECAP_E_VALUE: return "a scalar or per-head value is out of range";
+    case RECAP_E_WORKSPACE: return "workspace missing or too small";
+    case RECAP_E_DEVICE: return "no current gfx950 HIP device";
+    case RECAP_E_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int recap_workspace_size(int op, const recap_desc* d, size_t* bytes) {
+  if (bytes == nullptr) return RECAP_E_NULL;
+  const int s = validate_desc(d);
+  if (s != RECAP_OK) return s;
+  if (op < RECAP_OP_BLOCK_SCORES || op > RECAP_OP_DENSE_CAPTURE) return RECAP_E_VALUE;
+  *bytes = workspace_for(op, d);
+  return RECAP_OK;
+}
+
+int recap_block_scores(const recap_desc* d, const void* q, const void* k, float sm_scale,
+                       float* probs, void* ws, size_t ws_bytes, void* stream) {
+  int s = validate_desc(d);
+  if (s != RECAP_OK) return s;
+  if (q == nullptr || k == nullptr || probs == nullptr) return RECAP_E_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(probs)) return RECAP_E_ALIGN;
+  if (!isfinite(sm_scale) || !(sm_scale > 0.f)) return RECAP_E_VALUE;
+  if ((s = check_workspace(RECAP_OP_BLOCK_SCORES, d, ws, ws_bytes)) != RECAP_OK) return s;
+  if ((s = check_device()) != RECAP_OK) return s;
+
+  hipStream_t st = (hipStream_t)stream;
+  const int M = num_blocks(d);
+  float* qbar = (float*)ws;
+  float* kbar = (float*)((char*)ws + pooled_bytes(d));
+  hipError_t e = launch_pool((const bf16_t*)q, (const bf16_t*)k, strides_of(d), d->batch,
+                             d->heads, d->seq, d->head_dim, d->block, qbar, kbar, st);
+  if (e == hipSuccess)
+    e = launch_scores(qbar, kbar, d->batch * d->heads, M, d->head_dim,
+                      (float)((double)sm_scale * 1.4426950408889634), probs, st);
+  return launched(e);
+}
+
+int recap_topp_mask(const recap_desc* d, const float* probs, const float* top_p_host,
+                    int32_t* kept_count, int32_t* kept_idx, uint8_t* mask_opt,
+                    float* kept_mass_opt, void* stream) {
+  int s = validate_desc(d);
+  if (s != RECAP_OK) return s;
+  if (probs == nullptr || top_p_host == nullptr || kept_count == nullptr || kept_idx == nullptr)
+    return RECAP_E_NULL;
+  if (!aligned16(probs) || !aligned16(kept_count) || !aligned16(kept_idx) ||
+      (mask_opt && !aligned16(mask_opt)) || (kept_mass_opt && !aligned16(kept_mass_opt)))
+    return RECAP_E_ALIGN;
+  HeadScalars tp;
+  memset(&tp, 0, sizeof(tp));
+  for (int h = 0; h < d->heads; ++h) {
+    const float p = top_p_host[h];
+    if (!(p >= 0.f && p <= 1.f)) return RECAP_E_VALUE;  // also rejects NaN
+    tp.v[h] = p;
+  }
+  if ((s = check_device()) != RECAP_OK) return s;
+  return launched(launch_topp(probs, d->batch, d->heads, num_blocks(d), tp, kept_count, kept_idx,
+                              mask_opt, kept_mass_opt, (hipStream_t)stream));
+}
+
+int recap_block_sparse_attn(const recap_desc* d, const void* q, const void* k, const void* v,
+                            const int32_t* kept_count, const int32_t* kept_idx, float sm_scale,
+                            const void* residual_opt, const float* res_scale_host, void* out,
+                            void* ws, size_t ws_bytes, void* stream) {
+  int s = validate_desc(d);
+  if (s != RECAP_OK) return s;
+  if (q == nullptr || k == nullptr || v == nullptr || kept_count == nullptr ||
+      kept_idx == nullptr || out == nullptr)
+    return RECAP_E_NULL;
+  if (residual_opt != nullptr && res_scale_host == nullptr) return RECAP_E_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
+      !aligned16(kept_count) || !aligned16(kept_idx) ||
+      (residual_opt != nullptr && !aligned16(residual_opt)))
+    return RECAP_E_ALIGN;
+  if (!isfinite(sm_scale) || !(sm_scale > 0.f)) return RECAP_E_VALUE;
+  if (out == q || out == k || out == v || (residual_opt != nullptr && out == residual_opt))
+    return RECAP_E_VALUE;
+  AttnParams p;
+  memset(&p, 0, sizeof(p));
+  if (residual_opt != nullptr) {
+    for (int h = 0; h < d->heads; ++h) {
+      if (!isfinite(res_scale_host[h])) return RECAP_E_VALUE;
+      p.res_scale.v[h] = res_scale_host[h];
+    }
+  }
+  if ((s = check_workspace(RECAP_OP_SPARSE, d, ws, ws_bytes)) != RECAP_OK) return s;
+  if ((s = check_device()) != RECAP_OK) return s;
+
+  hipStream_t st = (hipStream_t)stream;
+  const int M = num_blocks(d);
+  const int npad = M * d->block;
+  bf16_t* vt = (bf16_t*)ws;
+  hipError_t e = launch_pack_vt((const bf16_t*)v, strides_of(d), d->batch, d->heads, d->seq,
+                                d->head_dim, npad, vt, st);
+  if (e != hipSuccess) return launched(e);
+  p.q = (const bf16_t*)q;
+  p.k = (const bf16_t*)k;
+  p.vt = vt;
+  p.st = strides_of(d);
+  p.H = d->heads;
+  p.N = d->seq;
+  p.M = M;
+  p.block = d->block;
+  p.npad = npad;
+  p.scale_log2 = (float)((double)sm_scale * 1.4426950408889634);
+  p.count = kept_count;
+  p.idx = kept_idx;
+  p.res = (const bf16_t*)residual_opt;
+  p.out = (bf16_t*)out;
+  return launched(launch_attention(p, d->batch, d->head_dim, kSparse, st));
+}
+
+int recap_dense_attn(const recap_desc* d, const void* q, const void* k, const void* v,
+                     float sm_scale, const int32_t* kept_count_opt, const int32_t* kept_idx_opt,
+                     void* out, void* residual_out_opt, void* ws, size_t ws_bytes,
+                     void* stream) {
+  int s = validate_desc(d);
+  if (s != RECAP_OK) return s;
+  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr) return RECAP_E_NULL;
+  const bool capture = residual_out_opt != nullptr;
+  if (capture && (kept_count_opt == nullptr || kept_idx_opt == nullptr)) return RECAP_E_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
+      (capture && (!aligned16(residual_out_opt) || !aligned16(kept_count_opt) ||
+                   !aligned16(kept_idx_opt))))
+    return RECAP_E_ALIGN;
+  if (!isfinite(sm_scale) || !(sm_scale > 0.f)) return RECAP_E_VALUE;
+  if (out == q || out == k || out == v || (capture && (residual_out_opt == out ||
+                                                       residual_out_opt == q ||
+                                                       residual_out_opt == k ||
+                                                       residual_out_opt == v)))
+    return RECAP_E_VALUE;
+  const int op = capture ? RECAP_OP_DENSE_CAPTURE : RECAP_OP_DENSE;
+  if ((s = check_workspace(op, d, ws, ws_bytes)) != RECAP_OK) return s;
+  if ((s = check_device()) != RECAP_OK) return s;
+
+  hipStream_t st = (hipStream_t)stream;
+  const int M = num_blocks(d);
+  const int npad = M * d->block;
+  bf16_t* vt = (bf16_t*)ws;
+  hipError_t e = launch_pack_vt((const bf16_t*)v, strides_of(d), d->batch, d->heads, d->seq,
+                                d->head_dim, npad, vt, st);
+  if (e != hipSuccess) return launched(e);
+  AttnParams p;
+  memset(&p, 0, sizeof(p));
+  p.q = (const bf16_t*)q;
+  p.k = (const bf16_t*)k;
+  p.vt = vt;
+  p.st = strides_of(d);
+  p.H = d->heads;
+  p.N = d->seq;
+  p.M = M;
+  p.block = d->block;
+  p.npad = npad;
+  p.scale_log2 = (float)((double)sm_scale * 1.4426950408889634);
+  p.count = kept_count_opt;
+  p.idx = kept_idx_opt;
+  p.out = (bf16_t*)out;
+  p.res_out = (bf16_t*)residual_out_opt;
+  p.os_ws = capture ? (float*)((char*)ws + vt_bytes(d)) : nullptr;
+  return launched(launch_attention(p, d->batch, d->head_dim, capture ? kCapture : kDense, st));
+}
+
+}  // extern "C"

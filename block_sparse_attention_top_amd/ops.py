@@ -1,0 +1,174 @@
+"""torch-tensor marshalling for the librecap.so entry points (same names as the C functions).
+
+Every step of the computation runs in the HIP library; this module checks dtypes, devices and
+strides, allocates outputs and workspace with torch, and passes raw device pointers plus the
+current HIP stream. There is no CPU or PyTorch fallback: a missing library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+from typing import Optional, Sequence
+
+import torch
+
+from . import _lib
+from ._lib import RecapDesc, check
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _host_floats(vals: Sequence[float], heads: int, what: str):
+    vals = [float(x) for x in (vals if hasattr(vals, "__len__") else [vals] * heads)]
+    if len(vals) != heads:
+        raise ValueError(f"{what}: expected {heads} per-head values, got {len(vals)}")
+    return (ctypes.c_float * heads)(*vals)
+
+
+def make_desc(q: torch.Tensor, block: int) -> RecapDesc:
+    """Descriptor for a [B, H, N, D] bf16 view (any element strides with D contiguous)."""
+    if q.dim() != 4:
+        raise ValueError("expected a 4-d [B, H, N, D] tensor view")
+    B, H, N, D = q.shape
+    sb, sh, sn, sd = q.stride()
+    if sd != 1:
+        raise ValueError("head dimension must be contiguous")
+    return RecapDesc(B, H, N, D, int(block), 0, sb, sh, sn)
+
+
+def _same_layout(desc: RecapDesc, *ts: Optional[torch.Tensor]) -> None:
+    for t in ts:
+        if t is None:
+            continue
+        if t.dtype != torch.bfloat16 or not t.is_cuda:
+            raise TypeError("q, k, v, out and residual must be bf16 device tensors")
+        if tuple(t.shape) != (desc.batch, desc.heads, desc.seq, desc.head_dim) or \
+                tuple(t.stride()) != (desc.stride_b, desc.stride_h, desc.stride_n, 1):
+            raise ValueError("q, k, v, out and residual must share shape and strides")
+
+
+def num_blocks(desc: RecapDesc) -> int:
+    return -(-desc.seq // desc.block)
+
+
+def recap_workspace_size(op: int, desc: RecapDesc) -> int:
+    n = ctypes.c_size_t(0)
+    check(_lib.load().recap_workspace_size(op, ctypes.byref(desc), ctypes.byref(n)),
+          "recap_workspace_size")
+    return int(n.value)
+
+
+def _workspace(op: int, desc: RecapDesc, device, given: Optional[torch.Tensor]):
+    need = recap_workspace_size(op, desc)
+    if need == 0:
+        return None, 0
+    if given is not None:
+        if given.numel() * given.element_size() < need:
+            raise ValueError("workspace too small")
+        return given, given.numel() * given.element_size()
+    return torch.empty(need, dtype=torch.uint8, device=device), need
+
+
+def _like_out(t: torch.Tensor) -> torch.Tensor:
+    return torch.empty_strided(t.shape, t.stride(), dtype=t.dtype, device=t.device)
+
+
+def recap_block_scores(desc: RecapDesc, q, k, sm_scale: Optional[float] = None, probs=None,
+                       workspace=None, stream=None) -> torch.Tensor:
+    """fp32 [B,H,M,M] block-pair softmax of mean-pooled Q and K (see include/recap.h)."""
+    _same_layout(desc, q, k)
+    M = num_blocks(desc)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(desc.head_dim)
+    if probs is None:
+        probs = torch.empty((desc.batch, desc.heads, M, M), dtype=torch.float32, device=q.device)
+    ws, nbytes = _workspace(_lib.OP_BLOCK_SCORES, desc, q.device, workspace)
+    check(_lib.load().recap_block_scores(ctypes.byref(desc), _ptr(q), _ptr(k), float(sm_scale),
+                                         _ptr(probs), _ptr(ws), nbytes, _stream(stream)),
+          "recap_block_scores")
+    return probs
+
+
+def recap_topp_mask(desc: RecapDesc, probs, top_p, kept_count=None, kept_idx=None,
+                    want_mask: bool = False, want_mass: bool = False, stream=None):
+    """Top-p selection per query block: (count [B,H,M], idx [B,H,M,M], mask|None, mass|None)."""
+    M = num_blocks(desc)
+    if probs.dtype != torch.float32 or tuple(probs.shape) != (desc.batch, desc.heads, M, M) \
+            or not probs.is_contiguous():
+        raise ValueError("probs must be contiguous fp32 [B, H, M, M]")
+    dev = probs.device
+    if kept_count is None:
+        kept_count = torch.empty((desc.batch, desc.heads, M), dtype=torch.int32, device=dev)
+    if kept_idx is None:
+        kept_idx = torch.empty((desc.batch, desc.heads, M, M), dtype=torch.int32, device=dev)
+    mask = torch.empty((desc.batch, desc.heads, M, M), dtype=torch.uint8, device=dev) \
+        if want_mask else None
+    mass = torch.empty((desc.batch, desc.heads, M), dtype=torch.float32, device=dev) \
+        if want_mass else None
+    tp = _host_floats(top_p, desc.heads, "top_p")
+    check(_lib.load().recap_topp_mask(ctypes.byref(desc), _ptr(probs), tp, _ptr(kept_count),
+                                      _ptr(kept_idx), _ptr(mask), _ptr(mass), _stream(stream)),
+          "recap_topp_mask")
+    return kept_count, kept_idx, mask, mass
+
+
+def recap_block_sparse_attn(desc: RecapDesc, q, k, v, kept_count, kept_idx,
+                            sm_scale: Optional[float] = None, residual=None, res_scale=None,
+                            out=None, workspace=None, stream=None) -> torch.Tensor:
+    """Attention over the kept blocks, optionally O += c_h * R (bf16, q's layout)."""
+    _same_layout(desc, q, k, v, out, residual)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(desc.head_dim)
+    if out is None:
+        out = _like_out(q)
+    rs = None
+    if residual is not None:
+        if res_scale is None:
+            raise ValueError("res_scale is required with a residual")
+        rs = _host_floats(res_scale, desc.heads, "res_scale")
+    ws, nbytes = _workspace(_lib.OP_SPARSE, desc, q.device, workspace)
+    check(_lib.load().recap_block_sparse_attn(
+        ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(kept_count), _ptr(kept_idx),
+        float(sm_scale), _ptr(residual), rs, _ptr(out), _ptr(ws), nbytes, _stream(stream)),
+        "recap_block_sparse_attn")
+    return out
+
+
+def recap_dense_attn(desc: RecapDesc, q, k, v, sm_scale: Optional[float] = None,
+                     kept_count=None, kept_idx=None, out=None, residual_out=None,
+                     capture: bool = False, workspace=None, stream=None):
+    """Dense attention; with capture=True (or residual_out) also R = O_dense - O_sparse.
+    Returns out, or (out, residual) when capturing."""
+    _same_layout(desc, q, k, v, out, residual_out)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(desc.head_dim)
+    if out is None:
+        out = _like_out(q)
+    capture = capture or residual_out is not None
+    if capture and residual_out is None:
+        residual_out = _like_out(q)
+    op = _lib.OP_DENSE_CAPTURE if capture else _lib.OP_DENSE
+    ws, nbytes = _workspace(op, desc, q.device, workspace)
+    check(_lib.load().recap_dense_attn(
+        ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), float(sm_scale), _ptr(kept_count),
+        _ptr(kept_idx), _ptr(out), _ptr(residual_out), _ptr(ws), nbytes, _stream(stream)),
+        "recap_dense_attn")
+    return (out, residual_out) if capture else out
+
+
+def sparse_step(desc: RecapDesc, q, k, v, top_p, sm_scale: Optional[float] = None,
+                residual=None, res_scale=None, out=None, stream=None):
+    """One corrected sparse attention call: block scores -> top-p -> sparse attention
+    (+ epilogue). Returns (out, kept_count, kept_idx)."""
+    probs = recap_block_scores(desc, q, k, sm_scale, stream=stream)
+    count, idx, _, _ = recap_topp_mask(desc, probs, top_p, stream=stream)
+    o = recap_block_sparse_attn(desc, q, k, v, count, idx, sm_scale, residual, res_scale, out,
+                                stream=stream)
+    return o, count, idx

@@ -1,0 +1,164 @@
+/*
+ * recap.h -- C ABI of the block-sparse top-p attention library for MI355X (gfx950).
+ *
+ * The library implements the attention-layer hot path of training-free block-sparse
+ * attention for video diffusion transformers, with a RECAP-style cached-residual epilogue:
+ *
+ *   1. recap_block_scores  mean-pool Q and K over token blocks and score every block pair
+ *                          with a row softmax (mask prediction);
+ *   2. recap_topp_mask     keep, per query block, the fewest key blocks whose probability
+ *                          mass reaches the head's threshold p_h (top-p);
+ *   3. recap_block_sparse_attn
+ *                          online-softmax attention over the kept blocks only, with an
+ *                          optional fused epilogue  O' = O + c_h * R;
+ *   4. recap_dense_attn    dense refresh over all keys, optionally capturing the residual
+ *                          R = O_dense - O_sparse on a given kept set.
+ *
+ * Sources (page title, section / figure):
+ *   RECAP: Reciprocal Sparse Attention and Hierarchical Caching for Efficient Video Diffusion
+ *     (paperpeel.com/paper/2610.26244): Sec. 3.2 (block means as coarse estimates; cached
+ *     dense refinement added to the fresh estimate, error d_h - d_t vanishing at the refresh
+ *     step; state kept per layer and head), Sec. 4.1 (dense refreshes vs. block-sparse
+ *     "selected interactions"), Sec. 1 and 5 (fresh sparse statistics regulate how strongly
+ *     the aging refinement is applied), Sec. 2 (dense-minus-window residuals).
+ *   The same title at thelatestinai.com/papers/2610.26244: first abstract (online top-p mask
+ *     prediction with per-head thresholds), third abstract (top-p selection).
+ *   CalibAtt (thelatestinai.com/papers/2603.05503): Fig. 5 (threshold the top key blocks of
+ *     each query block), Table S6 and Fig. S14 (query x key block sizes).
+ *
+ * Conventions shared by every entry point
+ *   - Tensors q, k, v, out, residual are bf16 device arrays addressed as
+ *       base + b*stride_b + h*stride_h + n*stride_n + d      (element strides, d contiguous),
+ *     so both [B,H,N,D] and [B,N,H,D] storage work. Bases must be 16-byte aligned and every
+ *     stride a multiple of 8 elements.
+ *   - Blocks: b = desc.block; M = ceil(N / b). Block j holds tokens [j*b, min(N,(j+1)*b)); the
+ *     same partition is used for queries and keys. The last block may be short: it is pooled
+ *     over its valid tokens, padded keys carry no weight, padded query rows are not written.
+ *   - probs is fp32 [B,H,M,M] contiguous; kept_count int32 [B,H,M]; kept_idx int32 [B,H,M,M]
+ *     (row r holds kept_count[r] key-block indices, ascending; later entries unspecified);
+ *     mask uint8 [B,H,M,M] (1 = kept); kept_mass fp32 [B,H,M].
+ *   - Host arrays (top_p_host, res_scale_host) have H entries and are copied into the kernel
+ *     arguments before the call returns.
+ *   - Ownership: the caller owns every buffer. The library allocates no device memory;
+ *     scratch comes from the caller's workspace (size from recap_workspace_size), which must
+ *     stay untouched until the stream has run the call. No pointer is kept after returning.
+ *   - Streams: `stream` is a hipStream_t passed as void* (NULL = the null stream). Calls are
+ *     asynchronous and never synchronise the host.
+ *   - Errors: every argument is validated before the first HIP call; on a validation error
+ *     nothing is launched and no buffer is written. RECAP_E_DEVICE means no usable gfx950
+ *     device is current; RECAP_E_LAUNCH means a kernel launch failed (outputs undefined).
+ *   - Thread safety: calls may come from several host threads; the only global state is a
+ *     per-device property cache filled once.
+ */
+#ifndef RECAP_H
+#define RECAP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RECAP_ABI_VERSION 1
+#define RECAP_MAX_HEADS 128   /* per-head host arrays are passed by value to the kernels */
+#define RECAP_MAX_BLOCKS 8192 /* M = ceil(N / block) upper bound (top-p sorts a row in LDS) */
+
+typedef struct recap_desc {
+  int32_t batch;    /* B >= 1 */
+  int32_t heads;    /* 1 <= H <= RECAP_MAX_HEADS */
+  int32_t seq;      /* N >= 1 tokens; queries and keys share it (self-attention) */
+  int32_t head_dim; /* D in {64, 128} */
+  int32_t block;    /* b in {64, 128}; M = ceil(N / b) <= RECAP_MAX_BLOCKS */
+  int32_t reserved; /* must be 0 */
+  int64_t stride_b; /* element strides of q, k, v, out and residual (all share them) */
+  int64_t stride_h;
+  int64_t stride_n;
+} recap_desc;
+
+enum recap_status {
+  RECAP_OK = 0,
+  RECAP_E_NULL = -1,      /* a required pointer is NULL */
+  RECAP_E_SHAPE = -2,     /* B, H, N, D or block out of the supported set */
+  RECAP_E_STRIDE = -3,    /* a stride is not a positive multiple of 8 elements, or overlaps */
+  RECAP_E_ALIGN = -4,     /* a base pointer is not 16-byte aligned */
+  RECAP_E_VALUE = -5,     /* a scalar or host-array value is out of range (NaN, p not in [0,1]) */
+  RECAP_E_WORKSPACE = -6, /* workspace missing or smaller than recap_workspace_size */
+  RECAP_E_DEVICE = -7,    /* no current HIP device, or it is not gfx950 */
+  RECAP_E_LAUNCH = -8     /* a kernel launch failed */
+};
+
+enum recap_op {
+  RECAP_OP_BLOCK_SCORES = 0,
+  RECAP_OP_TOPP = 1,
+  RECAP_OP_SPARSE = 2,
+  RECAP_OP_DENSE = 3,         /* dense refresh without capture */
+  RECAP_OP_DENSE_CAPTURE = 4  /* dense refresh that also writes the residual */
+};
+
+/* Version of this ABI (RECAP_ABI_VERSION of the built library). */
+int recap_abi_version(void);
+
+/* Static English text for a status code; never NULL. */
+const char* recap_status_string(int status);
+
+/* Bytes of device workspace that entry point `op` needs for descriptor `d`, written to
+ * *bytes. Returns RECAP_OK, RECAP_E_NULL or the descriptor's validation error. Pure host
+ * computation: makes no HIP call. */
+int recap_workspace_size(int op, const recap_desc* d, size_t* bytes);
+
+/* Mask prediction, part 1 (RECAP Sec. 3.2 block means; first abstract of the RECAP page at
+ * thelatestinai.com: online top-p mask prediction).
+ *   Q̄_i = mean of the valid query tokens of block i, K̄_j likewise (fp32 accumulation);
+ *   probs[b,h,i,:] = softmax_j(sm_scale * Q̄_i . K̄_j) in fp32.
+ * q, k: bf16 device tensors (layout above). sm_scale: finite and > 0 (1/sqrt(D) typical).
+ * probs: fp32 device [B,H,M,M], written in full. ws: device workspace of at least
+ * recap_workspace_size(RECAP_OP_BLOCK_SCORES) bytes, 256-byte aligned. */
+int recap_block_scores(const recap_desc* d, const void* q, const void* k, float sm_scale,
+                       float* probs, void* ws, size_t ws_bytes, void* stream);
+
+/* Mask prediction, part 2: top-p selection per query-block row (thelatestinai.com RECAP page,
+ * first and third abstracts; CalibAtt Fig. 5). Key blocks are ordered by probability,
+ * descending, equal values by lower index first; k* is the smallest k whose running mass
+ * reaches p_h (inclusive), or M when p_h >= 1 or when no prefix reaches p_h; the first k*
+ * ordered blocks are kept. The running mass is accumulated in fp64 on the fp32 probs.
+ * probs: fp32 device [B,H,M,M]. top_p_host: host array of H values in [0, 1].
+ * kept_count, kept_idx: int32 device outputs (kept indices ascending). mask_opt (uint8
+ * [B,H,M,M]) and kept_mass_opt (fp32 [B,H,M], mass of the kept set) may be NULL. */
+int recap_topp_mask(const recap_desc* d, const float* probs, const float* top_p_host,
+                    int32_t* kept_count, int32_t* kept_idx, uint8_t* mask_opt,
+                    float* kept_mass_opt, void* stream);
+
+/* Block-sparse attention over the kept blocks (RECAP Sec. 4.1 "selected interactions") with
+ * an optional fused residual epilogue (RECAP Sec. 3.2):
+ *   O_t = sum_u softmax_u(sm_scale * Q_t . K_u) V_u over the valid tokens u of the kept key
+ *         blocks of t's query block; then O_t += c_h * R_t when residual_opt is given.
+ * fp32 online softmax, bf16 MFMA products, fp32 accumulation, bf16 (RNE) output.
+ * kept_count/kept_idx: int32 device lists as written by recap_topp_mask (indices outside
+ * [0, M) are clamped; a row with count 0 outputs zeros before the epilogue).
+ * residual_opt: bf16 device tensor in the q/out layout, or NULL. res_scale_host: host array
+ * of H finite scales c_h, required iff residual_opt is not NULL. out: bf16 device tensor,
+ * must not alias q, k, v or the residual. ws: recap_workspace_size(RECAP_OP_SPARSE) bytes. */
+int recap_block_sparse_attn(const recap_desc* d, const void* q, const void* k, const void* v,
+                            const int32_t* kept_count, const int32_t* kept_idx, float sm_scale,
+                            const void* residual_opt, const float* res_scale_host, void* out,
+                            void* ws, size_t ws_bytes, void* stream);
+
+/* Dense refresh (RECAP Sec. 4.1) over all N keys, written to out. When residual_out_opt is
+ * given, the kept lists are required and the call also writes the residual
+ *   R = O_dense - O_sparse
+ * with O_sparse the block-sparse output on the same inputs and kept set (RECAP Sec. 3.2:
+ * the discrepancy cached at the refresh step; Sec. 2: dense-minus-window residuals), in bf16.
+ * Kept blocks are visited first, so O_sparse is the same fp32 state a sparse pass reaches;
+ * with every block kept R is exactly zero. ws: recap_workspace_size(RECAP_OP_DENSE) bytes,
+ * or RECAP_OP_DENSE_CAPTURE when capturing. */
+int recap_dense_attn(const recap_desc* d, const void* q, const void* k, const void* v,
+                     float sm_scale, const int32_t* kept_count_opt, const int32_t* kept_idx_opt,
+                     void* out, void* residual_out_opt, void* ws, size_t ws_bytes,
+                     void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RECAP_H */

@@ -1,0 +1,158 @@
+"""Host side of the C ABI, without a GPU: the library loads, exports every symbol that
+include/recap.h declares, sizes workspaces, and rejects bad arguments before any HIP call.
+
+Validation tests pass fake device addresses; they run only where no GPU is visible, so a
+validation bug could never turn into a launch with bogus pointers."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+from block_sparse_attention_top_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "recap.h")
+NO_GPU = torch.cuda.device_count() == 0
+cpu_only = pytest.mark.skipif(not NO_GPU, reason="fake-pointer validation runs only without a GPU")
+
+FAKE = 0x100000  # 16-byte aligned, never dereferenced
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(recap_[a-z_]+)\s*\(", text)))
+
+
+def test_header_symbols_exported():
+    lib = _lib.load()
+    names = _declared()
+    assert set(names) == set(_lib.SIGNATURES), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings():
+    lib = _lib.load()
+    assert lib.recap_abi_version() == 1
+    for st in list(_lib.STATUS_NAMES) + [-99]:
+        s = lib.recap_status_string(st)
+        assert s and len(s.decode()) > 1
+
+
+def desc(B=1, H=2, N=4096, D=64, block=64, layout="bhnd"):
+    if layout == "bhnd":
+        sb, sh, sn = H * N * D, N * D, D
+    else:  # bnhd
+        sb, sh, sn = N * H * D, D, H * D
+    return _lib.RecapDesc(B, H, N, D, block, 0, sb, sh, sn)
+
+
+def ws_size(op, d):
+    n = ctypes.c_size_t(0)
+    st = _lib.load().recap_workspace_size(op, ctypes.byref(d), ctypes.byref(n))
+    return st, n.value
+
+
+def test_workspace_sizes():
+    d = desc(B=1, H=40, N=75600, D=128, block=64)
+    M = 1182
+    st, n = ws_size(_lib.OP_BLOCK_SCORES, d)
+    assert st == 0 and n == 2 * M * 40 * 128 * 4
+    assert ws_size(_lib.OP_TOPP, d) == (0, 0)
+    st, n = ws_size(_lib.OP_SPARSE, d)
+    assert st == 0 and n == 40 * 128 * M * 64 * 2
+    st, n2 = ws_size(_lib.OP_DENSE_CAPTURE, d)
+    assert st == 0 and n2 == n + 40 * M * 64 * 128 * 4
+    assert ws_size(99, d)[0] == -5
+    assert _lib.load().recap_workspace_size(0, ctypes.byref(d), None) == -1
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("batch", 0, -2), ("heads", 0, -2), ("heads", 129, -2), ("seq", 0, -2),
+    ("head_dim", 96, -2), ("block", 32, -2), ("reserved", 1, -2), ("seq", 8192 * 64 + 1, -2),
+    ("stride_n", 60, -3), ("stride_n", 0, -3), ("stride_h", -8, -3), ("stride_n", 32, -3),
+])
+def test_descriptor_validation(field, value, status):
+    d = desc()
+    setattr(d, field, value)
+    assert ws_size(_lib.OP_SPARSE, d)[0] == status
+
+
+def test_layouts_accepted():
+    for layout in ("bhnd", "bnhd"):
+        assert ws_size(_lib.OP_SPARSE, desc(B=2, H=3, N=1000, layout=layout))[0] == 0
+    d = desc(B=2, H=3, N=1000)
+    d.stride_h = d.stride_n * 999  # heads overlap the last token of the previous head
+    assert ws_size(_lib.OP_SPARSE, d)[0] == -3
+
+
+def _p(x=FAKE):
+    return ctypes.c_void_p(x)
+
+
+@cpu_only
+def test_block_scores_validation():
+    lib = _lib.load()
+    d = desc()
+    _, need = ws_size(_lib.OP_BLOCK_SCORES, d)
+    call = lambda q=_p(), k=_p(), s=0.125, pr=_p(), ws=_p(), n=need: \
+        lib.recap_block_scores(ctypes.byref(d), q, k, s, pr, ws, n, None)
+    assert call(q=None) == -1
+    assert call(pr=None) == -1
+    assert call(q=_p(FAKE + 2)) == -4
+    assert call(s=float("nan")) == -5
+    assert call(s=0.0) == -5
+    assert call(s=float("inf")) == -5
+    assert call(ws=None) == -6
+    assert call(n=need - 1) == -6
+    assert call(ws=_p(FAKE + 16)) == -4
+    assert call() == -7  # valid arguments, no device
+
+
+@cpu_only
+def test_topp_validation():
+    lib = _lib.load()
+    d = desc(H=2)
+    good = (ctypes.c_float * 2)(0.9, 0.5)
+    call = lambda tp=good, pr=_p(): lib.recap_topp_mask(ctypes.byref(d), pr, tp, _p(), _p(),
+                                                       None, None, None)
+    assert call(pr=None) == -1
+    assert call(tp=None) == -1
+    assert call(tp=(ctypes.c_float * 2)(0.9, 1.5)) == -5
+    assert call(tp=(ctypes.c_float * 2)(-0.1, 0.5)) == -5
+    assert call(tp=(ctypes.c_float * 2)(float("nan"), 0.5)) == -5
+    assert call() == -7
+
+
+@cpu_only
+def test_sparse_and_dense_validation():
+    lib = _lib.load()
+    d = desc(H=2)
+    _, need = ws_size(_lib.OP_SPARSE, d)
+    sc = (ctypes.c_float * 2)(0.5, 1.0)
+
+    def sparse(res=None, rs=None, out=_p(FAKE + 4096), ws=_p(), n=need, s=0.125):
+        return lib.recap_block_sparse_attn(ctypes.byref(d), _p(), _p(FAKE + 1024),
+                                           _p(FAKE + 2048), _p(), _p(), s, res, rs, out, ws, n,
+                                           None)
+    assert sparse(res=_p(FAKE + 8192)) == -1  # residual without scales
+    assert sparse(out=None) == -1
+    assert sparse(out=_p(FAKE)) == -5  # out aliases q
+    assert sparse(res=_p(FAKE + 8192), rs=(ctypes.c_float * 2)(0.5, float("inf"))) == -5
+    assert sparse(n=need - 256) == -6
+    assert sparse(s=-1.0) == -5
+    assert sparse(res=_p(FAKE + 8192), rs=sc) == -7
+
+    _, need_c = ws_size(_lib.OP_DENSE_CAPTURE, d)
+
+    def dense(cnt=None, idx=None, rout=None, ws=_p(), n=need):
+        return lib.recap_dense_attn(ctypes.byref(d), _p(), _p(FAKE + 1024), _p(FAKE + 2048),
+                                    0.125, cnt, idx, _p(FAKE + 4096), rout, ws, n, None)
+    assert dense(rout=_p(FAKE + 8192)) == -1  # capture needs kept lists
+    assert dense(cnt=_p(), idx=_p(), rout=_p(FAKE + 8192)) == -6  # capture workspace larger
+    assert dense(cnt=_p(), idx=_p(), rout=_p(FAKE + 4096), n=need_c) == -5  # R aliases out
+    assert dense() == -7
+    assert dense(cnt=_p(), idx=_p(), rout=_p(FAKE + 8192), n=need_c) == -7

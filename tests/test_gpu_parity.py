@@ -1,0 +1,273 @@
+"""HIP library vs the CPU oracle on the same seeded inputs, through the C ABI.
+
+Small cases are compared in full (several tiles, ragged tails, degenerate sizes, both tensor
+layouts, D in {64, 128}, block in {64, 128}, p = 0 and p = 1). The full-size workloads run in
+the launch configuration the benchmark times and are compared on sampled heads and rows.
+"""
+import numpy as np
+import pytest
+import torch
+
+import parity
+import synth
+from oracle import oracle as O
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+@pytest.fixture(scope="module")
+def bsa():
+    import block_sparse_attention_top_amd as m
+
+    m.load()
+    assert torch.cuda.is_available()
+    return m
+
+
+def to_dev(x, layout="bhnd"):
+    if layout == "bnhd":
+        x = x.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+    t = x.to(DEV)
+    assert t.stride() == x.stride()
+    return t
+
+
+def f64(t):
+    return synth.to_f64(t.cpu())
+
+
+def run_small(bsa, cfg, seq=None, layout="bhnd", top_p=None, res_scale=None):
+    q, k, v = synth.make_qkv(cfg, seq=seq)
+    r = synth.make_residual(cfg, seq=seq)
+    N = q.shape[2]
+    M = -(-N // cfg.block)
+    p_def, c_def = synth.head_params(cfg)
+    p = p_def if top_p is None else np.broadcast_to(np.asarray(top_p, float), (cfg.heads,))
+    c = np.full(cfg.heads, 0.5) if res_scale is None else np.asarray(res_scale, float)
+    s = cfg.head_dim ** -0.5
+    say(f"[case] B={cfg.batch} H={cfg.heads} D={cfg.head_dim} N={N} block={cfg.block} "
+        f"layout={layout} p={np.round(p, 3).tolist()}")
+    qd, kd, vd, rd = (to_dev(x, layout) for x in (q, k, v, r))
+    desc = bsa.make_desc(qd, cfg.block)
+    probs = bsa.recap_block_scores(desc, qd, kd, s)
+    count, idx, mask, mass = bsa.recap_topp_mask(desc, probs, p.tolist(), want_mask=True,
+                                                 want_mass=True)
+    out = bsa.recap_block_sparse_attn(desc, qd, kd, vd, count, idx, s)
+    out_e = bsa.recap_block_sparse_attn(desc, qd, kd, vd, count, idx, s, residual=rd,
+                                        res_scale=c.tolist())
+    od = bsa.recap_dense_attn(desc, qd, kd, vd, s)
+    od2, rcap = bsa.recap_dense_attn(desc, qd, kd, vd, s, count, idx, capture=True)
+    torch.cuda.synchronize()
+
+    q64, k64, v64, r64 = (synth.to_f64(x) for x in (q, k, v, r))
+    ref_probs = O.block_scores(q64, k64, cfg.block, s)
+    parity.check_probs(probs.cpu().numpy().astype(np.float64), ref_probs)
+    sel = O.topp_select(ref_probs, p)
+    gmask = mask.cpu().numpy().astype(bool)
+    cnt, ix = count.cpu().numpy(), idx.cpu().numpy()
+    parity.check_lists(cnt, ix, M, gmask)
+    assert np.array_equal(O.mask_from_lists(cnt, ix, M), gmask)
+    parity.check_mask(gmask, ref_probs, sel["mask"], p)
+    gm = mass.cpu().numpy().astype(np.float64)
+    assert np.abs(gm - (ref_probs * gmask).sum(-1)).max() <= 2e-5
+    ref_s = O.masked_attention(q64, k64, v64, cfg.block, s, gmask)
+    parity.check_out(f64(out), ref_s, "sparse")
+    parity.check_out(f64(out_e), O.residual_epilogue(ref_s, r64, c), "sparse + epilogue")
+    ref_d = O.dense_attention(q64, k64, v64, s, block=cfg.block)
+    parity.check_out(f64(od), ref_d, "dense")
+    parity.check_out(f64(od2), ref_d, "dense (capture pass)")
+    parity.check_out(ref_s + f64(rcap), ref_d, "sparse + captured residual")
+    return dict(count=cnt, M=M, desc=desc, dev=(qd, kd, vd, rd), p=p, s=s)
+
+
+SMALL = {
+    "tiny": dict(name="tiny"),
+    "ragged_d128_b64_bnhd": dict(name="tiny", batch=2, heads=3, head_dim=128, seq=1000,
+                                 layout="bnhd", top_p=[0.5, 0.9, 0.99]),
+    "ragged_d128_b128": dict(name="tiny", heads=2, head_dim=128, block=128, seq=1500),
+    "b128_short_last_block": dict(name="tiny", heads=2, head_dim=128, block=128, seq=128 * 5 + 20),
+    "d64_b128": dict(name="tiny", heads=2, head_dim=64, block=128, seq=2000),
+    "single_partial_block": dict(name="tiny", heads=2, head_dim=128, seq=37),
+    "one_token_last_block": dict(name="tiny", heads=1, head_dim=64, seq=129),
+    "p_one_is_dense": dict(name="tiny", heads=2, head_dim=128, seq=700, top_p=1.0),
+    "p_zero_one_block": dict(name="tiny", heads=2, head_dim=64, seq=900, top_p=0.0),
+}
+
+
+@pytest.mark.parametrize("case", list(SMALL))
+def test_small_case(bsa, case):
+    kw = dict(SMALL[case])
+    name = kw.pop("name")
+    seq = kw.pop("seq", None)
+    layout = kw.pop("layout", "bhnd")
+    top_p = kw.pop("top_p", None)
+    grid = synth.WORKLOADS[name].grid
+    if seq is not None:
+        grid = (1, 1, seq)
+    cfg = synth.workload(name, grid=grid, **kw)
+    say(f"[test] {case}")
+    res = run_small(bsa, cfg, layout=layout, top_p=top_p)
+    if top_p == 1.0:
+        assert np.all(res["count"] == res["M"])
+    if top_p == 0.0:
+        assert np.all(res["count"] == 1)
+
+
+def test_all_kept_capture_is_exactly_zero(bsa):
+    say("[test] all-kept capture")
+    cfg = synth.workload("tiny", head_dim=128, grid=(1, 1, 1100))
+    q, k, v = synth.make_qkv(cfg)
+    qd, kd, vd = (to_dev(x) for x in (q, k, v))
+    desc = bsa.make_desc(qd, cfg.block)
+    M = cfg.num_blocks
+    count = torch.full((1, cfg.heads, M), M, dtype=torch.int32, device=DEV)
+    idx = torch.arange(M, dtype=torch.int32, device=DEV).expand(1, cfg.heads, M, M).contiguous()
+    od, rcap = bsa.recap_dense_attn(desc, qd, kd, vd, None, count, idx, capture=True)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(rcap).item() == 0
+    out = bsa.recap_block_sparse_attn(desc, qd, kd, vd, count, idx)
+    assert torch.equal(out, od)
+
+
+def test_deterministic_poison_and_guards(bsa):
+    say("[test] determinism, NaN poison, guard bands")
+    cfg = synth.workload("tiny", heads=2, head_dim=128, grid=(1, 1, 1333))
+    q, k, v = synth.make_qkv(cfg)
+    r = synth.make_residual(cfg)
+    qd, kd, vd, rd = (to_dev(x) for x in (q, k, v, r))
+    desc = bsa.make_desc(qd, cfg.block)
+    _, count, idx = bsa.sparse_step(desc, qd, kd, vd, [0.9, 0.8])
+    guard = 1 << 14
+    big = torch.full((qd.numel() + 2 * guard,), float("nan"), dtype=torch.bfloat16, device=DEV)
+    big[:guard] = 7.0
+    big[-guard:] = 7.0
+    out = big[guard:guard + qd.numel()].view_as(qd)
+    bsa.recap_block_sparse_attn(desc, qd, kd, vd, count, idx, None, rd, [0.5, 0.25], out=out)
+    first = out.clone()
+    bsa.recap_block_sparse_attn(desc, qd, kd, vd, count, idx, None, rd, [0.5, 0.25], out=out)
+    torch.cuda.synchronize()
+    assert not torch.isnan(out).any()
+    assert torch.equal(first, out)
+    assert torch.all(big[:guard] == 7.0) and torch.all(big[-guard:] == 7.0)
+    p1 = bsa.recap_block_scores(desc, qd, kd)
+    p2 = bsa.recap_block_scores(desc, qd, kd)
+    torch.cuda.synchronize()
+    assert torch.equal(p1, p2)
+
+
+# ------------------------------------------------------------------------- full-size workloads
+def _sample_rows(m, n, seed):
+    g = np.random.default_rng(seed)
+    rows = {0, m - 1} | set(g.choice(m, size=min(n, m), replace=False).tolist())
+    return sorted(rows)
+
+
+def _check_head(probs_g, mask_g, cnt_g, idx_g, q64, k64, v64, cfg, p_h, s, rows, h,
+                out_g=None, extra=None):
+    """Oracle checks for one head: full probs and mask rows of the head, attention rows."""
+    ref_probs = O.block_scores(q64, k64, cfg.block, s)
+    parity.check_probs(probs_g, ref_probs)
+    sel = O.topp_select(ref_probs, p_h)
+    parity.check_lists(cnt_g, idx_g, cfg.num_blocks, mask_g)
+    parity.check_mask(mask_g, ref_probs, sel["mask"], p_h)
+    if out_g is not None:
+        ref = O.masked_attention(q64, k64, v64, cfg.block, s, mask_g, rows=[(0, 0, i) for i in rows])
+        if extra is not None:
+            ref = extra(ref)
+        for i in rows:
+            lo, hi = i * cfg.block, min(cfg.seq, (i + 1) * cfg.block)
+            parity.check_out(out_g[:, :, lo:hi], ref[:, :, lo:hi], f"head {h} block {i}")
+
+
+def _head(x, h):
+    return synth.to_f64(x[:, h:h + 1])
+
+
+@pytest.mark.parametrize("name,heads", [("wan13b_480p", [0, 11]), ("wan14b_480p", [0, 17, 39]),
+                                        ("hunyuan_720p", [0, 23])])
+def test_full_size_sparse(bsa, name, heads):
+    cfg = synth.WORKLOADS[name]
+    say(f"[test] full-size {name}: generating inputs")
+    q, k, v = synth.make_qkv(cfg)
+    p, c = synth.head_params(cfg)
+    s = cfg.head_dim ** -0.5
+    r = synth.make_residual(cfg) if cfg.residual else None
+    qd, kd, vd = (to_dev(x) for x in (q, k, v))
+    rd = to_dev(r) if r is not None else None
+    desc = bsa.make_desc(qd, cfg.block)
+    say(f"[gpu] {name}: scores, top-p, sparse attention")
+    probs = bsa.recap_block_scores(desc, qd, kd, s)
+    count, idx, mask, _ = bsa.recap_topp_mask(desc, probs, p.tolist(), want_mask=True)
+    out = bsa.recap_block_sparse_attn(desc, qd, kd, vd, count, idx, s, rd,
+                                      c.tolist() if rd is not None else None)
+    torch.cuda.synchronize()
+    say(f"[check] {name}: oracle on heads {heads}")
+    for h in heads:
+        rows = _sample_rows(cfg.num_blocks, 6, h)
+        extra = None
+        if r is not None:
+            r64 = _head(r, h)
+            extra = lambda ref, r64=r64, ch=c[h]: O.residual_epilogue(ref, r64, [ch])
+        _check_head(probs[:, h:h + 1].cpu().numpy().astype(np.float64),
+                    mask[:, h:h + 1].cpu().numpy().astype(bool),
+                    count[:, h:h + 1].cpu().numpy(), idx[:, h:h + 1].cpu().numpy(),
+                    _head(q, h), _head(k, h), _head(v, h), cfg, p[h:h + 1], s, rows, h,
+                    out_g=f64(out[:, h:h + 1]), extra=extra)
+
+
+def test_full_size_refresh_then_sparse(bsa):
+    """Wan2.1-14B 720p layer: dense refresh with residual capture, then a drifted sparse step
+    that reuses the captured residual at scale 1."""
+    cfg = synth.WORKLOADS["wan14b_720p"]
+    heads = [0, 21]
+    say("[test] full-size wan14b_720p: generating inputs")
+    q, k, v = synth.make_qkv(cfg)
+    p, c = synth.head_params(cfg)
+    s = cfg.head_dim ** -0.5
+    qd, kd, vd = (to_dev(x) for x in (q, k, v))
+    desc = bsa.make_desc(qd, cfg.block)
+    say("[gpu] wan14b_720p: refresh (scores, top-p, dense + capture)")
+    probs = bsa.recap_block_scores(desc, qd, kd, s)
+    count, idx, mask, _ = bsa.recap_topp_mask(desc, probs, p.tolist(), want_mask=True)
+    od, rcap = bsa.recap_dense_attn(desc, qd, kd, vd, s, count, idx, capture=True)
+    torch.cuda.synchronize()
+    say("[check] refresh rows")
+    for h in heads:
+        rows = _sample_rows(cfg.num_blocks, 3, 100 + h)
+        q64, k64, v64 = _head(q, h), _head(k, h), _head(v, h)
+        m_h = mask[:, h:h + 1].cpu().numpy().astype(bool)
+        _check_head(probs[:, h:h + 1].cpu().numpy().astype(np.float64), m_h,
+                    count[:, h:h + 1].cpu().numpy(), idx[:, h:h + 1].cpu().numpy(),
+                    q64, k64, v64, cfg, p[h:h + 1], s, rows, h)
+        sel = [(0, 0, i) for i in rows]
+        ref_d = O.dense_attention(q64, k64, v64, s, rows=sel, block=cfg.block)
+        ref_s = O.masked_attention(q64, k64, v64, cfg.block, s, m_h, rows=sel)
+        od_h, r_h = f64(od[:, h:h + 1]), f64(rcap[:, h:h + 1])
+        for i in rows:
+            lo, hi = i * cfg.block, min(cfg.seq, (i + 1) * cfg.block)
+            parity.check_out(od_h[:, :, lo:hi], ref_d[:, :, lo:hi], f"dense h{h} b{i}")
+            parity.check_out(ref_s[:, :, lo:hi] + r_h[:, :, lo:hi], ref_d[:, :, lo:hi],
+                             f"capture identity h{h} b{i}")
+    del od
+    say("[gpu] wan14b_720p: drifted sparse step 1 with the captured residual")
+    q1, k1, v1 = synth.drifted(q, "q", 1), synth.drifted(k, "k", 1), synth.drifted(v, "v", 1)
+    q1d, k1d, v1d = (to_dev(x) for x in (q1, k1, v1))
+    out, count1, idx1 = bsa.sparse_step(desc, q1d, k1d, v1d, p.tolist(), s, residual=rcap,
+                                        res_scale=c.tolist())
+    torch.cuda.synchronize()
+    for h in heads:
+        rows = _sample_rows(cfg.num_blocks, 3, 200 + h)
+        m_h = O.mask_from_lists(count1[:, h:h + 1].cpu().numpy(), idx1[:, h:h + 1].cpu().numpy(),
+                                cfg.num_blocks)
+        q64, k64, v64 = _head(q1, h), _head(k1, h), _head(v1, h)
+        ref = O.masked_attention(q64, k64, v64, cfg.block, s, m_h, rows=[(0, 0, i) for i in rows])
+        ref = O.residual_epilogue(ref, f64(rcap[:, h:h + 1]), [c[h]])
+        got = f64(out[:, h:h + 1])
+        for i in rows:
+            lo, hi = i * cfg.block, min(cfg.seq, (i + 1) * cfg.block)
+            parity.check_out(got[:, :, lo:hi], ref[:, :, lo:hi], f"step1 h{h} b{i}")
