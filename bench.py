@@ -1,0 +1,319 @@
+#!/usr/bin/env python3
+"""Benchmark of one attention layer's hot path on one MI355X.
+
+A step is one pass of the whole path over one batch of synthetic input. For the default
+workload (Wan2.1-14B-like 720p layer: B=1, H=40, D=128, N=75,600 tokens = 21 x 45 x 80, block
+64, top-p 0.95) a step is:
+  * a dense refresh on X_0: block scores -> top-p -> dense attention with residual capture;
+  * three sparse calls on drifted inputs X_1..X_3: block scores -> top-p -> block-sparse
+    attention with the fused epilogue O + 1.0 * R using the captured residual.
+Other workloads (--workload) run one sparse call per step (+ epilogue where configured).
+
+Reported (one JSON line): computed-block TFLOP/s over the step (value), ms per step, ms per
+sparse call, sparse-attention TFLOP/s, the roofline of the dominant kernel (and of the sparse
+and mask-prediction kernels), and the CPU oracle timed on a bounded sample of the same work.
+Inputs are resident in HBM before the timed region. Timing uses HIP events on the stream the
+library launches on (torch's current stream).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "block-sparse attn ms/call + computed-block TFLOP/s (% bf16 MFMA peak), 1 GPU"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
+ATTN_SRC = os.path.join(ROOT, "block_sparse_attention_top_amd", "csrc", "attn_kernels.hip")
+MASK_SRC = os.path.join(ROOT, "block_sparse_attention_top_amd", "csrc", "mask_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def src_hash(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel_key):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if the kernel source is
+    unchanged since they were taken; else None."""
+    try:
+        table = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    ent = table.get(kernel_key)
+    if not ent:
+        return None
+    src = ATTN_SRC if ent.get("source") == "attn" else MASK_SRC
+    if ent.get("source_sha") != src_hash(src):
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def kept_token_pairs(count, idx, N, block):
+    """sum over kept (i, j) of n_i * n_j, from kept lists (torch tensors, on device)."""
+    import torch
+
+    B, H, M = count.shape
+    n = torch.full((M,), block, dtype=torch.float64, device=count.device)
+    n[-1] = N - (M - 1) * block
+    cols = torch.arange(M, device=count.device).view(1, 1, 1, M)
+    valid = cols < count.unsqueeze(-1)
+    nj = torch.where(valid, n[idx.clamp(0, M - 1).long()], torch.zeros((), dtype=torch.float64,
+                                                                       device=count.device))
+    per_row = nj.sum(-1)  # [B, H, M]
+    return float((per_row * n.view(1, 1, M)).sum().item())
+
+
+def cpu_baseline(cfg, q, k, v, p, seconds):
+    """The oracle as it stands on a bounded sample of the same work (head 0): full mask
+    prediction for the head, then sparse attention on query blocks spread over the sequence
+    until the time budget is spent, plus the dense refresh on one query block when the
+    workload refreshes. Returns the JSON object."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import synth
+    from oracle import oracle as O
+
+    s = cfg.head_dim ** -0.5
+    q64, k64, v64 = (synth.to_f64(x[:, :1]) for x in (q, k, v))
+    M, blk, N, D = cfg.num_blocks, cfg.block, cfg.seq, cfg.head_dim
+    nblk = np.full(M, blk, dtype=np.float64)
+    nblk[-1] = N - (M - 1) * blk
+    t0 = time.perf_counter()
+    probs = O.block_scores(q64, k64, blk, s)
+    sel = O.topp_select(probs, p[:1])
+    mask = sel["mask"]
+    flops = 0.0
+    rows_done = 0
+    dense_rows = 0
+    if cfg.refresh_then_sparse:
+        O.dense_attention(q64, k64, v64, s, rows=[(0, 0, M // 2)], block=blk)
+        flops += 4.0 * D * nblk[M // 2] * N
+        dense_rows = 1
+    order = np.argsort((np.arange(M) * 0.6180339887) % 1.0)  # spread over the sequence
+    for i in order:
+        O.masked_attention(q64, k64, v64, blk, s, mask, rows=[(0, 0, int(i))])
+        flops += 4.0 * D * nblk[i] * float((mask[0, 0, i] * nblk).sum())
+        rows_done += 1
+        if time.perf_counter() - t0 > seconds:
+            break
+    dt = time.perf_counter() - t0
+    threads = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"head 0 of {cfg.name}: mask prediction for all {M} query blocks, "
+                   f"sparse attention on {rows_done} query blocks"
+                   + (f", dense refresh on {dense_rows} query block" if dense_rows else "")
+                   + f"; {dt:.1f} s, fp64 numpy"),
+        "seconds": dt,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="wan14b_720p")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="time budget of the CPU-oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the path is per-head independent and would shard heads across GPUs without "
+              "communication, which this benchmark does not run.", flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import block_sparse_attention_top_amd as bsa
+    import synth
+
+    bsa.load()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    cfg = synth.WORKLOADS[args.workload]
+    B, H, N, D, blk, M = cfg.batch, cfg.heads, cfg.seq, cfg.head_dim, cfg.block, cfg.num_blocks
+    s = D ** -0.5
+    log(f"generating {cfg.name}: B={B} H={H} N={N} D={D} block={blk} M={M}")
+    t_gen = time.time()
+    q, k, v = synth.make_qkv(cfg)
+    p, c = synth.head_params(cfg)
+    inputs = [(q, k, v)]
+    if cfg.refresh_then_sparse:
+        dq = synth.drift_series(q, "q", cfg.refresh_then_sparse)
+        dk = synth.drift_series(k, "k", cfg.refresh_then_sparse)
+        dv = synth.drift_series(v, "v", cfg.refresh_then_sparse)
+        inputs += list(zip(dq, dk, dv))
+    r_host = synth.make_residual(cfg) if (cfg.residual and not cfg.refresh_then_sparse) else None
+    log(f"inputs generated in {time.time() - t_gen:.1f}s; copying to HBM")
+    dev_inputs = [tuple(x.to(dev) for x in trip) for trip in inputs]
+    r_dev = r_host.to(dev) if r_host is not None else None
+    desc = bsa.make_desc(dev_inputs[0][0], blk)
+
+    # outputs and workspaces, allocated once outside the timed region
+    ncalls = len(dev_inputs)
+    probs = torch.empty((B, H, M, M), dtype=torch.float32, device=dev)
+    counts = [torch.empty((B, H, M), dtype=torch.int32, device=dev) for _ in range(ncalls)]
+    idxs = [torch.empty((B, H, M, M), dtype=torch.int32, device=dev) for _ in range(ncalls)]
+    out = torch.empty_like(dev_inputs[0][0])
+    rcap = torch.empty_like(dev_inputs[0][0]) if cfg.refresh_then_sparse else None
+    ws_sc = torch.empty(bsa.recap_workspace_size(0, desc), dtype=torch.uint8, device=dev)
+    ws_sp = torch.empty(bsa.recap_workspace_size(2, desc), dtype=torch.uint8, device=dev)
+    ws_dc = torch.empty(bsa.recap_workspace_size(4, desc), dtype=torch.uint8, device=dev) \
+        if cfg.refresh_then_sparse else None
+    plist, clist = p.tolist(), c.tolist()
+    res_scale = clist if cfg.res_scale is not None else None
+
+    def step(events):
+        def timed(name, fn):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            if events is not None:
+                events.append((name, e0, e1))
+
+        for ci, (qq, kk, vv) in enumerate(dev_inputs):
+            refresh = cfg.refresh_then_sparse and ci == 0
+            tag = "refresh" if refresh else "sparse"
+            timed(f"{tag}.scores", lambda: bsa.recap_block_scores(desc, qq, kk, s, probs, ws_sc))
+            timed(f"{tag}.topp", lambda: bsa.recap_topp_mask(desc, probs, plist, counts[ci],
+                                                             idxs[ci]))
+            if refresh:
+                timed("refresh.attn", lambda: bsa.recap_dense_attn(
+                    desc, qq, kk, vv, s, counts[ci], idxs[ci], out, rcap, workspace=ws_dc))
+            else:
+                res = rcap if cfg.refresh_then_sparse else r_dev
+                timed("sparse.attn", lambda: bsa.recap_block_sparse_attn(
+                    desc, qq, kk, vv, counts[ci], idxs[ci], s, res,
+                    res_scale if res is not None else None, out, ws_sp))
+
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step(None)
+    torch.cuda.synchronize()
+    events = []
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(events)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+
+    per = {}
+    for name, e0, e1 in events:
+        per.setdefault(name, []).append(e0.elapsed_time(e1))
+    avg = {k: float(np.mean(v)) for k, v in per.items()}
+
+    # computed-block work of one step
+    dense_flops = 4.0 * D * B * H * float(N) * float(N)
+    sparse_flops = []
+    sparsity = []
+    for ci in range(ncalls):
+        if cfg.refresh_then_sparse and ci == 0:
+            continue
+        sparse_flops.append(4.0 * D * kept_token_pairs(counts[ci], idxs[ci], N, blk))
+        sparsity.append(1.0 - counts[ci].double().mean().item() / M)
+    step_flops = sum(sparse_flops) + (dense_flops if cfg.refresh_then_sparse else 0.0)
+    value = step_flops / (ms_step * 1e-3) / 1e12
+    sp_attn_ms = avg["sparse.attn"]
+    sp_call_ms = avg["sparse.scores"] + avg["sparse.topp"] + sp_attn_ms
+    sp_tflops = float(np.mean(sparse_flops)) / (sp_attn_ms * 1e-3) / 1e12
+
+    # mask-prediction algorithmic bytes per call (pool, scores, top-p)
+    mean_kept = float(np.mean([counts[ci].double().mean().item() for ci in range(ncalls)]))
+    mask_bytes = (2 * B * H * N * D * 2 + 2 * B * H * M * D * 4  # pool: read Q, K; write means
+                  + 2 * B * H * M * D * 4 + B * H * M * M * 4  # scores: read means; write P
+                  + B * H * M * M * 4 + B * H * M * (mean_kept + 1) * 4)  # top-p
+    mask_ms = avg["sparse.scores"] + avg["sparse.topp"]
+
+    def roof(kernel, achieved, bound="mfma", traffic_key=None):
+        peak = PEAK_BF16_TFLOPS if bound == "mfma" else PEAK_HBM_GBS
+        return {"bound": bound, "achieved": achieved, "peak": peak,
+                "unit": "TFLOP/s" if bound == "mfma" else "GB/s", "frac": achieved / peak,
+                "traffic": measured_traffic(traffic_key) if traffic_key else None,
+                "kernel": kernel}
+
+    sparse_roof = roof("pack_vt + attn_kernel<D=128,block=64,sparse> (one recap_block_sparse_attn call)",
+                       sp_tflops, traffic_key="attn_sparse")
+    if cfg.refresh_then_sparse:
+        dense_ms = avg["refresh.attn"]
+        dense_tflops = dense_flops / (dense_ms * 1e-3) / 1e12
+        main_roof = roof("pack_vt + attn_kernel<D=128,block=64,capture> (one recap_dense_attn "
+                         "call with residual capture)", dense_tflops, traffic_key="attn_capture")
+    else:
+        dense_ms = None
+        main_roof = sparse_roof
+    mask_roof = roof("pool + score + topp kernels (one call's mask prediction)",
+                     mask_bytes / (mask_ms * 1e-3) / 1e9, bound="hbm")
+
+    result = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"{cfg.name}: one attention layer, B={B} H={H} D={D} N={N} "
+                         f"({'x'.join(map(str, cfg.grid))} tokens) block={blk} "
+                         + (f"top-p {cfg.top_p}" if not isinstance(cfg.top_p, tuple)
+                            else f"top-p U{cfg.top_p[1:]}")
+                         + ("; step = dense refresh with residual capture + "
+                            f"{cfg.refresh_then_sparse} drifted sparse calls with epilogue "
+                            "(scale 1)" if cfg.refresh_then_sparse else "; step = one sparse call"
+                            + (" with epilogue" if r_dev is not None else ""))),
+            "batch": B, "heads": H, "head_dim": D, "seq_len": N, "block": blk,
+            "parallelism": "single GPU",
+        },
+        "ms_per_sparse_call": sp_call_ms,
+        "ms_sparse_attn": sp_attn_ms,
+        "ms_mask_prediction": mask_ms,
+        "ms_refresh_call": (avg["refresh.scores"] + avg["refresh.topp"] + dense_ms)
+        if dense_ms is not None else None,
+        "sparse_attn_tflops": sp_tflops,
+        "sparse_attn_frac_bf16_peak": sp_tflops / PEAK_BF16_TFLOPS,
+        "block_sparsity": float(np.mean(sparsity)),
+        "per_op_ms": avg,
+        "roofline": main_roof,
+        "roofline_sparse": sparse_roof,
+        "roofline_mask": mask_roof,
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle on a bounded sample)")
+        cb = cpu_baseline(cfg, q, k, v, p, args.cpu_seconds)
+        result["cpu_baseline"] = {kk: vv for kk, vv in cb.items() if kk != "seconds"}
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

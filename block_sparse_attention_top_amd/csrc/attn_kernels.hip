@@ -316,6 +316,9 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnParams p) {
     lt = sm.l + __shfl_xor(sm.l, 32);
     inv = lt > 0.f ? 1.0f / lt : 0.f;
     if (qrow < p.N) {
+      // no FMA contraction of o * inv into the subtraction below: with every block kept the
+      // snapshot and the final state are identical and R must come out exactly zero
+#pragma clang fp contract(off)
       bf16_t* dst = p.out + base + (int64_t)qrow * p.st.n;
       bf16_t* rdst = p.res_out + base + (int64_t)qrow * p.st.n;
 #pragma unroll

@@ -162,14 +162,16 @@ __global__ __launch_bounds__(256) void score_kernel(const float* __restrict__ qb
     if (mw != -INFINITY) lrow += red_l[w][n] * __builtin_amdgcn_exp2f(mw - mrow);
   }
   const float inv = 1.0f / lrow;
-  if (qrow >= M) return;
-  float* prow = probs + ((int64_t)bh * M + qrow) * M;
+  // Lanes past the last query block stay active: every lane also supplies key rows to the
+  // collective MFMA operands, so only their stores are skipped.
+  const bool qvalid = qrow < M;
+  float* prow = probs + ((int64_t)bh * M + min(qrow, M - 1)) * M;
   for (int kt = wave; kt < nkt; kt += 4) {
     const f32x16 acc = score_tile<D>(kb, kt * 32, M, qv, n, half);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int key = kt * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
-      if (key < M) prow[key] = __builtin_amdgcn_exp2f(acc[r] * scale_log2 - mrow) * inv;
+      if (qvalid && key < M) prow[key] = __builtin_amdgcn_exp2f(acc[r] * scale_log2 - mrow) * inv;
     }
   }
 }

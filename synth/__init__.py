@@ -189,3 +189,16 @@ def random_bf16(shape, seed: int, scale: float = 1.0) -> torch.Tensor:
 def to_f64(x: torch.Tensor) -> np.ndarray:
     """Exact upcast of a bf16/fp32 CPU tensor to a float64 numpy array."""
     return x.detach().to("cpu").float().numpy().astype(np.float64)
+
+
+def drift_series(x: torch.Tensor, tensor: str, nsteps: int):
+    """[drifted(x, tensor, s) for s = 1..nsteps], drawing each head's E once."""
+    B, H, n, D = x.shape
+    outs = [torch.empty_like(x) for _ in range(nsteps)]
+    for b in range(B):
+        for h in range(H):
+            e = torch.randn((n, D), generator=_gen("e" + tensor, b, h), dtype=torch.float32)
+            base = x[b, h].float()
+            for s in range(1, nsteps + 1):
+                outs[s - 1][b, h] = (base + (0.05 * s) * e).to(torch.bfloat16)
+    return outs

@@ -96,6 +96,9 @@ SMALL = {
     "one_token_last_block": dict(name="tiny", heads=1, head_dim=64, seq=129),
     "p_one_is_dense": dict(name="tiny", heads=2, head_dim=128, seq=700, top_p=1.0),
     "p_zero_one_block": dict(name="tiny", heads=2, head_dim=64, seq=900, top_p=0.0),
+    # several 32-row score tiles with a ragged last one (46 and 33 query blocks)
+    "score_tiles_ragged_46": dict(name="tiny", heads=2, head_dim=64, seq=64 * 45 + 10),
+    "score_tiles_ragged_33": dict(name="tiny", heads=1, head_dim=128, seq=64 * 32 + 5),
 }
 
 

@@ -62,3 +62,11 @@ def test_drift_is_small_and_seeded():
     assert torch.equal(q1, q1b)
     d = (q1.float() - q.float()).std().item()
     assert 0.03 < d < 0.07
+
+
+def test_drift_series_matches_single_steps():
+    cfg = synth.workload("tiny", grid=(1, 8, 8))
+    q, _, _ = synth.make_qkv(cfg)
+    series = synth.drift_series(q, "q", 3)
+    for s in range(1, 4):
+        assert torch.equal(series[s - 1], synth.drifted(q, "q", s))
