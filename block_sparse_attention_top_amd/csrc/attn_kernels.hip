@@ -42,6 +42,13 @@ __device__ __forceinline__ void load_lds16(const void* src, void* lds_dst_unifor
   __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)lds_dst_uniform, 16, 0, 0);
 }
 
+// Hide a value from the optimiser so precomputed per-lane offsets are used as they are
+// (otherwise the address arithmetic gets re-derived per tile with 64-bit vector multiplies).
+__device__ __forceinline__ uint32_t opaque(uint32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 // Key order inside each 16-key group of packed V^T: position pos holds key swap23(pos).
 __device__ __forceinline__ int swap23(int p) { return (p & 3) | ((p & 4) << 1) | ((p & 8) >> 1); }
 
@@ -92,10 +99,15 @@ struct ListSeq {  // kept blocks, in list order
   __device__ int first() { c = 0; return n > 0 ? at(0) : -1; }
   __device__ int next() { ++c; return c < n ? at(c) : -1; }
 };
-struct AllSeq {  // every block, ascending
-  int c, M;
-  __device__ int first() { c = 0; return M > 0 ? 0 : -1; }
-  __device__ int next() { ++c; return c < M ? c : -1; }
+struct AllSeq {  // every block once, starting at `start` and wrapping around
+  int c, M, start;
+  __device__ int first() { c = 0; return M > 0 ? start : -1; }
+  __device__ int next() {
+    ++c;
+    if (c >= M) return -1;
+    const int j = start + c;
+    return j >= M ? j - M : j;
+  }
 };
 struct ComplementSeq {  // blocks whose bit is clear, ascending
   const uint32_t* bits;
@@ -110,44 +122,116 @@ struct ComplementSeq {  // blocks whose bit is clear, ascending
 
 template <int D, int NW>
 struct Tiles {
-  static constexpr int CH = D / 8;        // 16-byte chunks in a K row
-  static constexpr int LD = CH / NW;      // global->LDS instructions per wave per tensor tile
+  static constexpr int CH = D / 8;       // 16-byte chunks in a K row
+  static constexpr int ROWB = D * 2;     // bytes of a K row in LDS
+  static constexpr int LD = CH / NW;     // global->LDS instructions per wave per tensor tile
+  static constexpr int KROWS = 64 / CH;  // K rows written by one instruction
   static constexpr int TILE_BYTES = 64 * D * 2;
 };
 
+// Per-lane constants of the inner loop, computed once per work-group.
+//  K tile in LDS: row `key` (0..63) holds its 16-byte chunks XOR-swizzled, chunk c stored at
+//  position c ^ (key & (CH-1)). V^T tile: row d (0..D-1) of 64 keys, chunk c stored at
+//  c ^ ((d >> 1) & 7). Both make the 16-byte MFMA-fragment reads bank-conflict free, and
+//  both reduce to "lane base XOR (ks << 5)" plus an immediate offset per 32-row tile.
+template <int D, int NW>
+struct LaneConsts {
+  uint32_t k_rd, v_rd;      // LDS read bases (bytes)
+  uint32_t k_voff[4];       // K DMA source offsets (bytes), by instruction index mod 4
+  uint32_t v_voff[2];       // V^T DMA source offsets (bytes), by instruction index mod 2
+  __device__ void init(int lane, int64_t sn, int npad) {
+    constexpr int CH = Tiles<D, NW>::CH, ROWB = Tiles<D, NW>::ROWB, KROWS = Tiles<D, NW>::KROWS;
+    const int n = lane & 31, half = lane >> 5;
+    k_rd = n * ROWB + ((half ^ (n & (CH - 1))) << 4);
+    v_rd = n * 128 + ((half ^ ((n >> 1) & 7)) << 4);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int key = r * KROWS + lane / CH;  // row inside the tile, modulo the swizzle period
+      const int c = (lane % CH) ^ (key & (CH - 1));
+      k_voff[r] = opaque((uint32_t)((lane / CH) * sn * 2 + c * 16));
+    }
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int c = (lane & 7) ^ ((r * 4 + (lane >> 4)) & 7);
+      v_voff[r] = opaque((uint32_t)((lane >> 3) * npad * 2 + c * 16));
+    }
+    k_rd = opaque(k_rd);
+    v_rd = opaque(v_rd);
+  }
+};
+
+// Issue the global -> LDS loads of one 64-key K tile: rows [key0, key0 + 64) of this head.
+// Addresses are a uniform 64-bit base (first row of the tile) plus a 32-bit lane offset, so
+// the per-load cost is one 32-bit add.
 template <int D, int NW>
 __device__ __forceinline__ void issue_k(unsigned char* kbuf, const bf16_t* kp, int64_t sn, int N,
-                                        int key0, int wave, int lane) {
-  constexpr int CH = Tiles<D, NW>::CH, LD = Tiles<D, NW>::LD;
+                                        int key0, int wave, int lane,
+                                        const LaneConsts<D, NW>& lc) {
+  constexpr int CH = Tiles<D, NW>::CH, LD = Tiles<D, NW>::LD, KROWS = Tiles<D, NW>::KROWS;
+  const char* tile_base = (const char*)(kp + (int64_t)key0 * sn);
+  const uint32_t row_bytes = (uint32_t)(sn * 2);
+  if (key0 + 64 <= N) {
 #pragma unroll
-  for (int it = 0; it < LD; ++it) {
-    const int slot0 = (wave * LD + it) * 64;
-    const int slot = slot0 + lane;
-    const int key = slot / CH;
-    const int c = (slot % CH) ^ (key & (CH - 1));
-    const bf16_t* src = kp + (int64_t)min(key0 + key, N - 1) * sn + c * 8;
-    load_lds16(src, kbuf + slot0 * 16);
+    for (int it = 0; it < LD; ++it) {
+      const int x = wave * LD + it;
+      load_lds16(tile_base + (uint32_t)(x * KROWS * row_bytes + lc.k_voff[x & 3]), kbuf + x * 1024);
+    }
+  } else {
+    // last, partial block: rows past N are clamped to row N-1 (their scores are masked)
+    asm volatile("" ::: "memory");
+    const int last = N - 1 - key0;
+#pragma unroll
+    for (int it = 0; it < LD; ++it) {
+      const int slot0 = (wave * LD + it) * 64;
+      const int slot = slot0 + lane;
+      const int key = slot / CH;
+      const int c = (slot % CH) ^ (key & (CH - 1));
+      load_lds16(tile_base + (uint32_t)(min(key, last) * row_bytes + c * 16), kbuf + slot0 * 16);
+    }
   }
 }
 
 template <int D, int NW>
 __device__ __forceinline__ void issue_v(unsigned char* vbuf, const bf16_t* vtp, int npad,
-                                        int key0, int wave, int lane) {
+                                        int key0, int wave, const LaneConsts<D, NW>& lc) {
   constexpr int LD = Tiles<D, NW>::LD;
+  const char* tile_base = (const char*)(vtp + key0);
+  const uint32_t row_bytes = (uint32_t)npad * 2;
 #pragma unroll
   for (int it = 0; it < LD; ++it) {
-    const int slot0 = (wave * LD + it) * 64;
-    const int slot = slot0 + lane;
-    const int d = slot >> 3;
-    const int c = (slot & 7) ^ ((d >> 1) & 7);
-    const bf16_t* src = vtp + (int64_t)d * npad + key0 + c * 8;
-    load_lds16(src, vbuf + slot0 * 16);
+    const int x = wave * LD + it;
+    load_lds16(tile_base + (uint32_t)(x * 8 * row_bytes + lc.v_voff[x & 1]), vbuf + x * 1024);
   }
 }
 
 struct SoftmaxState {
-  float m, l;
+  float m, l;  // running max (log2 units, may lag the true max by < kLazy) and per-lane sum
 };
+
+// Rescale the running state only when some lane's max grows by more than kLazy (log2 units):
+// the probabilities of a row are exp2(x - m) for a per-row m that may lag its true max by up
+// to kLazy, so they stay below 2^kLazy (exact in fp32 / bf16 range); the final O / l is the
+// same quantity for any m.
+constexpr float kLazy = 8.0f;
+
+// max(a, b, c) in one instruction (fmaxf on matrix-core results would first canonicalise
+// every input against signalling NaNs, tripling the instruction count)
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+__device__ __forceinline__ float cross_half_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float cross_half_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 // One attention phase over a block sequence, continuing the online-softmax state (m, l, o).
 template <int D, int NW, class Seq>
@@ -155,14 +239,15 @@ __device__ __forceinline__ void attend_phase(Seq& seq, unsigned char* kbuf, unsi
                                              const bf16_t* kp, const bf16_t* vtp, int64_t sn,
                                              int N, int block, int npad, float scale_log2,
                                              const bf16x8 (&qf)[D / 16], f32x16 (&o)[D / 32],
-                                             SoftmaxState& sm, int wave, int lane) {
-  constexpr int CH = Tiles<D, NW>::CH, LD = Tiles<D, NW>::LD;
-  const int n = lane & 31, half = lane >> 5;
+                                             SoftmaxState& sm, int wave, int lane,
+                                             const LaneConsts<D, NW>& lc) {
+  constexpr int ROWB = Tiles<D, NW>::ROWB;
+  const int half = lane >> 5;
   int j = seq.first();
   if (j < 0) return;
   int st = 0;
-  issue_k<D, NW>(kbuf, kp, sn, N, j * block, wave, lane);
-  issue_v<D, NW>(vbuf, vtp, npad, j * block, wave, lane);
+  issue_k<D, NW>(kbuf, kp, sn, N, j * block, wave, lane, lc);
+  issue_v<D, NW>(vbuf, vtp, npad, j * block, wave, lc);
   while (true) {
     const int key0 = j * block + st * kKeyTile;
     int jn = j, stn = st + 1;
@@ -172,81 +257,89 @@ __device__ __forceinline__ void attend_phase(Seq& seq, unsigned char* kbuf, unsi
     }
     const bool has_next = jn >= 0;
 
-    // ---- S^T = K Q^T ----
-    wait_vmem<LD>();  // this wave's K(t) landed (V(t) may still be in flight)
-    lds_barrier();    // ... and every other wave's
+    wait_vmem<0>();  // this wave's K(t) and V^T(t) landed
+    lds_barrier();   // ... and every other wave's
+
+    // ---- S^T = K Q^T (raw dot products) ----
     f32x16 s0 = {}, s1 = {};
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
-      const int c = ks * 2 + half;
-      const int key_a = n, key_b = 32 + n;
-      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kbuf + (key_a * CH + (c ^ (key_a & (CH - 1)))) * 16);
-      const bf16x8 kb = *reinterpret_cast<const bf16x8*>(kbuf + (key_b * CH + (c ^ (key_b & (CH - 1)))) * 16);
+      const uint32_t a = lc.k_rd ^ (uint32_t)(ks << 5);
+      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kbuf + a);
+      const bf16x8 kb = *reinterpret_cast<const bf16x8*>(kbuf + a + 32 * ROWB);
       s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], s0, 0, 0, 0);
       s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb, qf[ks], s1, 0, 0, 0);
     }
-    lds_barrier();  // K buffer free
-    if (has_next) issue_k<D, NW>(kbuf, kp, sn, N, jn * block + stn * kKeyTile, wave, lane);
 
-    // ---- online softmax (base-2 domain) ----
-    float x[32];
-    float mx = -INFINITY;
-    const bool tail = key0 + kKeyTile > N;
+    // ---- online softmax in the base-2 domain, lazy rescale ----
+    if (key0 + kKeyTile > N) {
+      asm volatile("" ::: "memory");  // keep the rare tail tile a real (uniform) branch
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      x[r] = s0[r] * scale_log2;
-      x[16 + r] = s1[r] * scale_log2;
-    }
-    if (tail) {
-#pragma unroll
-      for (int r = 0; r < 32; ++r) {
-        const int key = key0 + (r >> 4) * 32 + ((r & 15) >> 2) * 8 + half * 4 + (r & 3);
-        if (key >= N) x[r] = -INFINITY;
+      for (int r = 0; r < 16; ++r) {
+        const int kr = ((r >> 2) << 3) + half * 4 + (r & 3);
+        if (key0 + kr >= N) s0[r] = -INFINITY;
+        if (key0 + 32 + kr >= N) s1[r] = -INFINITY;
       }
     }
+    float mx = max3(s0[0], s1[0], s0[1]);
 #pragma unroll
-    for (int r = 0; r < 32; ++r) mx = fmaxf(mx, x[r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mn = fmaxf(sm.m, mx);
-    const float alpha = __builtin_amdgcn_exp2f(sm.m - mn);
-    sm.m = mn;
-    sm.l *= alpha;
+    for (int r = 1; r < 16; ++r) mx = max3(mx, s1[r], r + 1 < 16 ? s0[r + 1] : s1[r]);
+    const float mt = cross_half_max(mx) * scale_log2;  // finite: a tile has a valid key
+    if (__builtin_amdgcn_ballot_w64(mt > sm.m + kLazy) != 0) {
+      const float mn = fmaxf(sm.m, mt);
+      const float alpha = __builtin_amdgcn_exp2f(sm.m - mn);
+      sm.m = mn;
+      sm.l *= alpha;
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) o[dt] *= alpha;
+      for (int dt = 0; dt < D / 32; ++dt) o[dt] *= alpha;
+    }
+    const float neg_m = -sm.m;
     bf16x8 pf[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const bf16_t pb = (bf16_t)__builtin_amdgcn_exp2f(x[ks * 8 + e] - mn);
-        pf[ks][e] = pb;
-        sm.l += (float)pb;
+        const float x = (ks < 2) ? s0[(ks & 1) * 8 + e] : s1[(ks & 1) * 8 + e];
+        pf[ks][e] = (bf16_t)__builtin_amdgcn_exp2f(__builtin_fmaf(x, scale_log2, neg_m));
       }
+    }
+    // row sum of the bf16-rounded probabilities (the ones the PV product uses)
+    {
+      typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+      const bf16x2 one = {(bf16_t)1.0f, (bf16_t)1.0f};
+      float acc = sm.l;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const bf16x2 pr = {pf[ks][e], pf[ks][e + 1]};
+          acc = __builtin_amdgcn_fdot2_f32_bf16(pr, one, acc, false);
+        }
+      }
+      sm.l = acc;
     }
 
     // ---- O^T += V^T P^T ----
-    if (has_next) wait_vmem<LD>(); else wait_vmem<0>();  // V(t) landed
-    lds_barrier();
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      const int c = ks * 2 + half;
+      const uint32_t a = lc.v_rd ^ (uint32_t)(ks << 5);
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
-        const int d = dt * 32 + n;
-        const bf16x8 va = *reinterpret_cast<const bf16x8*>(vbuf + (d * 8 + (c ^ ((d >> 1) & 7))) * 16);
+        const bf16x8 va = *reinterpret_cast<const bf16x8*>(vbuf + a + dt * 4096);
         o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[ks], o[dt], 0, 0, 0);
       }
     }
-    lds_barrier();  // V buffer free
+    lds_barrier();  // every wave is done reading both buffers
     if (!has_next) break;
-    issue_v<D, NW>(vbuf, vtp, npad, jn * block + stn * kKeyTile, wave, lane);
+    issue_k<D, NW>(kbuf, kp, sn, N, jn * block + stn * kKeyTile, wave, lane, lc);
+    issue_v<D, NW>(vbuf, vtp, npad, jn * block + stn * kKeyTile, wave, lc);
     j = jn;
     st = stn;
   }
 }
 
 template <int D, int NW, int MODE>
-__global__ __launch_bounds__(NW * 64) void attn_kernel(AttnParams p) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_kernel(AttnParams p) {
   __shared__ __align__(16) unsigned char kbuf[Tiles<D, NW>::TILE_BYTES];
   __shared__ __align__(16) unsigned char vbuf[Tiles<D, NW>::TILE_BYTES];
   __shared__ uint32_t bits[MODE == kCapture ? 8192 / 32 : 1];
@@ -260,6 +353,8 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnParams p) {
   const bf16_t* kp = p.k + base;
   const bf16_t* vtp = p.vt + (int64_t)bh * D * p.npad;
   const int qrow = qi * p.block + wave * 32 + n;
+  LaneConsts<D, NW> lc;
+  lc.init(lane, p.st.n, p.npad);
 
   bf16x8 qf[D / 16];
   {
@@ -276,9 +371,9 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnParams p) {
   const int nlist = MODE == kDense ? 0 : min(max(((cptr_i32)p.count)[tile], 0), p.M);
 
   if (MODE == kDense) {
-    AllSeq seq{0, p.M};
+    AllSeq seq{0, p.M, qi};  // staggered start: work-groups do not all stream the same tile
     attend_phase<D, NW>(seq, kbuf, vbuf, kp, vtp, p.st.n, p.N, p.block, p.npad, p.scale_log2, qf,
-                        o, sm, wave, lane);
+                        o, sm, wave, lane, lc);
   } else {
     if (MODE == kCapture) {
       for (int w = threadIdx.x; w < (p.M + 31) / 32; w += NW * 64) bits[w] = 0u;
@@ -291,10 +386,10 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnParams p) {
     }
     ListSeq seq{lst, nlist, 0, p.M};
     attend_phase<D, NW>(seq, kbuf, vbuf, kp, vtp, p.st.n, p.N, p.block, p.npad, p.scale_log2, qf,
-                        o, sm, wave, lane);
+                        o, sm, wave, lane, lc);
   }
 
-  float lt = sm.l + __shfl_xor(sm.l, 32);
+  float lt = cross_half_sum(sm.l);
   float inv = lt > 0.f ? 1.0f / lt : 0.f;
 
   if (MODE == kCapture) {
@@ -312,8 +407,8 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnParams p) {
     }
     ComplementSeq seq{bits, 0, p.M};
     attend_phase<D, NW>(seq, kbuf, vbuf, kp, vtp, p.st.n, p.N, p.block, p.npad, p.scale_log2, qf,
-                        o, sm, wave, lane);
-    lt = sm.l + __shfl_xor(sm.l, 32);
+                        o, sm, wave, lane, lc);
+    lt = cross_half_sum(sm.l);
     inv = lt > 0.f ? 1.0f / lt : 0.f;
     if (qrow < p.N) {
       // no FMA contraction of o * inv into the subtraction below: with every block kept the
