@@ -27,8 +27,6 @@
 
 namespace recap {
 
-typedef const __attribute__((address_space(1))) void* gptr_t;
-typedef __attribute__((address_space(3))) void* lptr_t;
 typedef const __attribute__((address_space(4))) int32_t* cptr_i32;
 
 __device__ __forceinline__ void lds_barrier() {
@@ -38,8 +36,26 @@ template <int N>
 __device__ __forceinline__ void wait_vmem() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
-__device__ __forceinline__ void load_lds16(const void* src, void* lds_dst_uniform) {
-  __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)lds_dst_uniform, 16, 0, 0);
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  return (uint32_t)(size_t)(const __attribute__((address_space(3))) void*)p;
+}
+// 16 bytes per lane global -> LDS (global_load_lds_dwordx4, SGPR base + 32-bit lane offset);
+// lane i lands at lds_dst + 16 * i. Written as asm with no output register so the compiler does
+// not insert a full vmcnt wait before every later LDS read; completion is tracked by hand with
+// wait_vmem<> in issue order. M0 (the LDS base operand, read at issue) is restored afterwards.
+__device__ __forceinline__ void load_lds16(const void* base_uniform, uint32_t voff,
+                                           const void* lds_dst_uniform) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, %3\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(__builtin_amdgcn_readfirstlane(lds_offset(lds_dst_uniform))), "v"(voff),
+        "s"(base_uniform)
+      : "memory");
 }
 
 // Hide a value from the optimiser so precomputed per-lane offsets are used as they are
@@ -109,15 +125,19 @@ struct AllSeq {  // every block once, starting at `start` and wrapping around
     return j >= M ? j - M : j;
   }
 };
-struct ComplementSeq {  // blocks whose bit is clear, ascending
+struct ComplementSeq {  // blocks whose bit is clear, starting at `start` and wrapping around
   const uint32_t* bits;
-  int c, M;
-  __device__ int scan(int j) {
-    while (j < M && ((bits[j >> 5] >> (j & 31)) & 1u)) ++j;
-    return j < M ? j : -1;
+  int c, M, start;  // c counts visited positions (0..M)
+  __device__ int scan() {
+    for (; c < M; ++c) {
+      int j = start + c;
+      j = j >= M ? j - M : j;
+      if (!((bits[j >> 5] >> (j & 31)) & 1u)) return j;
+    }
+    return -1;
   }
-  __device__ int first() { c = scan(0); return c; }
-  __device__ int next() { c = scan(c + 1); return c; }
+  __device__ int first() { c = 0; return scan(); }
+  __device__ int next() { ++c; return scan(); }
 };
 
 template <int D, int NW>
@@ -174,7 +194,7 @@ __device__ __forceinline__ void issue_k(unsigned char* kbuf, const bf16_t* kp, i
 #pragma unroll
     for (int it = 0; it < LD; ++it) {
       const int x = wave * LD + it;
-      load_lds16(tile_base + (uint32_t)(x * KROWS * row_bytes + lc.k_voff[x & 3]), kbuf + x * 1024);
+      load_lds16(tile_base, (uint32_t)(x * KROWS * row_bytes + lc.k_voff[x & 3]), kbuf + x * 1024);
     }
   } else {
     // last, partial block: rows past N are clamped to row N-1 (their scores are masked)
@@ -186,7 +206,7 @@ __device__ __forceinline__ void issue_k(unsigned char* kbuf, const bf16_t* kp, i
       const int slot = slot0 + lane;
       const int key = slot / CH;
       const int c = (slot % CH) ^ (key & (CH - 1));
-      load_lds16(tile_base + (uint32_t)(min(key, last) * row_bytes + c * 16), kbuf + slot0 * 16);
+      load_lds16(tile_base, (uint32_t)(min(key, last) * row_bytes + c * 16), kbuf + slot0 * 16);
     }
   }
 }
@@ -200,7 +220,7 @@ __device__ __forceinline__ void issue_v(unsigned char* vbuf, const bf16_t* vtp, 
 #pragma unroll
   for (int it = 0; it < LD; ++it) {
     const int x = wave * LD + it;
-    load_lds16(tile_base + (uint32_t)(x * 8 * row_bytes + lc.v_voff[x & 1]), vbuf + x * 1024);
+    load_lds16(tile_base, (uint32_t)(x * 8 * row_bytes + lc.v_voff[x & 1]), vbuf + x * 1024);
   }
 }
 
@@ -241,7 +261,7 @@ __device__ __forceinline__ void attend_phase(Seq& seq, unsigned char* kbuf, unsi
                                              const bf16x8 (&qf)[D / 16], f32x16 (&o)[D / 32],
                                              SoftmaxState& sm, int wave, int lane,
                                              const LaneConsts<D, NW>& lc) {
-  constexpr int ROWB = Tiles<D, NW>::ROWB;
+  constexpr int ROWB = Tiles<D, NW>::ROWB, LD = Tiles<D, NW>::LD;
   const int half = lane >> 5;
   int j = seq.first();
   if (j < 0) return;
@@ -257,8 +277,8 @@ __device__ __forceinline__ void attend_phase(Seq& seq, unsigned char* kbuf, unsi
     }
     const bool has_next = jn >= 0;
 
-    wait_vmem<0>();  // this wave's K(t) and V^T(t) landed
-    lds_barrier();   // ... and every other wave's
+    wait_vmem<LD>();  // this wave's K(t) landed (V^T(t), issued after it, may be in flight)
+    lds_barrier();    // ... and every other wave's
 
     // ---- S^T = K Q^T (raw dot products) ----
     f32x16 s0 = {}, s1 = {};
@@ -270,6 +290,8 @@ __device__ __forceinline__ void attend_phase(Seq& seq, unsigned char* kbuf, unsi
       s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], s0, 0, 0, 0);
       s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb, qf[ks], s1, 0, 0, 0);
     }
+    lds_barrier();  // every wave is done reading the K buffer
+    if (has_next) issue_k<D, NW>(kbuf, kp, sn, N, jn * block + stn * kKeyTile, wave, lane, lc);
 
     // ---- online softmax in the base-2 domain, lazy rescale ----
     if (key0 + kKeyTile > N) {
@@ -320,6 +342,8 @@ __device__ __forceinline__ void attend_phase(Seq& seq, unsigned char* kbuf, unsi
     }
 
     // ---- O^T += V^T P^T ----
+    if (has_next) wait_vmem<LD>(); else wait_vmem<0>();  // V^T(t) landed (K(t+1) may not)
+    lds_barrier();
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const uint32_t a = lc.v_rd ^ (uint32_t)(ks << 5);
@@ -329,9 +353,8 @@ __device__ __forceinline__ void attend_phase(Seq& seq, unsigned char* kbuf, unsi
         o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[ks], o[dt], 0, 0, 0);
       }
     }
-    lds_barrier();  // every wave is done reading both buffers
+    lds_barrier();  // every wave is done reading the V buffer
     if (!has_next) break;
-    issue_k<D, NW>(kbuf, kp, sn, N, jn * block + stn * kKeyTile, wave, lane, lc);
     issue_v<D, NW>(vbuf, vtp, npad, jn * block + stn * kKeyTile, wave, lc);
     j = jn;
     st = stn;
@@ -344,7 +367,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   __shared__ __align__(16) unsigned char vbuf[Tiles<D, NW>::TILE_BYTES];
   __shared__ uint32_t bits[MODE == kCapture ? 8192 / 32 : 1];
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wavefront
   const int n = lane & 31, half = lane >> 5;
   const int tile = xcd_remap(blockIdx.x, gridDim.x);  // = (b*H + h) * M + query block
   const int bh = tile / p.M, qi = tile - bh * p.M;
@@ -361,6 +385,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const bf16_t* src = p.q + base + (int64_t)min(qrow, p.N - 1) * p.st.n + half * 8;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(src + ks * 16);
+    // consume the fragments here, so the compiler's waits for these loads sit before the loop
+    // (the tile loads in the loop are invisible to its wait-count bookkeeping)
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) asm volatile("" ::"v"(qf[ks]));
   }
   f32x16 o[D / 32];
 #pragma unroll
@@ -405,7 +433,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         *reinterpret_cast<f32x4*>(ws + dt * 32 + g * 8 + half * 4) = v;
       }
     }
-    ComplementSeq seq{bits, 0, p.M};
+    ComplementSeq seq{bits, 0, p.M, qi};  // staggered like the dense walk
     attend_phase<D, NW>(seq, kbuf, vbuf, kp, vtp, p.st.n, p.N, p.block, p.npad, p.scale_log2, qf,
                         o, sm, wave, lane, lc);
     lt = cross_half_sum(sm.l);
