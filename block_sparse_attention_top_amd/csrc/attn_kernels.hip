@@ -5,9 +5,9 @@
 // dense refinement to the fresh sparse estimate. This file holds one kernel template for
 // three modes:
 //   kSparse   walk the compacted kept-block list; optional fused O += c_h * R epilogue;
-//   kDense    walk every key block;
-//   kCapture  walk the kept list, snapshot the normalised sparse output, continue over the
-//             remaining blocks, then write O_dense and R = O_dense - O_sparse.
+//   kDense    walk every key block (128 query rows per work-group); optionally also keep the
+//             fp32 output in a workspace;
+//   kCaptureR walk the kept list and write R = O_dense - O_sparse using that fp32 output.
 //
 // Layout of the work (one work-group per query block of `block` rows, one wavefront per 32
 // query rows, 64-key tiles):
@@ -124,20 +124,6 @@ struct AllSeq {  // every block once, starting at `start` and wrapping around
     const int j = start + c;
     return j >= M ? j - M : j;
   }
-};
-struct ComplementSeq {  // blocks whose bit is clear, starting at `start` and wrapping around
-  const uint32_t* bits;
-  int c, M, start;  // c counts visited positions (0..M)
-  __device__ int scan() {
-    for (; c < M; ++c) {
-      int j = start + c;
-      j = j >= M ? j - M : j;
-      if (!((bits[j >> 5] >> (j & 31)) & 1u)) return j;
-    }
-    return -1;
-  }
-  __device__ int first() { c = 0; return scan(); }
-  __device__ int next() { ++c; return scan(); }
 };
 
 template <int D, int NW>
@@ -365,18 +351,19 @@ template <int D, int NW, int MODE>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_kernel(AttnParams p) {
   __shared__ __align__(16) unsigned char kbuf[Tiles<D, NW>::TILE_BYTES];
   __shared__ __align__(16) unsigned char vbuf[Tiles<D, NW>::TILE_BYTES];
-  __shared__ uint32_t bits[MODE == kCapture ? 8192 / 32 : 1];
+  constexpr int QROWS = NW * 32;  // query rows of one work-group
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wavefront
   const int n = lane & 31, half = lane >> 5;
-  const int tile = xcd_remap(blockIdx.x, gridDim.x);  // = (b*H + h) * M + query block
-  const int bh = tile / p.M, qi = tile - bh * p.M;
+  // tile = (b*H + h) * mq + query tile; in the list modes a query tile is one query block
+  const int tile = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = tile / p.mq, qi = tile - bh * p.mq;
   const int b = bh / p.H, h = bh - b * p.H;
   const int64_t base = b * p.st.b + h * p.st.h;
   const bf16_t* kp = p.k + base;
   const bf16_t* vtp = p.vt + (int64_t)bh * D * p.npad;
-  const int qrow = qi * p.block + wave * 32 + n;
+  const int qrow = qi * QROWS + wave * 32 + n;
   LaneConsts<D, NW> lc;
   lc.init(lane, p.st.n, p.npad);
 
@@ -395,99 +382,71 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   for (int dt = 0; dt < D / 32; ++dt) o[dt] = f32x16{};
   SoftmaxState sm{-INFINITY, 0.f};
 
-  const int32_t* lst = p.idx + (int64_t)tile * p.M;
-  const int nlist = MODE == kDense ? 0 : min(max(((cptr_i32)p.count)[tile], 0), p.M);
-
+  int nlist = 0;
   if (MODE == kDense) {
-    AllSeq seq{0, p.M, qi};  // staggered start: work-groups do not all stream the same tile
+    // staggered start at the diagonal: neighbouring work-groups stream the same K/V tiles at
+    // nearly the same time, which keeps them in L2
+    AllSeq seq{0, p.M, min((qi * QROWS) / p.block, p.M - 1)};
     attend_phase<D, NW>(seq, kbuf, vbuf, kp, vtp, p.st.n, p.N, p.block, p.npad, p.scale_log2, qf,
                         o, sm, wave, lane, lc);
   } else {
-    if (MODE == kCapture) {
-      for (int w = threadIdx.x; w < (p.M + 31) / 32; w += NW * 64) bits[w] = 0u;
-      __syncthreads();
-      for (int c = threadIdx.x; c < nlist; c += NW * 64) {
-        const int j = min(max(lst[c], 0), p.M - 1);
-        atomicOr(&bits[j >> 5], 1u << (j & 31));
-      }
-      __syncthreads();
-    }
+    const int32_t* lst = p.idx + (int64_t)tile * p.M;
+    nlist = min(max(((cptr_i32)p.count)[tile], 0), p.M);
     ListSeq seq{lst, nlist, 0, p.M};
     attend_phase<D, NW>(seq, kbuf, vbuf, kp, vtp, p.st.n, p.N, p.block, p.npad, p.scale_log2, qf,
                         o, sm, wave, lane, lc);
   }
 
-  float lt = cross_half_sum(sm.l);
-  float inv = lt > 0.f ? 1.0f / lt : 0.f;
+  const float lt = cross_half_sum(sm.l);
+  const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+  if (qrow >= p.N) return;
+  const int64_t orow = base + (int64_t)qrow * p.st.n;
 
-  if (MODE == kCapture) {
-    // snapshot of the normalised sparse output, fp32, same lane reads it back below
-    float* ws = p.os_ws + ((int64_t)bh * p.npad + qrow) * D;
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        f32x4 v;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = o[dt][g * 4 + e] * inv;
-        *reinterpret_cast<f32x4*>(ws + dt * 32 + g * 8 + half * 4) = v;
-      }
-    }
-    ComplementSeq seq{bits, 0, p.M, qi};  // staggered like the dense walk
-    attend_phase<D, NW>(seq, kbuf, vbuf, kp, vtp, p.st.n, p.N, p.block, p.npad, p.scale_log2, qf,
-                        o, sm, wave, lane, lc);
-    lt = cross_half_sum(sm.l);
-    inv = lt > 0.f ? 1.0f / lt : 0.f;
-    if (qrow < p.N) {
-      // no FMA contraction of o * inv into the subtraction below: with every block kept the
-      // snapshot and the final state are identical and R must come out exactly zero
+  if (MODE == kCaptureR) {
+    // R = O_dense - O_sparse from the fp32 dense output of the same inputs; exactly zero when
+    // the kept list covers every key block (then both are the same attention)
 #pragma clang fp contract(off)
-      bf16_t* dst = p.out + base + (int64_t)qrow * p.st.n;
-      bf16_t* rdst = p.res_out + base + (int64_t)qrow * p.st.n;
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int d0 = dt * 32 + g * 8 + half * 4;
-          const f32x4 os = *reinterpret_cast<const f32x4*>(ws + d0);
-          bf16x4 wo, wr;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float od = o[dt][g * 4 + e] * inv;
-            wo[e] = (bf16_t)od;
-            wr[e] = (bf16_t)(od - os[e]);
-          }
-          *reinterpret_cast<bf16x4*>(dst + d0) = wo;
-          *reinterpret_cast<bf16x4*>(rdst + d0) = wr;
-        }
-      }
-    }
-    return;
-  }
-
-  if (qrow < p.N) {
-    bf16_t* dst = p.out + base + (int64_t)qrow * p.st.n;
-    const bool has_res = MODE == kSparse && p.res != nullptr;
-    const bf16_t* rsrc = has_res ? p.res + base + (int64_t)qrow * p.st.n : nullptr;
-    const float c = p.res_scale.v[h];
+    const float* od = p.od_ws + ((int64_t)bh * p.npad + qrow) * D;
+    const bool all_kept = nlist == p.M;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d0 = dt * 32 + g * 8 + half * 4;
-        float v[4];
+        const f32x4 dv = *reinterpret_cast<const f32x4*>(od + d0);
+        bf16x4 wr;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = o[dt][g * 4 + e] * inv;
-        if (has_res) {
-          const bf16x4 r4 = *reinterpret_cast<const bf16x4*>(rsrc + d0);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] += c * (float)r4[e];
-        }
-        bf16x4 w;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = (bf16_t)v[e];
-        *reinterpret_cast<bf16x4*>(dst + d0) = w;
+        for (int e = 0; e < 4; ++e) wr[e] = all_kept ? (bf16_t)0.0f : (bf16_t)(dv[e] - o[dt][g * 4 + e] * inv);
+        *reinterpret_cast<bf16x4*>(p.res_out + orow + d0) = wr;
       }
+    }
+    return;
+  }
+
+  bf16_t* dst = p.out + orow;
+  const bool has_res = MODE == kSparse && p.res != nullptr;
+  const bf16_t* rsrc = has_res ? p.res + orow : nullptr;
+  const float c = p.res_scale.v[h];
+  float* odw = (MODE == kDense && p.od_ws != nullptr)
+                   ? p.od_ws + ((int64_t)bh * p.npad + qrow) * D : nullptr;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d0 = dt * 32 + g * 8 + half * 4;
+      f32x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = o[dt][g * 4 + e] * inv;
+      if (odw != nullptr) *reinterpret_cast<f32x4*>(odw + d0) = v;
+      if (has_res) {
+        const bf16x4 r4 = *reinterpret_cast<const bf16x4*>(rsrc + d0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] += c * (float)r4[e];
+      }
+      bf16x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = (bf16_t)v[e];
+      *reinterpret_cast<bf16x4*>(dst + d0) = w;
     }
   }
 }
@@ -508,17 +467,21 @@ static void launch_mode(const AttnParams& p, int grid, AttnMode mode, hipStream_
   switch (mode) {
     case kSparse: attn_kernel<D, NW, kSparse><<<grid, NW * 64, 0, stream>>>(p); break;
     case kDense: attn_kernel<D, NW, kDense><<<grid, NW * 64, 0, stream>>>(p); break;
-    case kCapture: attn_kernel<D, NW, kCapture><<<grid, NW * 64, 0, stream>>>(p); break;
+    case kCaptureR: attn_kernel<D, NW, kCaptureR><<<grid, NW * 64, 0, stream>>>(p); break;
   }
 }
 
-hipError_t launch_attention(const AttnParams& p, int B, int D, AttnMode mode, hipStream_t stream) {
-  const int grid = B * p.H * p.M;
+// Dense work-groups always cover 128 query rows (4 wavefronts sharing every K/V tile); the
+// list modes cover one query block (block / 32 wavefronts).
+hipError_t launch_attention(AttnParams p, int B, int D, AttnMode mode, hipStream_t stream) {
+  const int nw = mode == kDense ? 4 : p.block / 32;
+  p.mq = mode == kDense ? (p.N + 127) / 128 : p.M;
+  const int grid = B * p.H * p.mq;
   if (D == 128) {
-    if (p.block == 64) launch_mode<128, 2>(p, grid, mode, stream);
+    if (nw == 2) launch_mode<128, 2>(p, grid, mode, stream);
     else launch_mode<128, 4>(p, grid, mode, stream);
   } else {
-    if (p.block == 64) launch_mode<64, 2>(p, grid, mode, stream);
+    if (nw == 2) launch_mode<64, 2>(p, grid, mode, stream);
     else launch_mode<64, 4>(p, grid, mode, stream);
   }
   return hipGetLastError();

@@ -46,7 +46,7 @@ hipError_t launch_topp(const float* probs, int B, int H, int M, const HeadScalar
 hipError_t launch_pack_vt(const bf16_t* v, Strides st, int B, int H, int N, int D, int npad,
                           bf16_t* vt, hipStream_t stream);
 
-enum AttnMode { kSparse = 0, kDense = 1, kCapture = 2 };
+enum AttnMode { kSparse = 0, kDense = 1, kCaptureR = 2 };
 
 struct AttnParams {
   const bf16_t* q;
@@ -54,16 +54,17 @@ struct AttnParams {
   const bf16_t* vt;  // packed V^T [B*H][D][npad]
   Strides st;
   int H, N, M, block, npad;
+  int mq;  // query tiles per (b, h); set by launch_attention
   float scale_log2;
   const int32_t* count;  // [B*H*M]
   const int32_t* idx;    // [B*H*M*M]
   const bf16_t* res;     // optional residual (sparse mode)
   bf16_t* out;
-  bf16_t* res_out;  // capture mode
-  float* os_ws;     // capture mode: fp32 sparse snapshot [B*H][npad][D]
+  bf16_t* res_out;  // capture: residual output
+  float* od_ws;     // capture: fp32 dense output [B*H][npad][D] (written by kDense, read by kCaptureR)
   HeadScalars res_scale;
 };
 
-hipError_t launch_attention(const AttnParams& p, int B, int D, AttnMode mode, hipStream_t stream);
+hipError_t launch_attention(AttnParams p, int B, int D, AttnMode mode, hipStream_t stream);
 
 }  // namespace recap

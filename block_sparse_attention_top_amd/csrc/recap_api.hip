@@ -292,8 +292,10 @@ int recap_dense_attn(const recap_desc* d, const void* q, const void* k, const vo
   p.idx = kept_idx_opt;
   p.out = (bf16_t*)out;
   p.res_out = (bf16_t*)residual_out_opt;
-  p.os_ws = capture ? (float*)((char*)ws + vt_bytes(d)) : nullptr;
-  return launched(launch_attention(p, d->batch, d->head_dim, capture ? kCapture : kDense, st));
+  p.od_ws = capture ? (float*)((char*)ws + vt_bytes(d)) : nullptr;
+  e = launch_attention(p, d->batch, d->head_dim, kDense, st);
+  if (e == hipSuccess && capture) e = launch_attention(p, d->batch, d->head_dim, kCaptureR, st);
+  return launched(e);
 }
 
 }  // extern "C"

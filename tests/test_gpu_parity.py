@@ -134,7 +134,10 @@ def test_all_kept_capture_is_exactly_zero(bsa):
     torch.cuda.synchronize()
     assert torch.count_nonzero(rcap).item() == 0
     out = bsa.recap_block_sparse_attn(desc, qd, kd, vd, count, idx)
-    assert torch.equal(out, od)
+    torch.cuda.synchronize()
+    # the same attention in a different key order; each is within the parity bound of the
+    # oracle (checked in the small cases), so they are within twice that bound of each other
+    assert (out.float() - od.float()).abs().max().item() <= 2 * parity.ATOL_OUT
 
 
 def test_deterministic_poison_and_guards(bsa):
