@@ -28,6 +28,7 @@
 namespace recap {
 
 typedef const __attribute__((address_space(4))) int32_t* cptr_i32;
+typedef const __attribute__((address_space(4))) uint8_t* cptr_u8;
 
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -240,13 +241,23 @@ __device__ __forceinline__ float cross_half_sum(float x) {
 }
 
 // One attention phase over a block sequence, continuing the online-softmax state (m, l, o).
-template <int D, int NW, class Seq>
+// Residual-capture side state: a second accumulator that sees only the kept key blocks of this
+// wavefront's query block (bitmap in LDS). It shares the running max and the probabilities of
+// the dense accumulator, so it costs only the extra PV products of kept tiles.
+template <int D>
+struct KeptAcc {
+  f32x16 o[D / 32];
+  float l;
+  const uint32_t* bits;
+};
+
+template <int D, int NW, bool CAP, class Seq>
 __device__ __forceinline__ void attend_phase(Seq& seq, unsigned char* kbuf, unsigned char* vbuf,
                                              const bf16_t* kp, const bf16_t* vtp, int64_t sn,
                                              int N, int block, int npad, float scale_log2,
                                              const bf16x8 (&qf)[D / 16], f32x16 (&o)[D / 32],
                                              SoftmaxState& sm, int wave, int lane,
-                                             const LaneConsts<D, NW>& lc) {
+                                             const LaneConsts<D, NW>& lc, KeptAcc<D>& ka) {
   constexpr int ROWB = Tiles<D, NW>::ROWB, LD = Tiles<D, NW>::LD;
   const int half = lane >> 5;
   int j = seq.first();
@@ -300,6 +311,11 @@ __device__ __forceinline__ void attend_phase(Seq& seq, unsigned char* kbuf, unsi
       sm.l *= alpha;
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) o[dt] *= alpha;
+      if (CAP) {
+        ka.l *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) ka.o[dt] *= alpha;
+      }
     }
     const float neg_m = -sm.m;
     bf16x8 pf[4];
@@ -312,10 +328,11 @@ __device__ __forceinline__ void attend_phase(Seq& seq, unsigned char* kbuf, unsi
       }
     }
     // row sum of the bf16-rounded probabilities (the ones the PV product uses)
+    float tile_sum;
     {
       typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
       const bf16x2 one = {(bf16_t)1.0f, (bf16_t)1.0f};
-      float acc = sm.l;
+      float acc = 0.f;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
@@ -324,8 +341,11 @@ __device__ __forceinline__ void attend_phase(Seq& seq, unsigned char* kbuf, unsi
           acc = __builtin_amdgcn_fdot2_f32_bf16(pr, one, acc, false);
         }
       }
-      sm.l = acc;
+      sm.l += acc;
+      tile_sum = acc;
     }
+    const bool kept = CAP && ((ka.bits[j >> 5] >> (j & 31)) & 1u);  // uniform per wavefront
+    if (kept) ka.l += tile_sum;
 
     // ---- O^T += V^T P^T ----
     if (has_next) wait_vmem<LD>(); else wait_vmem<0>();  // V^T(t) landed (K(t+1) may not)
@@ -337,6 +357,7 @@ __device__ __forceinline__ void attend_phase(Seq& seq, unsigned char* kbuf, unsi
       for (int dt = 0; dt < D / 32; ++dt) {
         const bf16x8 va = *reinterpret_cast<const bf16x8*>(vbuf + a + dt * 4096);
         o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[ks], o[dt], 0, 0, 0);
+        if (kept) ka.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[ks], ka.o[dt], 0, 0, 0);
       }
     }
     lds_barrier();  // every wave is done reading the V buffer
@@ -382,23 +403,96 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   for (int dt = 0; dt < D / 32; ++dt) o[dt] = f32x16{};
   SoftmaxState sm{-INFINITY, 0.f};
 
+  constexpr bool CAP = MODE == kDenseCapture;
+  constexpr int BLKS = CAP ? (QROWS / 64) : 1;  // query blocks of this work-group (block 64: 2)
+  __shared__ uint32_t kept_bits[CAP ? BLKS : 1][CAP ? kMaxBlocks / 32 : 1];
+  __shared__ int blk_flag[BLKS];
+  KeptAcc<D> ka;
+  int qb = 0;  // this wavefront's query block (capture mode)
+  if (CAP) {
+    // kept-block bitmaps of the query blocks covered by this work-group
+    const int nb = QROWS / p.block;  // 2 for block 64, 1 for block 128
+    qb = (qi * QROWS + wave * 32) / p.block;
+    for (int w = threadIdx.x; w < nb * ((p.M + 31) / 32); w += NW * 64)
+      kept_bits[w / ((p.M + 31) / 32)][w % ((p.M + 31) / 32)] = 0u;
+    if (threadIdx.x < BLKS) blk_flag[threadIdx.x] = 0;
+    __syncthreads();
+    for (int lb = 0; lb < nb; ++lb) {
+      const int blk = (qi * QROWS) / p.block + lb;
+      if (blk >= p.M) break;
+      const int64_t row = (int64_t)bh * p.M + blk;
+      const int cnt = min(max(p.count[row], 0), p.M);
+      for (int c = threadIdx.x; c < cnt; c += NW * 64) {
+        const int jj = min(max(p.idx[row * p.M + c], 0), p.M - 1);
+        atomicOr(&kept_bits[lb][jj >> 5], 1u << (jj & 31));
+      }
+    }
+    __syncthreads();
+    ka.bits = kept_bits[(wave * 32) / p.block];
+    ka.l = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) ka.o[dt] = f32x16{};
+  }
+
   int nlist = 0;
-  if (MODE == kDense) {
+  if (MODE == kDense || CAP) {
     // staggered start at the diagonal: neighbouring work-groups stream the same K/V tiles at
     // nearly the same time, which keeps them in L2
     AllSeq seq{0, p.M, min((qi * QROWS) / p.block, p.M - 1)};
-    attend_phase<D, NW>(seq, kbuf, vbuf, kp, vtp, p.st.n, p.N, p.block, p.npad, p.scale_log2, qf,
-                        o, sm, wave, lane, lc);
+    attend_phase<D, NW, CAP>(seq, kbuf, vbuf, kp, vtp, p.st.n, p.N, p.block, p.npad,
+                             p.scale_log2, qf, o, sm, wave, lane, lc, ka);
   } else {
     const int32_t* lst = p.idx + (int64_t)tile * p.M;
     nlist = min(max(((cptr_i32)p.count)[tile], 0), p.M);
+    if (MODE == kCaptureR && ((cptr_u8)p.flags)[tile] == 0) return;  // done in the dense pass
     ListSeq seq{lst, nlist, 0, p.M};
-    attend_phase<D, NW>(seq, kbuf, vbuf, kp, vtp, p.st.n, p.N, p.block, p.npad, p.scale_log2, qf,
-                        o, sm, wave, lane, lc);
+    attend_phase<D, NW, false>(seq, kbuf, vbuf, kp, vtp, p.st.n, p.N, p.block, p.npad,
+                               p.scale_log2, qf, o, sm, wave, lane, lc, ka);
   }
 
   const float lt = cross_half_sum(sm.l);
   const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+
+  if (CAP) {
+    // The kept accumulator shares the dense running max; if its mass underflowed (kept keys
+    // more than ~2^6 binary orders below the dense maximum) the block is left to the
+    // residual pass, which recomputes the sparse output with its own maximum.
+    const float ls = cross_half_sum(ka.l);
+    const bool bad = qrow < p.N && !(ls >= 0x1p-64f);
+    if (__builtin_amdgcn_ballot_w64(bad) != 0 && lane == 0) atomicOr(&blk_flag[(wave * 32) / p.block], 1);
+    __syncthreads();
+    const bool flagged = blk_flag[(wave * 32) / p.block] != 0;
+    if (qb < p.M && lane == 0 && (wave * 32) % p.block == 0)
+      p.flags[(int64_t)bh * p.M + qb] = flagged ? 1 : 0;
+    if (qrow >= p.N) return;
+    const int64_t orow = base + (int64_t)qrow * p.st.n;
+    const float invs = ls > 0.f ? 1.0f / ls : 0.f;
+    float* odw = p.od_ws + ((int64_t)bh * p.npad + qrow) * D;
+    {
+#pragma clang fp contract(off)
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = dt * 32 + g * 8 + half * 4;
+        f32x4 vd;
+        bf16x4 wo, wr;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          vd[e] = o[dt][g * 4 + e] * inv;
+          const float vs = ka.o[dt][g * 4 + e] * invs;
+          wo[e] = (bf16_t)vd[e];
+          wr[e] = (bf16_t)(vd[e] - vs);
+        }
+        *reinterpret_cast<bf16x4*>(p.out + orow + d0) = wo;
+        if (flagged) *reinterpret_cast<f32x4*>(odw + d0) = vd;
+        else *reinterpret_cast<bf16x4*>(p.res_out + orow + d0) = wr;
+      }
+    }
+    }
+    return;
+  }
+
   if (qrow >= p.N) return;
   const int64_t orow = base + (int64_t)qrow * p.st.n;
 
@@ -464,18 +558,21 @@ hipError_t launch_pack_vt(const bf16_t* v, Strides st, int B, int H, int N, int 
 
 template <int D, int NW>
 static void launch_mode(const AttnParams& p, int grid, AttnMode mode, hipStream_t stream) {
-  switch (mode) {
-    case kSparse: attn_kernel<D, NW, kSparse><<<grid, NW * 64, 0, stream>>>(p); break;
-    case kDense: attn_kernel<D, NW, kDense><<<grid, NW * 64, 0, stream>>>(p); break;
-    case kCaptureR: attn_kernel<D, NW, kCaptureR><<<grid, NW * 64, 0, stream>>>(p); break;
+  if constexpr (NW == 4) {  // dense modes always run 4-wavefront work-groups
+    if (mode == kDense) return (void)(attn_kernel<D, 4, kDense><<<grid, 256, 0, stream>>>(p));
+    if (mode == kDenseCapture)
+      return (void)(attn_kernel<D, 4, kDenseCapture><<<grid, 256, 0, stream>>>(p));
   }
+  if (mode == kSparse) attn_kernel<D, NW, kSparse><<<grid, NW * 64, 0, stream>>>(p);
+  if (mode == kCaptureR) attn_kernel<D, NW, kCaptureR><<<grid, NW * 64, 0, stream>>>(p);
 }
 
 // Dense work-groups always cover 128 query rows (4 wavefronts sharing every K/V tile); the
 // list modes cover one query block (block / 32 wavefronts).
 hipError_t launch_attention(AttnParams p, int B, int D, AttnMode mode, hipStream_t stream) {
-  const int nw = mode == kDense ? 4 : p.block / 32;
-  p.mq = mode == kDense ? (p.N + 127) / 128 : p.M;
+  const bool dense = mode == kDense || mode == kDenseCapture;
+  const int nw = dense ? 4 : p.block / 32;
+  p.mq = dense ? (p.N + 127) / 128 : p.M;
   const int grid = B * p.H * p.mq;
   if (D == 128) {
     if (nw == 2) launch_mode<128, 2>(p, grid, mode, stream);

@@ -13,6 +13,7 @@ typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 
 constexpr int kMaxHeads = 128;
+constexpr int kMaxBlocks = 8192;  // M upper bound (include/recap.h RECAP_MAX_BLOCKS)
 constexpr int kKeyTile = 64;  // keys per attention inner-loop tile
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -46,7 +47,7 @@ hipError_t launch_topp(const float* probs, int B, int H, int M, const HeadScalar
 hipError_t launch_pack_vt(const bf16_t* v, Strides st, int B, int H, int N, int D, int npad,
                           bf16_t* vt, hipStream_t stream);
 
-enum AttnMode { kSparse = 0, kDense = 1, kCaptureR = 2 };
+enum AttnMode { kSparse = 0, kDense = 1, kCaptureR = 2, kDenseCapture = 3 };
 
 struct AttnParams {
   const bf16_t* q;
@@ -61,7 +62,8 @@ struct AttnParams {
   const bf16_t* res;     // optional residual (sparse mode)
   bf16_t* out;
   bf16_t* res_out;  // capture: residual output
-  float* od_ws;     // capture: fp32 dense output [B*H][npad][D] (written by kDense, read by kCaptureR)
+  float* od_ws;     // capture: fp32 dense output [B*H][npad][D] of blocks left to the residual pass
+  uint8_t* flags;   // capture: [B*H*M] 1 = residual of this query block left to the residual pass
   HeadScalars res_scale;
 };
 

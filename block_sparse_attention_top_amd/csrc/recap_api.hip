@@ -63,13 +63,17 @@ size_t snapshot_bytes(const recap_desc* d) {
   return align_up((size_t)d->batch * d->heads * npad * d->head_dim * sizeof(float));
 }
 
+size_t flag_bytes(const recap_desc* d) {
+  return align_up((size_t)d->batch * d->heads * num_blocks(d));
+}
+
 size_t workspace_for(int op, const recap_desc* d) {
   switch (op) {
     case RECAP_OP_BLOCK_SCORES: return 2 * pooled_bytes(d);
     case RECAP_OP_TOPP: return 0;
     case RECAP_OP_SPARSE:
     case RECAP_OP_DENSE: return vt_bytes(d);
-    case RECAP_OP_DENSE_CAPTURE: return vt_bytes(d) + snapshot_bytes(d);
+    case RECAP_OP_DENSE_CAPTURE: return vt_bytes(d) + snapshot_bytes(d) + flag_bytes(d);
     default: return 0;
   }
 }
@@ -293,7 +297,10 @@ int recap_dense_attn(const recap_desc* d, const void* q, const void* k, const vo
   p.out = (bf16_t*)out;
   p.res_out = (bf16_t*)residual_out_opt;
   p.od_ws = capture ? (float*)((char*)ws + vt_bytes(d)) : nullptr;
-  e = launch_attention(p, d->batch, d->head_dim, kDense, st);
+  p.flags = capture ? (uint8_t*)ws + vt_bytes(d) + snapshot_bytes(d) : nullptr;
+  // capture: the dense pass also accumulates the kept blocks and writes R; the residual pass
+  // only recomputes query blocks the dense pass flagged (kept mass underflow), others exit
+  e = launch_attention(p, d->batch, d->head_dim, capture ? kDenseCapture : kDense, st);
   if (e == hipSuccess && capture) e = launch_attention(p, d->batch, d->head_dim, kCaptureR, st);
   return launched(e);
 }

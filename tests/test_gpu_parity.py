@@ -140,6 +140,36 @@ def test_all_kept_capture_is_exactly_zero(bsa):
     assert (out.float() - od.float()).abs().max().item() <= 2 * parity.ATOL_OUT
 
 
+def test_capture_when_kept_mass_underflows(bsa):
+    """A kept list that leaves out a key block whose logits exceed everything else by far more
+    than fp32 range: the dense pass's shared-maximum accumulator for the kept blocks underflows,
+    so the residual must come from the per-block fallback pass."""
+    say("[test] capture fallback (kept mass underflow)")
+    B, H, N, D, blk = 1, 1, 64 * 6, 64, 64
+    g = torch.Generator().manual_seed(5)
+    q = torch.ones((B, H, N, D))
+    k = 0.1 * torch.randn((B, H, N, D), generator=g)
+    k[:, :, :64] = 20.0  # block 0: logits ~ 160 (about 230 binary orders above the rest)
+    v = torch.randn((B, H, N, D), generator=g)
+    q, k, v = (x.to(torch.bfloat16) for x in (q, k, v))
+    qd, kd, vd = (to_dev(x) for x in (q, k, v))
+    desc = bsa.make_desc(qd, blk)
+    M = N // blk
+    count = torch.full((B, H, M), 2, dtype=torch.int32, device=DEV)
+    idx = torch.zeros((B, H, M, M), dtype=torch.int32, device=DEV)
+    idx[..., 0], idx[..., 1] = 2, 4  # kept: blocks 2 and 4 (block 0 left out)
+    od, rcap = bsa.recap_dense_attn(desc, qd, kd, vd, None, count, idx, capture=True)
+    torch.cuda.synchronize()
+    q64, k64, v64 = (synth.to_f64(x) for x in (q, k, v))
+    mask = np.zeros((B, H, M, M), bool)
+    mask[..., [2, 4]] = True
+    s = D ** -0.5
+    ref_d = O.dense_attention(q64, k64, v64, s, block=blk)
+    ref_s = O.masked_attention(q64, k64, v64, blk, s, mask)
+    parity.check_out(f64(od), ref_d, "dense")
+    parity.check_out(f64(rcap), ref_d - ref_s, "residual")
+
+
 def test_deterministic_poison_and_guards(bsa):
     say("[test] determinism, NaN poison, guard bands")
     cfg = synth.workload("tiny", heads=2, head_dim=128, grid=(1, 1, 1333))
