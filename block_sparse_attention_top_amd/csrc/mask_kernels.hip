@@ -321,6 +321,118 @@ __global__ __launch_bounds__(256) void topp_kernel(const float* __restrict__ pro
 }
 
 // ------------------------------------------------------------------------------------------
+// Top-p, one wavefront per row (rows of up to 64 * VPL blocks). The row stays in registers
+// (lane l holds blocks l, l+64, ...). Probabilities are non-negative, so their fp32 bit
+// patterns order like their values; a binary search over bit patterns finds the k*-th largest
+// value v* = the largest value t with mass(>= t) >= p (mass accumulated in fp64). Every block
+// above v* is kept; blocks equal to v* are taken in ascending index order until the running
+// mass reaches p. This is the same set as sorting by (probability desc, index asc) and
+// keeping the shortest prefix whose mass reaches p. No LDS, no barriers.
+// ------------------------------------------------------------------------------------------
+__device__ __forceinline__ double wave_sum(double x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+  return x;
+}
+
+template <int VPL>
+__global__ __launch_bounds__(256) void topp_wave_kernel(const float* __restrict__ probs, int H,
+                                                        int M, int rows, HeadScalars top_p,
+                                                        int32_t* __restrict__ count,
+                                                        int32_t* __restrict__ idx,
+                                                        uint8_t* __restrict__ mask,
+                                                        float* __restrict__ mass) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;  // the whole wavefront
+  const int h = (row / M) % H;
+  const float p = top_p.v[h];
+  const float* pr = probs + (int64_t)row * M;
+  uint32_t u[VPL];
+  float val[VPL];
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    const int j = i * 64 + lane;
+    const float x = j < M ? pr[j] : 0.f;
+    val[i] = x > 0.f ? x : 0.f;  // probabilities are >= 0; -0 and NaN map to 0
+    u[i] = j < M ? __float_as_uint(val[i]) : 0xffffffffu;  // padding: never >= a finite t
+  }
+  auto mass_at_least = [&](uint32_t t) {
+    double acc = 0.0;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i)
+      if (u[i] >= t && u[i] != 0xffffffffu) acc += (double)val[i];
+    return wave_sum(acc);
+  };
+
+  bool kept[VPL];
+  double kmass;
+  const double total = mass_at_least(0u);
+  if (p >= 1.0f || total < (double)p) {
+    // p >= 1, or rounding left the total below p: every block is kept
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) kept[i] = u[i] != 0xffffffffu;
+    kmass = total;
+  } else {
+    // largest t with mass(>= t) >= p (p = 0 behaves like the smallest positive mass, so v* is
+    // the maximum and exactly one block is kept)
+    const double target = p > 0.f ? (double)p : 1e-300;
+    uint32_t lo = 0u, hi = 0x7f800000u;  // mass(>= lo) >= target > mass(>= hi)
+    while (hi - lo > 1u) {
+      const uint32_t mid = lo + ((hi - lo) >> 1);
+      if (mass_at_least(mid) >= target) lo = mid; else hi = mid;
+    }
+    const uint32_t T = lo;
+    const float vstar = __uint_as_float(T);
+    double c = 0.0;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i)
+      if (u[i] > T && u[i] != 0xffffffffu) c += (double)val[i];
+    c = wave_sum(c);
+    // ties at v*, ascending index: position (i, lane) is index i*64 + lane
+    int need = 0;  // number of tie blocks to keep
+    {
+      double cc = c;
+      bool done = false;
+      for (int i = 0; i < VPL && !done; ++i) {
+        uint64_t m = __builtin_amdgcn_ballot_w64(u[i] == T);
+        while (m != 0ull) {
+          cc += (double)vstar;
+          ++need;
+          m &= m - 1ull;
+          if (cc >= (double)p) { done = true; break; }
+        }
+      }
+      kmass = cc;
+    }
+    int seen = 0;  // tie blocks before the current group of 64
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      const bool eq = u[i] == T;
+      const uint64_t m = __builtin_amdgcn_ballot_w64(eq);
+      const int rank = seen + (int)__builtin_popcountll(m & ((1ull << lane) - 1ull));
+      kept[i] = (u[i] > T && u[i] != 0xffffffffu) || (eq && rank < need);
+      seen += (int)__builtin_popcountll(m);
+    }
+  }
+
+  // ascending compaction, optional byte mask
+  int32_t* out_idx = idx + (int64_t)row * M;
+  int base = 0;
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    const uint64_t m = __builtin_amdgcn_ballot_w64(kept[i]);
+    if (kept[i]) out_idx[base + (int)__builtin_popcountll(m & ((1ull << lane) - 1ull))] = i * 64 + lane;
+    base += (int)__builtin_popcountll(m);
+    if (mask != nullptr && i * 64 + lane < M) mask[(int64_t)row * M + i * 64 + lane] = kept[i] ? 1 : 0;
+  }
+  if (lane == 0) {
+    count[row] = base;
+    if (mass != nullptr) mass[row] = (float)kmass;
+  }
+}
+
+// ------------------------------------------------------------------------------------------
 hipError_t launch_pool(const bf16_t* q, const bf16_t* k, Strides st, int B, int H, int N, int D,
                        int block, float* qbar, float* kbar, hipStream_t stream) {
   const int M = (N + block - 1) / block;
@@ -346,6 +458,25 @@ hipError_t launch_scores(const float* qbar, const float* kbar, int BH, int M, in
 hipError_t launch_topp(const float* probs, int B, int H, int M, const HeadScalars& top_p,
                        int32_t* count, int32_t* idx, uint8_t* mask, float* mass,
                        hipStream_t stream) {
+  const int rows = B * H * M;
+  const int grid = (rows + 3) / 4;
+  if (M <= 512) {
+    topp_wave_kernel<8><<<grid, 256, 0, stream>>>(probs, H, M, rows, top_p, count, idx, mask, mass);
+    return hipGetLastError();
+  }
+  if (M <= 1024) {
+    topp_wave_kernel<16><<<grid, 256, 0, stream>>>(probs, H, M, rows, top_p, count, idx, mask, mass);
+    return hipGetLastError();
+  }
+  if (M <= 1536) {
+    topp_wave_kernel<24><<<grid, 256, 0, stream>>>(probs, H, M, rows, top_p, count, idx, mask, mass);
+    return hipGetLastError();
+  }
+  if (M <= 2048) {
+    topp_wave_kernel<32><<<grid, 256, 0, stream>>>(probs, H, M, rows, top_p, count, idx, mask, mass);
+    return hipGetLastError();
+  }
+  // longer rows: one work-group per row, bitonic sort in LDS
   int P = 64;
   while (P < M) P <<= 1;
   const size_t lds = (size_t)P * 9;

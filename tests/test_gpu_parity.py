@@ -170,6 +170,46 @@ def test_capture_when_kept_mass_underflows(bsa):
     parity.check_out(f64(rcap), ref_d - ref_s, "residual")
 
 
+@pytest.mark.parametrize("m", [16, 100, 700, 1182, 2000, 2100])
+def test_topp_exact_ties(bsa, m):
+    """Hand-made probability rows with exact ties (dyadic values, so every running mass is
+    exact): the kept sets must equal the oracle's exactly, tie order included. Row lengths
+    cover each register-resident variant and the sorting fallback for long rows."""
+    say(f"[test] top-p exact ties, M={m}")
+    H, rows = 2, []
+    g = np.random.default_rng(m)
+    for r in range(m):
+        kind = r % 4
+        row = np.zeros(m)
+        if kind == 0:  # uniform
+            row[:] = 1.0 / m
+        elif kind == 1:  # a few equal large blocks at random places, the rest equal and small
+            big = g.choice(m, size=min(4, m), replace=False)
+            row[:] = 0.0
+            row[big] = 0.125
+            rest = np.setdiff1d(np.arange(m), big)
+            row[rest] = 0.5 / len(rest)
+        elif kind == 2:  # geometric with repeated pairs
+            vals = 0.5 ** (1 + np.arange(m) // 2)
+            row[g.permutation(m)] = vals
+        else:  # one dominant block
+            row[:] = 2.0 ** -20
+            row[g.integers(m)] = 1.0 - (m - 1) * 2.0 ** -20
+        rows.append(row.astype(np.float32))
+    probs = np.stack(rows)[None, None].repeat(H, axis=1)  # [1, H, M, M]
+    for p in ([0.0, 0.25], [0.5, 0.75], [0.9, 1.0], [0.3333, 0.999]):
+        desc = bsa.RecapDesc(1, H, m * 64, 64, 64, 0, H * m * 64 * 64, m * 64 * 64, 64)
+        pd = torch.from_numpy(probs).to(DEV)
+        count, idx, mask, mass = bsa.recap_topp_mask(desc, pd, p, want_mask=True, want_mass=True)
+        torch.cuda.synchronize()
+        ref = O.topp_select(probs.astype(np.float64), np.array(p, dtype=np.float32).astype(np.float64))
+        gm = mask.cpu().numpy().astype(bool)
+        assert np.array_equal(gm, ref["mask"]), (p, np.argwhere((gm != ref["mask"]).any(-1))[:5])
+        assert np.array_equal(count.cpu().numpy(), ref["count"])
+        parity.check_lists(count.cpu().numpy(), idx.cpu().numpy(), m, gm)
+        assert np.allclose(mass.cpu().numpy(), ref["mass"], rtol=1e-6, atol=1e-7)
+
+
 def test_deterministic_poison_and_guards(bsa):
     say("[test] determinism, NaN poison, guard bands")
     cfg = synth.workload("tiny", heads=2, head_dim=128, grid=(1, 1, 1333))
