@@ -25,7 +25,32 @@
 // the load of the next V^T tile overlaps the next QK^T.
 #include "common.h"
 
+// Build-time pipeline choices (defaults are the measured best on MI355X):
+//   RECAP_STAGES4   LDS stages of the 4-wavefront (128-row) work-groups: 1 or 2
+//   RECAP_PAIR      sparse calls with 64-row blocks run two query blocks per work-group
+//   RECAP_PRIO      raise the wavefront priority around MFMA bursts
+#ifndef RECAP_STAGES4
+#define RECAP_STAGES4 2
+#endif
+#ifndef RECAP_PAIR
+#define RECAP_PAIR 1
+#endif
+#ifndef RECAP_PRIO
+#define RECAP_PRIO 0
+#endif
+
 namespace recap {
+
+__device__ __forceinline__ void mfma_prio_hi() {
+#if RECAP_PRIO
+  __builtin_amdgcn_s_setprio(1);
+#endif
+}
+__device__ __forceinline__ void mfma_prio_lo() {
+#if RECAP_PRIO
+  __builtin_amdgcn_s_setprio(0);
+#endif
+}
 
 typedef const __attribute__((address_space(4))) int32_t* cptr_i32;
 typedef const __attribute__((address_space(4))) uint8_t* cptr_u8;
@@ -125,6 +150,23 @@ struct AllSeq {  // every block once, starting at `start` and wrapping around
     const int j = start + c;
     return j >= M ? j - M : j;
   }
+};
+
+struct UnionSeq {  // blocks set in either of two LDS bitmaps, ascending
+  const uint32_t* a;
+  const uint32_t* b;
+  int M, j;
+  __device__ int scan(int from) {
+    const int nw = (M + 31) >> 5;
+    for (int w = from >> 5; w < nw; ++w) {
+      uint32_t m = a[w] | b[w];
+      if (w == (from >> 5)) m &= ~0u << (from & 31);
+      if (m != 0u) return w * 32 + __builtin_ctz(m);
+    }
+    return -1;
+  }
+  __device__ int first() { j = scan(0); return j; }
+  __device__ int next() { j = j + 1 < M ? scan(j + 1) : -1; return j; }
 };
 
 template <int D, int NW>
@@ -240,7 +282,6 @@ __device__ __forceinline__ float cross_half_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// One attention phase over a block sequence, continuing the online-softmax state (m, l, o).
 // Residual-capture side state: a second accumulator that sees only the kept key blocks of this
 // wavefront's query block (bitmap in LDS). It shares the running max and the probabilities of
 // the dense accumulator, so it costs only the extra PV products of kept tiles.
@@ -251,127 +292,202 @@ struct KeptAcc {
   const uint32_t* bits;
 };
 
-template <int D, int NW, bool CAP, class Seq>
+// ---- per-tile math, shared by the pipeline drivers below ----
+
+// S^T = K Q^T for one 64-key tile in LDS (raw dot products).
+template <int D, int NW>
+__device__ __forceinline__ void tile_qk(const unsigned char* kb, const bf16x8 (&qf)[D / 16],
+                                        const LaneConsts<D, NW>& lc, f32x16& s0, f32x16& s1) {
+  constexpr int ROWB = Tiles<D, NW>::ROWB;
+  s0 = f32x16{};
+  s1 = f32x16{};
+  mfma_prio_hi();
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    const uint32_t a = lc.k_rd ^ (uint32_t)(ks << 5);
+    const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kb + a);
+    const bf16x8 kb2 = *reinterpret_cast<const bf16x8*>(kb + a + 32 * ROWB);
+    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb2, qf[ks], s1, 0, 0, 0);
+  }
+  mfma_prio_lo();
+}
+
+// Online softmax of one tile in the base-2 domain with lazy rescale; returns the bf16 P^T
+// operands and whether the tile also feeds the kept-block accumulator.
+template <int D, bool CAP>
+__device__ __forceinline__ bool tile_softmax(f32x16& s0, f32x16& s1, int j, int key0, int N,
+                                             float scale_log2, int half, f32x16 (&o)[D / 32],
+                                             SoftmaxState& sm, KeptAcc<D>& ka, bf16x8 (&pf)[4]) {
+  if (key0 + kKeyTile > N) {
+    asm volatile("" ::: "memory");  // keep the rare tail tile a real (uniform) branch
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int kr = ((r >> 2) << 3) + half * 4 + (r & 3);
+      if (key0 + kr >= N) s0[r] = -INFINITY;
+      if (key0 + 32 + kr >= N) s1[r] = -INFINITY;
+    }
+  }
+  float mx = max3(s0[0], s1[0], s0[1]);
+#pragma unroll
+  for (int r = 1; r < 16; ++r) mx = max3(mx, s1[r], r + 1 < 16 ? s0[r + 1] : s1[r]);
+  const float mt = cross_half_max(mx) * scale_log2;  // finite: a tile has a valid key
+  if (__builtin_amdgcn_ballot_w64(mt > sm.m + kLazy) != 0) {
+    const float mn = fmaxf(sm.m, mt);
+    const float alpha = __builtin_amdgcn_exp2f(sm.m - mn);
+    sm.m = mn;
+    sm.l *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) o[dt] *= alpha;
+    if (CAP) {
+      ka.l *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) ka.o[dt] *= alpha;
+    }
+  }
+  const float neg_m = -sm.m;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float x = (ks < 2) ? s0[(ks & 1) * 8 + e] : s1[(ks & 1) * 8 + e];
+      pf[ks][e] = (bf16_t)__builtin_amdgcn_exp2f(__builtin_fmaf(x, scale_log2, neg_m));
+    }
+  }
+  // row sum of the bf16-rounded probabilities (the ones the PV product uses)
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+  const bf16x2 one = {(bf16_t)1.0f, (bf16_t)1.0f};
+  float acc = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const bf16x2 pr = {pf[ks][e], pf[ks][e + 1]};
+      acc = __builtin_amdgcn_fdot2_f32_bf16(pr, one, acc, false);
+    }
+  }
+  sm.l += acc;
+  const bool kept = CAP && ((ka.bits[j >> 5] >> (j & 31)) & 1u);  // uniform per wavefront
+  if (kept) ka.l += acc;
+  return kept;
+}
+
+// O^T += V^T P^T for one tile (and the kept-block accumulator when `kept`).
+template <int D, int NW>
+__device__ __forceinline__ void tile_pv(const unsigned char* vb, const bf16x8 (&pf)[4],
+                                        const LaneConsts<D, NW>& lc, f32x16 (&o)[D / 32],
+                                        KeptAcc<D>& ka, bool kept) {
+  mfma_prio_hi();
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const uint32_t a = lc.v_rd ^ (uint32_t)(ks << 5);
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+      const bf16x8 va = *reinterpret_cast<const bf16x8*>(vb + a + dt * 4096);
+      o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[ks], o[dt], 0, 0, 0);
+      if (kept) ka.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[ks], ka.o[dt], 0, 0, 0);
+    }
+  }
+  mfma_prio_lo();
+}
+
+// Position in a block sequence: key block j (< 0: none) and its 64-key sub-tile st.
+struct TileCur {
+  int j, st;
+};
+template <class Seq>
+__device__ __forceinline__ TileCur advance(TileCur c, Seq& seq, int block, int N) {
+  if (c.j < 0) return c;
+  const int st = c.st + 1;
+  if (st * kKeyTile >= min(block, N - c.j * block)) return TileCur{seq.next(), 0};
+  return TileCur{c.j, st};
+}
+
+// One attention phase over a block sequence, continuing the online-softmax state (m, l, o).
+// STAGES = 1: one K and one V^T buffer; K(t+1) loads during softmax + PV of tile t and
+//             V^T(t+1) during the QK^T of tile t+1 (four barriers per tile).
+// STAGES = 2: two buffers each; tile t+2 loads into the buffers tile t has just released, so
+//             every tile has a full tile of compute to land (two barriers per tile).
+// SKIP: the work-group streams the union of two query blocks' kept sets; each wavefront
+//       computes only the tiles of its own block's kept set (bitmap `own`).
+template <int D, int NW, int STAGES, bool CAP, bool SKIP = false, class Seq>
 __device__ __forceinline__ void attend_phase(Seq& seq, unsigned char* kbuf, unsigned char* vbuf,
                                              const bf16_t* kp, const bf16_t* vtp, int64_t sn,
                                              int N, int block, int npad, float scale_log2,
                                              const bf16x8 (&qf)[D / 16], f32x16 (&o)[D / 32],
                                              SoftmaxState& sm, int wave, int lane,
-                                             const LaneConsts<D, NW>& lc, KeptAcc<D>& ka) {
-  constexpr int ROWB = Tiles<D, NW>::ROWB, LD = Tiles<D, NW>::LD;
+                                             const LaneConsts<D, NW>& lc, KeptAcc<D>& ka,
+                                             const uint32_t* own = nullptr) {
+  constexpr int LD = Tiles<D, NW>::LD, TB = Tiles<D, NW>::TILE_BYTES;
   const int half = lane >> 5;
-  int j = seq.first();
-  if (j < 0) return;
-  int st = 0;
-  issue_k<D, NW>(kbuf, kp, sn, N, j * block, wave, lane, lc);
-  issue_v<D, NW>(vbuf, vtp, npad, j * block, wave, lc);
-  while (true) {
-    const int key0 = j * block + st * kKeyTile;
-    int jn = j, stn = st + 1;
-    if (stn * kKeyTile >= min(block, N - j * block)) {
-      jn = seq.next();
-      stn = 0;
-    }
-    const bool has_next = jn >= 0;
+  TileCur cur{seq.first(), 0};
+  if (cur.j < 0) return;
+  auto issue_both = [&](TileCur t, int buf) {
+    const int key0 = t.j * block + t.st * kKeyTile;
+    issue_k<D, NW>(kbuf + buf * TB, kp, sn, N, key0, wave, lane, lc);
+    issue_v<D, NW>(vbuf + buf * TB, vtp, npad, key0, wave, lc);
+  };
+  auto active_for = [&](int j) { return !SKIP || ((own[j >> 5] >> (j & 31)) & 1u); };
 
-    wait_vmem<LD>();  // this wave's K(t) landed (V^T(t), issued after it, may be in flight)
-    lds_barrier();    // ... and every other wave's
-
-    // ---- S^T = K Q^T (raw dot products) ----
-    f32x16 s0 = {}, s1 = {};
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      const uint32_t a = lc.k_rd ^ (uint32_t)(ks << 5);
-      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kbuf + a);
-      const bf16x8 kb = *reinterpret_cast<const bf16x8*>(kbuf + a + 32 * ROWB);
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb, qf[ks], s1, 0, 0, 0);
-    }
-    lds_barrier();  // every wave is done reading the K buffer
-    if (has_next) issue_k<D, NW>(kbuf, kp, sn, N, jn * block + stn * kKeyTile, wave, lane, lc);
-
-    // ---- online softmax in the base-2 domain, lazy rescale ----
-    if (key0 + kKeyTile > N) {
-      asm volatile("" ::: "memory");  // keep the rare tail tile a real (uniform) branch
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kr = ((r >> 2) << 3) + half * 4 + (r & 3);
-        if (key0 + kr >= N) s0[r] = -INFINITY;
-        if (key0 + 32 + kr >= N) s1[r] = -INFINITY;
+  if constexpr (STAGES == 2) {
+    TileCur nxt = advance(cur, seq, block, N);
+    issue_both(cur, 0);
+    if (nxt.j >= 0) issue_both(nxt, 1);
+    int b = 0;
+    while (true) {
+      const bool has1 = nxt.j >= 0;
+      const TileCur nxt2 = advance(nxt, seq, block, N);
+      // in flight, oldest first: K(t), V(t) [, K(t+1), V(t+1)]
+      if (has1) wait_vmem<2 * LD>(); else wait_vmem<0>();
+      lds_barrier();
+      const int key0 = cur.j * block + cur.st * kKeyTile;
+      if (active_for(cur.j)) {
+        f32x16 s0, s1;
+        tile_qk<D, NW>(kbuf + b * TB, qf, lc, s0, s1);
+        bf16x8 pf[4];
+        const bool kept = tile_softmax<D, CAP>(s0, s1, cur.j, key0, N, scale_log2, half, o, sm, ka, pf);
+        tile_pv<D, NW>(vbuf + b * TB, pf, lc, o, ka, kept);
       }
+      lds_barrier();  // every wave is done with buffers b
+      if (!has1) break;
+      if (nxt2.j >= 0) issue_both(nxt2, b);
+      cur = nxt;
+      nxt = nxt2;
+      b ^= 1;
     }
-    float mx = max3(s0[0], s1[0], s0[1]);
-#pragma unroll
-    for (int r = 1; r < 16; ++r) mx = max3(mx, s1[r], r + 1 < 16 ? s0[r + 1] : s1[r]);
-    const float mt = cross_half_max(mx) * scale_log2;  // finite: a tile has a valid key
-    if (__builtin_amdgcn_ballot_w64(mt > sm.m + kLazy) != 0) {
-      const float mn = fmaxf(sm.m, mt);
-      const float alpha = __builtin_amdgcn_exp2f(sm.m - mn);
-      sm.m = mn;
-      sm.l *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) o[dt] *= alpha;
-      if (CAP) {
-        ka.l *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) ka.o[dt] *= alpha;
-      }
+  } else {
+    issue_both(cur, 0);
+    while (true) {
+      const TileCur nxt = advance(cur, seq, block, N);
+      const bool has_next = nxt.j >= 0;
+      const int key0 = cur.j * block + cur.st * kKeyTile;
+      const bool active = active_for(cur.j);
+      wait_vmem<LD>();  // this wave's K(t) landed (V^T(t), issued after it, may be in flight)
+      lds_barrier();    // ... and every other wave's
+      f32x16 s0, s1;
+      if (active) tile_qk<D, NW>(kbuf, qf, lc, s0, s1);
+      lds_barrier();  // every wave is done reading the K buffer
+      if (has_next)
+        issue_k<D, NW>(kbuf, kp, sn, N, nxt.j * block + nxt.st * kKeyTile, wave, lane, lc);
+      bf16x8 pf[4];
+      bool kept = false;
+      if (active) kept = tile_softmax<D, CAP>(s0, s1, cur.j, key0, N, scale_log2, half, o, sm, ka, pf);
+      if (has_next) wait_vmem<LD>(); else wait_vmem<0>();  // V^T(t) landed (K(t+1) may not)
+      lds_barrier();
+      if (active) tile_pv<D, NW>(vbuf, pf, lc, o, ka, kept);
+      lds_barrier();  // every wave is done reading the V buffer
+      if (!has_next) break;
+      issue_v<D, NW>(vbuf, vtp, npad, nxt.j * block + nxt.st * kKeyTile, wave, lc);
+      cur = nxt;
     }
-    const float neg_m = -sm.m;
-    bf16x8 pf[4];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float x = (ks < 2) ? s0[(ks & 1) * 8 + e] : s1[(ks & 1) * 8 + e];
-        pf[ks][e] = (bf16_t)__builtin_amdgcn_exp2f(__builtin_fmaf(x, scale_log2, neg_m));
-      }
-    }
-    // row sum of the bf16-rounded probabilities (the ones the PV product uses)
-    float tile_sum;
-    {
-      typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
-      const bf16x2 one = {(bf16_t)1.0f, (bf16_t)1.0f};
-      float acc = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const bf16x2 pr = {pf[ks][e], pf[ks][e + 1]};
-          acc = __builtin_amdgcn_fdot2_f32_bf16(pr, one, acc, false);
-        }
-      }
-      sm.l += acc;
-      tile_sum = acc;
-    }
-    const bool kept = CAP && ((ka.bits[j >> 5] >> (j & 31)) & 1u);  // uniform per wavefront
-    if (kept) ka.l += tile_sum;
-
-    // ---- O^T += V^T P^T ----
-    if (has_next) wait_vmem<LD>(); else wait_vmem<0>();  // V^T(t) landed (K(t+1) may not)
-    lds_barrier();
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const uint32_t a = lc.v_rd ^ (uint32_t)(ks << 5);
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) {
-        const bf16x8 va = *reinterpret_cast<const bf16x8*>(vbuf + a + dt * 4096);
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[ks], o[dt], 0, 0, 0);
-        if (kept) ka.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[ks], ka.o[dt], 0, 0, 0);
-      }
-    }
-    lds_barrier();  // every wave is done reading the V buffer
-    if (!has_next) break;
-    issue_v<D, NW>(vbuf, vtp, npad, jn * block + stn * kKeyTile, wave, lc);
-    j = jn;
-    st = stn;
   }
 }
 
 template <int D, int NW, int MODE>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_kernel(AttnParams p) {
-  __shared__ __align__(16) unsigned char kbuf[Tiles<D, NW>::TILE_BYTES];
-  __shared__ __align__(16) unsigned char vbuf[Tiles<D, NW>::TILE_BYTES];
+  constexpr int STAGES = NW == 4 ? RECAP_STAGES4 : 1;
+  __shared__ __align__(16) unsigned char kbuf[STAGES * Tiles<D, NW>::TILE_BYTES];
+  __shared__ __align__(16) unsigned char vbuf[STAGES * Tiles<D, NW>::TILE_BYTES];
   constexpr int QROWS = NW * 32;  // query rows of one work-group
 
   const int lane = threadIdx.x & 63;
@@ -404,12 +520,16 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   SoftmaxState sm{-INFINITY, 0.f};
 
   constexpr bool CAP = MODE == kDenseCapture;
-  constexpr int BLKS = CAP ? (QROWS / 64) : 1;  // query blocks of this work-group (block 64: 2)
-  __shared__ uint32_t kept_bits[CAP ? BLKS : 1][CAP ? kMaxBlocks / 32 : 1];
+  // sparse with 4 wavefronts and 64-row blocks: a pair of query blocks per work-group
+  constexpr bool PAIRABLE = MODE == kSparse && NW == 4;
+  constexpr bool BITS = CAP || PAIRABLE;
+  constexpr int BLKS = BITS ? (QROWS / 64) : 1;  // query blocks of this work-group (block 64: 2)
+  __shared__ uint32_t kept_bits[BITS ? BLKS : 1][BITS ? kMaxBlocks / 32 : 1];
   __shared__ int blk_flag[BLKS];
   KeptAcc<D> ka;
   int qb = 0;  // this wavefront's query block (capture mode)
-  if (CAP) {
+  const bool pair = PAIRABLE && p.block == 64;
+  if (CAP || pair) {
     // kept-block bitmaps of the query blocks covered by this work-group
     const int nb = QROWS / p.block;  // 2 for block 64, 1 for block 128
     qb = (qi * QROWS + wave * 32) / p.block;
@@ -435,18 +555,23 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   }
 
   int nlist = 0;
-  if (MODE == kDense || CAP) {
+  if (PAIRABLE && pair) {
+    UnionSeq seq{kept_bits[0], kept_bits[1], p.M, 0};
+    attend_phase<D, NW, STAGES, false, true>(seq, kbuf, vbuf, kp, vtp, p.st.n, p.N, p.block, p.npad,
+                                     p.scale_log2, qf, o, sm, wave, lane, lc, ka,
+                                     kept_bits[(wave * 32) / p.block]);
+  } else if (MODE == kDense || CAP) {
     // staggered start at the diagonal: neighbouring work-groups stream the same K/V tiles at
     // nearly the same time, which keeps them in L2
     AllSeq seq{0, p.M, min((qi * QROWS) / p.block, p.M - 1)};
-    attend_phase<D, NW, CAP>(seq, kbuf, vbuf, kp, vtp, p.st.n, p.N, p.block, p.npad,
+    attend_phase<D, NW, STAGES, CAP>(seq, kbuf, vbuf, kp, vtp, p.st.n, p.N, p.block, p.npad,
                              p.scale_log2, qf, o, sm, wave, lane, lc, ka);
   } else {
-    const int32_t* lst = p.idx + (int64_t)tile * p.M;
+    const int32_t* lst = p.idx + (int64_t)tile * p.M;  // one query block per work-group here
     nlist = min(max(((cptr_i32)p.count)[tile], 0), p.M);
     if (MODE == kCaptureR && ((cptr_u8)p.flags)[tile] == 0) return;  // done in the dense pass
     ListSeq seq{lst, nlist, 0, p.M};
-    attend_phase<D, NW, false>(seq, kbuf, vbuf, kp, vtp, p.st.n, p.N, p.block, p.npad,
+    attend_phase<D, NW, STAGES, false>(seq, kbuf, vbuf, kp, vtp, p.st.n, p.N, p.block, p.npad,
                                p.scale_log2, qf, o, sm, wave, lane, lc, ka);
   }
 
@@ -571,8 +696,9 @@ static void launch_mode(const AttnParams& p, int grid, AttnMode mode, hipStream_
 // list modes cover one query block (block / 32 wavefronts).
 hipError_t launch_attention(AttnParams p, int B, int D, AttnMode mode, hipStream_t stream) {
   const bool dense = mode == kDense || mode == kDenseCapture;
-  const int nw = dense ? 4 : p.block / 32;
-  p.mq = dense ? (p.N + 127) / 128 : p.M;
+  const bool pair = RECAP_PAIR && mode == kSparse && p.block == 64;  // two query blocks per WG
+  const int nw = (dense || pair) ? 4 : p.block / 32;
+  p.mq = dense ? (p.N + 127) / 128 : pair ? (p.M + 1) / 2 : p.M;
   const int grid = B * p.H * p.mq;
   if (D == 128) {
     if (nw == 2) launch_mode<128, 2>(p, grid, mode, stream);
