@@ -29,6 +29,7 @@
 //   RECAP_STAGES4   LDS stages of the 4-wavefront (128-row) work-groups: 1 or 2
 //   RECAP_PAIR      sparse calls with 64-row blocks run two query blocks per work-group
 //   RECAP_PRIO      raise the wavefront priority around MFMA bursts
+//   RECAP_WPE       wavefronts per SIMD targeted by register allocation
 #ifndef RECAP_STAGES4
 #define RECAP_STAGES4 2
 #endif
@@ -37,6 +38,9 @@
 #endif
 #ifndef RECAP_PRIO
 #define RECAP_PRIO 0
+#endif
+#ifndef RECAP_WPE  // wavefronts per SIMD the register allocation targets
+#define RECAP_WPE 2
 #endif
 
 namespace recap {
@@ -70,7 +74,7 @@ __device__ __forceinline__ uint32_t lds_offset(const void* p) {
 // not insert a full vmcnt wait before every later LDS read; completion is tracked by hand with
 // wait_vmem<> in issue order. M0 (the LDS base operand, read at issue) is restored afterwards.
 __device__ __forceinline__ void load_lds16(const void* base_uniform, uint32_t voff,
-                                           const void* lds_dst_uniform) {
+                                           uint32_t lds_dst_uniform) {
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
@@ -79,9 +83,16 @@ __device__ __forceinline__ void load_lds16(const void* base_uniform, uint32_t vo
       "global_load_lds_dwordx4 %2, %3\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
-      : "s"(__builtin_amdgcn_readfirstlane(lds_offset(lds_dst_uniform))), "v"(voff),
-        "s"(base_uniform)
+      : "s"(lds_dst_uniform), "v"(voff), "s"(base_uniform)
       : "memory");
+}
+// 16-byte LDS read at a byte address
+__device__ __forceinline__ bf16x8 lds_read16(uint32_t addr) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>((size_t)addr);
+}
+// Uniform LDS byte address of a __shared__ buffer (scalar register)
+__device__ __forceinline__ uint32_t lds_base(const void* p) {
+  return __builtin_amdgcn_readfirstlane(lds_offset(p));
 }
 
 // Hide a value from the optimiser so precomputed per-lane offsets are used as they are
@@ -185,35 +196,43 @@ struct Tiles {
 //  both reduce to "lane base XOR (ks << 5)" plus an immediate offset per 32-row tile.
 template <int D, int NW>
 struct LaneConsts {
-  uint32_t k_rd, v_rd;      // LDS read bases (bytes)
-  uint32_t k_voff[4];       // K DMA source offsets (bytes), by instruction index mod 4
-  uint32_t v_voff[2];       // V^T DMA source offsets (bytes), by instruction index mod 2
-  __device__ void init(int lane, int64_t sn, int npad) {
+  static constexpr int LD = Tiles<D, NW>::LD;
+  // K offsets repeat with the instruction index mod 4, V^T offsets mod 2. With enough
+  // instructions per wavefront that index is a compile-time constant; otherwise the
+  // wavefront's own instructions are folded in at init (never a run-time register index).
+  static constexpr int KP = LD >= 4 ? 4 : LD;
+  static constexpr int VP = LD >= 2 ? 2 : LD;
+  uint32_t k_rd, v_rd;   // LDS read offsets (bytes) within a tile buffer
+  uint32_t k_voff[KP];   // K DMA source offsets (bytes)
+  uint32_t v_voff[VP];   // V^T DMA source offsets (bytes)
+  __device__ void init(int lane, int wave, int64_t sn, int npad) {
     constexpr int CH = Tiles<D, NW>::CH, ROWB = Tiles<D, NW>::ROWB, KROWS = Tiles<D, NW>::KROWS;
     const int n = lane & 31, half = lane >> 5;
-    k_rd = n * ROWB + ((half ^ (n & (CH - 1))) << 4);
-    v_rd = n * 128 + ((half ^ ((n >> 1) & 7)) << 4);
+    k_rd = opaque(n * ROWB + ((half ^ (n & (CH - 1))) << 4));
+    v_rd = opaque(n * 128 + ((half ^ ((n >> 1) & 7)) << 4));
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int key = r * KROWS + lane / CH;  // row inside the tile, modulo the swizzle period
+    for (int r = 0; r < KP; ++r) {
+      const int x = LD >= 4 ? r : wave * LD + r;
+      const int key = x * KROWS + lane / CH;  // row inside the tile (swizzle period 4 in x)
       const int c = (lane % CH) ^ (key & (CH - 1));
       k_voff[r] = opaque((uint32_t)((lane / CH) * sn * 2 + c * 16));
     }
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int c = (lane & 7) ^ ((r * 4 + (lane >> 4)) & 7);
+    for (int r = 0; r < VP; ++r) {
+      const int x = LD >= 2 ? r : wave * LD + r;
+      const int c = (lane & 7) ^ ((x * 4 + (lane >> 4)) & 7);
       v_voff[r] = opaque((uint32_t)((lane >> 3) * npad * 2 + c * 16));
     }
-    k_rd = opaque(k_rd);
-    v_rd = opaque(v_rd);
   }
+  __device__ uint32_t kv(int x, int it) const { return k_voff[LD >= 4 ? (x & 3) : it]; }
+  __device__ uint32_t vv(int x, int it) const { return v_voff[LD >= 2 ? (x & 1) : it]; }
 };
 
 // Issue the global -> LDS loads of one 64-key K tile: rows [key0, key0 + 64) of this head.
 // Addresses are a uniform 64-bit base (first row of the tile) plus a 32-bit lane offset, so
 // the per-load cost is one 32-bit add.
 template <int D, int NW>
-__device__ __forceinline__ void issue_k(unsigned char* kbuf, const bf16_t* kp, int64_t sn, int N,
+__device__ __forceinline__ void issue_k(uint32_t kbuf, const bf16_t* kp, int64_t sn, int N,
                                         int key0, int wave, int lane,
                                         const LaneConsts<D, NW>& lc) {
   constexpr int CH = Tiles<D, NW>::CH, LD = Tiles<D, NW>::LD, KROWS = Tiles<D, NW>::KROWS;
@@ -223,7 +242,7 @@ __device__ __forceinline__ void issue_k(unsigned char* kbuf, const bf16_t* kp, i
 #pragma unroll
     for (int it = 0; it < LD; ++it) {
       const int x = wave * LD + it;
-      load_lds16(tile_base, (uint32_t)(x * KROWS * row_bytes + lc.k_voff[x & 3]), kbuf + x * 1024);
+      load_lds16(tile_base, (uint32_t)(x * KROWS * row_bytes + lc.kv(x, it)), kbuf + x * 1024);
     }
   } else {
     // last, partial block: rows past N are clamped to row N-1 (their scores are masked)
@@ -241,7 +260,7 @@ __device__ __forceinline__ void issue_k(unsigned char* kbuf, const bf16_t* kp, i
 }
 
 template <int D, int NW>
-__device__ __forceinline__ void issue_v(unsigned char* vbuf, const bf16_t* vtp, int npad,
+__device__ __forceinline__ void issue_v(uint32_t vbuf, const bf16_t* vtp, int npad,
                                         int key0, int wave, const LaneConsts<D, NW>& lc) {
   constexpr int LD = Tiles<D, NW>::LD;
   const char* tile_base = (const char*)(vtp + key0);
@@ -249,7 +268,7 @@ __device__ __forceinline__ void issue_v(unsigned char* vbuf, const bf16_t* vtp, 
 #pragma unroll
   for (int it = 0; it < LD; ++it) {
     const int x = wave * LD + it;
-    load_lds16(tile_base, (uint32_t)(x * 8 * row_bytes + lc.v_voff[x & 1]), vbuf + x * 1024);
+    load_lds16(tile_base, (uint32_t)(x * 8 * row_bytes + lc.vv(x, it)), vbuf + x * 1024);
   }
 }
 
@@ -295,18 +314,21 @@ struct KeptAcc {
 // ---- per-tile math, shared by the pipeline drivers below ----
 
 // S^T = K Q^T for one 64-key tile in LDS (raw dot products).
+// LDS buffers are 256-byte aligned, so base + (lane offset XOR (ks << 5)) equals
+// (base + lane offset) XOR (ks << 5): one opaque base per tile, one XOR per fragment.
 template <int D, int NW>
-__device__ __forceinline__ void tile_qk(const unsigned char* kb, const bf16x8 (&qf)[D / 16],
+__device__ __forceinline__ void tile_qk(uint32_t kb, const bf16x8 (&qf)[D / 16],
                                         const LaneConsts<D, NW>& lc, f32x16& s0, f32x16& s1) {
   constexpr int ROWB = Tiles<D, NW>::ROWB;
   s0 = f32x16{};
   s1 = f32x16{};
+  const uint32_t base = opaque(kb + lc.k_rd);
   mfma_prio_hi();
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
-    const uint32_t a = lc.k_rd ^ (uint32_t)(ks << 5);
-    const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kb + a);
-    const bf16x8 kb2 = *reinterpret_cast<const bf16x8*>(kb + a + 32 * ROWB);
+    const uint32_t a = base ^ (uint32_t)(ks << 5);
+    const bf16x8 ka = lds_read16(a);
+    const bf16x8 kb2 = lds_read16(a + 32 * ROWB);
     s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], s0, 0, 0, 0);
     s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb2, qf[ks], s1, 0, 0, 0);
   }
@@ -374,16 +396,17 @@ __device__ __forceinline__ bool tile_softmax(f32x16& s0, f32x16& s1, int j, int 
 
 // O^T += V^T P^T for one tile (and the kept-block accumulator when `kept`).
 template <int D, int NW>
-__device__ __forceinline__ void tile_pv(const unsigned char* vb, const bf16x8 (&pf)[4],
+__device__ __forceinline__ void tile_pv(uint32_t vb, const bf16x8 (&pf)[4],
                                         const LaneConsts<D, NW>& lc, f32x16 (&o)[D / 32],
                                         KeptAcc<D>& ka, bool kept) {
+  const uint32_t base = opaque(vb + lc.v_rd);
   mfma_prio_hi();
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
-    const uint32_t a = lc.v_rd ^ (uint32_t)(ks << 5);
+    const uint32_t a = base ^ (uint32_t)(ks << 5);
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) {
-      const bf16x8 va = *reinterpret_cast<const bf16x8*>(vb + a + dt * 4096);
+      const bf16x8 va = lds_read16(a + dt * 4096);
       o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[ks], o[dt], 0, 0, 0);
       if (kept) ka.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[ks], ka.o[dt], 0, 0, 0);
     }
@@ -422,10 +445,11 @@ __device__ __forceinline__ void attend_phase(Seq& seq, unsigned char* kbuf, unsi
   const int half = lane >> 5;
   TileCur cur{seq.first(), 0};
   if (cur.j < 0) return;
+  const uint32_t kb0 = lds_base(kbuf), vb0 = lds_base(vbuf);
   auto issue_both = [&](TileCur t, int buf) {
     const int key0 = t.j * block + t.st * kKeyTile;
-    issue_k<D, NW>(kbuf + buf * TB, kp, sn, N, key0, wave, lane, lc);
-    issue_v<D, NW>(vbuf + buf * TB, vtp, npad, key0, wave, lc);
+    issue_k<D, NW>(kb0 + buf * TB, kp, sn, N, key0, wave, lane, lc);
+    issue_v<D, NW>(vb0 + buf * TB, vtp, npad, key0, wave, lc);
   };
   auto active_for = [&](int j) { return !SKIP || ((own[j >> 5] >> (j & 31)) & 1u); };
 
@@ -443,10 +467,10 @@ __device__ __forceinline__ void attend_phase(Seq& seq, unsigned char* kbuf, unsi
       const int key0 = cur.j * block + cur.st * kKeyTile;
       if (active_for(cur.j)) {
         f32x16 s0, s1;
-        tile_qk<D, NW>(kbuf + b * TB, qf, lc, s0, s1);
+        tile_qk<D, NW>(kb0 + b * TB, qf, lc, s0, s1);
         bf16x8 pf[4];
         const bool kept = tile_softmax<D, CAP>(s0, s1, cur.j, key0, N, scale_log2, half, o, sm, ka, pf);
-        tile_pv<D, NW>(vbuf + b * TB, pf, lc, o, ka, kept);
+        tile_pv<D, NW>(vb0 + b * TB, pf, lc, o, ka, kept);
       }
       lds_barrier();  // every wave is done with buffers b
       if (!has1) break;
@@ -465,29 +489,29 @@ __device__ __forceinline__ void attend_phase(Seq& seq, unsigned char* kbuf, unsi
       wait_vmem<LD>();  // this wave's K(t) landed (V^T(t), issued after it, may be in flight)
       lds_barrier();    // ... and every other wave's
       f32x16 s0, s1;
-      if (active) tile_qk<D, NW>(kbuf, qf, lc, s0, s1);
+      if (active) tile_qk<D, NW>(kb0, qf, lc, s0, s1);
       lds_barrier();  // every wave is done reading the K buffer
       if (has_next)
-        issue_k<D, NW>(kbuf, kp, sn, N, nxt.j * block + nxt.st * kKeyTile, wave, lane, lc);
+        issue_k<D, NW>(kb0, kp, sn, N, nxt.j * block + nxt.st * kKeyTile, wave, lane, lc);
       bf16x8 pf[4];
       bool kept = false;
       if (active) kept = tile_softmax<D, CAP>(s0, s1, cur.j, key0, N, scale_log2, half, o, sm, ka, pf);
       if (has_next) wait_vmem<LD>(); else wait_vmem<0>();  // V^T(t) landed (K(t+1) may not)
       lds_barrier();
-      if (active) tile_pv<D, NW>(vbuf, pf, lc, o, ka, kept);
+      if (active) tile_pv<D, NW>(vb0, pf, lc, o, ka, kept);
       lds_barrier();  // every wave is done reading the V buffer
       if (!has_next) break;
-      issue_v<D, NW>(vbuf, vtp, npad, nxt.j * block + nxt.st * kKeyTile, wave, lc);
+      issue_v<D, NW>(vb0, vtp, npad, nxt.j * block + nxt.st * kKeyTile, wave, lc);
       cur = nxt;
     }
   }
 }
 
 template <int D, int NW, int MODE>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_kernel(AttnParams p) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RECAP_WPE, RECAP_WPE))) void attn_kernel(AttnParams p) {
   constexpr int STAGES = NW == 4 ? RECAP_STAGES4 : 1;
-  __shared__ __align__(16) unsigned char kbuf[STAGES * Tiles<D, NW>::TILE_BYTES];
-  __shared__ __align__(16) unsigned char vbuf[STAGES * Tiles<D, NW>::TILE_BYTES];
+  __shared__ __align__(256) unsigned char kbuf[STAGES * Tiles<D, NW>::TILE_BYTES];
+  __shared__ __align__(256) unsigned char vbuf[STAGES * Tiles<D, NW>::TILE_BYTES];
   constexpr int QROWS = NW * 32;  // query rows of one work-group
 
   const int lane = threadIdx.x & 63;
@@ -502,7 +526,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const bf16_t* vtp = p.vt + (int64_t)bh * D * p.npad;
   const int qrow = qi * QROWS + wave * 32 + n;
   LaneConsts<D, NW> lc;
-  lc.init(lane, p.st.n, p.npad);
+  lc.init(lane, wave, p.st.n, p.npad);
 
   bf16x8 qf[D / 16];
   {
