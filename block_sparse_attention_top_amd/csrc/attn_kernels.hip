@@ -3,11 +3,16 @@
 // RECAP (paperpeel.com/paper/2610.26244) Sec. 4.1 computes the selected block interactions
 // with a block-sparse kernel and dense refreshes with a dense one; Sec. 3.2 adds the cached
 // dense refinement to the fresh sparse estimate. This file holds one kernel template for
-// three modes:
-//   kSparse   walk the compacted kept-block list; optional fused O += c_h * R epilogue;
-//   kDense    walk every key block (128 query rows per work-group); optionally also keep the
-//             fp32 output in a workspace;
-//   kCaptureR walk the kept list and write R = O_dense - O_sparse using that fp32 output.
+// four modes:
+//   kSparse        walk the compacted kept-block list (two 64-row query blocks per work-group
+//                  over the union of their lists); optional fused O += c_h * R epilogue;
+//   kDense         walk every key block (128 query rows per work-group);
+//   kDenseCapture  as kDense, with a second accumulator over the kept key blocks that shares
+//                  the dense running maximum, so one pass writes O_dense and
+//                  R = O_dense - O_sparse; a query block whose kept weights underflow against
+//                  that maximum is flagged, and its fp32 dense output goes to a workspace;
+//   kCaptureR      for flagged query blocks only: recompute the sparse output over the kept
+//                  list with its own maximum and write R from the saved dense output.
 //
 // Layout of the work (one work-group per query block of `block` rows, one wavefront per 32
 // query rows, 64-key tiles):
@@ -603,9 +608,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RECAP_W
   const float inv = lt > 0.f ? 1.0f / lt : 0.f;
 
   if (CAP) {
-    // The kept accumulator shares the dense running max; if its mass underflowed (kept keys
-    // more than ~2^6 binary orders below the dense maximum) the block is left to the
-    // residual pass, which recomputes the sparse output with its own maximum.
+    // The kept accumulator shares the dense running max; if its weights sum to less than
+    // 2^-64 against that maximum (too few significant bits left after bf16 rounding of the
+    // weights), the block is left to the residual pass, which recomputes the sparse output
+    // with its own maximum.
     const float ls = cross_half_sum(ka.l);
     const bool bad = qrow < p.N && !(ls >= 0x1p-64f);
     if (__builtin_amdgcn_ballot_w64(bad) != 0 && lane == 0) atomicOr(&blk_flag[(wave * 32) / p.block], 1);
@@ -670,8 +676,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RECAP_W
   const bool has_res = MODE == kSparse && p.res != nullptr;
   const bf16_t* rsrc = has_res ? p.res + orow : nullptr;
   const float c = p.res_scale.v[h];
-  float* odw = (MODE == kDense && p.od_ws != nullptr)
-                   ? p.od_ws + ((int64_t)bh * p.npad + qrow) * D : nullptr;
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) {
 #pragma unroll
@@ -680,7 +684,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RECAP_W
       f32x4 v;
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] = o[dt][g * 4 + e] * inv;
-      if (odw != nullptr) *reinterpret_cast<f32x4*>(odw + d0) = v;
       if (has_res) {
         const bf16x4 r4 = *reinterpret_cast<const bf16x4*>(rsrc + d0);
 #pragma unroll
