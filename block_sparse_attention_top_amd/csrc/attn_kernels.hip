@@ -250,13 +250,16 @@ __device__ __forceinline__ void issue_k(uint32_t kbuf, const bf16_t* kp, int64_t
       load_lds16(tile_base, (uint32_t)(x * KROWS * row_bytes + lc.kv(x, it)), kbuf + x * 1024);
     }
   } else {
-    // last, partial block: rows past N are clamped to row N-1 (their scores are masked)
+    // last, partial block: rows past N are clamped to row N-1 (their scores are masked). The
+    // lane index is re-read opaquely so this rare path's address math is not hoisted out of
+    // the tile loop (where it would hold registers for the whole loop).
     asm volatile("" ::: "memory");
     const int last = N - 1 - key0;
+    const int ln = (int)opaque((uint32_t)lane);
 #pragma unroll
     for (int it = 0; it < LD; ++it) {
       const int slot0 = (wave * LD + it) * 64;
-      const int slot = slot0 + lane;
+      const int slot = slot0 + ln;
       const int key = slot / CH;
       const int c = (slot % CH) ^ (key & (CH - 1));
       load_lds16(tile_base, (uint32_t)(min(key, last) * row_bytes + c * 16), kbuf + slot0 * 16);

@@ -177,6 +177,103 @@ __global__ __launch_bounds__(256) void score_kernel(const float* __restrict__ qb
 }
 
 // ------------------------------------------------------------------------------------------
+// Scores in one pass for rows that fit in LDS: work-group = (b*h, strip of 16 query blocks).
+// The strip's scaled logits are computed once into LDS with the fp32 MFMA 16x16x4, as
+// S^T = K̄ Q̄^T so that lane l owns query block l % 16 and four consecutive key blocks of each
+// 16-key tile (the contraction over D is split as D index = (l / 16) * D/4 + step, identically
+// for both operands). Then each wavefront takes four rows: row max and sum from LDS, and the
+// normalised row written with consecutive lanes on consecutive key blocks.
+// ------------------------------------------------------------------------------------------
+constexpr int kStripRows = 16;
+// LDS budget of one strip: two work-groups per CU (160 KB of LDS) up to M = 1276
+constexpr size_t kStripLdsMax = 80 * 1024;
+
+__host__ __device__ constexpr int strip_stride(int M) { return ((M + 15) / 16) * 16 + 4; }
+
+template <int D>
+__global__ __launch_bounds__(256) void score_strip_kernel(const float* __restrict__ qbar,
+                                                          const float* __restrict__ kbar, int M,
+                                                          float scale_log2,
+                                                          float* __restrict__ probs) {
+  extern __shared__ float srow[];  // [kStripRows][strip_stride(M)]
+  constexpr int KS = D / 4;        // contraction steps; lane group g covers D indices [g*KS, ..)
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const int nst = (M + kStripRows - 1) / kStripRows;
+  // strips of one head on one XCD, so that head's K̄ stays in that XCD's L2
+  const int wg = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = wg / nst, st = wg - bh * nst;
+  const int stride = strip_stride(M);
+  const float* qb = qbar + (int64_t)bh * M * D;
+  const float* kb = kbar + (int64_t)bh * M * D;
+  float qv[KS];
+  {
+    const float* src = qb + (int64_t)min(st * kStripRows + col, M - 1) * D + grp * KS;
+#pragma unroll
+    for (int s = 0; s < KS; s += 4) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(src + s);
+      qv[s] = x[0];
+      qv[s + 1] = x[1];
+      qv[s + 2] = x[2];
+      qv[s + 3] = x[3];
+    }
+  }
+  const int nkt = (M + 15) >> 4;
+  // K̄ rows of a 16-key tile; the next tile's are loaded while this one is multiplied
+  auto load_k = [&](int kt, float (&kv)[KS]) {
+    const float* src = kb + (int64_t)min(kt * 16 + col, M - 1) * D + grp * KS;
+#pragma unroll
+    for (int s = 0; s < KS; s += 4) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(src + s);
+      kv[s] = x[0];
+      kv[s + 1] = x[1];
+      kv[s + 2] = x[2];
+      kv[s + 3] = x[3];
+    }
+  };
+  float kn[KS];
+  if (wave < nkt) load_k(wave, kn);
+  for (int kt = wave; kt < nkt; kt += 4) {
+    float kv[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) kv[s] = kn[s];
+    if (kt + 4 < nkt) load_k(kt + 4, kn);
+    f32x4 a0 = {}, a1 = {};
+#pragma unroll
+    for (int s = 0; s < KS; s += 2) {
+      a0 = __builtin_amdgcn_mfma_f32_16x16x4f32(kv[s], qv[s], a0, 0, 0, 0);
+      a1 = __builtin_amdgcn_mfma_f32_16x16x4f32(kv[s + 1], qv[s + 1], a1, 0, 0, 0);
+    }
+    // lane holds S^T[key = kt*16 + 4*grp + r][query = col], r = 0..3
+    f32x4 x;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int key = kt * 16 + grp * 4 + r;
+      x[r] = key < M ? (a0[r] + a1[r]) * scale_log2 : -INFINITY;
+    }
+    *reinterpret_cast<f32x4*>(srow + col * stride + kt * 16 + grp * 4) = x;
+  }
+  __syncthreads();
+  for (int rr = 0; rr < kStripRows / 4; ++rr) {
+    const int r = wave * (kStripRows / 4) + rr;
+    const int qrow = st * kStripRows + r;
+    if (qrow >= M) break;  // uniform per wavefront
+    const float* x = srow + r * stride;
+    float mx = -INFINITY;
+    for (int j = lane; j < M; j += 64) mx = fmaxf(mx, x[j]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    float l = 0.f;
+    for (int j = lane; j < M; j += 64) l += __builtin_amdgcn_exp2f(x[j] - mx);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) l += __shfl_xor(l, off);
+    const float inv = 1.0f / l;
+    float* prow = probs + ((int64_t)bh * M + qrow) * M;
+    for (int j = lane; j < M; j += 64) prow[j] = __builtin_amdgcn_exp2f(x[j] - mx) * inv;
+  }
+}
+
+// ------------------------------------------------------------------------------------------
 // Top-p: one work-group of 256 threads per query-block row. Keys (orderable probability bits
 // << 32 | ~index) are bitonic-sorted descending in LDS, which orders probabilities descending
 // and equal values by lower index first. Running mass: fp64 block scan over the sorted
@@ -323,16 +420,57 @@ __global__ __launch_bounds__(256) void topp_kernel(const float* __restrict__ pro
 // ------------------------------------------------------------------------------------------
 // Top-p, one wavefront per row (rows of up to 64 * VPL blocks). The row stays in registers
 // (lane l holds blocks l, l+64, ...). Probabilities are non-negative, so their fp32 bit
-// patterns order like their values; a binary search over bit patterns finds the k*-th largest
+// patterns order like their values; a search over bit patterns finds the k*-th largest
 // value v* = the largest value t with mass(>= t) >= p (mass accumulated in fp64). Every block
 // above v* is kept; blocks equal to v* are taken in ascending index order until the running
 // mass reaches p. This is the same set as sorting by (probability desc, index asc) and
 // keeping the shortest prefix whose mass reaches p. No LDS, no barriers.
+// The search keeps a bracket [lo, hi) with mass(>= lo) >= p > mass(>= hi), shrunk to the
+// smallest and largest value inside it and split between them, so it ends once a single
+// distinct value remains (about log2 M steps). Each mass test is first made in fp32: with
+// n additions on any path the fp32 sum is within n * 2^-24 * total of the exact sum, and the
+// fp64 sum is evaluated only when the fp32 one lies that close to p, so every decision is the
+// one the fp64 sum gives.
 // ------------------------------------------------------------------------------------------
 __device__ __forceinline__ double wave_sum(double x) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
   return x;
+}
+
+// Wavefront-wide reductions without LDS: DPP steps inside each row of 16 lanes (xor 1, xor 2,
+// rotate by 4 and by 8 within the row), then the four row results combined from lanes 0, 16,
+// 32 and 48. The result is uniform across the wavefront.
+template <class Op>
+__device__ __forceinline__ uint32_t row_reduce_u(uint32_t x, Op op) {
+  x = op(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xb1, 0xf, 0xf, false));   // quad [1,0,3,2]
+  x = op(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4e, 0xf, 0xf, false));   // quad [2,3,0,1]
+  x = op(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x124, 0xf, 0xf, false));  // row_ror:4
+  x = op(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x128, 0xf, 0xf, false));  // row_ror:8
+  return x;
+}
+__device__ __forceinline__ uint32_t wave_min_u(uint32_t x) {
+  auto mn = [](uint32_t a, uint32_t b) { return a < b ? a : b; };
+  x = row_reduce_u(x, mn);
+  const uint32_t a = __builtin_amdgcn_readlane(x, 0), b = __builtin_amdgcn_readlane(x, 16);
+  const uint32_t c = __builtin_amdgcn_readlane(x, 32), d = __builtin_amdgcn_readlane(x, 48);
+  return mn(mn(a, b), mn(c, d));
+}
+__device__ __forceinline__ uint32_t wave_max_u(uint32_t x) {
+  auto mx = [](uint32_t a, uint32_t b) { return a > b ? a : b; };
+  x = row_reduce_u(x, mx);
+  const uint32_t a = __builtin_amdgcn_readlane(x, 0), b = __builtin_amdgcn_readlane(x, 16);
+  const uint32_t c = __builtin_amdgcn_readlane(x, 32), d = __builtin_amdgcn_readlane(x, 48);
+  return mx(mx(a, b), mx(c, d));
+}
+__device__ __forceinline__ float wave_sum_f(float x) {
+  auto add = [](uint32_t a, uint32_t b) { return __float_as_uint(__uint_as_float(a) + __uint_as_float(b)); };
+  const uint32_t r = row_reduce_u(__float_as_uint(x), add);
+  const float a = __uint_as_float(__builtin_amdgcn_readlane(r, 0));
+  const float b = __uint_as_float(__builtin_amdgcn_readlane(r, 16));
+  const float c = __uint_as_float(__builtin_amdgcn_readlane(r, 32));
+  const float d = __uint_as_float(__builtin_amdgcn_readlane(r, 48));
+  return (a + b) + (c + d);
 }
 
 template <int VPL>
@@ -348,6 +486,7 @@ __global__ __launch_bounds__(256) void topp_wave_kernel(const float* __restrict_
   const int h = (row / M) % H;
   const float p = top_p.v[h];
   const float* pr = probs + (int64_t)row * M;
+  // slots past M hold value 0: they add no mass, and the selection below never takes them
   uint32_t u[VPL];
   float val[VPL];
 #pragma unroll
@@ -355,15 +494,16 @@ __global__ __launch_bounds__(256) void topp_wave_kernel(const float* __restrict_
     const int j = i * 64 + lane;
     const float x = j < M ? pr[j] : 0.f;
     val[i] = x > 0.f ? x : 0.f;  // probabilities are >= 0; -0 and NaN map to 0
-    u[i] = j < M ? __float_as_uint(val[i]) : 0xffffffffu;  // padding: never >= a finite t
+    u[i] = __float_as_uint(val[i]);
   }
   auto mass_at_least = [&](uint32_t t) {
     double acc = 0.0;
 #pragma unroll
     for (int i = 0; i < VPL; ++i)
-      if (u[i] >= t && u[i] != 0xffffffffu) acc += (double)val[i];
+      if (u[i] >= t) acc += (double)val[i];
     return wave_sum(acc);
   };
+  auto valid = [&](int i) { return i * 64 + lane < M; };
 
   bool kept[VPL];
   double kmass;
@@ -371,23 +511,47 @@ __global__ __launch_bounds__(256) void topp_wave_kernel(const float* __restrict_
   if (p >= 1.0f || total < (double)p) {
     // p >= 1, or rounding left the total below p: every block is kept
 #pragma unroll
-    for (int i = 0; i < VPL; ++i) kept[i] = u[i] != 0xffffffffu;
+    for (int i = 0; i < VPL; ++i) kept[i] = valid(i);
     kmass = total;
   } else {
     // largest t with mass(>= t) >= p (p = 0 behaves like the smallest positive mass, so v* is
     // the maximum and exactly one block is kept)
     const double target = p > 0.f ? (double)p : 1e-300;
-    uint32_t lo = 0u, hi = 0x7f800000u;  // mass(>= lo) >= target > mass(>= hi)
-    while (hi - lo > 1u) {
-      const uint32_t mid = lo + ((hi - lo) >> 1);
-      if (mass_at_least(mid) >= target) lo = mid; else hi = mid;
+    const double slack = (double)(VPL + 8) * 0x1p-23 * total;  // > twice the fp32 error bound
+    // bracket [vmin, vmax]: the values between lo and hi; start with the whole row
+    uint32_t a0 = 0xffffffffu, z0 = 0u;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      a0 = min(a0, u[i]);
+      z0 = max(z0, u[i]);
     }
-    const uint32_t T = lo;
+    uint32_t vmin = wave_min_u(a0), vmax = wave_max_u(z0);
+    // invariant: mass(>= vmin) >= target > mass(>= vmax + 1)
+    while (vmin < vmax) {
+      const uint32_t mid = vmin + ((vmax - vmin + 1u) >> 1);  // vmin < mid <= vmax
+      // one pass: mass of values >= mid (fp32), smallest value >= mid, largest value < mid
+      float acc = 0.f;
+      uint32_t a = 0xffffffffu, z = 0u;
+#pragma unroll
+      for (int i = 0; i < VPL; ++i) {
+        const bool ge = u[i] >= mid;
+        acc += ge ? val[i] : 0.f;
+        a = min(a, ge ? u[i] : 0xffffffffu);
+        z = max(z, ge ? 0u : u[i]);
+      }
+      const double d = (double)wave_sum_f(acc) - target;
+      const bool up = d > slack ? true : d < -slack ? false : mass_at_least(mid) >= target;
+      // values outside [vmin, vmax] lie below vmin or above vmax, so the smallest value >= mid
+      // is inside the bracket (vmax is a candidate), and so is the largest value < mid (vmin)
+      if (up) vmin = wave_min_u(a);  // mass(>= mid) >= target: the answer is >= mid
+      else vmax = wave_max_u(z);      // mass(>= mid) < target: the answer is < mid
+    }
+    const uint32_t T = vmin;
     const float vstar = __uint_as_float(T);
     double c = 0.0;
 #pragma unroll
     for (int i = 0; i < VPL; ++i)
-      if (u[i] > T && u[i] != 0xffffffffu) c += (double)val[i];
+      if (u[i] > T) c += (double)val[i];
     c = wave_sum(c);
     // ties at v*, ascending index: position (i, lane) is index i*64 + lane
     int need = 0;  // number of tie blocks to keep
@@ -395,7 +559,7 @@ __global__ __launch_bounds__(256) void topp_wave_kernel(const float* __restrict_
       double cc = c;
       bool done = false;
       for (int i = 0; i < VPL && !done; ++i) {
-        uint64_t m = __builtin_amdgcn_ballot_w64(u[i] == T);
+        uint64_t m = __builtin_amdgcn_ballot_w64(u[i] == T && valid(i));
         while (m != 0ull) {
           cc += (double)vstar;
           ++need;
@@ -408,10 +572,10 @@ __global__ __launch_bounds__(256) void topp_wave_kernel(const float* __restrict_
     int seen = 0;  // tie blocks before the current group of 64
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
-      const bool eq = u[i] == T;
+      const bool eq = u[i] == T && valid(i);
       const uint64_t m = __builtin_amdgcn_ballot_w64(eq);
       const int rank = seen + (int)__builtin_popcountll(m & ((1ull << lane) - 1ull));
-      kept[i] = (u[i] > T && u[i] != 0xffffffffu) || (eq && rank < need);
+      kept[i] = u[i] > T || (eq && rank < need);  // u > T >= 0 excludes the zero slots
       seen += (int)__builtin_popcountll(m);
     }
   }
@@ -447,6 +611,28 @@ hipError_t launch_pool(const bf16_t* q, const bf16_t* k, Strides st, int B, int 
 
 hipError_t launch_scores(const float* qbar, const float* kbar, int BH, int M, int D,
                          float scale_log2, float* probs, hipStream_t stream) {
+  const size_t lds = (size_t)kStripRows * strip_stride(M) * sizeof(float);
+  if (lds <= kStripLdsMax) {  // rows fit in LDS: one pass
+    const int sgrid = BH * ((M + kStripRows - 1) / kStripRows);
+    if (D == 128) {
+      if (lds > 64 * 1024) {
+        const hipError_t e = hipFuncSetAttribute((const void*)score_strip_kernel<128>,
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 (int)lds);
+        if (e != hipSuccess) return e;
+      }
+      score_strip_kernel<128><<<sgrid, 256, lds, stream>>>(qbar, kbar, M, scale_log2, probs);
+    } else {
+      if (lds > 64 * 1024) {
+        const hipError_t e = hipFuncSetAttribute((const void*)score_strip_kernel<64>,
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 (int)lds);
+        if (e != hipSuccess) return e;
+      }
+      score_strip_kernel<64><<<sgrid, 256, lds, stream>>>(qbar, kbar, M, scale_log2, probs);
+    }
+    return hipGetLastError();
+  }
   const int grid = BH * ((M + 31) / 32);
   if (D == 128)
     score_kernel<128><<<grid, 256, 0, stream>>>(qbar, kbar, M, scale_log2, probs);
@@ -464,8 +650,16 @@ hipError_t launch_topp(const float* probs, int B, int H, int M, const HeadScalar
     topp_wave_kernel<8><<<grid, 256, 0, stream>>>(probs, H, M, rows, top_p, count, idx, mask, mass);
     return hipGetLastError();
   }
+  if (M <= 768) {
+    topp_wave_kernel<12><<<grid, 256, 0, stream>>>(probs, H, M, rows, top_p, count, idx, mask, mass);
+    return hipGetLastError();
+  }
   if (M <= 1024) {
     topp_wave_kernel<16><<<grid, 256, 0, stream>>>(probs, H, M, rows, top_p, count, idx, mask, mass);
+    return hipGetLastError();
+  }
+  if (M <= 1280) {
+    topp_wave_kernel<20><<<grid, 256, 0, stream>>>(probs, H, M, rows, top_p, count, idx, mask, mass);
     return hipGetLastError();
   }
   if (M <= 1536) {

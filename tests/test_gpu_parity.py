@@ -121,6 +121,28 @@ def test_small_case(bsa, case):
         assert np.all(res["count"] == 1)
 
 
+@pytest.mark.parametrize("m,d", [(1276, 128), (1277, 64), (2100, 128)])
+def test_scores_and_topp_long_rows(bsa, m, d):
+    """Block scores and top-p for rows around the single-pass (LDS-resident row) limit of the
+    score kernel (M <= 1276) and past the register-resident top-p limit (M > 2048)."""
+    cfg = synth.workload("tiny", heads=1, head_dim=d)
+    N = m * cfg.block - 7  # ragged last block
+    q, k, _ = synth.make_qkv(cfg, seq=N)
+    s = d ** -0.5
+    p = np.array([0.9])
+    say(f"[case] scores+topp M={m} D={d} N={N}")
+    qd, kd = to_dev(q), to_dev(k)
+    desc = bsa.make_desc(qd, cfg.block)
+    probs = bsa.recap_block_scores(desc, qd, kd, s)
+    count, idx, mask, _ = bsa.recap_topp_mask(desc, probs, p.tolist(), want_mask=True)
+    torch.cuda.synchronize()
+    ref = O.block_scores(synth.to_f64(q), synth.to_f64(k), cfg.block, s)
+    parity.check_probs(probs.cpu().numpy().astype(np.float64), ref)
+    gmask = mask.cpu().numpy().astype(bool)
+    parity.check_lists(count.cpu().numpy(), idx.cpu().numpy(), m, gmask)
+    parity.check_mask(gmask, ref, O.topp_select(ref, p)["mask"], p)
+
+
 def test_all_kept_capture_is_exactly_zero(bsa):
     say("[test] all-kept capture")
     cfg = synth.workload("tiny", head_dim=128, grid=(1, 1, 1100))
