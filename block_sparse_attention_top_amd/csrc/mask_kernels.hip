@@ -176,6 +176,51 @@ __global__ __launch_bounds__(256) void score_kernel(const float* __restrict__ qb
   }
 }
 
+// Wavefront-wide reductions without LDS: DPP steps inside each row of 16 lanes (xor 1, xor 2,
+// rotate by 4 and by 8 within the row), then the four row results combined from lanes 0, 16,
+// 32 and 48. The result is uniform across the wavefront.
+template <class Op>
+__device__ __forceinline__ uint32_t row_reduce_u(uint32_t x, Op op) {
+  x = op(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xb1, 0xf, 0xf, false));   // quad [1,0,3,2]
+  x = op(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4e, 0xf, 0xf, false));   // quad [2,3,0,1]
+  x = op(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x124, 0xf, 0xf, false));  // row_ror:4
+  x = op(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x128, 0xf, 0xf, false));  // row_ror:8
+  return x;
+}
+__device__ __forceinline__ uint32_t wave_min_u(uint32_t x) {
+  auto mn = [](uint32_t a, uint32_t b) { return a < b ? a : b; };
+  x = row_reduce_u(x, mn);
+  const uint32_t a = __builtin_amdgcn_readlane(x, 0), b = __builtin_amdgcn_readlane(x, 16);
+  const uint32_t c = __builtin_amdgcn_readlane(x, 32), d = __builtin_amdgcn_readlane(x, 48);
+  return mn(mn(a, b), mn(c, d));
+}
+__device__ __forceinline__ uint32_t wave_max_u(uint32_t x) {
+  auto mx = [](uint32_t a, uint32_t b) { return a > b ? a : b; };
+  x = row_reduce_u(x, mx);
+  const uint32_t a = __builtin_amdgcn_readlane(x, 0), b = __builtin_amdgcn_readlane(x, 16);
+  const uint32_t c = __builtin_amdgcn_readlane(x, 32), d = __builtin_amdgcn_readlane(x, 48);
+  return mx(mx(a, b), mx(c, d));
+}
+__device__ __forceinline__ float wave_sum_f(float x) {
+  auto add = [](uint32_t a, uint32_t b) { return __float_as_uint(__uint_as_float(a) + __uint_as_float(b)); };
+  const uint32_t r = row_reduce_u(__float_as_uint(x), add);
+  const float a = __uint_as_float(__builtin_amdgcn_readlane(r, 0));
+  const float b = __uint_as_float(__builtin_amdgcn_readlane(r, 16));
+  const float c = __uint_as_float(__builtin_amdgcn_readlane(r, 32));
+  const float d = __uint_as_float(__builtin_amdgcn_readlane(r, 48));
+  return (a + b) + (c + d);
+}
+
+__device__ __forceinline__ float wave_max_f(float x) {
+  auto mx = [](uint32_t a, uint32_t b) { return __float_as_uint(fmaxf(__uint_as_float(a), __uint_as_float(b))); };
+  const uint32_t r = row_reduce_u(__float_as_uint(x), mx);
+  const float a = __uint_as_float(__builtin_amdgcn_readlane(r, 0));
+  const float b = __uint_as_float(__builtin_amdgcn_readlane(r, 16));
+  const float c = __uint_as_float(__builtin_amdgcn_readlane(r, 32));
+  const float d = __uint_as_float(__builtin_amdgcn_readlane(r, 48));
+  return fmaxf(fmaxf(a, b), fmaxf(c, d));
+}
+
 // ------------------------------------------------------------------------------------------
 // Scores in one pass for rows that fit in LDS: work-group = (b*h, strip of 16 query blocks).
 // The strip's scaled logits are computed once into LDS with the fp32 MFMA 16x16x4, as
@@ -185,8 +230,10 @@ __global__ __launch_bounds__(256) void score_kernel(const float* __restrict__ qb
 // normalised row written with consecutive lanes on consecutive key blocks.
 // ------------------------------------------------------------------------------------------
 constexpr int kStripRows = 16;
-// LDS budget of one strip: two work-groups per CU (160 KB of LDS) up to M = 1276
-constexpr size_t kStripLdsMax = 80 * 1024;
+// Rows of up to kStripMaxM blocks run in one pass: 16 rows x 1268 fp32 of LDS (79.25 KB, two
+// work-groups per CU) and up to kStripVals values per lane in registers
+constexpr int kStripMaxM = 1264;
+constexpr int kStripVals = 20;
 
 __host__ __device__ constexpr int strip_stride(int M) { return ((M + 15) / 16) * 16 + 4; }
 
@@ -254,22 +301,34 @@ __global__ __launch_bounds__(256) void score_strip_kernel(const float* __restric
     *reinterpret_cast<f32x4*>(srow + col * stride + kt * 16 + grp * 4) = x;
   }
   __syncthreads();
+  // each wavefront normalises four rows; a row (M <= 64 * kStripVals) sits in registers
   for (int rr = 0; rr < kStripRows / 4; ++rr) {
     const int r = wave * (kStripRows / 4) + rr;
     const int qrow = st * kStripRows + r;
     if (qrow >= M) break;  // uniform per wavefront
     const float* x = srow + r * stride;
+    float e[kStripVals];
     float mx = -INFINITY;
-    for (int j = lane; j < M; j += 64) mx = fmaxf(mx, x[j]);
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    for (int i = 0; i < kStripVals; ++i) {
+      const int j = i * 64 + lane;
+      e[i] = j < M ? x[j] : -INFINITY;
+      mx = fmaxf(mx, e[i]);
+    }
+    mx = wave_max_f(mx);
     float l = 0.f;
-    for (int j = lane; j < M; j += 64) l += __builtin_amdgcn_exp2f(x[j] - mx);
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) l += __shfl_xor(l, off);
-    const float inv = 1.0f / l;
+    for (int i = 0; i < kStripVals; ++i) {
+      e[i] = __builtin_amdgcn_exp2f(e[i] - mx);  // 0 past M
+      l += e[i];
+    }
+    const float inv = 1.0f / wave_sum_f(l);
     float* prow = probs + ((int64_t)bh * M + qrow) * M;
-    for (int j = lane; j < M; j += 64) prow[j] = __builtin_amdgcn_exp2f(x[j] - mx) * inv;
+#pragma unroll
+    for (int i = 0; i < kStripVals; ++i) {
+      const int j = i * 64 + lane;
+      if (j < M) prow[j] = e[i] * inv;
+    }
   }
 }
 
@@ -438,41 +497,6 @@ __device__ __forceinline__ double wave_sum(double x) {
   return x;
 }
 
-// Wavefront-wide reductions without LDS: DPP steps inside each row of 16 lanes (xor 1, xor 2,
-// rotate by 4 and by 8 within the row), then the four row results combined from lanes 0, 16,
-// 32 and 48. The result is uniform across the wavefront.
-template <class Op>
-__device__ __forceinline__ uint32_t row_reduce_u(uint32_t x, Op op) {
-  x = op(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xb1, 0xf, 0xf, false));   // quad [1,0,3,2]
-  x = op(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4e, 0xf, 0xf, false));   // quad [2,3,0,1]
-  x = op(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x124, 0xf, 0xf, false));  // row_ror:4
-  x = op(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x128, 0xf, 0xf, false));  // row_ror:8
-  return x;
-}
-__device__ __forceinline__ uint32_t wave_min_u(uint32_t x) {
-  auto mn = [](uint32_t a, uint32_t b) { return a < b ? a : b; };
-  x = row_reduce_u(x, mn);
-  const uint32_t a = __builtin_amdgcn_readlane(x, 0), b = __builtin_amdgcn_readlane(x, 16);
-  const uint32_t c = __builtin_amdgcn_readlane(x, 32), d = __builtin_amdgcn_readlane(x, 48);
-  return mn(mn(a, b), mn(c, d));
-}
-__device__ __forceinline__ uint32_t wave_max_u(uint32_t x) {
-  auto mx = [](uint32_t a, uint32_t b) { return a > b ? a : b; };
-  x = row_reduce_u(x, mx);
-  const uint32_t a = __builtin_amdgcn_readlane(x, 0), b = __builtin_amdgcn_readlane(x, 16);
-  const uint32_t c = __builtin_amdgcn_readlane(x, 32), d = __builtin_amdgcn_readlane(x, 48);
-  return mx(mx(a, b), mx(c, d));
-}
-__device__ __forceinline__ float wave_sum_f(float x) {
-  auto add = [](uint32_t a, uint32_t b) { return __float_as_uint(__uint_as_float(a) + __uint_as_float(b)); };
-  const uint32_t r = row_reduce_u(__float_as_uint(x), add);
-  const float a = __uint_as_float(__builtin_amdgcn_readlane(r, 0));
-  const float b = __uint_as_float(__builtin_amdgcn_readlane(r, 16));
-  const float c = __uint_as_float(__builtin_amdgcn_readlane(r, 32));
-  const float d = __uint_as_float(__builtin_amdgcn_readlane(r, 48));
-  return (a + b) + (c + d);
-}
-
 template <int VPL>
 __global__ __launch_bounds__(256) void topp_wave_kernel(const float* __restrict__ probs, int H,
                                                         int M, int rows, HeadScalars top_p,
@@ -612,7 +636,10 @@ hipError_t launch_pool(const bf16_t* q, const bf16_t* k, Strides st, int B, int 
 hipError_t launch_scores(const float* qbar, const float* kbar, int BH, int M, int D,
                          float scale_log2, float* probs, hipStream_t stream) {
   const size_t lds = (size_t)kStripRows * strip_stride(M) * sizeof(float);
-  if (lds <= kStripLdsMax) {  // rows fit in LDS: one pass
+  static_assert(kStripMaxM <= 64 * kStripVals, "a row must fit in the lanes' registers");
+  static_assert(kStripRows * strip_stride(kStripMaxM) * sizeof(float) <= 80 * 1024,
+                "two strips per CU");
+  if (M <= kStripMaxM) {  // rows fit in LDS and registers: one pass
     const int sgrid = BH * ((M + kStripRows - 1) / kStripRows);
     if (D == 128) {
       if (lds > 64 * 1024) {

@@ -121,10 +121,10 @@ def test_small_case(bsa, case):
         assert np.all(res["count"] == 1)
 
 
-@pytest.mark.parametrize("m,d", [(1276, 128), (1277, 64), (2100, 128)])
+@pytest.mark.parametrize("m,d", [(1264, 128), (1265, 64), (2100, 128)])
 def test_scores_and_topp_long_rows(bsa, m, d):
     """Block scores and top-p for rows around the single-pass (LDS-resident row) limit of the
-    score kernel (M <= 1276) and past the register-resident top-p limit (M > 2048)."""
+    score kernel (M <= 1264) and past the register-resident top-p limit (M > 2048)."""
     cfg = synth.workload("tiny", heads=1, head_dim=d)
     N = m * cfg.block - 7  # ragged last block
     q, k, _ = synth.make_qkv(cfg, seq=N)
