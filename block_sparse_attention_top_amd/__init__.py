@@ -2,14 +2,17 @@
 
 The compute path is the HIP library librecap.so (C ABI in include/recap.h); this package only
 marshals torch device tensors into its entry points. Functions carry the C names:
-recap_block_scores, recap_topp_mask, recap_block_sparse_attn, recap_dense_attn.
+recap_block_scores, recap_topp_mask, recap_block_sparse_attn, recap_dense_attn, and the
+row-statistics variants recap_block_sparse_attn_stats and recap_dense_attn_stats.
 """
 from ._lib import RecapDesc, RecapError, load  # noqa: F401
 from .ops import (  # noqa: F401
     make_desc,
     recap_block_scores,
     recap_block_sparse_attn,
+    recap_block_sparse_attn_stats,
     recap_dense_attn,
+    recap_dense_attn_stats,
     recap_topp_mask,
     recap_workspace_size,
     sparse_step,

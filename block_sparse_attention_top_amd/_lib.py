@@ -36,6 +36,8 @@ class RecapDesc(ctypes.Structure):
 _vp = ctypes.c_void_p
 _dp = ctypes.POINTER(RecapDesc)
 _fp = ctypes.POINTER(ctypes.c_float)
+ABI_VERSION = 2
+
 SIGNATURES = {
     "recap_abi_version": (ctypes.c_int, []),
     "recap_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -47,6 +49,11 @@ SIGNATURES = {
                                                _vp, _fp, _vp, _vp, ctypes.c_size_t, _vp]),
     "recap_dense_attn": (ctypes.c_int, [_dp, _vp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp, _vp,
                                         _vp, ctypes.c_size_t, _vp]),
+    "recap_block_sparse_attn_stats": (ctypes.c_int, [_dp, _vp, _vp, _vp, _vp, _vp,
+                                                     ctypes.c_float, _vp, _fp, _vp, _vp, _vp,
+                                                     ctypes.c_size_t, _vp]),
+    "recap_dense_attn_stats": (ctypes.c_int, [_dp, _vp, _vp, _vp, ctypes.c_float, _vp, _vp,
+                                              _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
 }
 
 _lock = threading.Lock()
@@ -72,7 +79,7 @@ def load() -> ctypes.CDLL:
                 fn = getattr(lib, name)
                 fn.restype = res
                 fn.argtypes = args
-            if lib.recap_abi_version() != 1:
+            if lib.recap_abi_version() != ABI_VERSION:
                 raise RuntimeError("librecap.so ABI version mismatch")
             _lib = lib
         return _lib

@@ -616,13 +616,23 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RECAP_W
     // weights), the block is left to the residual pass, which recomputes the sparse output
     // with its own maximum.
     const float ls = cross_half_sum(ka.l);
-    const bool bad = qrow < p.N && !(ls >= 0x1p-64f);
-    if (__builtin_amdgcn_ballot_w64(bad) != 0 && lane == 0) atomicOr(&blk_flag[(wave * 32) / p.block], 1);
-    __syncthreads();
-    const bool flagged = blk_flag[(wave * 32) / p.block] != 0;
-    if (qb < p.M && lane == 0 && (wave * 32) % p.block == 0)
-      p.flags[(int64_t)bh * p.M + qb] = flagged ? 1 : 0;
+    const bool want_r = p.res_out != nullptr;  // the same for the whole grid
+    bool flagged = false;
+    if (want_r) {
+      const bool bad = qrow < p.N && !(ls >= 0x1p-64f);
+      if (__builtin_amdgcn_ballot_w64(bad) != 0 && lane == 0)
+        atomicOr(&blk_flag[(wave * 32) / p.block], 1);
+      __syncthreads();
+      flagged = blk_flag[(wave * 32) / p.block] != 0;
+      if (qb < p.M && lane == 0 && (wave * 32) % p.block == 0)
+        p.flags[(int64_t)bh * p.M + qb] = flagged ? 1 : 0;
+    }
     if (qrow >= p.N) return;
+    if (half == 0) {
+      const int64_t srow = (int64_t)bh * p.N + qrow;
+      if (p.lse_out != nullptr) p.lse_out[srow] = (sm.m + log2f(lt)) * kLn2;
+      if (p.kmass_out != nullptr) p.kmass_out[srow] = ls / lt;
+    }
     const int64_t orow = base + (int64_t)qrow * p.st.n;
     const float invs = ls > 0.f ? 1.0f / ls : 0.f;
     float* odw = p.od_ws + ((int64_t)bh * p.npad + qrow) * D;
@@ -644,7 +654,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RECAP_W
         }
         *reinterpret_cast<bf16x4*>(p.out + orow + d0) = wo;
         if (flagged) *reinterpret_cast<f32x4*>(odw + d0) = vd;
-        else *reinterpret_cast<bf16x4*>(p.res_out + orow + d0) = wr;
+        else if (want_r) *reinterpret_cast<bf16x4*>(p.res_out + orow + d0) = wr;
       }
     }
     }
@@ -653,6 +663,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RECAP_W
 
   if (qrow >= p.N) return;
   const int64_t orow = base + (int64_t)qrow * p.st.n;
+  if (MODE != kCaptureR && p.lse_out != nullptr && half == 0)
+    p.lse_out[(int64_t)bh * p.N + qrow] = lt > 0.f ? (sm.m + log2f(lt)) * kLn2 : -INFINITY;
 
   if (MODE == kCaptureR) {
     // R = O_dense - O_sparse from the fp32 dense output of the same inputs; exactly zero when

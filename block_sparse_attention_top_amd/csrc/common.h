@@ -16,6 +16,7 @@ constexpr int kMaxHeads = 128;
 constexpr int kMaxBlocks = 8192;  // M upper bound (include/recap.h RECAP_MAX_BLOCKS)
 constexpr int kKeyTile = 64;  // keys per attention inner-loop tile
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 
 struct HeadScalars {
   float v[kMaxHeads];
@@ -64,6 +65,8 @@ struct AttnParams {
   bf16_t* res_out;  // capture: residual output
   float* od_ws;     // capture: fp32 dense output [B*H][npad][D] of blocks left to the residual pass
   uint8_t* flags;   // capture: [B*H*M] 1 = residual of this query block left to the residual pass
+  float* lse_out;   // optional [B*H][N]: natural-log log-sum-exp of the attended scores
+  float* kmass_out; // optional [B*H][N] (capture mode): kept share of the dense attention mass
   HeadScalars res_scale;
 };
 

@@ -198,10 +198,14 @@ int recap_topp_mask(const recap_desc* d, const float* probs, const float* top_p_
                               mask_opt, kept_mass_opt, (hipStream_t)stream));
 }
 
-int recap_block_sparse_attn(const recap_desc* d, const void* q, const void* k, const void* v,
-                            const int32_t* kept_count, const int32_t* kept_idx, float sm_scale,
-                            const void* residual_opt, const float* res_scale_host, void* out,
-                            void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int sparse_impl(const recap_desc* d, const void* q, const void* k, const void* v,
+                const int32_t* kept_count, const int32_t* kept_idx, float sm_scale,
+                const void* residual_opt, const float* res_scale_host, void* out,
+                float* lse_out, void* ws, size_t ws_bytes, void* stream) {
   int s = validate_desc(d);
   if (s != RECAP_OK) return s;
   if (q == nullptr || k == nullptr || v == nullptr || kept_count == nullptr ||
@@ -212,6 +216,7 @@ int recap_block_sparse_attn(const recap_desc* d, const void* q, const void* k, c
       !aligned16(kept_count) || !aligned16(kept_idx) ||
       (residual_opt != nullptr && !aligned16(residual_opt)))
     return RECAP_E_ALIGN;
+  if (lse_out != nullptr && !aligned16(lse_out)) return RECAP_E_ALIGN;
   if (!isfinite(sm_scale) || !(sm_scale > 0.f)) return RECAP_E_VALUE;
   if (out == q || out == k || out == v || (residual_opt != nullptr && out == residual_opt))
     return RECAP_E_VALUE;
@@ -247,27 +252,30 @@ int recap_block_sparse_attn(const recap_desc* d, const void* q, const void* k, c
   p.idx = kept_idx;
   p.res = (const bf16_t*)residual_opt;
   p.out = (bf16_t*)out;
+  p.lse_out = lse_out;
   return launched(launch_attention(p, d->batch, d->head_dim, kSparse, st));
 }
 
-int recap_dense_attn(const recap_desc* d, const void* q, const void* k, const void* v,
-                     float sm_scale, const int32_t* kept_count_opt, const int32_t* kept_idx_opt,
-                     void* out, void* residual_out_opt, void* ws, size_t ws_bytes,
-                     void* stream) {
+int dense_impl(const recap_desc* d, const void* q, const void* k, const void* v,
+               float sm_scale, const int32_t* kept_count_opt, const int32_t* kept_idx_opt,
+               void* out, void* residual_out_opt, float* lse_out, float* kmass_out,
+               void* ws, size_t ws_bytes, void* stream) {
   int s = validate_desc(d);
   if (s != RECAP_OK) return s;
   if (q == nullptr || k == nullptr || v == nullptr || out == nullptr) return RECAP_E_NULL;
-  const bool capture = residual_out_opt != nullptr;
+  // the kept-block accumulation runs for the residual and for the kept-mass output
+  const bool capture = residual_out_opt != nullptr || kmass_out != nullptr;
   if (capture && (kept_count_opt == nullptr || kept_idx_opt == nullptr)) return RECAP_E_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
-      (capture && (!aligned16(residual_out_opt) || !aligned16(kept_count_opt) ||
-                   !aligned16(kept_idx_opt))))
+      (residual_out_opt != nullptr && !aligned16(residual_out_opt)) ||
+      (capture && (!aligned16(kept_count_opt) || !aligned16(kept_idx_opt))) ||
+      (lse_out != nullptr && !aligned16(lse_out)) ||
+      (kmass_out != nullptr && !aligned16(kmass_out)))
     return RECAP_E_ALIGN;
   if (!isfinite(sm_scale) || !(sm_scale > 0.f)) return RECAP_E_VALUE;
-  if (out == q || out == k || out == v || (capture && (residual_out_opt == out ||
-                                                       residual_out_opt == q ||
-                                                       residual_out_opt == k ||
-                                                       residual_out_opt == v)))
+  if (out == q || out == k || out == v ||
+      (residual_out_opt != nullptr && (residual_out_opt == out || residual_out_opt == q ||
+                                       residual_out_opt == k || residual_out_opt == v)))
     return RECAP_E_VALUE;
   const int op = capture ? RECAP_OP_DENSE_CAPTURE : RECAP_OP_DENSE;
   if ((s = check_workspace(op, d, ws, ws_bytes)) != RECAP_OK) return s;
@@ -298,11 +306,55 @@ int recap_dense_attn(const recap_desc* d, const void* q, const void* k, const vo
   p.res_out = (bf16_t*)residual_out_opt;
   p.od_ws = capture ? (float*)((char*)ws + vt_bytes(d)) : nullptr;
   p.flags = capture ? (uint8_t*)ws + vt_bytes(d) + snapshot_bytes(d) : nullptr;
+  p.lse_out = lse_out;
+  p.kmass_out = kmass_out;
   // capture: the dense pass also accumulates the kept blocks and writes R; the residual pass
   // only recomputes query blocks the dense pass flagged (kept mass underflow), others exit
   e = launch_attention(p, d->batch, d->head_dim, capture ? kDenseCapture : kDense, st);
-  if (e == hipSuccess && capture) e = launch_attention(p, d->batch, d->head_dim, kCaptureR, st);
+  if (e == hipSuccess && residual_out_opt != nullptr)
+    e = launch_attention(p, d->batch, d->head_dim, kCaptureR, st);
   return launched(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+int recap_block_sparse_attn(const recap_desc* d, const void* q, const void* k, const void* v,
+                            const int32_t* kept_count, const int32_t* kept_idx, float sm_scale,
+                            const void* residual_opt, const float* res_scale_host, void* out,
+                            void* ws, size_t ws_bytes, void* stream) {
+  return sparse_impl(d, q, k, v, kept_count, kept_idx, sm_scale, residual_opt, res_scale_host,
+                     out, nullptr, ws, ws_bytes, stream);
+}
+
+int recap_block_sparse_attn_stats(const recap_desc* d, const void* q, const void* k,
+                                  const void* v, const int32_t* kept_count,
+                                  const int32_t* kept_idx, float sm_scale,
+                                  const void* residual_opt, const float* res_scale_host,
+                                  void* out, float* lse_out, void* ws, size_t ws_bytes,
+                                  void* stream) {
+  if (lse_out == nullptr) return RECAP_E_NULL;
+  return sparse_impl(d, q, k, v, kept_count, kept_idx, sm_scale, residual_opt, res_scale_host,
+                     out, lse_out, ws, ws_bytes, stream);
+}
+
+int recap_dense_attn(const recap_desc* d, const void* q, const void* k, const void* v,
+                     float sm_scale, const int32_t* kept_count_opt, const int32_t* kept_idx_opt,
+                     void* out, void* residual_out_opt, void* ws, size_t ws_bytes,
+                     void* stream) {
+  return dense_impl(d, q, k, v, sm_scale, kept_count_opt, kept_idx_opt, out, residual_out_opt,
+                    nullptr, nullptr, ws, ws_bytes, stream);
+}
+
+int recap_dense_attn_stats(const recap_desc* d, const void* q, const void* k, const void* v,
+                           float sm_scale, const int32_t* kept_count_opt,
+                           const int32_t* kept_idx_opt, void* out, void* residual_out_opt,
+                           float* lse_out, float* kept_mass_out_opt, void* ws,
+                           size_t ws_bytes, void* stream) {
+  if (lse_out == nullptr) return RECAP_E_NULL;
+  return dense_impl(d, q, k, v, sm_scale, kept_count_opt, kept_idx_opt, out, residual_out_opt,
+                    lse_out, kept_mass_out_opt, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

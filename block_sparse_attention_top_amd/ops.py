@@ -119,10 +119,22 @@ def recap_topp_mask(desc: RecapDesc, probs, top_p, kept_count=None, kept_idx=Non
     return kept_count, kept_idx, mask, mass
 
 
+def _row_stat(desc: RecapDesc, given: Optional[torch.Tensor], device) -> torch.Tensor:
+    if given is None:
+        return torch.empty((desc.batch, desc.heads, desc.seq), dtype=torch.float32, device=device)
+    if given.dtype != torch.float32 or tuple(given.shape) != (desc.batch, desc.heads, desc.seq) \
+            or not given.is_contiguous():
+        raise ValueError("row statistics are contiguous fp32 [B, H, N]")
+    return given
+
+
 def recap_block_sparse_attn(desc: RecapDesc, q, k, v, kept_count, kept_idx,
                             sm_scale: Optional[float] = None, residual=None, res_scale=None,
-                            out=None, workspace=None, stream=None) -> torch.Tensor:
-    """Attention over the kept blocks, optionally O += c_h * R (bf16, q's layout)."""
+                            out=None, workspace=None, stream=None, lse=None,
+                            want_lse: bool = False):
+    """Attention over the kept blocks, optionally O += c_h * R (bf16, q's layout). With
+    want_lse (or lse given) returns (out, lse) with lse the fp32 [B,H,N] log-sum-exp of the
+    attended scores (recap_block_sparse_attn_stats)."""
     _same_layout(desc, q, k, v, out, residual)
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(desc.head_dim)
@@ -134,6 +146,13 @@ def recap_block_sparse_attn(desc: RecapDesc, q, k, v, kept_count, kept_idx,
             raise ValueError("res_scale is required with a residual")
         rs = _host_floats(res_scale, desc.heads, "res_scale")
     ws, nbytes = _workspace(_lib.OP_SPARSE, desc, q.device, workspace)
+    if want_lse or lse is not None:
+        lse = _row_stat(desc, lse, q.device)
+        check(_lib.load().recap_block_sparse_attn_stats(
+            ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(kept_count), _ptr(kept_idx),
+            float(sm_scale), _ptr(residual), rs, _ptr(out), _ptr(lse), _ptr(ws), nbytes,
+            _stream(stream)), "recap_block_sparse_attn_stats")
+        return out, lse
     check(_lib.load().recap_block_sparse_attn(
         ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(kept_count), _ptr(kept_idx),
         float(sm_scale), _ptr(residual), rs, _ptr(out), _ptr(ws), nbytes, _stream(stream)),
@@ -143,9 +162,12 @@ def recap_block_sparse_attn(desc: RecapDesc, q, k, v, kept_count, kept_idx,
 
 def recap_dense_attn(desc: RecapDesc, q, k, v, sm_scale: Optional[float] = None,
                      kept_count=None, kept_idx=None, out=None, residual_out=None,
-                     capture: bool = False, workspace=None, stream=None):
+                     capture: bool = False, workspace=None, stream=None,
+                     want_lse: bool = False, want_kept_mass: bool = False):
     """Dense attention; with capture=True (or residual_out) also R = O_dense - O_sparse.
-    Returns out, or (out, residual) when capturing."""
+    Returns out, or (out, residual) when capturing. With want_lse / want_kept_mass the call
+    goes through recap_dense_attn_stats and returns a dict with the keys out, residual (or
+    None), lse and kept_mass (or None), each row statistic fp32 [B,H,N]."""
     _same_layout(desc, q, k, v, out, residual_out)
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(desc.head_dim)
@@ -154,13 +176,44 @@ def recap_dense_attn(desc: RecapDesc, q, k, v, sm_scale: Optional[float] = None,
     capture = capture or residual_out is not None
     if capture and residual_out is None:
         residual_out = _like_out(q)
-    op = _lib.OP_DENSE_CAPTURE if capture else _lib.OP_DENSE
+    stats = want_lse or want_kept_mass
+    op = _lib.OP_DENSE_CAPTURE if (capture or want_kept_mass) else _lib.OP_DENSE
     ws, nbytes = _workspace(op, desc, q.device, workspace)
+    if stats:
+        lse = _row_stat(desc, None, q.device)
+        kmass = _row_stat(desc, None, q.device) if want_kept_mass else None
+        check(_lib.load().recap_dense_attn_stats(
+            ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), float(sm_scale), _ptr(kept_count),
+            _ptr(kept_idx), _ptr(out), _ptr(residual_out), _ptr(lse), _ptr(kmass), _ptr(ws),
+            nbytes, _stream(stream)), "recap_dense_attn_stats")
+        return {"out": out, "residual": residual_out, "lse": lse, "kept_mass": kmass}
     check(_lib.load().recap_dense_attn(
         ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), float(sm_scale), _ptr(kept_count),
         _ptr(kept_idx), _ptr(out), _ptr(residual_out), _ptr(ws), nbytes, _stream(stream)),
         "recap_dense_attn")
     return (out, residual_out) if capture else out
+
+
+def recap_block_sparse_attn_stats(desc: RecapDesc, q, k, v, kept_count, kept_idx,
+                                  sm_scale: Optional[float] = None, residual=None,
+                                  res_scale=None, out=None, lse=None, workspace=None,
+                                  stream=None):
+    """(out, lse): recap_block_sparse_attn plus the fp32 [B,H,N] log-sum-exp of the scores
+    over each query's kept keys."""
+    return recap_block_sparse_attn(desc, q, k, v, kept_count, kept_idx, sm_scale, residual,
+                                   res_scale, out, workspace, stream, lse=lse, want_lse=True)
+
+
+def recap_dense_attn_stats(desc: RecapDesc, q, k, v, sm_scale: Optional[float] = None,
+                           kept_count=None, kept_idx=None, out=None, residual_out=None,
+                           capture: bool = False, want_kept_mass: bool = False,
+                           workspace=None, stream=None):
+    """recap_dense_attn plus the dense log-sum-exp and, with the kept lists and
+    want_kept_mass, the kept share of each row's dense attention mass; returns the dict of
+    recap_dense_attn(..., want_lse=True)."""
+    return recap_dense_attn(desc, q, k, v, sm_scale, kept_count, kept_idx, out, residual_out,
+                            capture, workspace, stream, want_lse=True,
+                            want_kept_mass=want_kept_mass)
 
 
 def sparse_step(desc: RecapDesc, q, k, v, top_p, sm_scale: Optional[float] = None,

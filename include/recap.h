@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define RECAP_ABI_VERSION 1
+#define RECAP_ABI_VERSION 2 /* 2: adds the *_stats entry points */
 #define RECAP_MAX_HEADS 128   /* per-head host arrays are passed by value to the kernels */
 #define RECAP_MAX_BLOCKS 8192 /* M = ceil(N / block) upper bound (top-p sorts a row in LDS) */
 
@@ -149,13 +149,43 @@ int recap_block_sparse_attn(const recap_desc* d, const void* q, const void* k, c
  *   R = O_dense - O_sparse
  * with O_sparse the block-sparse output on the same inputs and kept set (RECAP Sec. 3.2:
  * the discrepancy cached at the refresh step; Sec. 2: dense-minus-window residuals), in bf16.
- * Kept blocks are visited first, so O_sparse is the same fp32 state a sparse pass reaches;
- * with every block kept R is exactly zero. ws: recap_workspace_size(RECAP_OP_DENSE) bytes,
- * or RECAP_OP_DENSE_CAPTURE when capturing. */
+ * The kept blocks' products are also summed on their own, under the running max of the dense
+ * pass; a query block whose kept weights underflow against that max (sum below 2^-64) has
+ * its sparse output recomputed over its kept list alone. With every block kept R is exactly
+ * zero. ws: recap_workspace_size(RECAP_OP_DENSE) bytes, or RECAP_OP_DENSE_CAPTURE when
+ * capturing. */
 int recap_dense_attn(const recap_desc* d, const void* q, const void* k, const void* v,
                      float sm_scale, const int32_t* kept_count_opt, const int32_t* kept_idx_opt,
                      void* out, void* residual_out_opt, void* ws, size_t ws_bytes,
                      void* stream);
+
+/* Row statistics of the attention computed above, written from the softmax state of the same
+ * pass (the GSRS abstract on the RECAP page at thelatestinai.com: exact attention weights
+ * obtained inside the flash-attention computation; the DFSAttn page "Ride the Wave":
+ * attention recall of a block-sparse mask). Both outputs are fp32 device arrays indexed
+ * [b, h, t] (contiguous [B,H,N], 16-byte aligned), one value per query token t < N:
+ *   lse_out[b,h,t]       = ln sum_u exp(sm_scale * Q_t . K_u) over the keys u the call attends
+ *                          (kept key blocks for the sparse call, all N keys for the dense
+ *                          call); -inf for a row with an empty kept list;
+ *   kept_mass_out[b,h,t] = sum over the kept keys u of softmax_u(sm_scale * Q_t . K_u) taken
+ *                          over all N keys: the share of the dense attention mass the kept set
+ *                          holds, exp(lse_kept - lse_dense), in [0, 1].
+ * The weights behind both are the bf16-rounded ones the products use.
+ * recap_block_sparse_attn_stats: as recap_block_sparse_attn, plus lse_out (required).
+ * recap_dense_attn_stats: as recap_dense_attn, plus lse_out (required) and kept_mass_out
+ * (optional; needs the kept lists, and then the RECAP_OP_DENSE_CAPTURE workspace even
+ * without residual_out). */
+int recap_block_sparse_attn_stats(const recap_desc* d, const void* q, const void* k,
+                                  const void* v, const int32_t* kept_count,
+                                  const int32_t* kept_idx, float sm_scale,
+                                  const void* residual_opt, const float* res_scale_host,
+                                  void* out, float* lse_out, void* ws, size_t ws_bytes,
+                                  void* stream);
+int recap_dense_attn_stats(const recap_desc* d, const void* q, const void* k, const void* v,
+                           float sm_scale, const int32_t* kept_count_opt,
+                           const int32_t* kept_idx_opt, void* out, void* residual_out_opt,
+                           float* lse_out, float* kept_mass_out_opt, void* ws,
+                           size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -91,3 +91,10 @@ def masked_attention(q, k, v, n_tokens, block, sm_scale, mask_rows):
         toks = [u for u in range(n_tokens) if (u // block) in mask_rows[i]]
         out.append(attention_row(q[t], [k[u] for u in toks], [v[u] for u in toks], sm_scale))
     return out
+
+
+def lse_row(qt, keys, sm_scale):
+    """ln sum_u exp(s * q . k_u) for one query over a list of key rows, with plain floats."""
+    logits = [sm_scale * sum(a * b for a, b in zip(qt, ku)) for ku in keys]
+    mx = max(logits)
+    return mx + math.log(sum(math.exp(x - mx) for x in logits))

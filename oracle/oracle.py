@@ -208,6 +208,59 @@ def dense_with_capture(q, k, v, block: int, sm_scale: float, mask: np.ndarray, r
     return o_d, o_d - o_s
 
 
+def _attended_tokens(mask, b, h, i, starts, ends):
+    js = np.nonzero(mask[b, h, i])[0]
+    if len(js) == 0:
+        raise ValueError("a query block must keep at least one key block")
+    return np.concatenate([np.arange(starts[j], ends[j]) for j in js])
+
+
+def attention_lse(q, k, block: int, sm_scale: float, mask=None, rows=None) -> np.ndarray:
+    """Log-sum-exp of the scaled scores over the keys each query attends:
+    lse_t = ln sum_u exp(s * Q_t . K_u), u over the valid tokens of the query block's kept key
+    blocks (every key when mask is None). It is the normaliser a flash-attention pass ends
+    with, from which the exact attention weights follow as exp(s * Q_t . K_u - lse_t) (GSRS
+    abstract [GSRS]). Max-shifted in fp64. Returns float64 [B, H, N] (NaN outside
+    `rows`, an iterable of (b, h, i) query blocks)."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    B, H, N, _ = q.shape
+    starts, ends = block_partition(N, block)
+    M = len(starts)
+    out = np.full((B, H, N), np.nan, dtype=np.float64)
+    if rows is None:
+        rows = [(b, h, i) for b in range(B) for h in range(H) for i in range(M)]
+    for b, h, i in rows:
+        toks = np.arange(N) if mask is None else _attended_tokens(mask, b, h, i, starts, ends)
+        qs = slice(starts[i], ends[i])
+        sc = float(sm_scale) * (q[b, h, qs] @ k[b, h, toks].T)
+        mx = sc.max(axis=-1)
+        out[b, h, qs] = mx + np.log(np.exp(sc - mx[:, None]).sum(axis=-1))
+    return out
+
+
+def kept_attention_mass(q, k, block: int, sm_scale: float, mask, rows=None) -> np.ndarray:
+    """Share of each query's dense attention mass that falls on its kept key blocks:
+    sum over kept tokens u of softmax_u(s * Q_t . K_u) taken over all N keys. This is the
+    attention recall of the block mask ([DFS] abstract) measured exactly at a dense pass.
+    Returns float64 [B, H, N] in [0, 1] (NaN outside `rows`)."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    B, H, N, _ = q.shape
+    starts, ends = block_partition(N, block)
+    M = len(starts)
+    out = np.full((B, H, N), np.nan, dtype=np.float64)
+    if rows is None:
+        rows = [(b, h, i) for b in range(B) for h in range(H) for i in range(M)]
+    for b, h, i in rows:
+        qs = slice(starts[i], ends[i])
+        sc = float(sm_scale) * (q[b, h, qs] @ k[b, h].T)
+        w = np.exp(sc - sc.max(axis=-1, keepdims=True))
+        w /= w.sum(axis=-1, keepdims=True)
+        out[b, h, qs] = w[:, _attended_tokens(mask, b, h, i, starts, ends)].sum(axis=-1)
+    return out
+
+
 def block_sparsity(count: np.ndarray, m: int) -> float:
     """Fraction of skipped block pairs: 1 - mean(k*) / M."""
     return 1.0 - float(np.mean(count)) / float(m)

@@ -289,6 +289,86 @@ def check_epilogue_identities():
     assert np.all(r_all == 0.0)
 
 
+def check_lse_closed_forms():
+    """Zero queries score every key 0, so lse = ln(number of attended keys): ln N dense, and
+    ln(sum of the kept blocks' token counts) under a mask (ragged last block included). With
+    every key equal to k0, lse_t = s * q_t . k0 + ln n. Shifting every key by c shifts the
+    dense lse of query t by s * q_t . c."""
+    n, b, d, s = 150, 32, 8, 0.7  # blocks of 32, 32, 32, 32, 22
+    m = -(-n // b)
+    q0 = np.zeros((1, 1, n, d))
+    k = _rand((1, 1, n, d), 301)
+    assert np.allclose(O.attention_lse(q0, k, b, s), math.log(n), rtol=0, atol=1e-13)
+    mask = np.zeros((1, 1, m, m), bool)
+    mask[0, 0, :, 0] = True
+    mask[0, 0, 1, 4] = True
+    mask[0, 0, 3, 2:5] = True
+    sizes = np.array([32, 32, 32, 32, 22])
+    lse = O.attention_lse(q0, k, b, s, mask)
+    for i in range(m):
+        want = math.log(sizes[mask[0, 0, i]].sum())
+        assert np.allclose(lse[0, 0, i * b:min(n, (i + 1) * b)], want, rtol=0, atol=1e-13)
+    q = _rand((1, 1, n, d), 302)
+    k0 = _rand((d,), 303)
+    keq = np.broadcast_to(k0, (1, 1, n, d)).copy()
+    want = s * (q[0, 0] @ k0) + math.log(n)
+    assert np.allclose(O.attention_lse(q, keq, b, s)[0, 0], want, rtol=0, atol=1e-12)
+    c = _rand((d,), 304)
+    shifted = O.attention_lse(q, k + c, b, s) - O.attention_lse(q, k, b, s)
+    assert np.allclose(shifted[0, 0], s * (q[0, 0] @ c), rtol=0, atol=1e-12)
+
+
+def check_lse_vs_brute():
+    """Vectorised lse equals a scalar Python loop (dense and masked) on tiny inputs."""
+    n, b, d, s = 37, 8, 4, 0.9
+    m = -(-n // b)
+    q, k = _rand((1, 2, n, d), 311), _rand((1, 2, n, d), 312)
+    mask = np.zeros((1, 2, m, m), bool)
+    mask[0, 0, :, 0] = True
+    mask[0, 0, 2, 3] = True
+    mask[0, 1] = np.eye(m, dtype=bool)
+    mask[0, 1, 4, 1] = True
+    dense, masked = O.attention_lse(q, k, b, s), O.attention_lse(q, k, b, s, mask)
+    for h in range(2):
+        for t in range(n):
+            i = t // b
+            toks = [u for u in range(n) if mask[0, h, i, u // b]]
+            assert abs(dense[0, h, t] - brute.lse_row(q[0, h, t], list(k[0, h]), s)) < 1e-12
+            assert abs(masked[0, h, t] -
+                       brute.lse_row(q[0, h, t], [k[0, h, u] for u in toks], s)) < 1e-12
+
+
+def check_kept_mass_identities():
+    """Kept mass: 1 with every block kept; equals exp(lse_kept - lse_dense); the dense output
+    is the kept-mass mixture of the sparse output and the output over the other keys; grows
+    with p (nested kept sets) and stays in [0, 1]."""
+    n, b, d, s = 200, 32, 8, 0.4
+    m = -(-n // b)
+    q, k, v = (_rand((1, 2, n, d), 320 + i) for i in range(3))
+    probs = O.block_scores(q, k, b, s)
+    lo = O.topp_select(probs, 0.3)["mask"]
+    hi = O.topp_select(probs, 0.6)["mask"]
+    assert np.all(hi >= lo) and lo.sum() < hi.sum() < hi.size
+    ones = np.ones((1, 2, m, m), bool)
+    assert np.allclose(O.kept_attention_mass(q, k, b, s, ones), 1.0, rtol=0, atol=1e-14)
+    km_lo, km_hi = (O.kept_attention_mass(q, k, b, s, mk) for mk in (lo, hi))
+    assert np.all((km_lo > 0) & (km_lo <= km_hi + 1e-15) & (km_hi <= 1 + 1e-15))
+    assert np.any(km_hi < 1 - 1e-6)
+    lse_d = O.attention_lse(q, k, b, s)
+    for mk, km in ((lo, km_lo), (hi, km_hi)):
+        assert np.allclose(km, np.exp(O.attention_lse(q, k, b, s, mk) - lse_d), rtol=0,
+                           atol=1e-12)
+    o_d = O.dense_attention(q, k, v, s)
+    o_s = O.masked_attention(q, k, v, b, s, lo)
+    rows = [(0, h, i) for h in range(2) for i in range(m) if not lo[0, h, i].all()]
+    o_r = O.masked_attention(q, k, v, b, s, ~lo, rows=rows)
+    for _, h, i in rows:
+        sl = slice(i * b, min(n, (i + 1) * b))
+        w = km_lo[0, h, sl][:, None]
+        assert np.allclose(w * o_s[0, h, sl] + (1 - w) * o_r[0, h, sl], o_d[0, h, sl],
+                           rtol=0, atol=1e-12)
+
+
 ALL_CHECKS = [
     check_pool_block_constant,
     check_pool_closed_form_ragged,
@@ -307,6 +387,9 @@ ALL_CHECKS = [
     check_masked_vs_brute,
     check_attention_hull_and_single_token,
     check_epilogue_identities,
+    check_lse_closed_forms,
+    check_lse_vs_brute,
+    check_kept_mass_identities,
 ]
 
 

@@ -36,7 +36,7 @@ def test_header_symbols_exported():
 
 def test_version_and_status_strings():
     lib = _lib.load()
-    assert lib.recap_abi_version() == 1
+    assert lib.recap_abi_version() == _lib.ABI_VERSION == 2
     for st in list(_lib.STATUS_NAMES) + [-99]:
         s = lib.recap_status_string(st)
         assert s and len(s.decode()) > 1
@@ -157,3 +157,30 @@ def test_sparse_and_dense_validation():
     assert dense(cnt=_p(), idx=_p(), rout=_p(FAKE + 4096), n=need_c) == -5  # R aliases out
     assert dense() == -7
     assert dense(cnt=_p(), idx=_p(), rout=_p(FAKE + 8192), n=need_c) == -7
+
+
+@cpu_only
+def test_stats_validation():
+    lib = _lib.load()
+    d = desc(H=2)
+    _, need = ws_size(_lib.OP_SPARSE, d)
+    _, need_c = ws_size(_lib.OP_DENSE_CAPTURE, d)
+
+    def sparse(lse=_p(FAKE + 12288)):
+        return lib.recap_block_sparse_attn_stats(ctypes.byref(d), _p(), _p(FAKE + 1024),
+                                                 _p(FAKE + 2048), _p(), _p(), 0.125, None, None,
+                                                 _p(FAKE + 4096), lse, _p(), need, None)
+    assert sparse(lse=None) == -1  # the statistics output is the point of this entry point
+    assert sparse(lse=_p(FAKE + 12290)) == -4
+    assert sparse() == -7
+
+    def dense(cnt=None, idx=None, rout=None, lse=_p(FAKE + 12288), km=None, n=need):
+        return lib.recap_dense_attn_stats(ctypes.byref(d), _p(), _p(FAKE + 1024),
+                                          _p(FAKE + 2048), 0.125, cnt, idx, _p(FAKE + 4096),
+                                          rout, lse, km, _p(), n, None)
+    assert dense(lse=None) == -1
+    assert dense(km=_p(FAKE + 16384)) == -1  # kept mass needs the kept lists
+    assert dense(cnt=_p(), idx=_p(), km=_p(FAKE + 16384)) == -6  # and the capture workspace
+    assert dense(cnt=_p(), idx=_p(), km=_p(FAKE + 16388), n=need_c) == -4
+    assert dense() == -7
+    assert dense(cnt=_p(), idx=_p(), km=_p(FAKE + 16384), n=need_c) == -7

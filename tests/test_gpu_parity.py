@@ -62,7 +62,18 @@ def run_small(bsa, cfg, seq=None, layout="bhnd", top_p=None, res_scale=None):
                                         res_scale=c.tolist())
     od = bsa.recap_dense_attn(desc, qd, kd, vd, s)
     od2, rcap = bsa.recap_dense_attn(desc, qd, kd, vd, s, count, idx, capture=True)
+    # row statistics: the same kernels with extra writes, so outputs must agree bit for bit
+    out_st, lse_s = bsa.recap_block_sparse_attn_stats(desc, qd, kd, vd, count, idx, s)
+    st_d = bsa.recap_dense_attn_stats(desc, qd, kd, vd, s)
+    st_k = bsa.recap_dense_attn_stats(desc, qd, kd, vd, s, count, idx, want_kept_mass=True)
+    st_c = bsa.recap_dense_attn_stats(desc, qd, kd, vd, s, count, idx, capture=True,
+                                      want_kept_mass=True)
     torch.cuda.synchronize()
+    assert torch.equal(out_st, out) and torch.equal(st_d["out"], od)
+    assert torch.equal(st_k["out"], od2) and st_k["residual"] is None
+    assert torch.equal(st_c["out"], od2) and torch.equal(st_c["residual"], rcap)
+    assert torch.equal(st_k["kept_mass"], st_c["kept_mass"])
+    assert torch.equal(st_k["lse"], st_c["lse"])
 
     q64, k64, v64, r64 = (synth.to_f64(x) for x in (q, k, v, r))
     ref_probs = O.block_scores(q64, k64, cfg.block, s)
@@ -82,6 +93,13 @@ def run_small(bsa, cfg, seq=None, layout="bhnd", top_p=None, res_scale=None):
     parity.check_out(f64(od), ref_d, "dense")
     parity.check_out(f64(od2), ref_d, "dense (capture pass)")
     parity.check_out(ref_s + f64(rcap), ref_d, "sparse + captured residual")
+    lse_d_ref = O.attention_lse(q64, k64, cfg.block, s)
+    parity.check_row_stat(lse_s.cpu().numpy(), O.attention_lse(q64, k64, cfg.block, s, gmask),
+                          "sparse lse")
+    parity.check_row_stat(st_d["lse"].cpu().numpy(), lse_d_ref, "dense lse")
+    parity.check_row_stat(st_c["lse"].cpu().numpy(), lse_d_ref, "dense lse (capture pass)")
+    parity.check_row_stat(st_c["kept_mass"].cpu().numpy(),
+                          O.kept_attention_mass(q64, k64, cfg.block, s, gmask), "kept mass")
     return dict(count=cnt, M=M, desc=desc, dev=(qd, kd, vd, rd), p=p, s=s)
 
 
@@ -332,7 +350,9 @@ def test_full_size_refresh_then_sparse(bsa):
     say("[gpu] wan14b_720p: refresh (scores, top-p, dense + capture)")
     probs = bsa.recap_block_scores(desc, qd, kd, s)
     count, idx, mask, _ = bsa.recap_topp_mask(desc, probs, p.tolist(), want_mask=True)
-    od, rcap = bsa.recap_dense_attn(desc, qd, kd, vd, s, count, idx, capture=True)
+    st = bsa.recap_dense_attn_stats(desc, qd, kd, vd, s, count, idx, capture=True,
+                                    want_kept_mass=True)
+    od, rcap = st["out"], st["residual"]
     torch.cuda.synchronize()
     say("[check] refresh rows")
     for h in heads:
@@ -346,12 +366,18 @@ def test_full_size_refresh_then_sparse(bsa):
         ref_d = O.dense_attention(q64, k64, v64, s, rows=sel, block=cfg.block)
         ref_s = O.masked_attention(q64, k64, v64, cfg.block, s, m_h, rows=sel)
         od_h, r_h = f64(od[:, h:h + 1]), f64(rcap[:, h:h + 1])
+        parity.check_row_stat(st["lse"][:, h:h + 1].cpu().numpy(),
+                              O.attention_lse(q64, k64, cfg.block, s, rows=sel),
+                              f"dense lse h{h}")
+        parity.check_row_stat(st["kept_mass"][:, h:h + 1].cpu().numpy(),
+                              O.kept_attention_mass(q64, k64, cfg.block, s, m_h, rows=sel),
+                              f"kept mass h{h}")
         for i in rows:
             lo, hi = i * cfg.block, min(cfg.seq, (i + 1) * cfg.block)
             parity.check_out(od_h[:, :, lo:hi], ref_d[:, :, lo:hi], f"dense h{h} b{i}")
             parity.check_out(ref_s[:, :, lo:hi] + r_h[:, :, lo:hi], ref_d[:, :, lo:hi],
                              f"capture identity h{h} b{i}")
-    del od
+    del od, st
     say("[gpu] wan14b_720p: drifted sparse step 1 with the captured residual")
     q1, k1, v1 = synth.drifted(q, "q", 1), synth.drifted(k, "k", 1), synth.drifted(v, "v", 1)
     q1d, k1d, v1d = (to_dev(x) for x in (q1, k1, v1))

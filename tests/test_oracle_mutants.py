@@ -113,6 +113,27 @@ def _capture_sign(q, k, v, block, sm_scale, mask, rows=None):
     return o_d, -r
 
 
+def _lse_log2(q, k, block, sm_scale, mask=None, rows=None):
+    return _REAL["attention_lse"](q, k, block, sm_scale, mask, rows) / np.log(2.0)
+
+
+def _lse_no_scale(q, k, block, sm_scale, mask=None, rows=None):
+    return _REAL["attention_lse"](q, k, block, 1.0, mask, rows)
+
+
+def _lse_ignores_mask(q, k, block, sm_scale, mask=None, rows=None):
+    return _REAL["attention_lse"](q, k, block, sm_scale, None, rows)
+
+
+def _kept_mass_renormalised(q, k, block, sm_scale, mask, rows=None):
+    km = _REAL["kept_attention_mass"](q, k, block, sm_scale, mask, rows)
+    return np.where(np.isnan(km), km, 1.0)
+
+
+def _kept_mass_complement(q, k, block, sm_scale, mask, rows=None):
+    return 1.0 - _REAL["kept_attention_mass"](q, k, block, sm_scale, mask, rows)
+
+
 MUTANTS = {
     "pool divides by the full block size": ("block_mean_pool", _pool_divides_by_block),
     "pool takes the first token": ("block_mean_pool", _pool_first_token),
@@ -132,6 +153,11 @@ MUTANTS = {
     "epilogue subtracts the residual": ("residual_epilogue", _epilogue_minus),
     "epilogue scales reversed across heads": ("residual_epilogue", _epilogue_heads_reversed),
     "captured residual has the wrong sign": ("dense_with_capture", _capture_sign),
+    "lse in base 2": ("attention_lse", _lse_log2),
+    "lse drops the scale": ("attention_lse", _lse_no_scale),
+    "lse ignores the mask": ("attention_lse", _lse_ignores_mask),
+    "kept mass renormalised over the kept keys": ("kept_attention_mass", _kept_mass_renormalised),
+    "kept mass of the complement": ("kept_attention_mass", _kept_mass_complement),
 }
 
 
