@@ -6,6 +6,8 @@
 // CalibAtt (thelatestinai.com/papers/2603.05503) Fig. 5 thresholds the top key blocks of
 // every query block. Pooling and top-p are bound by HBM bandwidth and latency; the scores are
 // a small fp32 contraction done on the fp32 matrix cores.
+#include <atomic>
+
 #include "common.h"
 
 namespace recap {
@@ -633,6 +635,19 @@ hipError_t launch_pool(const bf16_t* q, const bf16_t* k, Strides st, int B, int 
   return hipGetLastError();
 }
 
+// Raise a kernel's dynamic-LDS limit to `bytes` once per device (the launches below then stay
+// plain stream work, with no driver call per launch).
+static hipError_t allow_lds_once(const void* kernel, int bytes, std::atomic<uint32_t>& done) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint32_t bit = dev < 32 ? 1u << dev : 0u;
+  if (bit != 0u && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess && bit != 0u) done.fetch_or(bit, std::memory_order_acq_rel);
+  return e;
+}
+
 hipError_t launch_scores(const float* qbar, const float* kbar, int BH, int M, int D,
                          float scale_log2, float* probs, hipStream_t stream) {
   const size_t lds = (size_t)kStripRows * strip_stride(M) * sizeof(float);
@@ -641,21 +656,15 @@ hipError_t launch_scores(const float* qbar, const float* kbar, int BH, int M, in
                 "two strips per CU");
   if (M <= kStripMaxM) {  // rows fit in LDS and registers: one pass
     const int sgrid = BH * ((M + kStripRows - 1) / kStripRows);
+    constexpr int kMaxLds = kStripRows * strip_stride(kStripMaxM) * sizeof(float);
+    static std::atomic<uint32_t> lds128{0u}, lds64{0u};
     if (D == 128) {
-      if (lds > 64 * 1024) {
-        const hipError_t e = hipFuncSetAttribute((const void*)score_strip_kernel<128>,
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                 (int)lds);
-        if (e != hipSuccess) return e;
-      }
+      const hipError_t e = allow_lds_once((const void*)score_strip_kernel<128>, kMaxLds, lds128);
+      if (e != hipSuccess) return e;
       score_strip_kernel<128><<<sgrid, 256, lds, stream>>>(qbar, kbar, M, scale_log2, probs);
     } else {
-      if (lds > 64 * 1024) {
-        const hipError_t e = hipFuncSetAttribute((const void*)score_strip_kernel<64>,
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                 (int)lds);
-        if (e != hipSuccess) return e;
-      }
+      const hipError_t e = allow_lds_once((const void*)score_strip_kernel<64>, kMaxLds, lds64);
+      if (e != hipSuccess) return e;
       score_strip_kernel<64><<<sgrid, 256, lds, stream>>>(qbar, kbar, M, scale_log2, probs);
     }
     return hipGetLastError();
@@ -701,11 +710,9 @@ hipError_t launch_topp(const float* probs, int B, int H, int M, const HeadScalar
   int P = 64;
   while (P < M) P <<= 1;
   const size_t lds = (size_t)P * 9;
-  if (lds > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute((const void*)topp_kernel,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-  }
+  static std::atomic<uint32_t> lds_topp{0u};
+  const hipError_t e = allow_lds_once((const void*)topp_kernel, kMaxBlocks * 9, lds_topp);
+  if (e != hipSuccess) return e;
   topp_kernel<<<B * H * M, 256, lds, stream>>>(probs, H, M, P, top_p, count, idx, mask, mass);
   return hipGetLastError();
 }

@@ -117,6 +117,8 @@ SMALL = {
     # several 32-row score tiles with a ragged last one (46 and 33 query blocks)
     "score_tiles_ragged_46": dict(name="tiny", heads=2, head_dim=64, seq=64 * 45 + 10),
     "score_tiles_ragged_33": dict(name="tiny", heads=1, head_dim=128, seq=64 * 32 + 5),
+    # the head limit of the C ABI (per-head p and c arrays of 128)
+    "max_heads_128": dict(name="tiny", heads=128, head_dim=64, seq=300),
 }
 
 
@@ -159,6 +161,100 @@ def test_scores_and_topp_long_rows(bsa, m, d):
     gmask = mask.cpu().numpy().astype(bool)
     parity.check_lists(count.cpu().numpy(), idx.cpu().numpy(), m, gmask)
     parity.check_mask(gmask, ref, O.topp_select(ref, p)["mask"], p)
+
+
+def test_max_blocks_8192(bsa):
+    """The block limit of the C ABI: M = 8192 key blocks (N = 524,285, ragged last block), so
+    the two-pass score kernel and the LDS-sort top-p run at their largest sizes. Checked on
+    sampled query blocks: probabilities, kept sets, and sparse attention rows."""
+    cfg = synth.workload("tiny", heads=1, head_dim=64, grid=(1, 1, 8192 * 64 - 3))
+    M, s, p = 8192, 64 ** -0.5, np.array([0.9])
+    say(f"[case] max blocks M={M} N={cfg.seq}")
+    q, k, v = synth.make_qkv(cfg)
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    desc = bsa.make_desc(qd, cfg.block)
+    probs = bsa.recap_block_scores(desc, qd, kd, s)
+    count, idx, _, _ = bsa.recap_topp_mask(desc, probs, p.tolist())
+    out = bsa.recap_block_sparse_attn(desc, qd, kd, vd, count, idx, s)
+    torch.cuda.synchronize()
+    rows = _sample_rows(M, 6, 8192)
+    q64, k64, v64 = synth.to_f64(q), synth.to_f64(k), synth.to_f64(v)
+    qb, kb = O.block_mean_pool(q64, cfg.block), O.block_mean_pool(k64, cfg.block)
+    ref = O.softmax_rows(s * np.matmul(qb[:, :, rows], np.swapaxes(kb, -1, -2)))
+    got = probs[:, :, rows].cpu().numpy().astype(np.float64)
+    parity.check_probs(got, ref)
+    cnt = count[:, :, rows].cpu().numpy()
+    ix = idx[:, :, rows].cpu().numpy()
+    gmask = np.zeros((1, 1, len(rows), M), bool)
+    for r in range(len(rows)):
+        gmask[0, 0, r, ix[0, 0, r, :cnt[0, 0, r]]] = True
+    parity.check_lists(cnt, ix, M, gmask)
+    parity.check_mask(gmask, ref, O.topp_select(ref, p)["mask"], p)
+    full = np.zeros((1, 1, M, M), bool)
+    full[0, 0, rows] = gmask[0, 0]
+    att = O.masked_attention(q64, k64, v64, cfg.block, s, full,
+                             rows=[(0, 0, i) for i in rows[:3]])
+    o64 = f64(out)
+    for i in rows[:3]:
+        lo, hi = i * cfg.block, min(cfg.seq, (i + 1) * cfg.block)
+        parity.check_out(o64[:, :, lo:hi], att[:, :, lo:hi], f"max-blocks block {i}")
+
+
+def test_graph_capture_replays(bsa):
+    """A refresh plus a corrected sparse step recorded in one HIP graph (the library allocates
+    nothing and never synchronises), replayed several times with eager work and new inputs in
+    between; every replay must equal the eager result bit for bit."""
+    cfg = synth.workload("tiny", heads=2, head_dim=128, grid=(1, 1, 3000))
+    s = cfg.head_dim ** -0.5
+    q, k, v = synth.make_qkv(cfg)
+    p, c = [0.9, 0.8], [1.0, 0.5]
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    q1d, k1d, v1d = (to_dev(synth.drifted(x, n, 1)) for x, n in ((q, "q"), (k, "k"), (v, "v")))
+    desc = bsa.make_desc(qd, cfg.block)
+    M = cfg.num_blocks
+    probs = torch.empty((1, 2, M, M), dtype=torch.float32, device=DEV)
+    cnt0, cnt1 = (torch.empty((1, 2, M), dtype=torch.int32, device=DEV) for _ in range(2))
+    idx0, idx1 = (torch.empty((1, 2, M, M), dtype=torch.int32, device=DEV) for _ in range(2))
+    od, rcap, out = (torch.empty_like(qd) for _ in range(3))
+    ws = {op: torch.empty(max(1, bsa.recap_workspace_size(op, desc)), dtype=torch.uint8,
+                          device=DEV) for op in (0, 2, 4)}
+
+    def step():
+        bsa.recap_block_scores(desc, qd, kd, s, probs=probs, workspace=ws[0])
+        bsa.recap_topp_mask(desc, probs, p, kept_count=cnt0, kept_idx=idx0)
+        bsa.recap_dense_attn(desc, qd, kd, vd, s, cnt0, idx0, out=od, residual_out=rcap,
+                             workspace=ws[4])
+        bsa.recap_block_scores(desc, q1d, k1d, s, probs=probs, workspace=ws[0])
+        bsa.recap_topp_mask(desc, probs, p, kept_count=cnt1, kept_idx=idx1)
+        bsa.recap_block_sparse_attn(desc, q1d, k1d, v1d, cnt1, idx1, s, residual=rcap,
+                                    res_scale=c, out=out, workspace=ws[2])
+
+    side = torch.cuda.Stream()  # default priority
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()  # eager on the side stream first (no first-use work inside the capture)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in (od, rcap, out, cnt1)]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(3):
+        for t in (od, rcap, out):
+            t.fill_(float("nan"))  # eager work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip((od, rcap, out, cnt1), eager):
+            assert torch.equal(a, b), f"replay {rep}"
+    # new inputs of the same shape flow through the recorded graph
+    qd.copy_(to_dev(synth.drifted(q, "q", 2)))
+    g.replay()
+    torch.cuda.synchronize()
+    replayed = out.clone()
+    step()
+    torch.cuda.synchronize()
+    assert torch.equal(replayed, out)
+    assert not torch.equal(replayed, eager[2])
 
 
 def test_all_kept_capture_is_exactly_zero(bsa):
