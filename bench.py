@@ -231,9 +231,20 @@ def main():
     ms_step = wall * 1e3 / args.steps
 
     per = {}
-    for name, e0, e1 in events:
-        per.setdefault(name, []).append(e0.elapsed_time(e1))
+    calls = {"refresh": [], "sparse": []}  # whole-call times (scores + top-p + attention)
+    for i, (name, e0, e1) in enumerate(events):
+        ms = e0.elapsed_time(e1)
+        per.setdefault(name, []).append(ms)
+        tag, op = name.split(".")
+        if op == "scores":
+            calls[tag].append(0.0)
+        calls[tag][-1] += ms
     avg = {k: float(np.mean(v)) for k, v in per.items()}
+
+    def dist(v):
+        v = np.asarray(v, dtype=np.float64)
+        return {"median": float(np.median(v)), "min": float(v.min()),
+                "p90": float(np.percentile(v, 90)), "n": int(v.size)}
 
     # computed-block work of one step
     dense_flops = 4.0 * D * B * H * float(N) * float(N)
@@ -315,7 +326,10 @@ def main():
         "sparse_attn_tflops": sp_tflops,
         "sparse_attn_frac_bf16_peak": sp_tflops / PEAK_BF16_TFLOPS,
         "block_sparsity": float(np.mean(sparsity)),
+        "sparse_call_tflops": float(np.mean(sparse_flops)) / (sp_call_ms * 1e-3) / 1e12,
         "per_op_ms": avg,
+        "per_op_ms_dist": {k: dist(v) for k, v in per.items()},
+        "per_call_ms_dist": {k: dist(v) for k, v in calls.items() if v},
         "roofline": main_roof,
         "roofline_sparse": sparse_roof,
         "roofline_mask": mask_roof,

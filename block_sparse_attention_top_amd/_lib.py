@@ -36,7 +36,7 @@ class RecapDesc(ctypes.Structure):
 _vp = ctypes.c_void_p
 _dp = ctypes.POINTER(RecapDesc)
 _fp = ctypes.POINTER(ctypes.c_float)
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 SIGNATURES = {
     "recap_abi_version": (ctypes.c_int, []),
@@ -54,6 +54,11 @@ SIGNATURES = {
                                                      ctypes.c_size_t, _vp]),
     "recap_dense_attn_stats": (ctypes.c_int, [_dp, _vp, _vp, _vp, ctypes.c_float, _vp, _vp,
                                               _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+    "recap_block_means": (ctypes.c_int, [_dp, _vp, _vp, _vp, _vp, _vp]),
+    "recap_scores_from_means": (ctypes.c_int, [_dp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp,
+                                               _vp]),
+    "recap_topp_mask_cand": (ctypes.c_int, [_dp, _vp, _vp, _vp, _fp, _vp, _vp, _vp, _vp, _vp]),
+    "recap_mean_drift": (ctypes.c_int, [_dp, _vp, _vp, _vp, _vp, _vp, _vp]),
 }
 
 _lock = threading.Lock()

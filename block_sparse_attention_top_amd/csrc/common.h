@@ -43,8 +43,14 @@ hipError_t launch_pool(const bf16_t* q, const bf16_t* k, Strides st, int B, int 
 hipError_t launch_scores(const float* qbar, const float* kbar, int BH, int M, int D,
                          float scale_log2, float* probs, hipStream_t stream);
 hipError_t launch_topp(const float* probs, int B, int H, int M, const HeadScalars& top_p,
-                       int32_t* count, int32_t* idx, uint8_t* mask, float* mass,
-                       hipStream_t stream);
+                       const int32_t* ccount, const int32_t* cidx, int32_t* count, int32_t* idx,
+                       uint8_t* mask, float* mass, hipStream_t stream);
+hipError_t launch_scores_cand(const float* qbar, const float* kbar, int BH, int M, int D,
+                              float scale_log2, const int32_t* ccount, const int32_t* cidx,
+                              float* probs, hipStream_t stream);
+hipError_t launch_mean_drift(const float* qbar, const float* kbar, const float* qref,
+                             const float* kref, int BH, int M, int D, float* drift,
+                             hipStream_t stream);
 hipError_t launch_pack_vt(const bf16_t* v, Strides st, int B, int H, int N, int D, int npad,
                           bf16_t* vt, hipStream_t stream);
 

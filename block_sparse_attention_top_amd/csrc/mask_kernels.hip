@@ -375,6 +375,8 @@ __device__ __forceinline__ T block_exclusive_scan(T v, T* wave_tot, T& total) {
 
 __global__ __launch_bounds__(256) void topp_kernel(const float* __restrict__ probs, int H, int M,
                                                    int P, HeadScalars top_p,
+                                                   const int32_t* __restrict__ ccount,
+                                                   const int32_t* __restrict__ cidx,
                                                    int32_t* __restrict__ count,
                                                    int32_t* __restrict__ idx,
                                                    uint8_t* __restrict__ mask,
@@ -392,13 +394,18 @@ __global__ __launch_bounds__(256) void topp_kernel(const float* __restrict__ pro
   const int h = (int)((row / M) % H);
   const float p = top_p.v[h];
   const float* pr = probs + row * M;
+  // with candidate lists the row is the first n positions, position r standing for block
+  // cidx[r] (ascending); otherwise position = block
+  const int n = ccount != nullptr ? min(max(ccount[row], 0), M) : M;
+  const int32_t* crow = cidx != nullptr ? cidx + row * M : nullptr;
+  auto block_of = [&](int pos) { return crow != nullptr ? min(max(crow[pos], 0), M - 1) : pos; };
 
   for (int t = tid; t < P; t += 256) {
-    keys[t] = t < M ? ((uint64_t)orderable(pr[t]) << 32) | (uint64_t)(0xffffffffu - (uint32_t)t)
+    keys[t] = t < n ? ((uint64_t)orderable(pr[t]) << 32) | (uint64_t)(0xffffffffu - (uint32_t)t)
                     : 0ull;
     flag[t] = 0;
   }
-  if (tid == 0) kstar_s = M;
+  if (tid == 0) kstar_s = n;
   __syncthreads();
 
   for (int kk = 2; kk <= P; kk <<= 1) {
@@ -423,7 +430,7 @@ __global__ __launch_bounds__(256) void topp_kernel(const float* __restrict__ pro
   double local = 0.0;
   for (int e = 0; e < E; ++e) {
     const int pos = lo + e;
-    if (pos < M) local += (double)from_orderable((uint32_t)(keys[pos] >> 32));
+    if (pos < n) local += (double)from_orderable((uint32_t)(keys[pos] >> 32));
   }
   double total;
   const double base = block_exclusive_scan<double>(local, wtot_d, total);
@@ -431,7 +438,7 @@ __global__ __launch_bounds__(256) void topp_kernel(const float* __restrict__ pro
     double c = base;
     for (int e = 0; e < E; ++e) {
       const int pos = lo + e;
-      if (pos >= M) break;
+      if (pos >= n) break;
       c += (double)from_orderable((uint32_t)(keys[pos] >> 32));
       if (c >= (double)p) {
         atomicMin(&kstar_s, pos + 1);
@@ -440,8 +447,8 @@ __global__ __launch_bounds__(256) void topp_kernel(const float* __restrict__ pro
     }
   }
   __syncthreads();
-  const int kstar = kstar_s;  // M when p >= 1 or when no prefix reaches p
-  if (kstar == M) {
+  const int kstar = kstar_s;  // n when p >= 1 or when no prefix reaches p
+  if (kstar == n) {
     if (tid == 0) mass_s = total;
   } else if (kstar - 1 >= lo && kstar - 1 < lo + E) {
     // the owner of position k*-1 recomputes the prefix it crossed p with
@@ -455,22 +462,30 @@ __global__ __launch_bounds__(256) void topp_kernel(const float* __restrict__ pro
   }
   __syncthreads();
 
-  // ascending compaction of the flagged indices
+  // ascending compaction of the flagged positions (ascending blocks)
   int cnt = 0;
   for (int e = 0; e < E; ++e) {
     const int jj = lo + e;
-    if (jj < M) cnt += flag[jj];
+    if (jj < n) cnt += flag[jj];
   }
   int tot_i;
   int off = block_exclusive_scan<int>(cnt, wtot_i, tot_i);
   int32_t* out_idx = idx + row * M;
   for (int e = 0; e < E; ++e) {
     const int jj = lo + e;
-    if (jj < M && flag[jj]) out_idx[off++] = jj;
+    if (jj < n && flag[jj]) out_idx[off++] = block_of(jj);
   }
   if (mask != nullptr) {
     uint8_t* mrow = mask + row * M;
-    for (int jj = tid; jj < M; jj += 256) mrow[jj] = flag[jj];
+    if (crow == nullptr) {
+      for (int jj = tid; jj < M; jj += 256) mrow[jj] = flag[jj];
+    } else {  // zeros everywhere, then ones at the kept blocks, ordered by a fence + barrier
+      for (int jj = tid; jj < M; jj += 256) mrow[jj] = 0;
+      __threadfence_block();
+      __syncthreads();
+      for (int jj = tid; jj < n; jj += 256)
+        if (flag[jj]) mrow[block_of(jj)] = 1;
+    }
   }
   if (tid == 0) {
     count[row] = kstar;
@@ -502,6 +517,8 @@ __device__ __forceinline__ double wave_sum(double x) {
 template <int VPL>
 __global__ __launch_bounds__(256) void topp_wave_kernel(const float* __restrict__ probs, int H,
                                                         int M, int rows, HeadScalars top_p,
+                                                        const int32_t* __restrict__ ccount,
+                                                        const int32_t* __restrict__ cidx,
                                                         int32_t* __restrict__ count,
                                                         int32_t* __restrict__ idx,
                                                         uint8_t* __restrict__ mask,
@@ -512,13 +529,17 @@ __global__ __launch_bounds__(256) void topp_wave_kernel(const float* __restrict_
   const int h = (row / M) % H;
   const float p = top_p.v[h];
   const float* pr = probs + (int64_t)row * M;
-  // slots past M hold value 0: they add no mass, and the selection below never takes them
+  // with candidate lists the row is the first n positions, position r standing for block
+  // cidx[r] (ascending); otherwise position = block
+  const int n = ccount != nullptr ? min(max(ccount[row], 0), M) : M;
+  const int32_t* crow = cidx != nullptr ? cidx + (int64_t)row * M : nullptr;
+  // slots past n hold value 0: they add no mass, and the selection below never takes them
   uint32_t u[VPL];
   float val[VPL];
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
     const int j = i * 64 + lane;
-    const float x = j < M ? pr[j] : 0.f;
+    const float x = j < n ? pr[j] : 0.f;
     val[i] = x > 0.f ? x : 0.f;  // probabilities are >= 0; -0 and NaN map to 0
     u[i] = __float_as_uint(val[i]);
   }
@@ -529,7 +550,7 @@ __global__ __launch_bounds__(256) void topp_wave_kernel(const float* __restrict_
       if (u[i] >= t) acc += (double)val[i];
     return wave_sum(acc);
   };
-  auto valid = [&](int i) { return i * 64 + lane < M; };
+  auto valid = [&](int i) { return i * 64 + lane < n; };
 
   bool kept[VPL];
   double kmass;
@@ -608,17 +629,120 @@ __global__ __launch_bounds__(256) void topp_wave_kernel(const float* __restrict_
 
   // ascending compaction, optional byte mask
   int32_t* out_idx = idx + (int64_t)row * M;
+  auto block_of = [&](int pos) { return crow != nullptr ? min(max(crow[pos], 0), M - 1) : pos; };
   int base = 0;
+  if (mask != nullptr && crow != nullptr) {  // zeros first; the kept blocks are set below
+    for (int j = lane; j < M; j += 64) mask[(int64_t)row * M + j] = 0;
+    __threadfence_block();
+  }
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
     const uint64_t m = __builtin_amdgcn_ballot_w64(kept[i]);
-    if (kept[i]) out_idx[base + (int)__builtin_popcountll(m & ((1ull << lane) - 1ull))] = i * 64 + lane;
+    if (kept[i])
+      out_idx[base + (int)__builtin_popcountll(m & ((1ull << lane) - 1ull))] = block_of(i * 64 + lane);
     base += (int)__builtin_popcountll(m);
-    if (mask != nullptr && i * 64 + lane < M) mask[(int64_t)row * M + i * 64 + lane] = kept[i] ? 1 : 0;
+    if (mask != nullptr) {
+      if (crow == nullptr) {
+        if (i * 64 + lane < M) mask[(int64_t)row * M + i * 64 + lane] = kept[i] ? 1 : 0;
+      } else if (kept[i]) {
+        mask[(int64_t)row * M + block_of(i * 64 + lane)] = 1;
+      }
+    }
   }
   if (lane == 0) {
     count[row] = base;
     if (mass != nullptr) mass[row] = (float)kmass;
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// Scores restricted to candidate key blocks (the reduced search of the GSRS abstract on the
+// RECAP page at thelatestinai.com: later searches run over a candidate set found earlier). One
+// wavefront per query-block row: for position r < n of the row's candidate list (block
+// j = cidx[r]) the logit s * Q̄_i . K̄_j is computed in fp32 (Q̄_i from LDS, K̄_j read as whole
+// 16-byte chunks) and parked in the output row; then the row max and sum over the candidates
+// (DPP reductions) and the normalised values written back at the same positions.
+// ------------------------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void score_cand_kernel(const float* __restrict__ qbar,
+                                                         const float* __restrict__ kbar, int M,
+                                                         int rows, float scale_log2,
+                                                         const int32_t* __restrict__ ccount,
+                                                         const int32_t* __restrict__ cidx,
+                                                         float* __restrict__ probs) {
+  __shared__ __align__(16) float qs[4][D];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int row = blockIdx.x * 4 + wave;
+  if (row >= rows) return;  // the whole wavefront; no block-wide barrier follows
+  const int64_t bh = row / M;
+  for (int d = lane; d < D; d += 64) qs[wave][d] = qbar[(int64_t)row * D + d];
+  __builtin_amdgcn_wave_barrier();
+  const float* kb = kbar + bh * M * D;
+  const int n = min(max(ccount[row], 0), M);
+  const int32_t* crow = cidx + (int64_t)row * M;
+  float* out = probs + (int64_t)row * M;
+  float mx = -INFINITY;
+  for (int r = lane; r < n; r += 64) {
+    const float* kr = kb + (int64_t)min(max(crow[r], 0), M - 1) * D;
+    float acc = 0.f;
+#pragma unroll 8
+    for (int d = 0; d < D; d += 4) {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(&qs[wave][d]);
+      const f32x4 b = *reinterpret_cast<const f32x4*>(kr + d);
+      acc = __builtin_fmaf(a[0], b[0], acc);
+      acc = __builtin_fmaf(a[1], b[1], acc);
+      acc = __builtin_fmaf(a[2], b[2], acc);
+      acc = __builtin_fmaf(a[3], b[3], acc);
+    }
+    const float x = acc * scale_log2;
+    out[r] = x;  // read back by this lane only
+    mx = fmaxf(mx, x);
+  }
+  mx = wave_max_f(mx);
+  float l = 0.f;
+  for (int r = lane; r < n; r += 64) l += __builtin_amdgcn_exp2f(out[r] - mx);
+  const float inv = 1.0f / wave_sum_f(l);
+  for (int r = lane; r < n; r += 64) out[r] = __builtin_amdgcn_exp2f(out[r] - mx) * inv;
+}
+
+// ------------------------------------------------------------------------------------------
+// Drift of the block means between two steps, per (b, h): ||X̄ - X̄_ref||_F / ||X̄_ref||_F for
+// X = Q and X = K, sums in fp64 over the M x D means (one work-group per (b, h)); a caller
+// reuses the mask of the reference step while both stay under its threshold.
+// ------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void mean_drift_kernel(const float* __restrict__ qbar,
+                                                         const float* __restrict__ kbar,
+                                                         const float* __restrict__ qref,
+                                                         const float* __restrict__ kref,
+                                                         int64_t per_head,
+                                                         float* __restrict__ drift) {
+  __shared__ double red[4][4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t off = (int64_t)blockIdx.x * per_head;
+  double dq = 0.0, rq = 0.0, dk = 0.0, rk = 0.0;
+  for (int64_t t = threadIdx.x; t < per_head; t += 256) {
+    const double a = qbar[off + t], ar = qref[off + t];
+    const double b = kbar[off + t], br = kref[off + t];
+    dq += (a - ar) * (a - ar);
+    rq += ar * ar;
+    dk += (b - br) * (b - br);
+    rk += br * br;
+  }
+  double v[4] = {dq, rq, dk, rk};
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v[c] += __shfl_xor(v[c], o);
+    if (lane == 0) red[wave][c] = v[c];
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double t[4] = {0.0, 0.0, 0.0, 0.0};
+    for (int w = 0; w < 4; ++w)
+      for (int c = 0; c < 4; ++c) t[c] += red[w][c];
+    drift[2 * blockIdx.x] = (float)(t[1] > 0.0 ? sqrt(t[0] / t[1]) : (t[0] > 0.0 ? INFINITY : 0.0));
+    drift[2 * blockIdx.x + 1] =
+        (float)(t[3] > 0.0 ? sqrt(t[2] / t[3]) : (t[2] > 0.0 ? INFINITY : 0.0));
   }
 }
 
@@ -678,32 +802,38 @@ hipError_t launch_scores(const float* qbar, const float* kbar, int BH, int M, in
 }
 
 hipError_t launch_topp(const float* probs, int B, int H, int M, const HeadScalars& top_p,
-                       int32_t* count, int32_t* idx, uint8_t* mask, float* mass,
-                       hipStream_t stream) {
+                       const int32_t* ccount, const int32_t* cidx, int32_t* count, int32_t* idx,
+                       uint8_t* mask, float* mass, hipStream_t stream) {
   const int rows = B * H * M;
   const int grid = (rows + 3) / 4;
   if (M <= 512) {
-    topp_wave_kernel<8><<<grid, 256, 0, stream>>>(probs, H, M, rows, top_p, count, idx, mask, mass);
+    topp_wave_kernel<8><<<grid, 256, 0, stream>>>(probs, H, M, rows, top_p, ccount, cidx, count,
+                                                   idx, mask, mass);
     return hipGetLastError();
   }
   if (M <= 768) {
-    topp_wave_kernel<12><<<grid, 256, 0, stream>>>(probs, H, M, rows, top_p, count, idx, mask, mass);
+    topp_wave_kernel<12><<<grid, 256, 0, stream>>>(probs, H, M, rows, top_p, ccount, cidx, count,
+                                                   idx, mask, mass);
     return hipGetLastError();
   }
   if (M <= 1024) {
-    topp_wave_kernel<16><<<grid, 256, 0, stream>>>(probs, H, M, rows, top_p, count, idx, mask, mass);
+    topp_wave_kernel<16><<<grid, 256, 0, stream>>>(probs, H, M, rows, top_p, ccount, cidx, count,
+                                                   idx, mask, mass);
     return hipGetLastError();
   }
   if (M <= 1280) {
-    topp_wave_kernel<20><<<grid, 256, 0, stream>>>(probs, H, M, rows, top_p, count, idx, mask, mass);
+    topp_wave_kernel<20><<<grid, 256, 0, stream>>>(probs, H, M, rows, top_p, ccount, cidx, count,
+                                                   idx, mask, mass);
     return hipGetLastError();
   }
   if (M <= 1536) {
-    topp_wave_kernel<24><<<grid, 256, 0, stream>>>(probs, H, M, rows, top_p, count, idx, mask, mass);
+    topp_wave_kernel<24><<<grid, 256, 0, stream>>>(probs, H, M, rows, top_p, ccount, cidx, count,
+                                                   idx, mask, mass);
     return hipGetLastError();
   }
   if (M <= 2048) {
-    topp_wave_kernel<32><<<grid, 256, 0, stream>>>(probs, H, M, rows, top_p, count, idx, mask, mass);
+    topp_wave_kernel<32><<<grid, 256, 0, stream>>>(probs, H, M, rows, top_p, ccount, cidx, count,
+                                                   idx, mask, mass);
     return hipGetLastError();
   }
   // longer rows: one work-group per row, bitonic sort in LDS
@@ -713,7 +843,29 @@ hipError_t launch_topp(const float* probs, int B, int H, int M, const HeadScalar
   static std::atomic<uint32_t> lds_topp{0u};
   const hipError_t e = allow_lds_once((const void*)topp_kernel, kMaxBlocks * 9, lds_topp);
   if (e != hipSuccess) return e;
-  topp_kernel<<<B * H * M, 256, lds, stream>>>(probs, H, M, P, top_p, count, idx, mask, mass);
+  topp_kernel<<<B * H * M, 256, lds, stream>>>(probs, H, M, P, top_p, ccount, cidx, count, idx,
+                                                mask, mass);
+  return hipGetLastError();
+}
+
+hipError_t launch_scores_cand(const float* qbar, const float* kbar, int BH, int M, int D,
+                              float scale_log2, const int32_t* ccount, const int32_t* cidx,
+                              float* probs, hipStream_t stream) {
+  const int rows = BH * M;
+  const int grid = (rows + 3) / 4;
+  if (D == 128)
+    score_cand_kernel<128><<<grid, 256, 0, stream>>>(qbar, kbar, M, rows, scale_log2, ccount,
+                                                     cidx, probs);
+  else
+    score_cand_kernel<64><<<grid, 256, 0, stream>>>(qbar, kbar, M, rows, scale_log2, ccount,
+                                                    cidx, probs);
+  return hipGetLastError();
+}
+
+hipError_t launch_mean_drift(const float* qbar, const float* kbar, const float* qref,
+                             const float* kref, int BH, int M, int D, float* drift,
+                             hipStream_t stream) {
+  mean_drift_kernel<<<BH, 256, 0, stream>>>(qbar, kbar, qref, kref, (int64_t)M * D, drift);
   return hipGetLastError();
 }
 

@@ -194,8 +194,9 @@ int recap_topp_mask(const recap_desc* d, const float* probs, const float* top_p_
     tp.v[h] = p;
   }
   if ((s = check_device()) != RECAP_OK) return s;
-  return launched(launch_topp(probs, d->batch, d->heads, num_blocks(d), tp, kept_count, kept_idx,
-                              mask_opt, kept_mass_opt, (hipStream_t)stream));
+  return launched(launch_topp(probs, d->batch, d->heads, num_blocks(d), tp, nullptr, nullptr,
+                              kept_count, kept_idx, mask_opt, kept_mass_opt,
+                              (hipStream_t)stream));
 }
 
 }  // extern "C"
@@ -319,6 +320,82 @@ int dense_impl(const recap_desc* d, const void* q, const void* k, const void* v,
 }  // namespace
 
 extern "C" {
+
+int recap_block_means(const recap_desc* d, const void* q, const void* k, float* qbar,
+                      float* kbar, void* stream) {
+  int s = validate_desc(d);
+  if (s != RECAP_OK) return s;
+  if (q == nullptr || k == nullptr || qbar == nullptr || kbar == nullptr) return RECAP_E_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(qbar) || !aligned16(kbar)) return RECAP_E_ALIGN;
+  if (qbar == kbar) return RECAP_E_VALUE;
+  if ((s = check_device()) != RECAP_OK) return s;
+  return launched(launch_pool((const bf16_t*)q, (const bf16_t*)k, strides_of(d), d->batch,
+                              d->heads, d->seq, d->head_dim, d->block, qbar, kbar,
+                              (hipStream_t)stream));
+}
+
+int recap_scores_from_means(const recap_desc* d, const float* qbar, const float* kbar,
+                            float sm_scale, const int32_t* cand_count_opt,
+                            const int32_t* cand_idx_opt, float* probs, void* stream) {
+  int s = validate_desc(d);
+  if (s != RECAP_OK) return s;
+  if (qbar == nullptr || kbar == nullptr || probs == nullptr) return RECAP_E_NULL;
+  if ((cand_count_opt == nullptr) != (cand_idx_opt == nullptr)) return RECAP_E_NULL;
+  if (!aligned16(qbar) || !aligned16(kbar) || !aligned16(probs) ||
+      (cand_count_opt != nullptr && (!aligned16(cand_count_opt) || !aligned16(cand_idx_opt))))
+    return RECAP_E_ALIGN;
+  if (!isfinite(sm_scale) || !(sm_scale > 0.f)) return RECAP_E_VALUE;
+  if ((s = check_device()) != RECAP_OK) return s;
+  const float sl2 = (float)((double)sm_scale * 1.4426950408889634);
+  const int BH = d->batch * d->heads, M = num_blocks(d);
+  hipStream_t st = (hipStream_t)stream;
+  if (cand_count_opt == nullptr)
+    return launched(launch_scores(qbar, kbar, BH, M, d->head_dim, sl2, probs, st));
+  return launched(launch_scores_cand(qbar, kbar, BH, M, d->head_dim, sl2, cand_count_opt,
+                                     cand_idx_opt, probs, st));
+}
+
+int recap_topp_mask_cand(const recap_desc* d, const float* probs, const int32_t* cand_count,
+                         const int32_t* cand_idx, const float* top_p_host, int32_t* kept_count,
+                         int32_t* kept_idx, uint8_t* mask_opt, float* kept_mass_opt,
+                         void* stream) {
+  int s = validate_desc(d);
+  if (s != RECAP_OK) return s;
+  if (probs == nullptr || cand_count == nullptr || cand_idx == nullptr ||
+      top_p_host == nullptr || kept_count == nullptr || kept_idx == nullptr)
+    return RECAP_E_NULL;
+  if (!aligned16(probs) || !aligned16(cand_count) || !aligned16(cand_idx) ||
+      !aligned16(kept_count) || !aligned16(kept_idx) || (mask_opt && !aligned16(mask_opt)) ||
+      (kept_mass_opt && !aligned16(kept_mass_opt)))
+    return RECAP_E_ALIGN;
+  if (kept_idx == cand_idx || kept_count == cand_count) return RECAP_E_VALUE;
+  HeadScalars tp;
+  memset(&tp, 0, sizeof(tp));
+  for (int h = 0; h < d->heads; ++h) {
+    const float p = top_p_host[h];
+    if (!(p >= 0.f && p <= 1.f)) return RECAP_E_VALUE;
+    tp.v[h] = p;
+  }
+  if ((s = check_device()) != RECAP_OK) return s;
+  return launched(launch_topp(probs, d->batch, d->heads, num_blocks(d), tp, cand_count,
+                              cand_idx, kept_count, kept_idx, mask_opt, kept_mass_opt,
+                              (hipStream_t)stream));
+}
+
+int recap_mean_drift(const recap_desc* d, const float* qbar, const float* kbar,
+                     const float* qbar_ref, const float* kbar_ref, float* drift, void* stream) {
+  int s = validate_desc(d);
+  if (s != RECAP_OK) return s;
+  if (qbar == nullptr || kbar == nullptr || qbar_ref == nullptr || kbar_ref == nullptr ||
+      drift == nullptr)
+    return RECAP_E_NULL;
+  if (!aligned16(qbar) || !aligned16(kbar) || !aligned16(qbar_ref) || !aligned16(kbar_ref) ||
+      !aligned16(drift))
+    return RECAP_E_ALIGN;
+  if ((s = check_device()) != RECAP_OK) return s;
+  return launched(launch_mean_drift(qbar, kbar, qbar_ref, kbar_ref, d->batch * d->heads,
+                                    num_blocks(d), d->head_dim, drift, (hipStream_t)stream));
+}
 
 int recap_block_sparse_attn(const recap_desc* d, const void* q, const void* k, const void* v,
                             const int32_t* kept_count, const int32_t* kept_idx, float sm_scale,

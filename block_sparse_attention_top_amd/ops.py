@@ -216,6 +216,82 @@ def recap_dense_attn_stats(desc: RecapDesc, q, k, v, sm_scale: Optional[float] =
                             want_kept_mass=want_kept_mass)
 
 
+def _means_shape(desc: RecapDesc):
+    return (desc.batch, desc.heads, num_blocks(desc), desc.head_dim)
+
+
+def _check_means(desc: RecapDesc, *ts) -> None:
+    for t in ts:
+        if t.dtype != torch.float32 or tuple(t.shape) != _means_shape(desc) or \
+                not t.is_contiguous():
+            raise ValueError("block means are contiguous fp32 [B, H, M, D]")
+
+
+def recap_block_means(desc: RecapDesc, q, k, qbar=None, kbar=None, stream=None):
+    """(Q̄, K̄): fp32 [B,H,M,D] block means (recap_block_means)."""
+    _same_layout(desc, q, k)
+    if qbar is None:
+        qbar = torch.empty(_means_shape(desc), dtype=torch.float32, device=q.device)
+    if kbar is None:
+        kbar = torch.empty(_means_shape(desc), dtype=torch.float32, device=q.device)
+    _check_means(desc, qbar, kbar)
+    check(_lib.load().recap_block_means(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(qbar),
+                                        _ptr(kbar), _stream(stream)), "recap_block_means")
+    return qbar, kbar
+
+
+def recap_scores_from_means(desc: RecapDesc, qbar, kbar, sm_scale: Optional[float] = None,
+                            cand_count=None, cand_idx=None, probs=None, stream=None):
+    """fp32 [B,H,M,M] block-pair softmax from given means; with candidate lists, each row's
+    softmax over its candidates at the candidate positions (recap_scores_from_means)."""
+    _check_means(desc, qbar, kbar)
+    M = num_blocks(desc)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(desc.head_dim)
+    if probs is None:
+        probs = torch.empty((desc.batch, desc.heads, M, M), dtype=torch.float32,
+                            device=qbar.device)
+    check(_lib.load().recap_scores_from_means(ctypes.byref(desc), _ptr(qbar), _ptr(kbar),
+                                              float(sm_scale), _ptr(cand_count), _ptr(cand_idx),
+                                              _ptr(probs), _stream(stream)),
+          "recap_scores_from_means")
+    return probs
+
+
+def recap_topp_mask_cand(desc: RecapDesc, probs, cand_count, cand_idx, top_p, kept_count=None,
+                         kept_idx=None, want_mask: bool = False, want_mass: bool = False,
+                         stream=None):
+    """Top-p over each row's candidate distribution: (count, idx, mask|None, mass|None) with
+    block indices (recap_topp_mask_cand)."""
+    M = num_blocks(desc)
+    dev = probs.device
+    if kept_count is None:
+        kept_count = torch.empty((desc.batch, desc.heads, M), dtype=torch.int32, device=dev)
+    if kept_idx is None:
+        kept_idx = torch.empty((desc.batch, desc.heads, M, M), dtype=torch.int32, device=dev)
+    mask = torch.empty((desc.batch, desc.heads, M, M), dtype=torch.uint8, device=dev) \
+        if want_mask else None
+    mass = torch.empty((desc.batch, desc.heads, M), dtype=torch.float32, device=dev) \
+        if want_mass else None
+    tp = _host_floats(top_p, desc.heads, "top_p")
+    check(_lib.load().recap_topp_mask_cand(ctypes.byref(desc), _ptr(probs), _ptr(cand_count),
+                                           _ptr(cand_idx), tp, _ptr(kept_count),
+                                           _ptr(kept_idx), _ptr(mask), _ptr(mass),
+                                           _stream(stream)), "recap_topp_mask_cand")
+    return kept_count, kept_idx, mask, mass
+
+
+def recap_mean_drift(desc: RecapDesc, qbar, kbar, qbar_ref, kbar_ref, drift=None, stream=None):
+    """fp32 [B,H,2]: relative Frobenius change of Q̄ and of K̄ against a reference step."""
+    _check_means(desc, qbar, kbar, qbar_ref, kbar_ref)
+    if drift is None:
+        drift = torch.empty((desc.batch, desc.heads, 2), dtype=torch.float32, device=qbar.device)
+    check(_lib.load().recap_mean_drift(ctypes.byref(desc), _ptr(qbar), _ptr(kbar),
+                                       _ptr(qbar_ref), _ptr(kbar_ref), _ptr(drift),
+                                       _stream(stream)), "recap_mean_drift")
+    return drift
+
+
 def sparse_step(desc: RecapDesc, q, k, v, top_p, sm_scale: Optional[float] = None,
                 residual=None, res_scale=None, out=None, stream=None):
     """One corrected sparse attention call: block scores -> top-p -> sparse attention

@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define RECAP_ABI_VERSION 2 /* 2: adds the *_stats entry points */
+#define RECAP_ABI_VERSION 3 /* 2: *_stats entry points; 3: mask reuse entry points */
 #define RECAP_MAX_HEADS 128   /* per-head host arrays are passed by value to the kernels */
 #define RECAP_MAX_BLOCKS 8192 /* M = ceil(N / block) upper bound (top-p sorts a row in LDS) */
 
@@ -186,6 +186,38 @@ int recap_dense_attn_stats(const recap_desc* d, const void* q, const void* k, co
                            const int32_t* kept_idx_opt, void* out, void* residual_out_opt,
                            float* lse_out, float* kept_mass_out_opt, void* ws,
                            size_t ws_bytes, void* stream);
+
+/* Mask reuse across steps (the GSRS abstract on the RECAP page at thelatestinai.com: blocks
+ * selected early keep most of the attention weight at later steps, so later searches can be
+ * restricted to an earlier candidate set; RECAP Sec. 2, related work: early-step block indices
+ * reused at later denoising steps). Four building blocks; the caller owns the policy.
+ *
+ * recap_block_means: the block means of recap_block_scores part 1 (RECAP Sec. 3.2) written to
+ *   qbar, kbar: fp32 device [B,H,M,D], contiguous, distinct.
+ * recap_scores_from_means: recap_block_scores part 2 from given means. Without candidate lists
+ *   it writes the full rows of probs [B,H,M,M]. With them (int32 [B,H,M] counts and
+ *   [B,H,M,M] lists of ascending key-block indices, as recap_topp_mask writes; both or neither)
+ *   row i holds the softmax over its n_i candidates only,
+ *     probs[b,h,i,r] = softmax_r(sm_scale * Q̄_i . K̄_{cand[r]}),  r < n_i,
+ *   at the candidate positions r; entries past n_i are unspecified.
+ * recap_topp_mask_cand: top-p (as recap_topp_mask) over each row's candidate distribution
+ *   (positions r < n_i of probs); the kept lists hold block indices cand[r] (ascending), the
+ *   optional mask is over blocks (0 outside the kept set), kept_mass is the candidate mass kept.
+ *   Ties: lower position = lower block index first. kept lists must not alias the candidates.
+ * recap_mean_drift: drift[b,h,0] = ||Q̄ - Q̄_ref||_F / ||Q̄_ref||_F and drift[b,h,1] likewise
+ *   for K̄, fp32 device [B,H,2] (sums in fp64; +inf when the reference is zero and the means
+ *   are not). */
+int recap_block_means(const recap_desc* d, const void* q, const void* k, float* qbar,
+                      float* kbar, void* stream);
+int recap_scores_from_means(const recap_desc* d, const float* qbar, const float* kbar,
+                            float sm_scale, const int32_t* cand_count_opt,
+                            const int32_t* cand_idx_opt, float* probs, void* stream);
+int recap_topp_mask_cand(const recap_desc* d, const float* probs, const int32_t* cand_count,
+                         const int32_t* cand_idx, const float* top_p_host, int32_t* kept_count,
+                         int32_t* kept_idx, uint8_t* mask_opt, float* kept_mass_opt,
+                         void* stream);
+int recap_mean_drift(const recap_desc* d, const float* qbar, const float* kbar,
+                     const float* qbar_ref, const float* kbar_ref, float* drift, void* stream);
 
 #ifdef __cplusplus
 }

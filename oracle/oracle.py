@@ -261,6 +261,59 @@ def kept_attention_mass(q, k, block: int, sm_scale: float, mask, rows=None) -> n
     return out
 
 
+def candidate_scores(q, k, block: int, sm_scale: float, cand: np.ndarray) -> np.ndarray:
+    """Block-pair softmax restricted to each query block's candidate key blocks ([GSRS]
+    reduced search: a later search runs only over blocks found earlier):
+    P_c[b,h,i,j] = exp(s * Q̄_i . K̄_j) / sum_{j' in C_i} exp(s * Q̄_i . K̄_j') for j in C_i,
+    0 elsewhere. cand: bool [B,H,M,M]. Returns float64 [B,H,M,M] (block space)."""
+    qb = block_mean_pool(q, block)
+    kb = block_mean_pool(k, block)
+    lg = float(sm_scale) * np.matmul(qb, np.swapaxes(kb, -1, -2))
+    lg = np.where(cand, lg, -np.inf)
+    mx = lg.max(axis=-1, keepdims=True)
+    w = np.where(cand, np.exp(lg - np.where(np.isfinite(mx), mx, 0.0)), 0.0)
+    tot = w.sum(axis=-1, keepdims=True)
+    return np.divide(w, tot, out=np.zeros_like(w), where=tot > 0)
+
+
+def topp_select_candidates(probs_c: np.ndarray, cand: np.ndarray, top_p) -> dict:
+    """Top-p over each row's candidate distribution: the rule of `topp_select` applied to the
+    row restricted to its candidates (in ascending block order, so ties go to the lower block),
+    mapped back to block indices. A row without candidates keeps nothing."""
+    probs_c = np.asarray(probs_c, dtype=np.float64)
+    B, H, R, M = probs_c.shape
+    p = np.broadcast_to(np.asarray(top_p, dtype=np.float64), (H,))
+    mask = np.zeros((B, H, R, M), dtype=bool)
+    count = np.zeros((B, H, R), dtype=np.int64)
+    mass = np.zeros((B, H, R), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            for i in range(R):
+                js = np.nonzero(cand[b, h, i])[0]
+                if len(js) == 0:
+                    continue
+                sub = topp_select(probs_c[b, h, i, js][None, None, None, :], [p[h]])
+                keep = sub["mask"][0, 0, 0]
+                mask[b, h, i, js[keep]] = True
+                count[b, h, i] = int(sub["count"][0, 0, 0])
+                mass[b, h, i] = float(sub["mass"][0, 0, 0])
+    return {"mask": mask, "count": count, "mass": mass}
+
+
+def mean_drift(qbar, kbar, qbar_ref, kbar_ref) -> np.ndarray:
+    """Relative Frobenius change of the block means per (b, h) against a reference step:
+    [..., 0] = ||Q̄ - Q̄_ref|| / ||Q̄_ref||, [..., 1] the same for K̄ (RECAP §2: reuse of
+    early-step block indices across nearby steps; the reuse test). float64 [B, H, 2]."""
+    out = []
+    for x, r in ((qbar, qbar_ref), (kbar, kbar_ref)):
+        x = np.asarray(x, dtype=np.float64)
+        r = np.asarray(r, dtype=np.float64)
+        num = np.sqrt(((x - r) ** 2).sum(axis=(-2, -1)))
+        den = np.sqrt((r ** 2).sum(axis=(-2, -1)))
+        out.append(np.divide(num, den, out=np.where(num > 0, np.inf, 0.0), where=den > 0))
+    return np.stack(out, axis=-1)
+
+
 def block_sparsity(count: np.ndarray, m: int) -> float:
     """Fraction of skipped block pairs: 1 - mean(k*) / M."""
     return 1.0 - float(np.mean(count)) / float(m)

@@ -369,6 +369,79 @@ def check_kept_mass_identities():
                            rtol=0, atol=1e-12)
 
 
+def check_candidate_scores():
+    """Restricted scores: with every block a candidate they are the block scores; otherwise
+    the block scores renormalised over the candidates (zero elsewhere, rows sum to 1), and a
+    scalar loop agrees on a tiny case."""
+    n, b, d, s = 300, 32, 8, 0.8
+    m = -(-n // b)
+    q, k = _rand((1, 2, n, d), 330, 2.0), _rand((1, 2, n, d), 331, 2.0)
+    full = O.block_scores(q, k, b, s)
+    every = np.ones((1, 2, m, m), bool)
+    assert np.allclose(O.candidate_scores(q, k, b, s, every), full, rtol=0, atol=1e-15)
+    rng = np.random.default_rng(332)
+    cand = rng.random((1, 2, m, m)) < 0.4
+    cand[..., 0] = True
+    pc = O.candidate_scores(q, k, b, s, cand)
+    assert np.all(pc[~cand] == 0.0)
+    assert np.allclose(pc.sum(-1), 1.0, rtol=0, atol=1e-14)
+    ren = np.where(cand, full, 0.0)
+    ren /= ren.sum(-1, keepdims=True)
+    assert np.allclose(pc, ren, rtol=1e-12, atol=1e-15)
+    qs, ks = q[0, 1, :70].tolist(), k[0, 1, :70].tolist()
+    tiny = brute.scores(qs, ks, 70, 16, d, s)  # 5 blocks
+    c5 = np.zeros((1, 1, 5, 5), bool)
+    c5[0, 0] = [[1, 0, 1, 0, 1], [0, 1, 1, 0, 0], [1, 1, 1, 1, 1], [0, 0, 0, 1, 0],
+                [1, 0, 0, 1, 1]]
+    pc5 = O.candidate_scores(q[:, 1:, :70], k[:, 1:, :70], 16, s, c5)
+    for i in range(5):
+        js = [j for j in range(5) if c5[0, 0, i, j]]
+        tot = sum(tiny[i][j] for j in js)
+        for j in js:
+            assert abs(pc5[0, 0, i, j] - tiny[i][j] / tot) < 1e-12
+
+
+def check_candidate_topp():
+    """Restricted top-p keeps only candidates; with every block a candidate it is top-p; when
+    the candidates contain the full top-p set at p, the restricted search at p / S (S the
+    candidates' share of the full mass) returns that same set; p = 1 keeps every candidate."""
+    rows = _random_prob_rows(24, 16, 340)  # [1, 1, 16, 24]
+    every = np.ones(rows.shape, bool)
+    for p in (0.3, 0.75, 0.95):
+        a = O.topp_select_candidates(rows, every, p)
+        bm = O.topp_select(rows, p)
+        assert np.array_equal(a["mask"], bm["mask"]) and np.array_equal(a["count"], bm["count"])
+    base = O.topp_select(rows, 0.6)["mask"]
+    rng = np.random.default_rng(341)
+    cand = base | (rng.random(rows.shape) < 0.3)
+    S = (rows * cand).sum(-1)
+    pc = np.where(cand, rows, 0.0) / S[..., None]
+    for r in range(rows.shape[2]):
+        got = O.topp_select_candidates(pc[:, :, r:r + 1], cand[:, :, r:r + 1],
+                                       0.6 / S[0, 0, r])["mask"]
+        assert np.array_equal(got[0, 0, 0], base[0, 0, r])
+    one = O.topp_select_candidates(pc, cand, 1.0)
+    assert np.array_equal(one["mask"], cand)
+    half = O.topp_select_candidates(pc, cand, 0.5)
+    assert np.all(half["mask"] <= cand) and np.all((pc * half["mask"]).sum(-1) >= 0.5 - 1e-12)
+
+
+def check_mean_drift():
+    """Drift is 0 for identical means, exactly eps for a (1 + eps) scaling, separate for Q̄
+    and K̄, and the Frobenius ratio of a hand-sized case."""
+    qb, kb = _rand((2, 3, 5, 4), 350), _rand((2, 3, 5, 4), 351)
+    assert np.all(O.mean_drift(qb, kb, qb, kb) == 0.0)
+    dr = O.mean_drift(qb * 1.25, kb, qb, kb)
+    assert np.allclose(dr[..., 0], 0.25, rtol=0, atol=1e-14) and np.all(dr[..., 1] == 0.0)
+    dr = O.mean_drift(qb, kb * 0.5, qb, kb)
+    assert np.all(dr[..., 0] == 0.0) and np.allclose(dr[..., 1], 0.5, rtol=0, atol=1e-14)
+    x = np.zeros((1, 1, 2, 2))
+    xr = x.copy()
+    xr[0, 0] = [[3.0, 0.0], [0.0, 4.0]]  # norm 5
+    x[0, 0] = [[3.0, 1.0], [0.0, 4.0]]   # difference norm 1
+    assert np.allclose(O.mean_drift(x, xr, xr, xr)[0, 0], [0.2, 0.0], rtol=0, atol=1e-15)
+
+
 ALL_CHECKS = [
     check_pool_block_constant,
     check_pool_closed_form_ragged,
@@ -390,6 +463,9 @@ ALL_CHECKS = [
     check_lse_closed_forms,
     check_lse_vs_brute,
     check_kept_mass_identities,
+    check_candidate_scores,
+    check_candidate_topp,
+    check_mean_drift,
 ]
 
 

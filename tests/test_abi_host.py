@@ -36,7 +36,7 @@ def test_header_symbols_exported():
 
 def test_version_and_status_strings():
     lib = _lib.load()
-    assert lib.recap_abi_version() == _lib.ABI_VERSION == 2
+    assert lib.recap_abi_version() == _lib.ABI_VERSION == 3
     for st in list(_lib.STATUS_NAMES) + [-99]:
         s = lib.recap_status_string(st)
         assert s and len(s.decode()) > 1

@@ -257,6 +257,74 @@ def test_graph_capture_replays(bsa):
     assert not torch.equal(replayed, eager[2])
 
 
+def _to_blocks(vals, count, idx, m):
+    """Candidate-position values -> block space (zeros outside each row's candidates)."""
+    out = np.zeros(vals.shape[:-1] + (m,))
+    for b, h, i in np.ndindex(*count.shape):
+        n = count[b, h, i]
+        out[b, h, i, idx[b, h, i, :n]] = vals[b, h, i, :n]
+    return out
+
+
+@pytest.mark.parametrize("m,d", [(300, 128), (2100, 64)])
+def test_mask_reuse(bsa, m, d):
+    """Mask-reuse building blocks against the oracle: block means; scores from means (equal
+    bit for bit to recap_block_scores); scores and top-p restricted to candidate lists (the
+    wavefront top-p for M <= 2048, the LDS sort beyond); a row with no candidates; drift of
+    the means between two steps."""
+    cfg = synth.workload("tiny", heads=2, head_dim=d, grid=(1, 1, m * 64 - 5))
+    s, M = d ** -0.5, m
+    say(f"[case] mask reuse M={M} D={d}")
+    q, k, _ = synth.make_qkv(cfg)
+    qd, kd = to_dev(q), to_dev(k)
+    desc = bsa.make_desc(qd, cfg.block)
+    qbar, kbar = bsa.recap_block_means(desc, qd, kd)
+    full = bsa.recap_scores_from_means(desc, qbar, kbar, s)
+    via_scores = bsa.recap_block_scores(desc, qd, kd, s)
+    cc, ci, _, _ = bsa.recap_topp_mask(desc, full, [0.99, 0.97])
+    pc = bsa.recap_scores_from_means(desc, qbar, kbar, s, cc, ci)
+    p = np.array([0.9, 0.8])
+    kc, ki, km, kmass = bsa.recap_topp_mask_cand(desc, pc, cc, ci, p.tolist(), want_mask=True,
+                                                 want_mass=True)
+    torch.cuda.synchronize()
+    assert torch.equal(full, via_scores)
+    q64, k64 = synth.to_f64(q), synth.to_f64(k)
+    qb, kb = O.block_mean_pool(q64, cfg.block), O.block_mean_pool(k64, cfg.block)
+    # fp32 sums of up to 64 bf16 values of magnitude <~ 8: error <= 64 * 2^-24 * 8 < 4e-5
+    assert np.abs(qbar.cpu().numpy() - qb).max() < 4e-5
+    assert np.abs(kbar.cpu().numpy() - kb).max() < 4e-5
+    cnt, idx = cc.cpu().numpy(), ci.cpu().numpy()
+    cand = O.mask_from_lists(cnt, idx, M)
+    assert cand.sum() < cand.size  # a real restriction
+    ref_c = O.candidate_scores(q64, k64, cfg.block, s, cand)
+    parity.check_probs(_to_blocks(pc.cpu().numpy().astype(np.float64), cnt, idx, M), ref_c)
+    ref_sel = O.topp_select_candidates(ref_c, cand, p)
+    gmask = km.cpu().numpy().astype(bool)
+    assert not (gmask & ~cand).any(), "kept blocks must be candidates"
+    parity.check_lists(kc.cpu().numpy(), ki.cpu().numpy(), M, gmask)
+    parity.check_mask(gmask, ref_c, ref_sel["mask"], p)
+    assert np.abs(kmass.cpu().numpy() - (ref_c * gmask).sum(-1)).max() <= 2e-5
+    # a row without candidates keeps nothing; the other rows are unchanged
+    cc2 = cc.clone()
+    cc2[0, 1, 3] = 0
+    kc2, ki2, _, _ = bsa.recap_topp_mask_cand(desc, pc, cc2, ci, p.tolist())
+    torch.cuda.synchronize()
+    assert int(kc2[0, 1, 3]) == 0
+    kc2[0, 1, 3] = kc[0, 1, 3]
+    assert torch.equal(kc2, kc)
+    # drift of the block means against a reference step
+    q2, k2 = synth.drifted(q, "q", 1), synth.drifted(k, "k", 1)
+    qbar2, kbar2 = bsa.recap_block_means(desc, to_dev(q2), to_dev(k2))
+    dr = bsa.recap_mean_drift(desc, qbar2, kbar2, qbar, kbar)
+    dr0 = bsa.recap_mean_drift(desc, qbar, kbar, qbar, kbar)
+    torch.cuda.synchronize()
+    assert torch.all(dr0 == 0)
+    ref_dr = O.mean_drift(O.block_mean_pool(synth.to_f64(q2), cfg.block),
+                          O.block_mean_pool(synth.to_f64(k2), cfg.block), qb, kb)
+    got_dr = dr.cpu().numpy().astype(np.float64)
+    assert np.all(ref_dr > 0) and np.abs(got_dr / ref_dr - 1).max() < 1e-3, (got_dr, ref_dr)
+
+
 def test_all_kept_capture_is_exactly_zero(bsa):
     say("[test] all-kept capture")
     cfg = synth.workload("tiny", head_dim=128, grid=(1, 1, 1100))

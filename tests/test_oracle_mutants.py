@@ -134,6 +134,29 @@ def _kept_mass_complement(q, k, block, sm_scale, mask, rows=None):
     return 1.0 - _REAL["kept_attention_mass"](q, k, block, sm_scale, mask, rows)
 
 
+def _cand_scores_over_all(q, k, block, sm_scale, cand):
+    return np.where(cand, O.block_scores(q, k, block, sm_scale), 0.0)
+
+
+def _cand_topp_keeps_all_at_one(probs_c, cand, top_p):
+    res = _REAL["topp_select_candidates"](probs_c, cand, top_p)
+    if np.all(np.asarray(top_p) >= 1.0):
+        res["mask"] = np.ones_like(res["mask"])
+    return res
+
+
+def _cand_topp_unrenormalised(probs_c, cand, top_p):
+    return _REAL["topp_select"](probs_c, top_p)
+
+
+def _drift_squared(qbar, kbar, qref, kref):
+    return _REAL["mean_drift"](qbar, kbar, qref, kref) ** 2
+
+
+def _drift_swapped(qbar, kbar, qref, kref):
+    return _REAL["mean_drift"](qbar, kbar, qref, kref)[..., ::-1]
+
+
 MUTANTS = {
     "pool divides by the full block size": ("block_mean_pool", _pool_divides_by_block),
     "pool takes the first token": ("block_mean_pool", _pool_first_token),
@@ -158,6 +181,13 @@ MUTANTS = {
     "lse ignores the mask": ("attention_lse", _lse_ignores_mask),
     "kept mass renormalised over the kept keys": ("kept_attention_mass", _kept_mass_renormalised),
     "kept mass of the complement": ("kept_attention_mass", _kept_mass_complement),
+    "candidate scores not renormalised": ("candidate_scores", _cand_scores_over_all),
+    "candidate top-p at p = 1 keeps every block": ("topp_select_candidates",
+                                                   _cand_topp_keeps_all_at_one),
+    "candidate top-p ignores the candidates": ("topp_select_candidates",
+                                               _cand_topp_unrenormalised),
+    "drift without the square root": ("mean_drift", _drift_squared),
+    "drift of Q and K swapped": ("mean_drift", _drift_swapped),
 }
 
 
