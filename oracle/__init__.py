@@ -7,23 +7,35 @@ code with the HIP library and never imports it.
 
 Parity status per function (pins live in tests/test_oracle_pins.py):
   block_partition, block_mean_pool, block_scores, softmax_rows, topp_select, kept_lists,
-  mask_from_lists, masked_attention, dense_attention, residual_epilogue, dense_with_capture:
+  mask_from_lists, masked_attention, dense_attention, residual_epilogue, dense_with_capture,
+  attention_lse, kept_attention_mass, candidate_scores, topp_select_candidates, mean_drift,
+  coarse_tail, exact_tail, tail_discrepancy, merge_attention, tail_reconstruction:
   pinned (closed forms, invariants, library special cases, brute force, planted mutants).
   The conventions the pages leave open (scale of the pooled logits, no log-block-size term,
   tie order, inclusive threshold) are readings; the pins fix the oracle to those readings.
 """
 from .oracle import (  # noqa: F401
+    attention_lse,
     block_mean_pool,
     block_partition,
     block_scores,
     block_sparsity,
+    candidate_scores,
+    coarse_tail,
     dense_attention,
     dense_with_capture,
+    exact_tail,
+    kept_attention_mass,
     kept_flops,
     kept_lists,
     mask_from_lists,
     masked_attention,
+    mean_drift,
+    merge_attention,
     residual_epilogue,
     softmax_rows,
+    tail_discrepancy,
+    tail_reconstruction,
     topp_select,
+    topp_select_candidates,
 )

@@ -98,3 +98,30 @@ def lse_row(qt, keys, sm_scale):
     logits = [sm_scale * sum(a * b for a, b in zip(qt, ku)) for ku in keys]
     mx = max(logits)
     return mx + math.log(sum(math.exp(x - mx) for x in logits))
+
+
+def coarse_tail_row(qt, k, v, n_tokens, block, tail_blocks, sm_scale):
+    """Block-mean estimate of one query's attention over the key blocks in `tail_blocks`:
+    each block j counts n_j keys equal to its mean key, carrying its mean value. Returns
+    (ln of the summed block masses, mass-weighted mean of the block values) with plain floats;
+    (-inf, zeros) for an empty tail."""
+    dim = len(v[0])
+    if not tail_blocks:
+        return -math.inf, [0.0] * dim
+    kb = pool(k, n_tokens, block, dim)
+    vb = pool(v, n_tokens, block, dim)
+    logm = []
+    for j in tail_blocks:
+        nj = min(n_tokens, (j + 1) * block) - j * block
+        dot = 0.0
+        for a, b in zip(qt, kb[j]):
+            dot += a * b
+        logm.append(math.log(nj) + sm_scale * dot)
+    mx = max(logm)
+    w = [math.exp(x - mx) for x in logm]
+    tot = sum(w)
+    out = [0.0] * dim
+    for wi, j in zip(w, tail_blocks):
+        for d in range(dim):
+            out[d] += wi / tot * vb[j][d]
+    return mx + math.log(tot), out

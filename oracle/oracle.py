@@ -25,7 +25,10 @@ Readings where the pages are silent (all listed in the design notes):
   * the threshold is inclusive (the crossing block is kept, so kept mass >= p); p >= 1 keeps
     every block; p = 0 keeps exactly the top block;
   * the residual epilogue adds c_h * R to the sparse output, R = O_dense - O_sparse captured
-    at a dense refresh on the same kept set.
+    at a dense refresh on the same kept set;
+  * the coarse tail (RECAP §3.2) uses each query token against the block means of the omitted
+    key blocks, a block's mass being its token count times exp(s * q . K̄_j); its moment
+    refinements are left out (formulas absent), and the cached discrepancy is added unscaled.
 """
 from __future__ import annotations
 
@@ -312,6 +315,119 @@ def mean_drift(qbar, kbar, qbar_ref, kbar_ref) -> np.ndarray:
         den = np.sqrt((r ** 2).sum(axis=(-2, -1)))
         out.append(np.divide(num, den, out=np.where(num > 0, np.inf, 0.0), where=den > 0))
     return np.stack(out, axis=-1)
+
+
+def _row_blocks(mask, rows, B, H, M):
+    if rows is None:
+        rows = [(b, h, i) for b in range(B) for h in range(H) for i in range(M)]
+    return rows
+
+
+def coarse_tail(q, k, v, block: int, sm_scale: float, mask, rows=None):
+    """Zeroth-order estimate of the attention over each query's omitted key blocks, from block
+    means ([RECAP] §3.2: block means give first estimates of the omitted tail's value and
+    normalising mass; the coarse log-mass is the log of the summed block masses, the coarse
+    output the block values weighted by their normalised masses; the estimate is recomputed at
+    every sparse evaluation).
+
+    For query t of block i and each key block j outside i's kept set, every key of block j is
+    replaced by the block mean K̄_j, so the block's mass is n_j * exp(s * Q_t . K̄_j), n_j its
+    token count (the last block may be short). Then
+        lse_bar_t = ln sum_j n_j exp(s * Q_t . K̄_j)
+        o_bar_t   = sum_j n_j exp(s * Q_t . K̄_j) V̄_j / sum_j n_j exp(s * Q_t . K̄_j).
+    The key-variance (COBS) and value-key-covariance (PISA) refinements named on the page are
+    not applied: their formulas are not on the pages. A query block that keeps every key block
+    has no tail: lse_bar = -inf, o_bar = 0.
+    q, k, v: [B, H, N, D]; mask: bool [B, H, M, M]. Returns (lse_bar float64 [B, H, N],
+    o_bar float64 [B, H, N, D]), NaN outside `rows` (an iterable of (b, h, i)).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    B, H, N, D = q.shape
+    starts, ends = block_partition(N, block)
+    M = len(starts)
+    kb = block_mean_pool(k, block)
+    vb = block_mean_pool(v, block)
+    n = (ends - starts).astype(np.float64)
+    lse = np.full((B, H, N), np.nan)
+    out = np.full((B, H, N, D), np.nan)
+    for b, h, i in _row_blocks(mask, rows, B, H, M):
+        qs = slice(starts[i], ends[i])
+        js = np.nonzero(~np.asarray(mask[b, h, i], dtype=bool))[0]
+        if len(js) == 0:
+            lse[b, h, qs] = -np.inf
+            out[b, h, qs] = 0.0
+            continue
+        logw = float(sm_scale) * (q[b, h, qs] @ kb[b, h, js].T) + np.log(n[js])[None, :]
+        mx = logw.max(axis=-1, keepdims=True)
+        w = np.exp(logw - mx)
+        tot = w.sum(axis=-1)
+        lse[b, h, qs] = mx[:, 0] + np.log(tot)
+        out[b, h, qs] = (w @ vb[b, h, js]) / tot[:, None]
+    return lse, out
+
+
+def exact_tail(q, k, v, block: int, sm_scale: float, mask, rows=None):
+    """The omitted tail itself: log-sum-exp and softmax attention over the valid tokens of the
+    key blocks outside each query block's kept set, i.e. `attention_lse` and
+    `masked_attention` on the complementary mask ([RECAP] §3.2: the tail quantity whose coarse
+    part the block means estimate; at a dense refresh it is available exactly). An empty tail
+    gives -inf and 0. Returns (lse_T [B, H, N], o_T [B, H, N, D]) float64, NaN outside rows."""
+    q = np.asarray(q, dtype=np.float64)
+    B, H, N, D = q.shape
+    M = -(-N // block)
+    comp = ~np.asarray(mask, dtype=bool)
+    rows = _row_blocks(mask, rows, B, H, M)
+    full = [r for r in rows if comp[r].any()]
+    empty = [r for r in rows if not comp[r].any()]
+    lse = attention_lse(q, k, block, sm_scale, mask=comp, rows=full)
+    out = masked_attention(q, k, v, block, sm_scale, comp, rows=full)
+    starts, ends = block_partition(N, block)
+    for b, h, i in empty:
+        lse[b, h, starts[i]:ends[i]] = -np.inf
+        out[b, h, starts[i]:ends[i]] = 0.0
+    return lse, out
+
+
+def tail_discrepancy(lse_t, o_t, lse_bar, o_bar):
+    """What the coarse estimate leaves unresolved, taken at a dense refresh ([RECAP] §3.2: a
+    tail quantity y_t = ȳ_t + d_t; d at the refresh step is cached):
+    d_lse = lse_T - lse_bar (0 where both are -inf: no tail), d_o = o_T - o_bar."""
+    lse_t = np.asarray(lse_t, dtype=np.float64)
+    lse_bar = np.asarray(lse_bar, dtype=np.float64)
+    both = np.isneginf(lse_t) & np.isneginf(lse_bar)
+    with np.errstate(invalid="ignore"):
+        d_lse = np.where(both, 0.0, lse_t - lse_bar)
+    return d_lse, np.asarray(o_t, dtype=np.float64) - np.asarray(o_bar, dtype=np.float64)
+
+
+def merge_attention(o_a, lse_a, o_b, lse_b):
+    """Attention over the union of two disjoint key sets from each part's output and
+    log-sum-exp: weights e^lse / (e^lse_a + e^lse_b), log-sum-exp logaddexp(lse_a, lse_b) (the
+    log-mass merge of the sparse part with the tail, [RECAP] §3.2). A part with lse = -inf has
+    no keys and weight 0. Returns (out, lse)."""
+    o_a = np.asarray(o_a, dtype=np.float64)
+    o_b = np.asarray(o_b, dtype=np.float64)
+    la = np.asarray(lse_a, dtype=np.float64)
+    lb = np.asarray(lse_b, dtype=np.float64)
+    lse = np.logaddexp(la, lb)
+    with np.errstate(invalid="ignore"):
+        wa = np.where(np.isneginf(la), 0.0, np.exp(la - lse))
+        wb = np.where(np.isneginf(lb), 0.0, np.exp(lb - lse))
+    out = wa[..., None] * o_a + wb[..., None] * o_b
+    return out, lse
+
+
+def tail_reconstruction(o_s, lse_s, lse_bar, o_bar, d_lse=None, d_o=None):
+    """RECAP's attention-level reconstruction at a sparse step ([RECAP] §3.2): the fresh coarse
+    tail plus the discrepancy cached at the last refresh, ŷ = ȳ + d_h for the log-mass and the
+    output, merged with the sparse part by log-mass. Without d the coarse tail is merged as is.
+    Returns float64 [B, H, N, D]."""
+    lse_t = np.asarray(lse_bar, dtype=np.float64)
+    o_t = np.asarray(o_bar, dtype=np.float64)
+    if d_lse is not None:
+        lse_t = lse_t + np.asarray(d_lse, dtype=np.float64)
+        o_t = o_t + np.asarray(d_o, dtype=np.float64)
+    return merge_attention(o_s, lse_s, o_t, lse_t)[0]
 
 
 def block_sparsity(count: np.ndarray, m: int) -> float:

@@ -442,6 +442,153 @@ def check_mean_drift():
     assert np.allclose(O.mean_drift(x, xr, xr, xr)[0, 0], [0.2, 0.0], rtol=0, atol=1e-15)
 
 
+# ----------------------------------------------------------------------------- coarse tail
+def _tail_case(n=200, b=32, d=8, seed=400, heads=2):
+    q, k, v = (_rand((1, heads, n, d), seed + i) for i in range(3))
+    m = -(-n // b)
+    rng = np.random.default_rng(seed + 9)
+    mask = rng.random((1, heads, m, m)) < 0.45
+    mask[..., 0] = True  # every row keeps block 0 and omits the (possibly short) last block
+    mask[..., -1] = False
+    return q, k, v, mask
+
+
+def check_tail_block_constant_keys():
+    """With every key and value constant over its block (a short last block included) the
+    block-mean estimate is exact: coarse tail == exact tail, log-mass and output. The per-token
+    query is kept: two queries of one block get different tails."""
+    n, b, d = 200, 32, 8  # blocks of 32 x 6 and a last block of 8
+    q, k, v, mask = _tail_case(n, b, d, 410)
+    kb = O.block_mean_pool(k, b)
+    vb = O.block_mean_pool(v, b)
+    st, en = O.block_partition(n, b)
+    for j in range(len(st)):
+        k[:, :, st[j]:en[j]] = kb[:, :, j:j + 1]
+        v[:, :, st[j]:en[j]] = vb[:, :, j:j + 1]
+    s = 0.9
+    cl, co = O.coarse_tail(q, k, v, b, s, mask)
+    el, eo = O.exact_tail(q, k, v, b, s, mask)
+    assert np.allclose(cl, el, rtol=0, atol=1e-12), np.abs(cl - el).max()
+    assert np.allclose(co, eo, rtol=0, atol=1e-12), np.abs(co - eo).max()
+    assert abs(cl[0, 0, 0] - cl[0, 0, 1]) > 1e-3
+
+
+def check_tail_closed_forms():
+    """One omitted block j: log-mass ln n_j + s * q . K̄_j and output V̄_j. Two omitted blocks:
+    output weights n_j e^{a_j} / (n_0 e^{a_0} + n_1 e^{a_1}) (a logistic in a_1 - a_0)."""
+    n, b, d = 150, 32, 4  # last block (index 4) has 22 tokens
+    q, k, v, _ = _tail_case(n, b, d, 420, heads=1)
+    m = 5
+    kb = O.block_mean_pool(k, b)[0, 0]
+    vb = O.block_mean_pool(v, b)[0, 0]
+    s = 0.7
+    mask = np.ones((1, 1, m, m), bool)
+    mask[0, 0, 2, 4] = False  # row 2 omits only the short last block
+    mask[0, 0, 1, [0, 3]] = False
+    cl, co = O.coarse_tail(q, k, v, b, s, mask)
+    for t in range(64, 96):
+        a = s * q[0, 0, t] @ kb[4]
+        assert abs(cl[0, 0, t] - (math.log(22.0) + a)) < 1e-12
+        assert np.allclose(co[0, 0, t], vb[4], rtol=0, atol=1e-12)
+    for t in range(32, 64):
+        a0, a1 = s * q[0, 0, t] @ kb[0], s * q[0, 0, t] @ kb[3]
+        w1 = 1.0 / (1.0 + math.exp(a0 - a1))  # both blocks hold 32 tokens
+        assert np.allclose(co[0, 0, t], (1 - w1) * vb[0] + w1 * vb[3], rtol=0, atol=1e-12)
+        assert abs(cl[0, 0, t] - (math.log(32.0) + np.logaddexp(a0, a1))) < 1e-12
+    assert np.all(np.isneginf(cl[0, 0, :32])) and np.all(co[0, 0, :32] == 0.0)
+
+
+def check_tail_vs_brute():
+    """Coarse tail against the scalar brute force on a ragged tiny case."""
+    n, b, d = 70, 16, 5  # 5 blocks, the last of 6 tokens
+    q, k, v, mask = _tail_case(n, b, d, 430, heads=1)
+    s = 0.6
+    cl, co = O.coarse_tail(q, k, v, b, s, mask)
+    qs, ks, vs = q[0, 0].tolist(), k[0, 0].tolist(), v[0, 0].tolist()
+    for t in range(0, n, 3):
+        tail = [j for j in range(5) if not mask[0, 0, t // b, j]]
+        bl, bo = brute.coarse_tail_row(qs[t], ks, vs, n, b, tail, s)
+        assert abs(cl[0, 0, t] - bl) < 1e-12, (t, cl[0, 0, t], bl)
+        assert np.allclose(co[0, 0, t], bo, rtol=0, atol=1e-12)
+
+
+def check_tail_key_shift():
+    """Adding a vector c to every key shifts each query's score by s * q_t . c: both tail
+    log-masses move by exactly that per-token amount and the outputs do not change."""
+    n, b, d = 130, 32, 6
+    q, k, v, mask = _tail_case(n, b, d, 440)
+    c = _rand((d,), 441, 0.5)
+    s = 0.8
+    shift = s * q @ c  # [1, H, N]
+    for fn in (O.coarse_tail, O.exact_tail):
+        l0, o0 = fn(q, k, v, b, s, mask)
+        l1, o1 = fn(q, k + c, v, b, s, mask)
+        assert np.allclose(l1 - l0, shift, rtol=0, atol=1e-11), fn.__name__
+        assert np.allclose(o1, o0, rtol=0, atol=1e-11), fn.__name__
+
+
+def check_tail_partition_identity():
+    """The kept and the omitted key sets partition the keys: merging the block-sparse output
+    and log-sum-exp with the exact tail gives dense attention and the dense log-sum-exp."""
+    n, b, d = 200, 32, 8
+    q, k, v, mask = _tail_case(n, b, d, 450)
+    s = 0.5
+    o_s = O.masked_attention(q, k, v, b, s, mask)
+    l_s = O.attention_lse(q, k, b, s, mask)
+    l_t, o_t = O.exact_tail(q, k, v, b, s, mask)
+    out, lse = O.merge_attention(o_s, l_s, o_t, l_t)
+    assert np.allclose(out, _sdpa64(q, k, v, s), rtol=0, atol=1e-12)
+    sc = s * np.einsum("bhnd,bhmd->bhnm", q, k)
+    mx = sc.max(-1)
+    assert np.allclose(lse, mx + np.log(np.exp(sc - mx[..., None]).sum(-1)), rtol=0, atol=1e-12)
+
+
+def check_tail_refresh_identity():
+    """At the refresh step the discrepancy makes the reconstruction exact (its error d_h - d_t
+    vanishes at t = h): sparse output merged with coarse tail + d equals dense attention. At
+    later inputs the reconstructed tail misses the exact one by exactly d_h - d_t."""
+    n, b, d = 200, 32, 8
+    q, k, v, mask = _tail_case(n, b, d, 460)
+    s = 0.5
+    cl, co = O.coarse_tail(q, k, v, b, s, mask)
+    el, eo = O.exact_tail(q, k, v, b, s, mask)
+    dl, do = O.tail_discrepancy(el, eo, cl, co)
+    o_s = O.masked_attention(q, k, v, b, s, mask)
+    l_s = O.attention_lse(q, k, b, s, mask)
+    rec = O.tail_reconstruction(o_s, l_s, cl, co, dl, do)
+    assert np.allclose(rec, _sdpa64(q, k, v, s), rtol=0, atol=1e-12)
+    q2, k2, v2 = (x + _rand(x.shape, 470 + i, 0.1) for i, x in enumerate((q, k, v)))
+    cl2, co2 = O.coarse_tail(q2, k2, v2, b, s, mask)
+    el2, eo2 = O.exact_tail(q2, k2, v2, b, s, mask)
+    dl2, do2 = O.tail_discrepancy(el2, eo2, cl2, co2)
+    assert np.allclose((cl2 + dl) - el2, dl - dl2, rtol=0, atol=1e-12)
+    assert np.allclose((co2 + do) - eo2, do - do2, rtol=0, atol=1e-12)
+    coarse_only = O.tail_reconstruction(o_s, l_s, cl, co)
+    assert np.abs(coarse_only - rec).max() > 1e-6  # the cached discrepancy matters here
+
+
+def check_tail_empty_and_merge():
+    """Every block kept: no tail (-inf, 0), zero discrepancy, and the reconstruction is the
+    sparse output itself. merge_attention weighs parts by e^lse: lse ln 3 against ln 1 gives
+    3/4 and 1/4, and a part with lse -inf has no weight."""
+    n, b, d = 96, 32, 4
+    q, k, v, _ = _tail_case(n, b, d, 480)
+    every = np.ones((1, 2, 3, 3), bool)
+    cl, co = O.coarse_tail(q, k, v, b, 0.5, every)
+    el, eo = O.exact_tail(q, k, v, b, 0.5, every)
+    assert np.all(np.isneginf(cl)) and np.all(co == 0.0) and np.all(np.isneginf(el))
+    dl, do = O.tail_discrepancy(el, eo, cl, co)
+    assert np.all(dl == 0.0) and np.all(do == 0.0)
+    o_s = O.dense_attention(q, k, v, 0.5, block=b)
+    l_s = O.attention_lse(q, k, b, 0.5)
+    assert np.array_equal(O.tail_reconstruction(o_s, l_s, cl, co, dl, do), o_s)
+    oa, ob = np.full((1, 1, 1, 2), 4.0), np.full((1, 1, 1, 2), -8.0)
+    out, lse = O.merge_attention(oa, np.full((1, 1, 1), math.log(3.0)), ob, np.zeros((1, 1, 1)))
+    assert np.allclose(out, 1.0, rtol=0, atol=1e-15) and abs(lse[0, 0, 0] - math.log(4.0)) < 1e-15
+    out, _ = O.merge_attention(oa, np.full((1, 1, 1), -np.inf), ob, np.zeros((1, 1, 1)))
+    assert np.array_equal(out, ob)
+
+
 ALL_CHECKS = [
     check_pool_block_constant,
     check_pool_closed_form_ragged,
@@ -466,6 +613,13 @@ ALL_CHECKS = [
     check_candidate_scores,
     check_candidate_topp,
     check_mean_drift,
+    check_tail_block_constant_keys,
+    check_tail_closed_forms,
+    check_tail_vs_brute,
+    check_tail_key_shift,
+    check_tail_partition_identity,
+    check_tail_refresh_identity,
+    check_tail_empty_and_merge,
 ]
 
 

@@ -157,6 +157,65 @@ def _drift_swapped(qbar, kbar, qref, kref):
     return _REAL["mean_drift"](qbar, kbar, qref, kref)[..., ::-1]
 
 
+def _coarse_variant(no_count=False, full_count=False, pooled_query=False, with_kept=False):
+    def f(q, k, v, block, sm_scale, mask, rows=None):
+        q = np.asarray(q, dtype=np.float64)
+        B, H, N, D = q.shape
+        st, en = O.block_partition(N, block)
+        M = len(st)
+        kb, vb = O.block_mean_pool(k, block), O.block_mean_pool(v, block)
+        qb = O.block_mean_pool(q, block)
+        n = np.full(M, float(block)) if full_count else (en - st).astype(np.float64)
+        lse, out = np.full((B, H, N), np.nan), np.full((B, H, N, D), np.nan)
+        for b in range(B):
+            for h in range(H):
+                for i in range(M):
+                    qs = slice(st[i], en[i])
+                    js = np.arange(M) if with_kept else np.nonzero(~mask[b, h, i])[0]
+                    if len(js) == 0:
+                        lse[b, h, qs], out[b, h, qs] = -np.inf, 0.0
+                        continue
+                    qq = np.broadcast_to(qb[b, h, i], q[b, h, qs].shape) if pooled_query \
+                        else q[b, h, qs]
+                    lw = sm_scale * (qq @ kb[b, h, js].T)
+                    if not no_count:
+                        lw = lw + np.log(n[js])[None, :]
+                    mx = lw.max(-1, keepdims=True)
+                    w = np.exp(lw - mx)
+                    lse[b, h, qs] = mx[:, 0] + np.log(w.sum(-1))
+                    out[b, h, qs] = (w @ vb[b, h, js]) / w.sum(-1)[:, None]
+        return lse, out
+    return f
+
+
+def _exact_tail_of_kept(q, k, v, block, sm_scale, mask, rows=None):
+    return _REAL["exact_tail"](q, k, v, block, sm_scale, ~np.asarray(mask, dtype=bool) | (
+        np.arange(mask.shape[-1]) == 0), rows)
+
+
+def _discrepancy_sign(lse_t, o_t, lse_bar, o_bar):
+    dl, do = _REAL["tail_discrepancy"](lse_t, o_t, lse_bar, o_bar)
+    return -dl, -do
+
+
+def _merge_swapped(o_a, lse_a, o_b, lse_b):
+    return _REAL["merge_attention"](o_b, lse_a, o_a, lse_b)
+
+
+def _merge_linear_weights(o_a, lse_a, o_b, lse_b):
+    la, lb = np.asarray(lse_a, dtype=np.float64), np.asarray(lse_b, dtype=np.float64)
+    wa = np.where(np.isneginf(la), 0.0, np.abs(la))
+    wb = np.where(np.isneginf(lb), 0.0, np.abs(lb))
+    tot = np.where(wa + wb > 0, wa + wb, 1.0)
+    out = (wa / tot)[..., None] * o_a + (wb / tot)[..., None] * o_b
+    return out, np.logaddexp(la, lb)
+
+
+def _reconstruction_without_lse_shift(o_s, lse_s, lse_bar, o_bar, d_lse=None, d_o=None):
+    return _REAL["tail_reconstruction"](o_s, lse_s, lse_bar, o_bar,
+                                        None if d_lse is None else np.zeros_like(d_lse), d_o)
+
+
 MUTANTS = {
     "pool divides by the full block size": ("block_mean_pool", _pool_divides_by_block),
     "pool takes the first token": ("block_mean_pool", _pool_first_token),
@@ -188,6 +247,16 @@ MUTANTS = {
                                                _cand_topp_unrenormalised),
     "drift without the square root": ("mean_drift", _drift_squared),
     "drift of Q and K swapped": ("mean_drift", _drift_swapped),
+    "coarse tail without block token counts": ("coarse_tail", _coarse_variant(no_count=True)),
+    "coarse tail counts a full last block": ("coarse_tail", _coarse_variant(full_count=True)),
+    "coarse tail scores the pooled query": ("coarse_tail", _coarse_variant(pooled_query=True)),
+    "coarse tail includes the kept blocks": ("coarse_tail", _coarse_variant(with_kept=True)),
+    "exact tail over the kept blocks": ("exact_tail", _exact_tail_of_kept),
+    "discrepancy coarse minus exact": ("tail_discrepancy", _discrepancy_sign),
+    "merge pairs weights with the wrong outputs": ("merge_attention", _merge_swapped),
+    "merge weighs by lse, not e^lse": ("merge_attention", _merge_linear_weights),
+    "reconstruction drops the log-mass discrepancy": ("tail_reconstruction",
+                                                      _reconstruction_without_lse_shift),
 }
 
 
