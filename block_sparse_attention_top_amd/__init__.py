@@ -5,7 +5,8 @@ marshals torch device tensors into its entry points. Functions carry the C names
 recap_block_scores, recap_topp_mask, recap_block_sparse_attn, recap_dense_attn, and the
 row-statistics variants recap_block_sparse_attn_stats and recap_dense_attn_stats, and the
 mask-reuse building blocks recap_block_means, recap_scores_from_means, recap_topp_mask_cand and
-recap_mean_drift.
+recap_mean_drift, and the tail reconstruction recap_tail_estimate, recap_dense_attn_tail and
+recap_block_sparse_attn_tail.
 """
 from ._lib import RecapDesc, RecapError, load  # noqa: F401
 from .ops import (  # noqa: F401
@@ -14,10 +15,13 @@ from .ops import (  # noqa: F401
     recap_block_scores,
     recap_block_sparse_attn,
     recap_block_sparse_attn_stats,
+    recap_block_sparse_attn_tail,
     recap_dense_attn,
     recap_dense_attn_stats,
+    recap_dense_attn_tail,
     recap_mean_drift,
     recap_scores_from_means,
+    recap_tail_estimate,
     recap_topp_mask,
     recap_topp_mask_cand,
     recap_workspace_size,

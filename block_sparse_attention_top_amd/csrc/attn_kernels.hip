@@ -321,15 +321,17 @@ struct KeptAcc {
 
 // ---- per-tile math, shared by the pipeline drivers below ----
 
-// S^T = K Q^T for one 64-key tile in LDS (raw dot products).
+// S^T = K Q^T for one 64-key tile in LDS (raw dot products); ACC adds to s0, s1 instead.
 // LDS buffers are 256-byte aligned, so base + (lane offset XOR (ks << 5)) equals
 // (base + lane offset) XOR (ks << 5): one opaque base per tile, one XOR per fragment.
-template <int D, int NW>
+template <int D, int NW, bool ACC = false>
 __device__ __forceinline__ void tile_qk(uint32_t kb, const bf16x8 (&qf)[D / 16],
                                         const LaneConsts<D, NW>& lc, f32x16& s0, f32x16& s1) {
   constexpr int ROWB = Tiles<D, NW>::ROWB;
-  s0 = f32x16{};
-  s1 = f32x16{};
+  if (!ACC) {
+    s0 = f32x16{};
+    s1 = f32x16{};
+  }
   const uint32_t base = opaque(kb + lc.k_rd);
   mfma_prio_hi();
 #pragma unroll
@@ -343,12 +345,8 @@ __device__ __forceinline__ void tile_qk(uint32_t kb, const bf16x8 (&qf)[D / 16],
   mfma_prio_lo();
 }
 
-// Online softmax of one tile in the base-2 domain with lazy rescale; returns the bf16 P^T
-// operands and whether the tile also feeds the kept-block accumulator.
-template <int D, bool CAP>
-__device__ __forceinline__ bool tile_softmax(f32x16& s0, f32x16& s1, int j, int key0, int N,
-                                             float scale_log2, int half, f32x16 (&o)[D / 32],
-                                             SoftmaxState& sm, KeptAcc<D>& ka, bf16x8 (&pf)[4]) {
+// Keys past N in the last, partial tile get score -inf (a rare, uniform branch).
+__device__ __forceinline__ void mask_tail(f32x16& s0, f32x16& s1, int key0, int N, int half) {
   if (key0 + kKeyTile > N) {
     asm volatile("" ::: "memory");  // keep the rare tail tile a real (uniform) branch
 #pragma unroll
@@ -358,10 +356,21 @@ __device__ __forceinline__ bool tile_softmax(f32x16& s0, f32x16& s1, int j, int 
       if (key0 + 32 + kr >= N) s1[r] = -INFINITY;
     }
   }
+}
+
+// Row maximum of one tile's scores in log2 units.
+__device__ __forceinline__ float tile_rowmax(const f32x16& s0, const f32x16& s1, float scale_log2) {
   float mx = max3(s0[0], s1[0], s0[1]);
 #pragma unroll
   for (int r = 1; r < 16; ++r) mx = max3(mx, s1[r], r + 1 < 16 ? s0[r + 1] : s1[r]);
-  const float mt = cross_half_max(mx) * scale_log2;  // finite: a tile has a valid key
+  return cross_half_max(mx) * scale_log2;
+}
+
+// Lazy rescale: raise the running max to the tile max mt only when some lane's max grows by
+// more than kLazy, rescaling the accumulators (and the kept-block ones under capture).
+template <int D, bool CAP>
+__device__ __forceinline__ void raise_max(float mt, SoftmaxState& sm, f32x16 (&o)[D / 32],
+                                          KeptAcc<D>& ka) {
   if (__builtin_amdgcn_ballot_w64(mt > sm.m + kLazy) != 0) {
     const float mn = fmaxf(sm.m, mt);
     const float alpha = __builtin_amdgcn_exp2f(sm.m - mn);
@@ -375,7 +384,13 @@ __device__ __forceinline__ bool tile_softmax(f32x16& s0, f32x16& s1, int j, int 
       for (int dt = 0; dt < D / 32; ++dt) ka.o[dt] *= alpha;
     }
   }
-  const float neg_m = -sm.m;
+}
+
+// Weights of one tile, p = exp2(s * scale - m) rounded to bf16 (the P^T operands of the PV
+// product), and the per-lane sum of exactly those rounded weights.
+__device__ __forceinline__ float tile_exp(const f32x16& s0, const f32x16& s1, float scale_log2,
+                                          float m, bf16x8 (&pf)[4]) {
+  const float neg_m = -m;
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
@@ -384,7 +399,6 @@ __device__ __forceinline__ bool tile_softmax(f32x16& s0, f32x16& s1, int j, int 
       pf[ks][e] = (bf16_t)__builtin_amdgcn_exp2f(__builtin_fmaf(x, scale_log2, neg_m));
     }
   }
-  // row sum of the bf16-rounded probabilities (the ones the PV product uses)
   typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
   const bf16x2 one = {(bf16_t)1.0f, (bf16_t)1.0f};
   float acc = 0.f;
@@ -396,6 +410,18 @@ __device__ __forceinline__ bool tile_softmax(f32x16& s0, f32x16& s1, int j, int 
       acc = __builtin_amdgcn_fdot2_f32_bf16(pr, one, acc, false);
     }
   }
+  return acc;
+}
+
+// Online softmax of one tile in the base-2 domain with lazy rescale; returns the bf16 P^T
+// operands and whether the tile also feeds the kept-block accumulator.
+template <int D, bool CAP>
+__device__ __forceinline__ bool tile_softmax(f32x16& s0, f32x16& s1, int j, int key0, int N,
+                                             float scale_log2, int half, f32x16 (&o)[D / 32],
+                                             SoftmaxState& sm, KeptAcc<D>& ka, bf16x8 (&pf)[4]) {
+  mask_tail(s0, s1, key0, N, half);  // finite max: a tile has a valid key
+  raise_max<D, CAP>(tile_rowmax(s0, s1, scale_log2), sm, o, ka);
+  const float acc = tile_exp(s0, s1, scale_log2, sm.m, pf);
   sm.l += acc;
   const bool kept = CAP && ((ka.bits[j >> 5] >> (j & 31)) & 1u);  // uniform per wavefront
   if (kept) ka.l += acc;
@@ -616,6 +642,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RECAP_W
     // weights), the block is left to the residual pass, which recomputes the sparse output
     // with its own maximum.
     const float ls = cross_half_sum(ka.l);
+    // the keys outside the kept set: the dense sums minus the kept ones (same running max)
+    const float ltail = cross_half_sum(sm.l - ka.l);
     const bool want_r = p.res_out != nullptr;  // the same for the whole grid
     bool flagged = false;
     if (want_r) {
@@ -632,10 +660,26 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RECAP_W
       const int64_t srow = (int64_t)bh * p.N + qrow;
       if (p.lse_out != nullptr) p.lse_out[srow] = (sm.m + log2f(lt)) * kLn2;
       if (p.kmass_out != nullptr) p.kmass_out[srow] = ls / lt;
+      if (p.tail_lse != nullptr)
+        p.tail_lse[srow] = ltail > 0.f ? (sm.m + log2f(ltail)) * kLn2 : -INFINITY;
+    }
+    if (p.tail_o != nullptr) {
+      const float invt = ltail > 0.f ? 1.0f / ltail : 0.f;
+      float* to = p.tail_o + ((int64_t)bh * p.N + qrow) * D;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          f32x4 x;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[e] = (o[dt][g * 4 + e] - ka.o[dt][g * 4 + e]) * invt;
+          *reinterpret_cast<f32x4*>(to + dt * 32 + g * 8 + half * 4) = x;
+        }
+      }
     }
     const int64_t orow = base + (int64_t)qrow * p.st.n;
     const float invs = ls > 0.f ? 1.0f / ls : 0.f;
-    float* odw = p.od_ws + ((int64_t)bh * p.npad + qrow) * D;
+    const int64_t odrow = ((int64_t)bh * p.npad + qrow) * D;  // od_ws is NULL without residual
     {
 #pragma clang fp contract(off)
 #pragma unroll
@@ -653,7 +697,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RECAP_W
           wr[e] = (bf16_t)(vd[e] - vs);
         }
         *reinterpret_cast<bf16x4*>(p.out + orow + d0) = wo;
-        if (flagged) *reinterpret_cast<f32x4*>(odw + d0) = vd;
+        if (flagged) *reinterpret_cast<f32x4*>(p.od_ws + odrow + d0) = vd;
         else if (want_r) *reinterpret_cast<bf16x4*>(p.res_out + orow + d0) = wr;
       }
     }
@@ -691,6 +735,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RECAP_W
   const bool has_res = MODE == kSparse && p.res != nullptr;
   const bf16_t* rsrc = has_res ? p.res + orow : nullptr;
   const float c = p.res_scale.v[h];
+  float* dst32 = (MODE == kSparse && p.o32_out != nullptr)
+                     ? p.o32_out + ((int64_t)bh * p.N + qrow) * D : nullptr;
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) {
 #pragma unroll
@@ -699,6 +745,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RECAP_W
       f32x4 v;
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] = o[dt][g * 4 + e] * inv;
+      if (dst32 != nullptr) {  // fp32 output for a later merge (no epilogue on this path)
+        *reinterpret_cast<f32x4*>(dst32 + d0) = v;
+        continue;
+      }
       if (has_res) {
         const bf16x4 r4 = *reinterpret_cast<const bf16x4*>(rsrc + d0);
 #pragma unroll
@@ -710,6 +760,234 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RECAP_W
       *reinterpret_cast<bf16x4*>(dst + d0) = w;
     }
   }
+}
+
+// ------------------------------------------------------------------------------------------
+// Coarse tail of RECAP's attention-level reconstruction (paperpeel.com RECAP Sec. 3.2: for the
+// omitted interactions, block means give initial estimates of the normalisation mass and the
+// value). For query token t of query block i, over the pooled key blocks j outside i's kept
+// set: weights n_j * exp(s * q_t . K̄_j), values V̄_j. The coarse log-mass is ln of the summed
+// weights, the coarse output the weighted mean of the V̄_j. Zeroth order: the key-variance and
+// value-key-covariance refinements the page names are not applied.
+// Same tile math as attn_kernel (4 wavefronts, 128 query rows, 64 pooled keys per tile, one
+// LDS stage: a row has only ceil(M / 64) tiles), with the pooled scores from the hi + lo key
+// pair. Kept blocks and pooled keys past M get score -inf; the last pooled key's weight
+// carries its shorter block.
+// ------------------------------------------------------------------------------------------
+// Pooled keys as a pair of bf16 values, hi = bf16(K̄) and lo = bf16(K̄ - hi) (about 16
+// significant bits, so the pooled scores are as accurate as the token scores, whose bf16
+// operands are exact), pooled values as bf16. Element e of [B*H][mpad][D]; rows >= M are zero.
+template <int D>
+__global__ __launch_bounds__(256) void tail_keys_kernel(const float* __restrict__ kbar,
+                                                        const float* __restrict__ vbar, int M,
+                                                        int mpad, int64_t total,
+                                                        bf16_t* __restrict__ kb_hi,
+                                                        bf16_t* __restrict__ kb_lo,
+                                                        bf16_t* __restrict__ vb16) {
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * 256) {
+    const int64_t bh = e / ((int64_t)mpad * D);
+    const int64_t r = e - bh * mpad * D;
+    const int j = (int)(r / D), d = (int)(r - (int64_t)j * D);
+    const int64_t src = (bh * M + j) * D + d;
+    const float kx = j < M ? kbar[src] : 0.f;
+    const bf16_t hi = (bf16_t)kx;
+    kb_hi[e] = hi;
+    kb_lo[e] = (bf16_t)(kx - (float)hi);
+    vb16[e] = (bf16_t)(j < M ? vbar[src] : 0.f);
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void tail_kernel(TailParams p) {
+  constexpr int NW = 4, QROWS = 128;
+  __shared__ __align__(256) unsigned char kbuf[Tiles<D, NW>::TILE_BYTES];
+  __shared__ __align__(256) unsigned char klbuf[Tiles<D, NW>::TILE_BYTES];
+  __shared__ __align__(256) unsigned char vbuf[Tiles<D, NW>::TILE_BYTES];
+  __shared__ uint32_t kept_bits[2][kMaxBlocks / 32];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 31, half = lane >> 5;
+  const int tile = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = tile / p.mq, qi = tile - bh * p.mq;
+  const int b = bh / p.H, h = bh - b * p.H;
+  const int64_t base = b * p.st.b + h * p.st.h;
+  const int qrow = qi * QROWS + wave * 32 + n;
+  LaneConsts<D, NW> lc;
+  lc.init(lane, wave, (int64_t)D, p.mpad);
+  bf16x8 qf[D / 16];
+  {
+    const bf16_t* src = p.q + base + (int64_t)min(qrow, p.N - 1) * p.st.n + half * 8;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(src + ks * 16);
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) asm volatile("" ::"v"(qf[ks]));
+  }
+  // kept-block bitmaps of the query blocks of this work-group
+  const int nb = QROWS / p.block;  // 2 for block 64, 1 for block 128
+  const int words = (p.M + 31) / 32;
+  for (int w = threadIdx.x; w < nb * words; w += NW * 64) kept_bits[w / words][w % words] = 0u;
+  __syncthreads();
+  for (int lb = 0; lb < nb; ++lb) {
+    const int blk = (qi * QROWS) / p.block + lb;
+    if (blk >= p.M) break;
+    const int64_t row = (int64_t)bh * p.M + blk;
+    const int cnt = min(max(p.count[row], 0), p.M);
+    for (int c = threadIdx.x; c < cnt; c += NW * 64) {
+      const int jj = min(max(p.idx[row * p.M + c], 0), p.M - 1);
+      atomicOr(&kept_bits[lb][jj >> 5], 1u << (jj & 31));
+    }
+  }
+  __syncthreads();
+  const uint32_t* own = kept_bits[(wave * 32) / p.block];
+
+  f32x16 o[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) o[dt] = f32x16{};
+  SoftmaxState sm{-INFINITY, 0.f};
+  KeptAcc<D> none;
+  const uint32_t kb0 = lds_base(kbuf), kl0 = lds_base(klbuf), vb0 = lds_base(vbuf);
+  const bf16_t* kp = p.kb + (int64_t)bh * p.mpad * D;
+  const bf16_t* klp = p.kb_lo + (int64_t)bh * p.mpad * D;
+  const bf16_t* vtp = p.vt + (int64_t)bh * D * p.mpad;
+  const int ntile = (p.M + kKeyTile - 1) / kKeyTile;
+  for (int t = 0; t < ntile; ++t) {
+    const int key0 = t * kKeyTile;
+    issue_k<D, NW>(kb0, kp, (int64_t)D, p.M, key0, wave, lane, lc);
+    issue_k<D, NW>(kl0, klp, (int64_t)D, p.M, key0, wave, lane, lc);
+    issue_v<D, NW>(vb0, vtp, p.mpad, key0, wave, lc);
+    wait_vmem<0>();
+    lds_barrier();
+    f32x16 s0, s1;
+    tile_qk<D, NW>(kb0, qf, lc, s0, s1);
+    tile_qk<D, NW, true>(kl0, qf, lc, s0, s1);  // + q . (K̄ - hi)
+    // scores in log2 units; kept blocks and pooled keys past M get -inf, the last pooled key
+    // the log2 of its share of a full block
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int kr = ((r >> 2) << 3) + half * 4 + (r & 3);
+      const int j0 = key0 + kr, j1 = key0 + 32 + kr;
+      const bool m0 = j0 >= p.M || ((own[min(j0, p.M - 1) >> 5] >> (j0 & 31)) & 1u);
+      const bool m1 = j1 >= p.M || ((own[min(j1, p.M - 1) >> 5] >> (j1 & 31)) & 1u);
+      const float x0 = s0[r] * p.scale_log2, x1 = s1[r] * p.scale_log2;
+      s0[r] = m0 ? -INFINITY : (j0 == p.M - 1 ? x0 + p.last_bias : x0);
+      s1[r] = m1 ? -INFINITY : (j1 == p.M - 1 ? x1 + p.last_bias : x1);
+    }
+    // the mask depends only on the key and the wavefront's query block: a tile is either
+    // fully masked for all lanes of a wavefront (no raise) or has a finite maximum for all
+    raise_max<D, false>(tile_rowmax(s0, s1, 1.0f), sm, o, none);
+    // while every key so far is masked, m = -inf: use +inf so the weights are 0, not NaN
+    bf16x8 pf[4];
+    sm.l += tile_exp(s0, s1, 1.0f, sm.m == -INFINITY ? INFINITY : sm.m, pf);
+    tile_pv<D, NW>(vb0, pf, lc, o, none, false);
+    lds_barrier();  // every wave is done with the tile buffers
+  }
+  const float lt = cross_half_sum(sm.l);
+  if (qrow >= p.N) return;
+  const int64_t srow = (int64_t)bh * p.N + qrow;
+  if (half == 0) p.tail_lse[srow] = lt > 0.f ? (sm.m + log2f(lt)) * kLn2 + p.ln_block : -INFINITY;
+  const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+  float* to = p.tail_o + srow * D;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      f32x4 x;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = o[dt][g * 4 + e] * inv;
+      *reinterpret_cast<f32x4*>(to + dt * 32 + g * 8 + half * 4) = x;
+    }
+  }
+}
+
+// Discrepancy and merge of RECAP's reconstruction (paperpeel.com RECAP Sec. 3.2: a tail
+// quantity y_t = coarse + discrepancy; the discrepancy d_h taken exactly at a dense refresh is
+// cached, and later sparse steps use coarse + d_h). One thread per (token, 4 head dims); the
+// fp32 arrays are [B*H][N] and [B*H][N][D] contiguous, `out` is bf16 in the q layout.
+// mode 0: d_lse = exact_lse - coarse_lse (0 when both are -inf: no keys outside the kept set),
+//         d_o = exact_o - coarse_o (fp32: d_o is a difference of tail outputs, as large as the
+//         values, and a bf16 copy would add its rounding to every later merge);
+// mode 1: lT = coarse_lse + d_lse, oT = coarse_o + d_o (d optional), and with the sparse
+//         output O_s of log-mass lse_s: out = w O_s + (1 - w) oT, w = 1 / (1 + exp(lT - lse_s))
+//         (w = 1 when lT = -inf).
+template <int D>
+__global__ __launch_bounds__(256) void tail_combine_kernel(int mode, int H, int N, Strides st,
+                                                           int64_t total,
+                                                           const float* __restrict__ a_lse,
+                                                           const float* __restrict__ a_o,
+                                                           const float* __restrict__ c_lse,
+                                                           const float* __restrict__ c_o,
+                                                           const float* __restrict__ d_lse,
+                                                           const float* __restrict__ d_o,
+                                                           float* __restrict__ d_lse_out,
+                                                           float* __restrict__ d_o_out,
+                                                           bf16_t* __restrict__ out) {
+  constexpr int G = D / 4;
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * 256) {
+    const int64_t row = e / G;  // (b*H + h)*N + t
+    const int d0 = (int)(e - row * G) * 4;
+    const f32x4 co = *reinterpret_cast<const f32x4*>(c_o + row * D + d0);
+    const f32x4 ao = *reinterpret_cast<const f32x4*>(a_o + row * D + d0);
+    const float cl = c_lse[row];
+    const float al = a_lse[row];
+    if (mode == 0) {
+      if (d0 == 0) d_lse_out[row] = (al == -INFINITY && cl == -INFINITY) ? 0.f : al - cl;
+      *reinterpret_cast<f32x4*>(d_o_out + row * D + d0) = ao - co;
+    } else {
+      const bool has_d = d_lse != nullptr;
+      const float lT = cl + (has_d ? d_lse[row] : 0.f);
+      const float w = lT == -INFINITY ? 1.f : 1.0f / (1.0f + __expf(lT - al));
+      const f32x4 dd = has_d ? *reinterpret_cast<const f32x4*>(d_o + row * D + d0) : f32x4{};
+      const int64_t bh = row / N;
+      const int t = (int)(row - bh * N);
+      const int64_t b = bh / H, h = bh - b * H;
+      bf16x4 w4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w4[i] = (bf16_t)(w * ao[i] + (1.f - w) * (co[i] + dd[i]));
+      *reinterpret_cast<bf16x4*>(out + b * st.b + h * st.h + (int64_t)t * st.n + d0) = w4;
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+hipError_t launch_tail_keys(const float* kbar, const float* vbar, int BH, int M, int D, int mpad,
+                            bf16_t* kb_hi, bf16_t* kb_lo, bf16_t* vb16, hipStream_t stream) {
+  const int64_t total = (int64_t)BH * mpad * D;
+  const int grid = (int)(total < 65536LL * 256 ? (total + 255) / 256 : 65536);
+  if (D == 128)
+    tail_keys_kernel<128><<<grid, 256, 0, stream>>>(kbar, vbar, M, mpad, total, kb_hi, kb_lo,
+                                                    vb16);
+  else
+    tail_keys_kernel<64><<<grid, 256, 0, stream>>>(kbar, vbar, M, mpad, total, kb_hi, kb_lo,
+                                                   vb16);
+  return hipGetLastError();
+}
+
+hipError_t launch_tail(TailParams p, int B, int D, hipStream_t stream) {
+  p.mq = (p.N + 127) / 128;
+  const int grid = B * p.H * p.mq;
+  if (D == 128)
+    tail_kernel<128><<<grid, 256, 0, stream>>>(p);
+  else
+    tail_kernel<64><<<grid, 256, 0, stream>>>(p);
+  return hipGetLastError();
+}
+
+hipError_t launch_tail_combine(int mode, int B, int H, int N, int D, Strides st,
+                               const float* a_lse, const float* a_o, const float* c_lse,
+                               const float* c_o, const float* d_lse, const float* d_o,
+                               float* d_lse_out, float* d_o_out, bf16_t* out,
+                               hipStream_t stream) {
+  const int64_t total = (int64_t)B * H * N * (D / 4);
+  const int grid = (int)(total < 65536LL * 256 ? (total + 255) / 256 : 65536);
+  if (D == 128)
+    tail_combine_kernel<128><<<grid, 256, 0, stream>>>(mode, H, N, st, total, a_lse, a_o, c_lse,
+                                                       c_o, d_lse, d_o, d_lse_out, d_o_out, out);
+  else
+    tail_combine_kernel<64><<<grid, 256, 0, stream>>>(mode, H, N, st, total, a_lse, a_o, c_lse,
+                                                      c_o, d_lse, d_o, d_lse_out, d_o_out, out);
+  return hipGetLastError();
 }
 
 // ------------------------------------------------------------------------------------------

@@ -73,9 +73,41 @@ struct AttnParams {
   uint8_t* flags;   // capture: [B*H*M] 1 = residual of this query block left to the residual pass
   float* lse_out;   // optional [B*H][N]: natural-log log-sum-exp of the attended scores
   float* kmass_out; // optional [B*H][N] (capture mode): kept share of the dense attention mass
+  float* o32_out;   // optional [B*H][N][D] (sparse mode): fp32 output instead of bf16 `out`
+  float* tail_lse;  // optional [B*H][N] (capture mode): log-mass of the keys outside the kept set
+  float* tail_o;    // optional [B*H][N][D] (capture mode): attention output over those keys
   HeadScalars res_scale;
 };
 
 hipError_t launch_attention(AttnParams p, int B, int D, AttnMode mode, hipStream_t stream);
+
+// Coarse tail of the attention-level reconstruction: attention over the pooled key blocks
+// outside each query block's kept set (block means stand for their tokens).
+struct TailParams {
+  const bf16_t* q;
+  Strides st;          // q strides
+  const bf16_t* kb;    // pooled keys, bf16 [B*H][mpad][D] (rows >= M zero): hi part
+  const bf16_t* kb_lo; // bf16(K̄ - hi), same layout
+  const bf16_t* vt;    // pooled values, packed V^T [B*H][D][mpad]
+  int H, N, M, block, mpad, mq;
+  float scale_log2;
+  float last_bias;     // added to the log2-unit score of pooled key M-1: log2(n_last / block)
+  float ln_block;      // ln(block): each pooled key stands for `block` tokens
+  const int32_t* count;
+  const int32_t* idx;
+  float* tail_lse;     // [B*H][N]
+  float* tail_o;       // [B*H][N][D]
+};
+hipError_t launch_tail_keys(const float* kbar, const float* vbar, int BH, int M, int D, int mpad,
+                            bf16_t* kb_hi, bf16_t* kb_lo, bf16_t* vb16, hipStream_t stream);
+hipError_t launch_tail(TailParams p, int B, int D, hipStream_t stream);
+// mode 0: d = exact - coarse (d_lse [B*H][N], d_o [B*H][N][D], fp32);
+// mode 1: out (bf16, q layout) = merge of the fp32 sparse output (log-mass lse_s) with the
+// tail (coarse + d, d optional)
+hipError_t launch_tail_combine(int mode, int B, int H, int N, int D, Strides st,
+                               const float* a_lse, const float* a_o, const float* c_lse,
+                               const float* c_o, const float* d_lse, const float* d_o,
+                               float* d_lse_out, float* d_o_out, bf16_t* out,
+                               hipStream_t stream);
 
 }  // namespace recap

@@ -67,6 +67,26 @@ size_t flag_bytes(const recap_desc* d) {
   return align_up((size_t)d->batch * d->heads * num_blocks(d));
 }
 
+// Coarse tail: pooled keys and values padded to whole 64-key tiles.
+inline int pooled_pad(const recap_desc* d) { return (num_blocks(d) + 63) / 64 * 64; }
+size_t pooled16_bytes(const recap_desc* d) {
+  return align_up((size_t)d->batch * d->heads * pooled_pad(d) * d->head_dim * 2);
+}
+size_t row_bytes(const recap_desc* d) {
+  return align_up((size_t)d->batch * d->heads * d->seq * sizeof(float));
+}
+size_t row_d_bytes(const recap_desc* d) {
+  return align_up((size_t)d->batch * d->heads * d->seq * d->head_dim * sizeof(float));
+}
+// K̄, V̄ (fp32), K̄ hi and lo, V̄ (bf16), packed V̄^T (bf16)
+size_t tail_estimate_bytes(const recap_desc* d) {
+  return 2 * pooled_bytes(d) + 4 * pooled16_bytes(d);
+}
+// V^T; one attention part (log-sum-exp, fp32 output); the coarse tail (same); the estimate
+size_t tail_merge_bytes(const recap_desc* d) {
+  return vt_bytes(d) + 2 * (row_bytes(d) + row_d_bytes(d)) + tail_estimate_bytes(d);
+}
+
 size_t workspace_for(int op, const recap_desc* d) {
   switch (op) {
     case RECAP_OP_BLOCK_SCORES: return 2 * pooled_bytes(d);
@@ -74,6 +94,9 @@ size_t workspace_for(int op, const recap_desc* d) {
     case RECAP_OP_SPARSE:
     case RECAP_OP_DENSE: return vt_bytes(d);
     case RECAP_OP_DENSE_CAPTURE: return vt_bytes(d) + snapshot_bytes(d) + flag_bytes(d);
+    case RECAP_OP_TAIL: return tail_estimate_bytes(d);
+    case RECAP_OP_DENSE_TAIL:
+    case RECAP_OP_SPARSE_TAIL: return tail_merge_bytes(d);
     default: return 0;
   }
 }
@@ -149,7 +172,7 @@ int recap_workspace_size(int op, const recap_desc* d, size_t* bytes) {
   if (bytes == nullptr) return RECAP_E_NULL;
   const int s = validate_desc(d);
   if (s != RECAP_OK) return s;
-  if (op < RECAP_OP_BLOCK_SCORES || op > RECAP_OP_DENSE_CAPTURE) return RECAP_E_VALUE;
+  if (op < RECAP_OP_BLOCK_SCORES || op > RECAP_OP_SPARSE_TAIL) return RECAP_E_VALUE;
   *bytes = workspace_for(op, d);
   return RECAP_OK;
 }
@@ -432,6 +455,205 @@ int recap_dense_attn_stats(const recap_desc* d, const void* q, const void* k, co
   if (lse_out == nullptr) return RECAP_E_NULL;
   return dense_impl(d, q, k, v, sm_scale, kept_count_opt, kept_idx_opt, out, residual_out_opt,
                     lse_out, kept_mass_out_opt, ws, ws_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+constexpr double kLog2e = 1.4426950408889634;
+
+// Coarse tail over each query block's omitted key blocks (log-mass c_lse [B*H][N], output c_o
+// [B*H][N][D], fp32) from the block means of k and v; tws: tail_estimate_bytes(d) of workspace.
+hipError_t coarse_tail(const recap_desc* d, const void* q, const void* k, const void* v,
+                       const int32_t* count, const int32_t* idx, float sm_scale, float* c_lse,
+                       float* c_o, void* tws, hipStream_t st) {
+  const int M = num_blocks(d), mpad = pooled_pad(d), H = d->heads, D = d->head_dim;
+  char* w = (char*)tws;
+  float* kbar = (float*)w;
+  float* vbar = (float*)(w + pooled_bytes(d));
+  char* w16 = w + 2 * pooled_bytes(d);
+  bf16_t* kb_hi = (bf16_t*)w16;
+  bf16_t* kb_lo = (bf16_t*)(w16 + pooled16_bytes(d));
+  bf16_t* vb16 = (bf16_t*)(w16 + 2 * pooled16_bytes(d));
+  bf16_t* vt = (bf16_t*)(w16 + 3 * pooled16_bytes(d));
+  hipError_t e = launch_pool((const bf16_t*)k, (const bf16_t*)v, strides_of(d), d->batch, H,
+                             d->seq, D, d->block, kbar, vbar, st);
+  if (e == hipSuccess)
+    e = launch_tail_keys(kbar, vbar, d->batch * H, M, D, mpad, kb_hi, kb_lo, vb16, st);
+  if (e == hipSuccess) {
+    const Strides ps{(int64_t)H * mpad * D, (int64_t)mpad * D, (int64_t)D};
+    e = launch_pack_vt(vb16, ps, d->batch, H, M, D, mpad, vt, st);
+  }
+  if (e != hipSuccess) return e;
+  TailParams p;
+  memset(&p, 0, sizeof(p));
+  p.q = (const bf16_t*)q;
+  p.st = strides_of(d);
+  p.kb = kb_hi;
+  p.kb_lo = kb_lo;
+  p.vt = vt;
+  p.H = H;
+  p.N = d->seq;
+  p.M = M;
+  p.block = d->block;
+  p.mpad = mpad;
+  p.scale_log2 = (float)((double)sm_scale * kLog2e);
+  const int n_last = d->seq - (M - 1) * d->block;
+  p.last_bias = (float)log2((double)n_last / d->block);
+  p.ln_block = (float)log((double)d->block);
+  p.count = count;
+  p.idx = idx;
+  p.tail_lse = c_lse;
+  p.tail_o = c_o;
+  return launch_tail(p, d->batch, D, st);
+}
+
+// Shared validation of the tail entry points: q, k, v, kept lists, scale, workspace, device.
+int check_tail_args(int op, const recap_desc* d, const void* q, const void* k, const void* v,
+                    const int32_t* count, const int32_t* idx, float sm_scale, const void* ws,
+                    size_t ws_bytes) {
+  int s = validate_desc(d);
+  if (s != RECAP_OK) return s;
+  if (q == nullptr || k == nullptr || v == nullptr || count == nullptr || idx == nullptr)
+    return RECAP_E_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(count) || !aligned16(idx))
+    return RECAP_E_ALIGN;
+  if (!isfinite(sm_scale) || !(sm_scale > 0.f)) return RECAP_E_VALUE;
+  return check_workspace(op, d, ws, ws_bytes);
+}
+
+// Workspace carving shared by the dense and sparse tail calls (tail_merge_bytes).
+struct TailWs {
+  bf16_t* vt;
+  float *a_lse, *a_o, *c_lse, *c_o;
+  void* est;
+};
+TailWs carve_tail_ws(const recap_desc* d, void* ws) {
+  char* w = (char*)ws;
+  TailWs t;
+  t.vt = (bf16_t*)w;
+  w += vt_bytes(d);
+  t.a_lse = (float*)w;
+  w += row_bytes(d);
+  t.a_o = (float*)w;
+  w += row_d_bytes(d);
+  t.c_lse = (float*)w;
+  w += row_bytes(d);
+  t.c_o = (float*)w;
+  w += row_d_bytes(d);
+  t.est = w;
+  return t;
+}
+
+void fill_attn(AttnParams& p, const recap_desc* d, const void* q, const void* k,
+               const bf16_t* vt, float sm_scale, const int32_t* count, const int32_t* idx) {
+  memset(&p, 0, sizeof(p));
+  p.q = (const bf16_t*)q;
+  p.k = (const bf16_t*)k;
+  p.vt = vt;
+  p.st = strides_of(d);
+  p.H = d->heads;
+  p.N = d->seq;
+  p.M = num_blocks(d);
+  p.block = d->block;
+  p.npad = p.M * d->block;
+  p.scale_log2 = (float)((double)sm_scale * kLog2e);
+  p.count = count;
+  p.idx = idx;
+}
+
+}  // namespace
+
+extern "C" {
+
+int recap_tail_estimate(const recap_desc* d, const void* q, const void* k, const void* v,
+                        const int32_t* kept_count, const int32_t* kept_idx, float sm_scale,
+                        float* tail_lse, float* tail_out, void* ws, size_t ws_bytes,
+                        void* stream) {
+  int s = check_tail_args(RECAP_OP_TAIL, d, q, k, v, kept_count, kept_idx, sm_scale, ws,
+                          ws_bytes);
+  if (s != RECAP_OK) return s;
+  if (tail_lse == nullptr || tail_out == nullptr) return RECAP_E_NULL;
+  if (!aligned16(tail_lse) || !aligned16(tail_out)) return RECAP_E_ALIGN;
+  if ((void*)tail_lse == (void*)tail_out) return RECAP_E_VALUE;
+  if ((s = check_device()) != RECAP_OK) return s;
+  return launched(coarse_tail(d, q, k, v, kept_count, kept_idx, sm_scale, tail_lse, tail_out,
+                              ws, (hipStream_t)stream));
+}
+
+int recap_dense_attn_tail(const recap_desc* d, const void* q, const void* k, const void* v,
+                          float sm_scale, const int32_t* kept_count, const int32_t* kept_idx,
+                          void* out, float* tail_dlse, float* tail_dout, void* ws,
+                          size_t ws_bytes, void* stream) {
+  int s = check_tail_args(RECAP_OP_DENSE_TAIL, d, q, k, v, kept_count, kept_idx, sm_scale, ws,
+                          ws_bytes);
+  if (s != RECAP_OK) return s;
+  if (out == nullptr || tail_dlse == nullptr || tail_dout == nullptr) return RECAP_E_NULL;
+  if (!aligned16(out) || !aligned16(tail_dlse) || !aligned16(tail_dout)) return RECAP_E_ALIGN;
+  if (out == q || out == k || out == v || (void*)tail_dout == out ||
+      (void*)tail_dout == (void*)tail_dlse)
+    return RECAP_E_VALUE;
+  if ((s = check_device()) != RECAP_OK) return s;
+
+  hipStream_t st = (hipStream_t)stream;
+  const TailWs t = carve_tail_ws(d, ws);
+  hipError_t e = launch_pack_vt((const bf16_t*)v, strides_of(d), d->batch, d->heads, d->seq,
+                                d->head_dim, num_blocks(d) * d->block, t.vt, st);
+  if (e != hipSuccess) return launched(e);
+  // dense pass with the kept-block accumulator: the exact tail is the dense sums minus the
+  // kept ones (no residual, so no snapshot or flags)
+  AttnParams p;
+  fill_attn(p, d, q, k, t.vt, sm_scale, kept_count, kept_idx);
+  p.out = (bf16_t*)out;
+  p.tail_lse = t.a_lse;
+  p.tail_o = t.a_o;
+  e = launch_attention(p, d->batch, d->head_dim, kDenseCapture, st);
+  if (e == hipSuccess)
+    e = coarse_tail(d, q, k, v, kept_count, kept_idx, sm_scale, t.c_lse, t.c_o, t.est, st);
+  if (e == hipSuccess)
+    e = launch_tail_combine(0, d->batch, d->heads, d->seq, d->head_dim, strides_of(d), t.a_lse,
+                            t.a_o, t.c_lse, t.c_o, nullptr, nullptr, tail_dlse, tail_dout,
+                            nullptr, st);
+  return launched(e);
+}
+
+int recap_block_sparse_attn_tail(const recap_desc* d, const void* q, const void* k,
+                                 const void* v, const int32_t* kept_count,
+                                 const int32_t* kept_idx, float sm_scale,
+                                 const float* tail_dlse_opt, const float* tail_dout_opt,
+                                 void* out, void* ws, size_t ws_bytes, void* stream) {
+  int s = check_tail_args(RECAP_OP_SPARSE_TAIL, d, q, k, v, kept_count, kept_idx, sm_scale, ws,
+                          ws_bytes);
+  if (s != RECAP_OK) return s;
+  if (out == nullptr) return RECAP_E_NULL;
+  if ((tail_dlse_opt == nullptr) != (tail_dout_opt == nullptr)) return RECAP_E_NULL;
+  if (!aligned16(out) || (tail_dlse_opt != nullptr && (!aligned16(tail_dlse_opt) ||
+                                                       !aligned16(tail_dout_opt))))
+    return RECAP_E_ALIGN;
+  if (out == q || out == k || out == v ||
+      (tail_dout_opt != nullptr && (const void*)tail_dout_opt == (const void*)out))
+    return RECAP_E_VALUE;
+  if ((s = check_device()) != RECAP_OK) return s;
+
+  hipStream_t st = (hipStream_t)stream;
+  const TailWs t = carve_tail_ws(d, ws);
+  hipError_t e = launch_pack_vt((const bf16_t*)v, strides_of(d), d->batch, d->heads, d->seq,
+                                d->head_dim, num_blocks(d) * d->block, t.vt, st);
+  if (e != hipSuccess) return launched(e);
+  AttnParams p;
+  fill_attn(p, d, q, k, t.vt, sm_scale, kept_count, kept_idx);
+  p.out = (bf16_t*)out;  // not written: the fp32 output goes to the merge
+  p.o32_out = t.a_o;
+  p.lse_out = t.a_lse;
+  e = launch_attention(p, d->batch, d->head_dim, kSparse, st);
+  if (e == hipSuccess)
+    e = coarse_tail(d, q, k, v, kept_count, kept_idx, sm_scale, t.c_lse, t.c_o, t.est, st);
+  if (e == hipSuccess)
+    e = launch_tail_combine(1, d->batch, d->heads, d->seq, d->head_dim, strides_of(d), t.a_lse,
+                            t.a_o, t.c_lse, t.c_o, tail_dlse_opt, tail_dout_opt, nullptr,
+                            nullptr, (bf16_t*)out, st);
+  return launched(e);
 }
 
 }  // extern "C"

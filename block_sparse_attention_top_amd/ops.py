@@ -292,6 +292,74 @@ def recap_mean_drift(desc: RecapDesc, qbar, kbar, qbar_ref, kbar_ref, drift=None
     return drift
 
 
+def recap_tail_estimate(desc: RecapDesc, q, k, v, kept_count, kept_idx,
+                        sm_scale: Optional[float] = None, tail_lse=None, tail_out=None,
+                        workspace=None, stream=None):
+    """Coarse tail from block means over each query block's omitted key blocks: (tail_lse fp32
+    [B,H,N], tail_out fp32 [B,H,N,D] contiguous)."""
+    _same_layout(desc, q, k, v)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(desc.head_dim)
+    tail_lse = _row_stat(desc, tail_lse, q.device)
+    tail_out = _row_vec(desc, tail_out, q.device, "tail_out")
+    ws, nbytes = _workspace(_lib.OP_TAIL, desc, q.device, workspace)
+    check(_lib.load().recap_tail_estimate(
+        ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(kept_count), _ptr(kept_idx),
+        float(sm_scale), _ptr(tail_lse), _ptr(tail_out), _ptr(ws), nbytes, _stream(stream)),
+        "recap_tail_estimate")
+    return tail_lse, tail_out
+
+
+def _row_vec(desc: RecapDesc, given: Optional[torch.Tensor], device, what: str):
+    shp = (desc.batch, desc.heads, desc.seq, desc.head_dim)
+    if given is None:
+        return torch.empty(shp, dtype=torch.float32, device=device)
+    if given.dtype != torch.float32 or tuple(given.shape) != shp or not given.is_contiguous():
+        raise ValueError(f"{what} is contiguous fp32 [B, H, N, D]")
+    return given
+
+
+def recap_dense_attn_tail(desc: RecapDesc, q, k, v, kept_count, kept_idx,
+                          sm_scale: Optional[float] = None, out=None, tail_dlse=None,
+                          tail_dout=None, workspace=None, stream=None):
+    """Dense refresh that also writes the tail discrepancy on the kept set: (out bf16,
+    tail_dlse fp32 [B,H,N], tail_dout fp32 [B,H,N,D])."""
+    _same_layout(desc, q, k, v, out)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(desc.head_dim)
+    out = _like_out(q) if out is None else out
+    tail_dout = _row_vec(desc, tail_dout, q.device, "tail_dout")
+    tail_dlse = _row_stat(desc, tail_dlse, q.device)
+    ws, nbytes = _workspace(_lib.OP_DENSE_TAIL, desc, q.device, workspace)
+    check(_lib.load().recap_dense_attn_tail(
+        ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), float(sm_scale), _ptr(kept_count),
+        _ptr(kept_idx), _ptr(out), _ptr(tail_dlse), _ptr(tail_dout), _ptr(ws), nbytes,
+        _stream(stream)), "recap_dense_attn_tail")
+    return out, tail_dlse, tail_dout
+
+
+def recap_block_sparse_attn_tail(desc: RecapDesc, q, k, v, kept_count, kept_idx,
+                                 sm_scale: Optional[float] = None, tail_dlse=None,
+                                 tail_dout=None, out=None, workspace=None, stream=None):
+    """Block-sparse attention merged by log-mass with the fresh coarse tail plus the cached
+    discrepancy (both or neither of tail_dlse, tail_dout); bf16 out in q's layout."""
+    _same_layout(desc, q, k, v, out)
+    if (tail_dlse is None) != (tail_dout is None):
+        raise ValueError("tail_dlse and tail_dout go together")
+    if tail_dlse is not None:
+        _row_stat(desc, tail_dlse, q.device)
+        _row_vec(desc, tail_dout, q.device, "tail_dout")
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(desc.head_dim)
+    out = _like_out(q) if out is None else out
+    ws, nbytes = _workspace(_lib.OP_SPARSE_TAIL, desc, q.device, workspace)
+    check(_lib.load().recap_block_sparse_attn_tail(
+        ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(kept_count), _ptr(kept_idx),
+        float(sm_scale), _ptr(tail_dlse), _ptr(tail_dout), _ptr(out), _ptr(ws), nbytes,
+        _stream(stream)), "recap_block_sparse_attn_tail")
+    return out
+
+
 def sparse_step(desc: RecapDesc, q, k, v, top_p, sm_scale: Optional[float] = None,
                 residual=None, res_scale=None, out=None, stream=None):
     """One corrected sparse attention call: block scores -> top-p -> sparse attention

@@ -13,6 +13,9 @@
  *                          optional fused epilogue  O' = O + c_h * R;
  *   4. recap_dense_attn    dense refresh over all keys, optionally capturing the residual
  *                          R = O_dense - O_sparse on a given kept set.
+ * Beside them: row statistics (*_stats), mask reuse across steps, and RECAP's tail
+ * reconstruction (*_tail: a coarse estimate of the omitted attention from block means plus a
+ * discrepancy cached at the dense refresh, merged with the sparse part by log-mass).
  *
  * Sources (page title, section / figure):
  *   RECAP: Reciprocal Sparse Attention and Hierarchical Caching for Efficient Video Diffusion
@@ -60,7 +63,7 @@
 extern "C" {
 #endif
 
-#define RECAP_ABI_VERSION 3 /* 2: *_stats entry points; 3: mask reuse entry points */
+#define RECAP_ABI_VERSION 4 /* 2: *_stats entry points; 3: mask reuse; 4: coarse tail */
 #define RECAP_MAX_HEADS 128   /* per-head host arrays are passed by value to the kernels */
 #define RECAP_MAX_BLOCKS 8192 /* M = ceil(N / block) upper bound (top-p sorts a row in LDS) */
 
@@ -93,7 +96,10 @@ enum recap_op {
   RECAP_OP_TOPP = 1,
   RECAP_OP_SPARSE = 2,
   RECAP_OP_DENSE = 3,         /* dense refresh without capture */
-  RECAP_OP_DENSE_CAPTURE = 4  /* dense refresh that also writes the residual */
+  RECAP_OP_DENSE_CAPTURE = 4, /* dense refresh that also writes the residual */
+  RECAP_OP_TAIL = 5,          /* recap_tail_estimate */
+  RECAP_OP_DENSE_TAIL = 6,    /* recap_dense_attn_tail */
+  RECAP_OP_SPARSE_TAIL = 7    /* recap_block_sparse_attn_tail */
 };
 
 /* Version of this ABI (RECAP_ABI_VERSION of the built library). */
@@ -218,6 +224,53 @@ int recap_topp_mask_cand(const recap_desc* d, const float* probs, const int32_t*
                          void* stream);
 int recap_mean_drift(const recap_desc* d, const float* qbar, const float* kbar,
                      const float* qbar_ref, const float* kbar_ref, float* drift, void* stream);
+
+/* RECAP's attention-level reconstruction of the omitted tail (paperpeel.com RECAP Sec. 3.2):
+ * a fresh coarse estimate of the attention over the key blocks a query block omits, from block
+ * means, plus the discrepancy d the estimate leaves, taken exactly at a dense refresh and
+ * cached; at a sparse step the tail is estimated again and d added (y = coarse + d, whose
+ * error d_h - d_t vanishes at the refresh step), and the result is merged with the sparse
+ * attention by log-mass. Zeroth order: the page's key-variance and value-key-covariance
+ * refinements of the estimate are not applied (their formulas are not on the pages).
+ *
+ * Coarse tail of query token t in query block i, over the key blocks j outside i's kept set,
+ * with n_j the token count of block j and K̄_j, V̄_j block means (fp32 pooling; K̄ then held
+ * as a bf16 pair hi + lo, about 16 significant bits, V̄ as bf16):
+ *   lse_bar_t = ln sum_j n_j exp(sm_scale * Q_t . K̄_j)           (-inf when i keeps all blocks)
+ *   o_bar_t   = sum_j n_j exp(sm_scale * Q_t . K̄_j) V̄_j / sum_j n_j exp(...)   (0 when empty)
+ * computed like attention over the pooled keys (bf16 products, fp32 sums).
+ * Exact tail at a refresh: lse_T_t = ln sum_u exp(sm_scale * Q_t . K_u) and o_T_t the softmax
+ * attention output over the tokens u of those blocks, taken from the dense pass as its sums
+ * minus the kept blocks' sums (same running maximum).
+ * Discrepancy: d_lse = lse_T - lse_bar (0 when both are -inf), d_o = o_T - o_bar.
+ * Merge at a sparse step with the block-sparse output O_s of log-sum-exp lse_s:
+ *   l = lse_bar + d_lse, o = o_bar + d_o (d omitted: coarse alone),
+ *   out = w O_s + (1 - w) o,  w = 1 / (1 + exp(l - lse_s))  (w = 1 when l = -inf).
+ *
+ * recap_tail_estimate: the coarse tail alone. tail_lse fp32 [B,H,N], tail_out fp32 [B,H,N,D]
+ *   (contiguous, distinct). ws: recap_workspace_size(RECAP_OP_TAIL).
+ * recap_dense_attn_tail: dense refresh (out as recap_dense_attn) that also writes the
+ *   discrepancy on the given kept set: tail_dlse fp32 [B,H,N] and tail_dout fp32 [B,H,N,D]
+ *   (contiguous; fp32 because d_o is a difference of tail outputs, as large as the values, and
+ *   its rounding would enter every later merge; neither may alias out). ws: RECAP_OP_DENSE_TAIL.
+ * recap_block_sparse_attn_tail: block-sparse attention merged with the coarse tail plus the
+ *   cached discrepancy (tail_dlse_opt and tail_dout_opt, both or neither), out bf16.
+ *   ws: RECAP_OP_SPARSE_TAIL. With the refresh's inputs and kept lists it reproduces the
+ *   dense output (up to rounding).
+ * Kept lists as for recap_block_sparse_attn (indices clamped into [0, M)). */
+int recap_tail_estimate(const recap_desc* d, const void* q, const void* k, const void* v,
+                        const int32_t* kept_count, const int32_t* kept_idx, float sm_scale,
+                        float* tail_lse, float* tail_out, void* ws, size_t ws_bytes,
+                        void* stream);
+int recap_dense_attn_tail(const recap_desc* d, const void* q, const void* k, const void* v,
+                          float sm_scale, const int32_t* kept_count, const int32_t* kept_idx,
+                          void* out, float* tail_dlse, float* tail_dout, void* ws,
+                          size_t ws_bytes, void* stream);
+int recap_block_sparse_attn_tail(const recap_desc* d, const void* q, const void* k,
+                                 const void* v, const int32_t* kept_count,
+                                 const int32_t* kept_idx, float sm_scale,
+                                 const float* tail_dlse_opt, const float* tail_dout_opt,
+                                 void* out, void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -36,7 +36,7 @@ def test_header_symbols_exported():
 
 def test_version_and_status_strings():
     lib = _lib.load()
-    assert lib.recap_abi_version() == _lib.ABI_VERSION == 3
+    assert lib.recap_abi_version() == _lib.ABI_VERSION == 4
     for st in list(_lib.STATUS_NAMES) + [-99]:
         s = lib.recap_status_string(st)
         assert s and len(s.decode()) > 1
@@ -67,6 +67,15 @@ def test_workspace_sizes():
     st, n2 = ws_size(_lib.OP_DENSE_CAPTURE, d)
     flags = -(-40 * M // 256) * 256  # one byte per query block, 256-byte aligned
     assert st == 0 and n2 == n + 40 * M * 64 * 128 * 4 + flags
+    # coarse tail: K̄, V̄ fp32, then K̄ hi, K̄ lo, V̄, V̄^T bf16 over M padded to 1216 pooled keys
+    pooled = 40 * M * 128 * 4
+    p16 = 40 * 1216 * 128 * 2
+    st, nt = ws_size(_lib.OP_TAIL, d)
+    assert st == 0 and nt == 2 * pooled + 4 * p16
+    rows = 40 * 75600 * 4
+    for op in (_lib.OP_DENSE_TAIL, _lib.OP_SPARSE_TAIL):
+        assert ws_size(op, d) == (0, n + 2 * (rows + rows * 128) + nt)
+    assert ws_size(8, d)[0] == -5
     assert ws_size(99, d)[0] == -5
     assert _lib.load().recap_workspace_size(0, ctypes.byref(d), None) == -1
 
@@ -184,3 +193,45 @@ def test_stats_validation():
     assert dense(cnt=_p(), idx=_p(), km=_p(FAKE + 16388), n=need_c) == -4
     assert dense() == -7
     assert dense(cnt=_p(), idx=_p(), km=_p(FAKE + 16384), n=need_c) == -7
+
+
+@cpu_only
+def test_tail_validation():
+    lib = _lib.load()
+    d = desc(H=2)
+    _, need_t = ws_size(_lib.OP_TAIL, d)
+    _, need_m = ws_size(_lib.OP_SPARSE_TAIL, d)
+    q, k, v = _p(), _p(FAKE + 1024), _p(FAKE + 2048)
+
+    def est(cnt=_p(), lse=_p(FAKE + 8192), to=_p(FAKE + 16384), n=need_t, s=0.125):
+        return lib.recap_tail_estimate(ctypes.byref(d), q, k, v, cnt, _p(), s, lse, to, _p(), n,
+                                       None)
+    assert est(cnt=None) == -1
+    assert est(lse=None) == -1
+    assert est(to=_p(FAKE + 16388)) == -4
+    assert est(to=_p(FAKE + 8192)) == -5  # outputs alias
+    assert est(s=float("nan")) == -5
+    assert est(n=need_t - 1) == -6
+    assert est() == -7
+
+    def dense(out=_p(FAKE + 4096), dl=_p(FAKE + 8192), do=_p(FAKE + 16384), n=need_m):
+        return lib.recap_dense_attn_tail(ctypes.byref(d), q, k, v, 0.125, _p(), _p(), out, dl, do,
+                                         _p(), n, None)
+    assert dense(dl=None) == -1
+    assert dense(do=None) == -1
+    assert dense(do=_p(FAKE + 4096)) == -5  # discrepancy aliases out
+    assert dense(do=_p(FAKE + 8192)) == -5  # the two discrepancy outputs alias
+    assert dense(out=_p(FAKE)) == -5        # out aliases q
+    assert dense(n=need_m - 256) == -6
+    assert dense() == -7
+
+    def sparse(dl=None, do=None, out=_p(FAKE + 4096), n=need_m):
+        return lib.recap_block_sparse_attn_tail(ctypes.byref(d), q, k, v, _p(), _p(), 0.125, dl,
+                                                do, out, _p(), n, None)
+    assert sparse(dl=_p(FAKE + 8192)) == -1  # both or neither
+    assert sparse(do=_p(FAKE + 16384)) == -1
+    assert sparse(out=None) == -1
+    assert sparse(dl=_p(FAKE + 8194), do=_p(FAKE + 16384)) == -4
+    assert sparse(n=need_t) == -6
+    assert sparse() == -7
+    assert sparse(dl=_p(FAKE + 8192), do=_p(FAKE + 16384)) == -7

@@ -12,33 +12,9 @@ import parity
 import synth
 from oracle import oracle as O
 
+from gpu_common import DEV, bsa, f64, say, to_dev  # noqa: F401
+
 pytestmark = pytest.mark.gpu
-DEV = "cuda:0"
-
-
-def say(msg):
-    print(msg, flush=True)
-
-
-@pytest.fixture(scope="module")
-def bsa():
-    import block_sparse_attention_top_amd as m
-
-    m.load()
-    assert torch.cuda.is_available()
-    return m
-
-
-def to_dev(x, layout="bhnd"):
-    if layout == "bnhd":
-        x = x.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
-    t = x.to(DEV)
-    assert t.stride() == x.stride()
-    return t
-
-
-def f64(t):
-    return synth.to_f64(t.cpu())
 
 
 def run_small(bsa, cfg, seq=None, layout="bhnd", top_p=None, res_scale=None):

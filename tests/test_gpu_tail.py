@@ -1,0 +1,145 @@
+"""RECAP tail reconstruction on the GPU (coarse tail from block means, discrepancy at a dense
+refresh, log-mass merge at a sparse step) against the CPU oracle, through the C ABI.
+
+The kept lists come from the GPU's own top-p (both sides then use the same kept set). Bounds:
+  * coarse log-mass: the row-statistics bound plus the largest score change that bf16 block
+    means can cause (computed from the data, parity.coarse_lse_atol);
+  * discrepancy d_lse: the coarse bound, plus the bf16-weight bound of the exact tail, plus the
+    fp32 summation bound of the dense pass amplified by 1 / (tail share), since the exact tail
+    is the dense sums minus the kept sums;
+  * outputs (coarse fp32 output, discrepancy d_o on rows with a tail share >= 1e-2, the
+    refresh-step reconstruction against dense attention): the attention-output rule of
+    parity.check_out;
+  * merges at other inputs: parity.check_merged, the attention-output rule per merged part
+    plus the coarse-tail terms that do not cancel and the merge-weight error.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import parity
+import synth
+from gpu_common import bsa, f64, say, to_dev  # noqa: F401
+from oracle import oracle as O
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_inf_pattern(got, ref, what):
+    g, r = np.isneginf(got), np.isneginf(ref)
+    assert np.array_equal(g, r), f"{what}: -inf pattern differs on {int((g != r).sum())} rows"
+
+
+def _drift(x, name):
+    return synth.drifted(x, name, 1)
+
+
+def _merge_weights(o_s, l_s, l_t, o_t):
+    """Oracle weight w of the sparse part in the log-mass merge and max_d |O_s - o_T| per row."""
+    with np.errstate(invalid="ignore", over="ignore"):
+        w = np.where(np.isneginf(l_t), 1.0, 1.0 / (1.0 + np.exp(l_t - l_s)))
+    spread = np.where(np.isneginf(l_t)[..., None], 0.0, np.abs(o_s - o_t)).max(axis=-1)
+    return w, spread
+
+
+TAIL = {
+    "tiny": dict(),
+    "ragged_d128_b64_bnhd": dict(batch=2, heads=3, head_dim=128, seq=1000, layout="bnhd",
+                                 top_p=[0.5, 0.9, 0.99]),
+    "b128_short_last_block": dict(heads=2, head_dim=128, block=128, seq=128 * 5 + 20),
+    "d64_b128": dict(heads=2, head_dim=64, block=128, seq=2000),
+    "one_token_last_block": dict(heads=1, head_dim=64, seq=129),
+    # 131 pooled keys: three 64-key tiles in the coarse pass, the last one ragged
+    "several_pooled_tiles": dict(heads=1, head_dim=64, seq=64 * 130 + 10, top_p=0.6),
+    "single_block_no_tail": dict(heads=2, head_dim=128, seq=37),
+    "p_one_no_tail": dict(heads=2, head_dim=128, seq=700, top_p=1.0),
+}
+
+
+@pytest.mark.parametrize("case", list(TAIL))
+def test_tail_case(bsa, case):
+    kw = dict(TAIL[case])
+    seq = kw.pop("seq", None)
+    layout = kw.pop("layout", "bhnd")
+    top_p = kw.pop("top_p", None)
+    grid = synth.WORKLOADS["tiny"].grid if seq is None else (1, 1, seq)
+    cfg = synth.workload("tiny", grid=grid, **kw)
+    q, k, v = synth.make_qkv(cfg)
+    q2, k2, v2 = _drift(q, "q"), _drift(k, "k"), _drift(v, "v")
+    N = q.shape[2]
+    M = -(-N // cfg.block)
+    p_def, _ = synth.head_params(cfg)
+    p = p_def if top_p is None else np.broadcast_to(np.asarray(top_p, float), (cfg.heads,))
+    s = cfg.head_dim ** -0.5
+    say(f"[test] tail {case}: B={cfg.batch} H={cfg.heads} D={cfg.head_dim} N={N} "
+        f"block={cfg.block} layout={layout} p={np.round(p, 3).tolist()}")
+    qd, kd, vd, q2d, k2d, v2d = (to_dev(x, layout) for x in (q, k, v, q2, k2, v2))
+    desc = bsa.make_desc(qd, cfg.block)
+    probs = bsa.recap_block_scores(desc, qd, kd, s)
+    count, idx, _, _ = bsa.recap_topp_mask(desc, probs, p.tolist())
+    c_lse, c_o = bsa.recap_tail_estimate(desc, qd, kd, vd, count, idx, s)
+    out_d, d_lse, d_o = bsa.recap_dense_attn_tail(desc, qd, kd, vd, count, idx, s)
+    out_h = bsa.recap_block_sparse_attn_tail(desc, qd, kd, vd, count, idx, s, d_lse, d_o)
+    out_c = bsa.recap_block_sparse_attn_tail(desc, qd, kd, vd, count, idx, s)
+    out_2 = bsa.recap_block_sparse_attn_tail(desc, q2d, k2d, v2d, count, idx, s, d_lse, d_o)
+    od_cap, _ = bsa.recap_dense_attn(desc, qd, kd, vd, s, count, idx, capture=True)
+    o_sp = bsa.recap_block_sparse_attn(desc, qd, kd, vd, count, idx, s)
+    torch.cuda.synchronize()
+    # the refresh's dense output comes from the same capture pass (extra writes only)
+    assert torch.equal(out_d, od_cap)
+
+    cnt, ix = count.cpu().numpy(), idx.cpu().numpy()
+    gmask = O.mask_from_lists(cnt, ix, M)
+    q64, k64, v64 = (synth.to_f64(x) for x in (q, k, v))
+    q2_64, k2_64, v2_64 = (synth.to_f64(x) for x in (q2, k2, v2))
+    cl, co = O.coarse_tail(q64, k64, v64, cfg.block, s, gmask)
+    el, eo = O.exact_tail(q64, k64, v64, cfg.block, s, gmask)
+    dl, do = O.tail_discrepancy(el, eo, cl, co)
+    ref_d = O.dense_attention(q64, k64, v64, s, block=cfg.block)
+    o_s = O.masked_attention(q64, k64, v64, cfg.block, s, gmask)
+    l_s = O.attention_lse(q64, k64, cfg.block, s, gmask)
+    lse_d = O.attention_lse(q64, k64, cfg.block, s)
+
+    # coarse tail
+    g_cl = c_lse.cpu().numpy().astype(np.float64)
+    _check_inf_pattern(g_cl, cl, "coarse lse")
+    kbar = O.block_mean_pool(k64, cfg.block)
+    tol_c = parity.coarse_lse_atol(q64, kbar, s)
+    parity.check_rows_within(g_cl, cl, tol_c, "coarse lse")
+    parity.check_out(c_o.cpu().numpy().astype(np.float64), co, "coarse output")
+
+    # discrepancy at the refresh
+    g_dl = d_lse.cpu().numpy().astype(np.float64)
+    notail = np.isneginf(cl) & np.isneginf(el)
+    assert np.all(g_dl[notail] == 0.0), "d_lse must be exactly 0 without a tail"
+    with np.errstate(invalid="ignore"):
+        share = np.exp(el - lse_d)  # exact tail share of the dense mass (0 without a tail)
+    sel = share >= 1e-6
+    assert np.all(np.isfinite(g_dl[sel])), "d_lse not finite on rows with a tail"
+    bound = tol_c + math.log1p(parity.U_BF16) + (N / 2) * parity.U_F32 / np.where(sel, share, 1)
+    parity.check_rows_within(np.where(sel, g_dl, np.nan), np.where(sel, dl, np.nan), bound,
+                             "discrepancy d_lse")
+    big = share >= 1e-2
+    if big.any():
+        parity.check_out(f64(d_o)[big], do[big], "discrepancy d_o")
+
+    # merges: at the refresh inputs the reconstruction is the dense output
+    parity.check_out(f64(out_h), ref_d, "refresh-step reconstruction vs dense")
+    lse_tol = 2 * parity.ATOL_STAT + 2 * tol_c
+    w, spread = _merge_weights(o_s, l_s, cl, co)
+    parity.check_merged(f64(out_c), O.tail_reconstruction(o_s, l_s, cl, co), w, spread, lse_tol,
+                        0, "coarse-only merge")
+    o_s2 = O.masked_attention(q2_64, k2_64, v2_64, cfg.block, s, gmask)
+    l_s2 = O.attention_lse(q2_64, k2_64, cfg.block, s, gmask)
+    cl2, co2 = O.coarse_tail(q2_64, k2_64, v2_64, cfg.block, s, gmask)
+    # the coarse tails of this step and of the refresh both enter (their errors do not cancel)
+    w2, spread2 = _merge_weights(o_s2, l_s2, cl2 + dl, co2 + do)
+    parity.check_merged(f64(out_2), O.tail_reconstruction(o_s2, l_s2, cl2, co2, dl, do), w2,
+                        spread2, lse_tol, 2, "next-step reconstruction")
+
+    if not (~gmask).any():  # no tail anywhere: the merge is the sparse output itself
+        assert np.all(np.isneginf(g_cl)) and np.all(g_dl == 0.0)
+        assert torch.count_nonzero(d_o) == 0
+        assert torch.equal(out_h, o_sp) and torch.equal(out_c, o_sp)
