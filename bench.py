@@ -12,6 +12,8 @@ Other workloads (--workload) run one sparse call per step (+ epilogue where conf
 Reported (one JSON line): computed-block TFLOP/s over the step (value), ms per step, ms per
 sparse call, sparse-attention TFLOP/s, the roofline of the dominant kernel (and of the sparse
 and mask-prediction kernels), and the CPU oracle timed on a bounded sample of the same work.
+With --tail, RECAP's tail-reconstruction calls are also timed (a "tail" object, outside the
+step and its figures).
 Inputs are resident in HBM before the timed region. Timing uses HIP events on the stream the
 library launches on (torch's current stream).
 """
@@ -131,6 +133,74 @@ def cpu_baseline(cfg, q, k, v, p, seconds):
     }
 
 
+def bench_tail(bsa, cfg, desc, dev_inputs, counts, idxs, s, avg, args, roof):
+    """RECAP's tail reconstruction timed apart from the step, on the same inputs and kept
+    lists: the refresh with the discrepancy (recap_dense_attn_tail on X_0), each drifted sparse
+    call merged with the fresh coarse tail plus that discrepancy (recap_block_sparse_attn_tail
+    on X_1..), and the coarse estimate alone (recap_tail_estimate on X_1). The roofline is the
+    estimate's: 4 D FLOPs per (query token, omitted key block) pair over its call time."""
+    import numpy as np
+    import torch
+
+    B, H, N, D, blk, M = cfg.batch, cfg.heads, cfg.seq, cfg.head_dim, cfg.block, cfg.num_blocks
+    dev = dev_inputs[0][0].device
+    d_lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    d_o = torch.empty((B, H, N, D), dtype=torch.float32, device=dev)
+    t_lse = torch.empty_like(d_lse)
+    t_out = torch.empty_like(d_o)
+    out = torch.empty_like(dev_inputs[0][0])
+    ws_m = torch.empty(bsa.recap_workspace_size(7, desc), dtype=torch.uint8, device=dev)
+    ws_e = torch.empty(bsa.recap_workspace_size(5, desc), dtype=torch.uint8, device=dev)
+
+    def run(events):
+        def timed(name, fn):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            if events is not None:
+                events.append((name, e0, e1))
+        q0, k0, v0 = dev_inputs[0]
+        timed("refresh", lambda: bsa.recap_dense_attn_tail(desc, q0, k0, v0, counts[0], idxs[0], s,
+                                                           out, d_lse, d_o, ws_m))
+        for ci in range(1, len(dev_inputs)):
+            qq, kk, vv = dev_inputs[ci]
+            timed("sparse", lambda: bsa.recap_block_sparse_attn_tail(
+                desc, qq, kk, vv, counts[ci], idxs[ci], s, d_lse, d_o, out, ws_m))
+        q1, k1, v1 = dev_inputs[1]
+        timed("estimate", lambda: bsa.recap_tail_estimate(desc, q1, k1, v1, counts[1], idxs[1],
+                                                          s, t_lse, t_out, ws_e))
+
+    log("tail reconstruction: warmup 1, timing")
+    run(None)
+    torch.cuda.synchronize()
+    events = []
+    for _ in range(max(1, args.steps // 2)):
+        run(events)
+    torch.cuda.synchronize()
+    per = {}
+    for name, e0, e1 in events:
+        per.setdefault(name, []).append(e0.elapsed_time(e1))
+    t = {k: float(np.median(v)) for k, v in per.items()}
+    # omitted (query token, key block) pairs of the estimate's kept lists
+    starts = torch.arange(M, device=dev) * blk
+    n_q = (torch.clamp(starts + blk, max=N) - starts).double()
+    omitted = ((M - counts[1].double()) * n_q).sum().item()
+    est_tflops = 4.0 * D * omitted / (t["estimate"] * 1e-3) / 1e12
+    return {
+        "ms_refresh_call_with_discrepancy": t["refresh"],
+        "ms_sparse_call_with_tail": t["sparse"],
+        "ms_tail_estimate": t["estimate"],
+        "refresh_overhead_ms": t["refresh"] - avg["refresh.attn"],
+        "sparse_overhead_ms": t["sparse"] - avg["sparse.attn"],
+        "n_timed": {k: len(v) for k, v in per.items()},
+        "roofline_estimate": roof("pool + tail_keys + pack + tail_kernel (one recap_tail_estimate "
+                                  "call; algorithmic FLOPs on omitted pairs only)", est_tflops,
+                                  traffic_key="tail"),
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -140,6 +210,10 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="time budget of the CPU-oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--tail", action="store_true",
+                    help="also time the tail-reconstruction calls (reported apart from the step; "
+                         "they launch the step's attention kernels with extra outputs, so they "
+                         "are left out of the default run and its per-kernel profile)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -334,6 +408,8 @@ def main():
         "roofline_sparse": sparse_roof,
         "roofline_mask": mask_roof,
     }
+    if cfg.refresh_then_sparse and args.tail:
+        result["tail"] = bench_tail(bsa, cfg, desc, dev_inputs, counts, idxs, s, avg, args, roof)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle on a bounded sample)")
         cb = cpu_baseline(cfg, q, k, v, p, args.cpu_seconds)

@@ -3,7 +3,7 @@
 // RECAP (paperpeel.com/paper/2610.26244) Sec. 4.1 computes the selected block interactions
 // with a block-sparse kernel and dense refreshes with a dense one; Sec. 3.2 adds the cached
 // dense refinement to the fresh sparse estimate. This file holds one kernel template for
-// four modes:
+// five modes:
 //   kSparse        walk the compacted kept-block list (two 64-row query blocks per work-group
 //                  over the union of their lists); optional fused O += c_h * R epilogue;
 //   kDense         walk every key block (128 query rows per work-group);
@@ -12,7 +12,11 @@
 //                  R = O_dense - O_sparse; a query block whose kept weights underflow against
 //                  that maximum is flagged, and its fp32 dense output goes to a workspace;
 //   kCaptureR      for flagged query blocks only: recompute the sparse output over the kept
-//                  list with its own maximum and write R from the saved dense output.
+//                  list with its own maximum and write R from the saved dense output;
+//   kDenseTail     as kDenseCapture, and also the exact attention over the keys outside the
+//                  kept set (the dense sums minus the kept sums), for RECAP's tail
+//                  reconstruction (an instantiation of its own, so the capture kernel carries
+//                  none of its code).
 //
 // Layout of the work (one work-group per query block of `block` rows, one wavefront per 32
 // query rows, 64-key tiles):
@@ -577,7 +581,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RECAP_W
   for (int dt = 0; dt < D / 32; ++dt) o[dt] = f32x16{};
   SoftmaxState sm{-INFINITY, 0.f};
 
-  constexpr bool CAP = MODE == kDenseCapture;
+  constexpr bool TAIL = MODE == kDenseTail;
+  constexpr bool CAP = MODE == kDenseCapture || TAIL;
   // sparse with 4 wavefronts and 64-row blocks: a pair of query blocks per work-group
   constexpr bool PAIRABLE = MODE == kSparse && NW == 4;
   constexpr bool BITS = CAP || PAIRABLE;
@@ -642,8 +647,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RECAP_W
     // weights), the block is left to the residual pass, which recomputes the sparse output
     // with its own maximum.
     const float ls = cross_half_sum(ka.l);
-    // the keys outside the kept set: the dense sums minus the kept ones (same running max)
-    const float ltail = cross_half_sum(sm.l - ka.l);
     const bool want_r = p.res_out != nullptr;  // the same for the whole grid
     bool flagged = false;
     if (want_r) {
@@ -660,10 +663,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RECAP_W
       const int64_t srow = (int64_t)bh * p.N + qrow;
       if (p.lse_out != nullptr) p.lse_out[srow] = (sm.m + log2f(lt)) * kLn2;
       if (p.kmass_out != nullptr) p.kmass_out[srow] = ls / lt;
-      if (p.tail_lse != nullptr)
-        p.tail_lse[srow] = ltail > 0.f ? (sm.m + log2f(ltail)) * kLn2 : -INFINITY;
     }
-    if (p.tail_o != nullptr) {
+    if (TAIL) {
+      // the keys outside the kept set: the dense sums minus the kept ones (same running max)
+      const float ltail = cross_half_sum(sm.l - ka.l);
+      if (half == 0)
+        p.tail_lse[(int64_t)bh * p.N + qrow] =
+            ltail > 0.f ? (sm.m + log2f(ltail)) * kLn2 : -INFINITY;
       const float invt = ltail > 0.f ? 1.0f / ltail : 0.f;
       float* to = p.tail_o + ((int64_t)bh * p.N + qrow) * D;
 #pragma unroll
@@ -1007,6 +1013,8 @@ static void launch_mode(const AttnParams& p, int grid, AttnMode mode, hipStream_
     if (mode == kDense) return (void)(attn_kernel<D, 4, kDense><<<grid, 256, 0, stream>>>(p));
     if (mode == kDenseCapture)
       return (void)(attn_kernel<D, 4, kDenseCapture><<<grid, 256, 0, stream>>>(p));
+    if (mode == kDenseTail)
+      return (void)(attn_kernel<D, 4, kDenseTail><<<grid, 256, 0, stream>>>(p));
   }
   if (mode == kSparse) attn_kernel<D, NW, kSparse><<<grid, NW * 64, 0, stream>>>(p);
   if (mode == kCaptureR) attn_kernel<D, NW, kCaptureR><<<grid, NW * 64, 0, stream>>>(p);
@@ -1015,7 +1023,7 @@ static void launch_mode(const AttnParams& p, int grid, AttnMode mode, hipStream_
 // Dense work-groups always cover 128 query rows (4 wavefronts sharing every K/V tile); the
 // list modes cover one query block (block / 32 wavefronts).
 hipError_t launch_attention(AttnParams p, int B, int D, AttnMode mode, hipStream_t stream) {
-  const bool dense = mode == kDense || mode == kDenseCapture;
+  const bool dense = mode == kDense || mode == kDenseCapture || mode == kDenseTail;
   const bool pair = RECAP_PAIR && mode == kSparse && p.block == 64;  // two query blocks per WG
   const int nw = (dense || pair) ? 4 : p.block / 32;
   p.mq = dense ? (p.N + 127) / 128 : pair ? (p.M + 1) / 2 : p.M;

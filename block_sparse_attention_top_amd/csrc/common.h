@@ -54,7 +54,7 @@ hipError_t launch_mean_drift(const float* qbar, const float* kbar, const float* 
 hipError_t launch_pack_vt(const bf16_t* v, Strides st, int B, int H, int N, int D, int npad,
                           bf16_t* vt, hipStream_t stream);
 
-enum AttnMode { kSparse = 0, kDense = 1, kCaptureR = 2, kDenseCapture = 3 };
+enum AttnMode { kSparse = 0, kDense = 1, kCaptureR = 2, kDenseCapture = 3, kDenseTail = 4 };
 
 struct AttnParams {
   const bf16_t* q;
@@ -74,8 +74,8 @@ struct AttnParams {
   float* lse_out;   // optional [B*H][N]: natural-log log-sum-exp of the attended scores
   float* kmass_out; // optional [B*H][N] (capture mode): kept share of the dense attention mass
   float* o32_out;   // optional [B*H][N][D] (sparse mode): fp32 output instead of bf16 `out`
-  float* tail_lse;  // optional [B*H][N] (capture mode): log-mass of the keys outside the kept set
-  float* tail_o;    // optional [B*H][N][D] (capture mode): attention output over those keys
+  float* tail_lse;  // kDenseTail: [B*H][N] log-mass of the keys outside the kept set
+  float* tail_o;    // kDenseTail: [B*H][N][D] attention output over those keys
   HeadScalars res_scale;
 };
 

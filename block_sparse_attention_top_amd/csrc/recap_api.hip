@@ -608,7 +608,7 @@ int recap_dense_attn_tail(const recap_desc* d, const void* q, const void* k, con
   p.out = (bf16_t*)out;
   p.tail_lse = t.a_lse;
   p.tail_o = t.a_o;
-  e = launch_attention(p, d->batch, d->head_dim, kDenseCapture, st);
+  e = launch_attention(p, d->batch, d->head_dim, kDenseTail, st);
   if (e == hipSuccess)
     e = coarse_tail(d, q, k, v, kept_count, kept_idx, sm_scale, t.c_lse, t.c_o, t.est, st);
   if (e == hipSuccess)

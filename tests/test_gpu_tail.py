@@ -143,3 +143,76 @@ def test_tail_case(bsa, case):
         assert np.all(np.isneginf(g_cl)) and np.all(g_dl == 0.0)
         assert torch.count_nonzero(d_o) == 0
         assert torch.equal(out_h, o_sp) and torch.equal(out_c, o_sp)
+
+
+def _rows_of(blocks, block, n):
+    return [(0, 0, i) for i in blocks], [(i * block, min(n, (i + 1) * block)) for i in blocks]
+
+
+def test_full_size_tail(bsa):
+    """Wan2.1-14B 720p layer (B=1, H=40, D=128, N=75,600, block 64): refresh with the tail
+    discrepancy, the reconstruction at the refresh inputs, and a drifted step that reuses the
+    refresh's kept lists and discrepancy; sampled heads and query blocks against the oracle."""
+    cfg = synth.WORKLOADS["wan14b_720p"]
+    heads = [0, 21]
+    say("[test] full-size tail wan14b_720p: generating inputs")
+    q, k, v = synth.make_qkv(cfg)
+    q1, k1, v1 = _drift(q, "q"), _drift(k, "k"), _drift(v, "v")
+    p, _ = synth.head_params(cfg)
+    s = cfg.head_dim ** -0.5
+    N, blk, M = cfg.seq, cfg.block, cfg.num_blocks
+    qd, kd, vd, q1d, k1d, v1d = (to_dev(x) for x in (q, k, v, q1, k1, v1))
+    desc = bsa.make_desc(qd, blk)
+    say("[gpu] scores, top-p, tail estimate, dense refresh with discrepancy, merges")
+    probs = bsa.recap_block_scores(desc, qd, kd, s)
+    count, idx, _, _ = bsa.recap_topp_mask(desc, probs, p.tolist())
+    del probs
+    c_lse, c_o = bsa.recap_tail_estimate(desc, qd, kd, vd, count, idx, s)
+    out_d, d_lse, d_o = bsa.recap_dense_attn_tail(desc, qd, kd, vd, count, idx, s)
+    out_h = bsa.recap_block_sparse_attn_tail(desc, qd, kd, vd, count, idx, s, d_lse, d_o)
+    out_1 = bsa.recap_block_sparse_attn_tail(desc, q1d, k1d, v1d, count, idx, s, d_lse, d_o)
+    torch.cuda.synchronize()
+    for h in heads:
+        blocks = sorted({0, M - 1} | set(np.random.default_rng(300 + h).choice(M, 2, False).tolist()))
+        sel, spans = _rows_of(blocks, blk, N)
+        say(f"[check] head {h} blocks {blocks}")
+        cnt, ix = count[:, h:h + 1].cpu().numpy(), idx[:, h:h + 1].cpu().numpy()
+        m_h = O.mask_from_lists(cnt, ix, M)
+        q64, k64, v64 = (synth.to_f64(x[:, h:h + 1]) for x in (q, k, v))
+        cl, co = O.coarse_tail(q64, k64, v64, blk, s, m_h, rows=sel)
+        el, eo = O.exact_tail(q64, k64, v64, blk, s, m_h, rows=sel)
+        dl, do = O.tail_discrepancy(el, eo, cl, co)
+        ref_d = O.dense_attention(q64, k64, v64, s, rows=sel, block=blk)
+        lse_d = O.attention_lse(q64, k64, blk, s, rows=sel)
+        q_rows = np.concatenate([q64[:, :, lo:hi] for lo, hi in spans], axis=2)
+        tol_c = parity.coarse_lse_atol(q_rows, O.block_mean_pool(k64, blk), s)
+        g = {name: t[:, h:h + 1].cpu().numpy().astype(np.float64)
+             for name, t in (("cl", c_lse), ("co", c_o), ("dl", d_lse), ("do", d_o))}
+        g.update({name: f64(t[:, h:h + 1]) for name, t in (("out_d", out_d), ("out_h", out_h),
+                                                             ("out_1", out_1))})
+        q1_64, k1_64, v1_64 = (synth.to_f64(x[:, h:h + 1]) for x in (q1, k1, v1))
+        o_s1 = O.masked_attention(q1_64, k1_64, v1_64, blk, s, m_h, rows=sel)
+        l_s1 = O.attention_lse(q1_64, k1_64, blk, s, m_h, rows=sel)
+        cl1, co1 = O.coarse_tail(q1_64, k1_64, v1_64, blk, s, m_h, rows=sel)
+        ref_1 = O.tail_reconstruction(o_s1, l_s1, cl1, co1, dl, do)
+        w1, spread1 = _merge_weights(o_s1, l_s1, cl1 + dl, co1 + do)
+        with np.errstate(invalid="ignore"):
+            share = np.exp(el - lse_d)
+        for lo, hi in spans:
+            r = slice(lo, hi)
+            _check_inf_pattern(g["cl"][:, :, r], cl[:, :, r], f"h{h} coarse lse")
+            parity.check_rows_within(g["cl"][:, :, r], cl[:, :, r], tol_c, f"h{h} coarse lse")
+            parity.check_out(g["co"][:, :, r], co[:, :, r], f"h{h} coarse output")
+            sh = share[:, :, r]
+            ok = sh >= 1e-6
+            bound = tol_c + math.log1p(parity.U_BF16) + (N / 2) * parity.U_F32 / np.where(ok, sh, 1)
+            parity.check_rows_within(np.where(ok, g["dl"][:, :, r], np.nan),
+                                     np.where(ok, dl[:, :, r], np.nan), bound, f"h{h} d_lse")
+            big = sh >= 1e-2
+            if big.any():
+                parity.check_out(g["do"][:, :, r][big], do[:, :, r][big], f"h{h} d_o")
+            parity.check_out(g["out_d"][:, :, r], ref_d[:, :, r], f"h{h} dense")
+            parity.check_out(g["out_h"][:, :, r], ref_d[:, :, r], f"h{h} refresh reconstruction")
+            parity.check_merged(g["out_1"][:, :, r], ref_1[:, :, r], w1[:, :, r],
+                                spread1[:, :, r], 2 * parity.ATOL_STAT + 2 * tol_c, 2,
+                                f"h{h} step-1 reconstruction")
