@@ -9,7 +9,8 @@ Parity status per function (pins live in tests/test_oracle_pins.py):
   block_partition, block_mean_pool, block_scores, softmax_rows, topp_select, kept_lists,
   mask_from_lists, masked_attention, dense_attention, residual_epilogue, dense_with_capture,
   attention_lse, kept_attention_mass, candidate_scores, topp_select_candidates, mean_drift,
-  coarse_tail, exact_tail, tail_discrepancy, merge_attention, tail_reconstruction:
+  coarse_tail, exact_tail, tail_discrepancy, merge_attention, tail_reconstruction,
+  e4m3_round, mx_scale_exponents, mx_quantize, masked_attention_mx:
   pinned (closed forms, invariants, library special cases, brute force, planted mutants).
   The conventions the pages leave open (scale of the pooled logits, no log-block-size term,
   tie order, inclusive threshold) are readings; the pins fix the oracle to those readings.
@@ -24,14 +25,18 @@ from .oracle import (  # noqa: F401
     coarse_tail,
     dense_attention,
     dense_with_capture,
+    e4m3_round,
     exact_tail,
     kept_attention_mass,
     kept_flops,
     kept_lists,
     mask_from_lists,
     masked_attention,
+    masked_attention_mx,
     mean_drift,
     merge_attention,
+    mx_quantize,
+    mx_scale_exponents,
     residual_epilogue,
     softmax_rows,
     tail_discrepancy,

@@ -125,3 +125,37 @@ def coarse_tail_row(qt, k, v, n_tokens, block, tail_blocks, sm_scale):
         for d in range(dim):
             out[d] += wi / tot * vb[j][d]
     return mx + math.log(tot), out
+
+
+def e4m3_value(code: int) -> float:
+    """Value of an 8-bit OCP E4M3 code from its bit fields (sign, exponent with bias 7, 3-bit
+    mantissa; exponent field 0 is subnormal; S.1111.111 is NaN)."""
+    s, e, m = (code >> 7) & 1, (code >> 3) & 15, code & 7
+    if e == 15 and m == 7:
+        return math.nan
+    v = (m / 8.0) * 2.0 ** -6 if e == 0 else (1.0 + m / 8.0) * 2.0 ** (e - 7)
+    return -v if s else v
+
+
+def e4m3_nearest(x: float) -> float:
+    """Nearest finite E4M3 value by exhaustive search over all 256 codes; a tie goes to the
+    code with an even mantissa (its lowest bit clear)."""
+    best, best_code, best_d = None, None, None
+    for c in range(256):
+        v = e4m3_value(c)
+        if math.isnan(v):
+            continue
+        d = abs(v - x)
+        if best is None or d < best_d or (d == best_d and (c & 1) == 0 and (best_code & 1) == 1):
+            best, best_code, best_d = v, c, d
+    return best
+
+
+def mx_quantize_group(vals, group_max_exp_offset: int = 7):
+    """MX quantisation of one block (a list of floats): E = floor(log2(max |x|)) - 7, each element
+    divided by 2^E, rounded with `e4m3_nearest`, multiplied back; an all-zero block stays zero."""
+    amax = max(abs(v) for v in vals)
+    if amax == 0.0:
+        return [0.0 for _ in vals]
+    e = max(-127, min(127, math.floor(math.log2(amax)) - group_max_exp_offset))
+    return [e4m3_nearest(v / 2.0 ** e) * 2.0 ** e for v in vals]

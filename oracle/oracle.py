@@ -430,6 +430,65 @@ def tail_reconstruction(o_s, lse_s, lse_bar, o_bar, d_lse=None, d_o=None):
     return merge_attention(o_s, lse_s, o_t, lse_t)[0]
 
 
+# ------------------------------------------------------------------ FP8 (MXFP8) products
+E4M3_MAX = 448.0  # largest finite OCP E4M3 value (1.75 * 2^8)
+
+
+def e4m3_round(y) -> np.ndarray:
+    """Round to the nearest OCP FP8 E4M3 value, ties to even (sign, 4 exponent bits with bias 7,
+    3 mantissa bits; normal values 2^-6..448 carry 4 significant bits, below 2^-6 the spacing
+    is 2^-9). Inputs must lie within +-464 (half a step above 448); the MX scaling below keeps
+    every magnitude under 256. Returns float64 values (the rounded numbers, not codes)."""
+    y = np.asarray(y, dtype=np.float64)
+    a = np.abs(y)
+    if np.any(a >= 464.0) or np.any(~np.isfinite(a)):
+        raise ValueError("value outside the E4M3 range")
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.maximum(e, -6.0)            # subnormals share the spacing of the smallest binade
+    step = np.exp2(e - 3.0)            # 3 mantissa bits
+    q = np.round(a / step) * step      # numpy rounds halves to even
+    return np.where(y < 0, -q, q)
+
+
+def mx_scale_exponents(x, axis: int = -1, group: int = 32) -> np.ndarray:
+    """Shared power-of-two exponent of each group of `group` consecutive elements along `axis`
+    (OCP microscaling: one 8-bit exponent per block of 32 elements): E = floor(log2(amax)) - 7,
+    so the largest magnitude of a block scales into [128, 256) and never reaches the E4M3 limit;
+    clamped to [-127, 127] (the E8M0 range); an all-zero block gets -127. A ragged last group
+    covers the remaining elements. Returns float64 exponents, one per group."""
+    x = np.moveaxis(np.asarray(x, dtype=np.float64), axis, -1)
+    n = x.shape[-1]
+    g = -(-n // group)
+    pad = np.zeros(x.shape[:-1] + (g * group - n,))
+    a = np.abs(np.concatenate([x, pad], axis=-1)).reshape(x.shape[:-1] + (g, group)).max(-1)
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0))) - 7.0
+    return np.where(a > 0, np.clip(e, -127.0, 127.0), -127.0)
+
+
+def mx_quantize(x, axis: int = -1, group: int = 32) -> np.ndarray:
+    """MXFP8 (E4M3) quantisation along `axis`: each element is divided by its block's scale
+    2^E (`mx_scale_exponents`), rounded to E4M3 (`e4m3_round`) and multiplied back. Returns
+    the dequantised float64 array (same shape): exactly the values FP8 products consume. Reading
+    for the FP8 variant of the attention products (the pages name FP8 quantisation with fused
+    kernels without a format): OCP MX blocks of 32 along each product's contraction dimension."""
+    x = np.asarray(x, dtype=np.float64)
+    xm = np.moveaxis(x, axis, -1)
+    n = xm.shape[-1]
+    e = mx_scale_exponents(xm, -1, group)
+    sc = np.exp2(np.repeat(e, group, axis=-1)[..., :n])
+    return np.moveaxis(e4m3_round(xm / sc) * sc, -1, axis)
+
+
+def masked_attention_mx(q, k, v, block: int, sm_scale: float, mask: np.ndarray, rows=None):
+    """The FP8 variant of block-sparse attention on its defining inputs: Q and K quantised to
+    MXFP8 along the head dimension (blocks of 32 dims per token), V along the token axis
+    (blocks of 32 tokens per channel, counted from token 0), then `masked_attention` in fp64 on
+    the dequantised tensors. The attention weights are rounded to FP8 as well inside the fused
+    kernel; that rounding depends on its running maximum and is left to the error bound."""
+    return masked_attention(mx_quantize(q, -1), mx_quantize(k, -1), mx_quantize(v, 2), block,
+                            sm_scale, mask, rows=rows)
+
+
 def block_sparsity(count: np.ndarray, m: int) -> float:
     """Fraction of skipped block pairs: 1 - mean(k*) / M."""
     return 1.0 - float(np.mean(count)) / float(m)

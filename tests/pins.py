@@ -589,6 +589,116 @@ def check_tail_empty_and_merge():
     assert np.array_equal(out, ob)
 
 
+# ----------------------------------------------------------------------------- FP8 (MX)
+def _e4m3_grid():
+    return np.array(sorted({brute.e4m3_value(c) for c in range(256)
+                            if not math.isnan(brute.e4m3_value(c))}))
+
+
+def check_e4m3_rounding_vs_brute():
+    """E4M3 rounding against an exhaustive nearest-code search over the bit layout: every
+    finite value maps to itself, every midpoint between neighbours goes to the even mantissa,
+    quarter points go to the nearer value, and random values agree."""
+    grid = _e4m3_grid()
+    assert len(grid) == 253 and grid.max() == 448.0 and grid.min() == -448.0
+    assert np.array_equal(O.e4m3_round(grid), grid)
+    mids = (grid[1:] + grid[:-1]) / 2
+    quarters = grid[:-1] + (grid[1:] - grid[:-1]) / 4
+    rng = np.random.default_rng(500)
+    rand = np.concatenate([rng.uniform(-460, 460, 300), rng.normal(0, 0.02, 300)])
+    for xs in (mids, quarters, rand):
+        got = O.e4m3_round(xs)
+        want = np.array([brute.e4m3_nearest(float(x)) for x in xs])
+        assert np.array_equal(got, want), xs[np.argmax(got != want)]
+
+
+def check_mx_scale_closed_forms():
+    """Block exponents: max magnitude 1 -> -7, 255 -> 0, 256 -> 1, 2^-3 -> -10; an all-zero
+    block -> -127; blocks of 32 along the axis with a ragged last block; every block's largest
+    scaled magnitude lies in [128, 256)."""
+    x = np.zeros((2, 70))
+    x[0, :32] = 0.5
+    x[0, 3] = -1.0
+    x[0, 32:64] = 255.0
+    x[0, 64:] = 256.0
+    x[1, 5] = 0.125
+    e = O.mx_scale_exponents(x)
+    assert e.shape == (2, 3)
+    assert np.array_equal(e, [[-7, 0, 1], [-10, -127, -127]]), e
+    y = _rand((4, 3, 96), 510, 3.0)
+    ey = O.mx_scale_exponents(y, axis=-1)
+    top = np.abs(y).reshape(4, 3, 3, 32).max(-1) / np.exp2(ey)
+    assert np.all((top >= 128) & (top < 256))
+    ez = O.mx_scale_exponents(np.moveaxis(y, -1, 0), axis=0)
+    assert np.array_equal(ez, ey)
+    # the 32 elements share one scale: next to 192 (E = 0) a value 0.001 lies below 2^-6 and
+    # lands on the subnormal spacing 2^-9 of that scale (0.001 -> 2^-9, 0.0004 -> 0)
+    b = np.full(32, 0.001)
+    b[:16] = 192.0
+    b[20] = 0.0004
+    qb = O.mx_quantize(b)
+    assert qb[0] == 192.0 and qb[16] == 2.0 ** -9 and qb[20] == 0.0
+
+
+def _on_mx_grid(shape, axis, seed):
+    """A tensor that MX quantisation along `axis` leaves unchanged: in each block of 32, E4M3
+    values with the largest magnitude in [128, 240], times a random power of two per block."""
+    rng = np.random.default_rng(seed)
+    g = _e4m3_grid()
+    x = np.moveaxis(rng.choice(g[np.abs(g) <= 240], size=shape), axis, -1).copy()
+    n = x.shape[-1]
+    for lo in range(0, n, 32):
+        x[..., lo] = rng.choice([-1.0, 1.0], size=x.shape[:-1]) * rng.choice(g[(g >= 128) & (g <= 240)], size=x.shape[:-1])
+        x[..., lo:lo + 32] *= np.exp2(rng.integers(-12, 3, size=x.shape[:-1] + (1,)))
+    return np.moveaxis(x, -1, axis)
+
+
+def check_mx_quantize_invariants():
+    """MX quantisation keeps 4 significant bits (relative error <= 2^-4 above the block's
+    subnormal edge, absolute <= 2^E * 2^-10 below it), commutes with power-of-two scaling,
+    keeps signs, maps a tensor already on the MX grid of its axis onto itself, and agrees with a
+    scalar per-block spelling on a ragged case."""
+    x = _rand((3, 5, 100), 520, 2.0)
+    qx = O.mx_quantize(x)
+    sc = np.exp2(np.repeat(O.mx_scale_exponents(x), 32, axis=-1)[..., :100])
+    normal = np.abs(x) >= sc * 2.0 ** -6
+    assert np.all(np.abs(qx - x)[normal] <= 2.0 ** -4 * np.abs(x)[normal] + 1e-300)
+    assert np.all(np.abs(qx - x)[~normal] <= sc[~normal] * 2.0 ** -10)
+    assert np.array_equal(O.mx_quantize(x * 8.0), qx * 8.0)
+    assert np.array_equal(O.mx_quantize(-x), -qx)
+    on = _on_mx_grid((2, 3, 96, 64), 2, 521)
+    assert np.array_equal(O.mx_quantize(on, 2), on)
+    assert not np.array_equal(O.mx_quantize(on, -1), on)
+    row = x[1, 2].tolist()
+    want = []
+    for lo in range(0, 100, 32):
+        want += brute.mx_quantize_group(row[lo:lo + 32])
+    assert np.array_equal(qx[1, 2], np.array(want))
+    row = x[1, 2].tolist()
+    want = []
+    for lo in range(0, 100, 32):
+        want += brute.mx_quantize_group(row[lo:lo + 32])
+    assert np.array_equal(qx[1, 2], np.array(want))
+
+
+def check_attention_mx_definition():
+    """The FP8 attention is plain masked attention on MX-quantised Q, K (blocks along the head
+    dimension) and V (blocks along the tokens): inputs already on those grids give the bf16-path
+    definition exactly, and quantising along the wrong axis does not."""
+    q, k, v, mask = _tail_case(192, 32, 64, 530)
+    s = 0.125
+    qq, kk = _on_mx_grid(q.shape, -1, 531) * 2.0 ** -7, _on_mx_grid(k.shape, -1, 532) * 2.0 ** -7
+    vv = _on_mx_grid(v.shape, 2, 533)
+    ref = O.masked_attention(qq, kk, vv, 32, s, mask)
+    got = O.masked_attention_mx(qq, kk, vv, 32, s, mask)
+    assert np.array_equal(got, ref)
+    assert np.abs(O.masked_attention(qq, kk, O.mx_quantize(vv, -1), 32, s, mask) - ref).max() > 0
+    assert np.abs(O.masked_attention(O.mx_quantize(qq, 2), kk, vv, 32, s, mask) - ref).max() > 0
+    raw = O.masked_attention(q, k, v, 32, s, mask)
+    err = np.abs(O.masked_attention_mx(q, k, v, 32, s, mask) - raw).max()
+    assert 1e-4 < err < 0.5, err  # FP8 inputs move the output, but boundedly
+
+
 ALL_CHECKS = [
     check_pool_block_constant,
     check_pool_closed_form_ragged,
@@ -620,6 +730,10 @@ ALL_CHECKS = [
     check_tail_partition_identity,
     check_tail_refresh_identity,
     check_tail_empty_and_merge,
+    check_e4m3_rounding_vs_brute,
+    check_mx_scale_closed_forms,
+    check_mx_quantize_invariants,
+    check_attention_mx_definition,
 ]
 
 

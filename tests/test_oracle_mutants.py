@@ -216,6 +216,40 @@ def _reconstruction_without_lse_shift(o_s, lse_s, lse_bar, o_bar, d_lse=None, d_
                                         None if d_lse is None else np.zeros_like(d_lse), d_o)
 
 
+def _e4m3_variant(away=False, bits=3, sub_floor=-6.0):
+    def f(y):
+        y = np.asarray(y, dtype=np.float64)
+        a = np.abs(y)
+        if np.any(a >= 464.0):
+            raise ValueError("value outside the E4M3 range")
+        e = np.maximum(np.floor(np.log2(np.where(a > 0, a, 1.0))), sub_floor)
+        step = np.exp2(e - bits)
+        q = (np.floor(a / step + 0.5) if away else np.round(a / step)) * step
+        return np.where(y < 0, -q, q)
+    return f
+
+
+def _mx_exp_offset(off):
+    def f(x, axis=-1, group=32):
+        x = np.moveaxis(np.asarray(x, dtype=np.float64), axis, -1)
+        n = x.shape[-1]
+        g = -(-n // group)
+        pad = np.zeros(x.shape[:-1] + (g * group - n,))
+        a = np.abs(np.concatenate([x, pad], axis=-1)).reshape(x.shape[:-1] + (g, group)).max(-1)
+        e = np.floor(np.log2(np.where(a > 0, a, 1.0))) - off
+        return np.where(a > 0, np.clip(e, -127.0, 127.0), -127.0)
+    return f
+
+
+def _mx_group16(x, axis=-1, group=32):
+    return _REAL["mx_quantize"](x, axis, 16)
+
+
+def _attention_mx_v_wrong_axis(q, k, v, block, sm_scale, mask, rows=None):
+    return O.masked_attention(O.mx_quantize(q, -1), O.mx_quantize(k, -1), O.mx_quantize(v, -1),
+                              block, sm_scale, mask, rows=rows)
+
+
 MUTANTS = {
     "pool divides by the full block size": ("block_mean_pool", _pool_divides_by_block),
     "pool takes the first token": ("block_mean_pool", _pool_first_token),
@@ -257,6 +291,14 @@ MUTANTS = {
     "merge weighs by lse, not e^lse": ("merge_attention", _merge_linear_weights),
     "reconstruction drops the log-mass discrepancy": ("tail_reconstruction",
                                                       _reconstruction_without_lse_shift),
+    "E4M3 ties away from zero": ("e4m3_round", _e4m3_variant(away=True)),
+    "E4M3 with two mantissa bits": ("e4m3_round", _e4m3_variant(bits=2)),
+    "E4M3 subnormal spacing one binade too low": ("e4m3_round", _e4m3_variant(sub_floor=-7.0)),
+    "MX block exponent offset 8 (overflows E4M3)": ("mx_scale_exponents", _mx_exp_offset(8)),
+    "MX block exponent offset 6": ("mx_scale_exponents", _mx_exp_offset(6)),
+    "MX blocks of 16": ("mx_quantize", _mx_group16),
+    "FP8 attention quantises V along the head dimension": ("masked_attention_mx",
+                                                           _attention_mx_v_wrong_axis),
 }
 
 
