@@ -5,8 +5,9 @@ marshals torch device tensors into its entry points. Functions carry the C names
 recap_block_scores, recap_topp_mask, recap_block_sparse_attn, recap_dense_attn, and the
 row-statistics variants recap_block_sparse_attn_stats and recap_dense_attn_stats, and the
 mask-reuse building blocks recap_block_means, recap_scores_from_means, recap_topp_mask_cand and
-recap_mean_drift, and the tail reconstruction recap_tail_estimate, recap_dense_attn_tail and
-recap_block_sparse_attn_tail.
+recap_mean_drift, the tail reconstruction recap_tail_estimate, recap_dense_attn_tail and
+recap_block_sparse_attn_tail, and the FP8 variant recap_block_sparse_attn_fp8 with its encoder
+recap_mx_quantize.
 """
 from ._lib import RecapDesc, RecapError, load  # noqa: F401
 from .ops import (  # noqa: F401
@@ -14,12 +15,14 @@ from .ops import (  # noqa: F401
     recap_block_means,
     recap_block_scores,
     recap_block_sparse_attn,
+    recap_block_sparse_attn_fp8,
     recap_block_sparse_attn_stats,
     recap_block_sparse_attn_tail,
     recap_dense_attn,
     recap_dense_attn_stats,
     recap_dense_attn_tail,
     recap_mean_drift,
+    recap_mx_quantize,
     recap_scores_from_means,
     recap_tail_estimate,
     recap_topp_mask,

@@ -15,7 +15,7 @@ STATUS_NAMES = {
     -8: "RECAP_E_LAUNCH",
 }
 OP_BLOCK_SCORES, OP_TOPP, OP_SPARSE, OP_DENSE, OP_DENSE_CAPTURE = 0, 1, 2, 3, 4
-OP_TAIL, OP_DENSE_TAIL, OP_SPARSE_TAIL = 5, 6, 7
+OP_TAIL, OP_DENSE_TAIL, OP_SPARSE_TAIL, OP_SPARSE_FP8 = 5, 6, 7, 8
 MAX_HEADS = 128
 MAX_BLOCKS = 8192
 
@@ -37,7 +37,7 @@ class RecapDesc(ctypes.Structure):
 _vp = ctypes.c_void_p
 _dp = ctypes.POINTER(RecapDesc)
 _fp = ctypes.POINTER(ctypes.c_float)
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 SIGNATURES = {
     "recap_abi_version": (ctypes.c_int, []),
@@ -67,6 +67,10 @@ SIGNATURES = {
     "recap_block_sparse_attn_tail": (ctypes.c_int, [_dp, _vp, _vp, _vp, _vp, _vp,
                                                     ctypes.c_float, _vp, _vp, _vp, _vp,
                                                     ctypes.c_size_t, _vp]),
+    "recap_block_sparse_attn_fp8": (ctypes.c_int, [_dp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float,
+                                                   _vp, _fp, _vp, _vp, _vp, ctypes.c_size_t,
+                                                   _vp]),
+    "recap_mx_quantize": (ctypes.c_int, [_dp, _vp, ctypes.c_int, _vp, _vp, _vp]),
 }
 
 _lock = threading.Lock()

@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG, "librecap.so")
-SOURCES = ["mask_kernels.hip", "attn_kernels.hip", "recap_api.hip"]
+SOURCES = ["mask_kernels.hip", "attn_kernels.hip", "attn_fp8.hip", "recap_api.hip"]
 ARCH = "gfx950"
 
 

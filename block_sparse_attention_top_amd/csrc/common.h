@@ -110,4 +110,29 @@ hipError_t launch_tail_combine(int mode, int B, int H, int N, int D, Strides st,
                                float* d_lse_out, float* d_o_out, bf16_t* out,
                                hipStream_t stream);
 
+// FP8 (MXFP8) block-sparse attention: Q codes and scales token-major, K and V as packed
+// 64-key tiles (codes then scales, 66*D bytes each).
+struct MxParams {
+  const uint8_t* q8;  // [B*H][N][D] E4M3 codes
+  const uint8_t* qs;  // [B*H][N][D/32] E8M0 scales
+  const uint8_t* kt;  // [B*H][ntile] packed K tiles
+  const uint8_t* vt;  // [B*H][ntile] packed V tiles
+  Strides st;         // out / residual strides
+  int H, N, M, block, ntile, mq;
+  float scale_log2;
+  const int32_t* count;
+  const int32_t* idx;
+  const bf16_t* res;  // optional residual (epilogue O + c_h R)
+  bf16_t* out;
+  float* lse_out;     // optional [B*H][N]
+  HeadScalars res_scale;
+};
+hipError_t launch_mx_rows(const bf16_t* x, Strides st, int B, int H, int N, int D,
+                          uint8_t* codes, uint8_t* scales, hipStream_t stream);
+hipError_t launch_mx_cols(const bf16_t* x, Strides st, int B, int H, int N, int D,
+                          uint8_t* codes, uint8_t* scales, hipStream_t stream);
+hipError_t launch_mx_kv_tiles(const bf16_t* k, const bf16_t* v, Strides st, int B, int H, int N,
+                              int D, int ntile, uint8_t* kt, uint8_t* vt, hipStream_t stream);
+hipError_t launch_attention_mx(MxParams p, int B, int D, hipStream_t stream);
+
 }  // namespace recap

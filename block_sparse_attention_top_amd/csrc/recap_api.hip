@@ -87,6 +87,24 @@ size_t tail_merge_bytes(const recap_desc* d) {
   return vt_bytes(d) + 2 * (row_bytes(d) + row_d_bytes(d)) + tail_estimate_bytes(d);
 }
 
+// FP8 sparse call: Q codes [B*H][N][D] and scales [B*H][N][D/32], packed K and V tiles
+// (66*D bytes per 64-key tile)
+inline int64_t fp8_tiles(const recap_desc* d) {
+  return (int64_t)d->batch * d->heads * ((int64_t)num_blocks(d) * d->block / 64);
+}
+size_t fp8_q_bytes(const recap_desc* d) {
+  return align_up((size_t)d->batch * d->heads * d->seq * d->head_dim);
+}
+size_t fp8_qs_bytes(const recap_desc* d) {
+  return align_up((size_t)d->batch * d->heads * d->seq * (d->head_dim / 32));
+}
+size_t fp8_tile_bytes(const recap_desc* d) {
+  return align_up((size_t)fp8_tiles(d) * 66 * d->head_dim);
+}
+size_t fp8_bytes(const recap_desc* d) {
+  return fp8_q_bytes(d) + fp8_qs_bytes(d) + 2 * fp8_tile_bytes(d);
+}
+
 size_t workspace_for(int op, const recap_desc* d) {
   switch (op) {
     case RECAP_OP_BLOCK_SCORES: return 2 * pooled_bytes(d);
@@ -97,6 +115,7 @@ size_t workspace_for(int op, const recap_desc* d) {
     case RECAP_OP_TAIL: return tail_estimate_bytes(d);
     case RECAP_OP_DENSE_TAIL:
     case RECAP_OP_SPARSE_TAIL: return tail_merge_bytes(d);
+    case RECAP_OP_SPARSE_FP8: return fp8_bytes(d);
     default: return 0;
   }
 }
@@ -172,7 +191,7 @@ int recap_workspace_size(int op, const recap_desc* d, size_t* bytes) {
   if (bytes == nullptr) return RECAP_E_NULL;
   const int s = validate_desc(d);
   if (s != RECAP_OK) return s;
-  if (op < RECAP_OP_BLOCK_SCORES || op > RECAP_OP_SPARSE_TAIL) return RECAP_E_VALUE;
+  if (op < RECAP_OP_BLOCK_SCORES || op > RECAP_OP_SPARSE_FP8) return RECAP_E_VALUE;
   *bytes = workspace_for(op, d);
   return RECAP_OK;
 }
@@ -461,7 +480,7 @@ int recap_dense_attn_stats(const recap_desc* d, const void* q, const void* k, co
 
 namespace {
 
-constexpr double kLog2e = 1.4426950408889634;
+constexpr double kLog2eD = 1.4426950408889634;
 
 // Coarse tail over each query block's omitted key blocks (log-mass c_lse [B*H][N], output c_o
 // [B*H][N][D], fp32) from the block means of k and v; tws: tail_estimate_bytes(d) of workspace.
@@ -498,7 +517,7 @@ hipError_t coarse_tail(const recap_desc* d, const void* q, const void* k, const 
   p.M = M;
   p.block = d->block;
   p.mpad = mpad;
-  p.scale_log2 = (float)((double)sm_scale * kLog2e);
+  p.scale_log2 = (float)((double)sm_scale * kLog2eD);
   const int n_last = d->seq - (M - 1) * d->block;
   p.last_bias = (float)log2((double)n_last / d->block);
   p.ln_block = (float)log((double)d->block);
@@ -558,7 +577,7 @@ void fill_attn(AttnParams& p, const recap_desc* d, const void* q, const void* k,
   p.M = num_blocks(d);
   p.block = d->block;
   p.npad = p.M * d->block;
-  p.scale_log2 = (float)((double)sm_scale * kLog2e);
+  p.scale_log2 = (float)((double)sm_scale * kLog2eD);
   p.count = count;
   p.idx = idx;
 }
@@ -654,6 +673,90 @@ int recap_block_sparse_attn_tail(const recap_desc* d, const void* q, const void*
                             t.a_o, t.c_lse, t.c_o, tail_dlse_opt, tail_dout_opt, nullptr,
                             nullptr, (bf16_t*)out, st);
   return launched(e);
+}
+
+}  // extern "C"
+
+extern "C" {
+
+int recap_mx_quantize(const recap_desc* d, const void* x, int along_tokens, uint8_t* codes,
+                      uint8_t* scales, void* stream) {
+  int s = validate_desc(d);
+  if (s != RECAP_OK) return s;
+  if (x == nullptr || codes == nullptr || scales == nullptr) return RECAP_E_NULL;
+  if (!aligned16(x) || !aligned16(codes)) return RECAP_E_ALIGN;
+  if (along_tokens != 0 && along_tokens != 1) return RECAP_E_VALUE;
+  if ((const void*)codes == x || (const void*)scales == x || (void*)codes == (void*)scales)
+    return RECAP_E_VALUE;
+  if ((s = check_device()) != RECAP_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  if (along_tokens == 0)
+    return launched(launch_mx_rows((const bf16_t*)x, strides_of(d), d->batch, d->heads, d->seq,
+                                   d->head_dim, codes, scales, st));
+  return launched(launch_mx_cols((const bf16_t*)x, strides_of(d), d->batch, d->heads, d->seq,
+                                 d->head_dim, codes, scales, st));
+}
+
+int recap_block_sparse_attn_fp8(const recap_desc* d, const void* q, const void* k, const void* v,
+                                const int32_t* kept_count, const int32_t* kept_idx,
+                                float sm_scale, const void* residual_opt,
+                                const float* res_scale_host, void* out, float* lse_out_opt,
+                                void* ws, size_t ws_bytes, void* stream) {
+  int s = validate_desc(d);
+  if (s != RECAP_OK) return s;
+  if (q == nullptr || k == nullptr || v == nullptr || kept_count == nullptr ||
+      kept_idx == nullptr || out == nullptr)
+    return RECAP_E_NULL;
+  if (residual_opt != nullptr && res_scale_host == nullptr) return RECAP_E_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
+      !aligned16(kept_count) || !aligned16(kept_idx) ||
+      (residual_opt != nullptr && !aligned16(residual_opt)) ||
+      (lse_out_opt != nullptr && !aligned16(lse_out_opt)))
+    return RECAP_E_ALIGN;
+  if (!isfinite(sm_scale) || !(sm_scale > 0.f)) return RECAP_E_VALUE;
+  if (out == q || out == k || out == v || (residual_opt != nullptr && out == residual_opt))
+    return RECAP_E_VALUE;
+  MxParams p;
+  memset(&p, 0, sizeof(p));
+  if (residual_opt != nullptr) {
+    for (int h = 0; h < d->heads; ++h) {
+      if (!isfinite(res_scale_host[h])) return RECAP_E_VALUE;
+      p.res_scale.v[h] = res_scale_host[h];
+    }
+  }
+  if ((s = check_workspace(RECAP_OP_SPARSE_FP8, d, ws, ws_bytes)) != RECAP_OK) return s;
+  if ((s = check_device()) != RECAP_OK) return s;
+
+  hipStream_t st = (hipStream_t)stream;
+  char* w = (char*)ws;
+  uint8_t* q8 = (uint8_t*)w;
+  uint8_t* qs = (uint8_t*)(w + fp8_q_bytes(d));
+  uint8_t* kt = (uint8_t*)(w + fp8_q_bytes(d) + fp8_qs_bytes(d));
+  uint8_t* vt = kt + fp8_tile_bytes(d);
+  const int ntile = num_blocks(d) * d->block / 64;
+  hipError_t e = launch_mx_rows((const bf16_t*)q, strides_of(d), d->batch, d->heads, d->seq,
+                                d->head_dim, q8, qs, st);
+  if (e == hipSuccess)
+    e = launch_mx_kv_tiles((const bf16_t*)k, (const bf16_t*)v, strides_of(d), d->batch,
+                           d->heads, d->seq, d->head_dim, ntile, kt, vt, st);
+  if (e != hipSuccess) return launched(e);
+  p.q8 = q8;
+  p.qs = qs;
+  p.kt = kt;
+  p.vt = vt;
+  p.st = strides_of(d);
+  p.H = d->heads;
+  p.N = d->seq;
+  p.M = num_blocks(d);
+  p.block = d->block;
+  p.ntile = ntile;
+  p.scale_log2 = (float)((double)sm_scale * kLog2eD);
+  p.count = kept_count;
+  p.idx = kept_idx;
+  p.res = (const bf16_t*)residual_opt;
+  p.out = (bf16_t*)out;
+  p.lse_out = lse_out_opt;
+  return launched(launch_attention_mx(p, d->batch, d->head_dim, st));
 }
 
 }  // extern "C"

@@ -360,6 +360,45 @@ def recap_block_sparse_attn_tail(desc: RecapDesc, q, k, v, kept_count, kept_idx,
     return out
 
 
+def recap_block_sparse_attn_fp8(desc: RecapDesc, q, k, v, kept_count, kept_idx,
+                                sm_scale: Optional[float] = None, residual=None, res_scale=None,
+                                out=None, workspace=None, stream=None, lse=None,
+                                want_lse: bool = False):
+    """Block-sparse attention with MXFP8 products (bf16 in and out). Returns out, or
+    (out, lse) with want_lse / lse given."""
+    _same_layout(desc, q, k, v, out, residual)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(desc.head_dim)
+    out = _like_out(q) if out is None else out
+    rs = None
+    if residual is not None:
+        if res_scale is None:
+            raise ValueError("res_scale is required with a residual")
+        rs = _host_floats(res_scale, desc.heads, "res_scale")
+    if want_lse or lse is not None:
+        lse = _row_stat(desc, lse, q.device)
+    ws, nbytes = _workspace(_lib.OP_SPARSE_FP8, desc, q.device, workspace)
+    check(_lib.load().recap_block_sparse_attn_fp8(
+        ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(kept_count), _ptr(kept_idx),
+        float(sm_scale), _ptr(residual), rs, _ptr(out), _ptr(lse), _ptr(ws), nbytes,
+        _stream(stream)), "recap_block_sparse_attn_fp8")
+    return (out, lse) if lse is not None else out
+
+
+def recap_mx_quantize(desc: RecapDesc, x, along_tokens: bool = False, stream=None):
+    """MXFP8 encoding of a bf16 [B,H,N,D] view: (codes uint8 [B,H,N,D], scales uint8:
+    [B,H,N,D/32] per token, or [B,H,ceil(N/32),D] per 32-token group with along_tokens)."""
+    _same_layout(desc, x)
+    B, H, N, D = desc.batch, desc.heads, desc.seq, desc.head_dim
+    codes = torch.empty((B, H, N, D), dtype=torch.uint8, device=x.device)
+    shp = (B, H, -(-N // 32), D) if along_tokens else (B, H, N, D // 32)
+    scales = torch.empty(shp, dtype=torch.uint8, device=x.device)
+    check(_lib.load().recap_mx_quantize(ctypes.byref(desc), _ptr(x), int(bool(along_tokens)),
+                                        _ptr(codes), _ptr(scales), _stream(stream)),
+          "recap_mx_quantize")
+    return codes, scales
+
+
 def sparse_step(desc: RecapDesc, q, k, v, top_p, sm_scale: Optional[float] = None,
                 residual=None, res_scale=None, out=None, stream=None):
     """One corrected sparse attention call: block scores -> top-p -> sparse attention

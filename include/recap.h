@@ -13,9 +13,10 @@
  *                          optional fused epilogue  O' = O + c_h * R;
  *   4. recap_dense_attn    dense refresh over all keys, optionally capturing the residual
  *                          R = O_dense - O_sparse on a given kept set.
- * Beside them: row statistics (*_stats), mask reuse across steps, and RECAP's tail
+ * Beside them: row statistics (*_stats), mask reuse across steps, RECAP's tail
  * reconstruction (*_tail: a coarse estimate of the omitted attention from block means plus a
- * discrepancy cached at the dense refresh, merged with the sparse part by log-mass).
+ * discrepancy cached at the dense refresh, merged with the sparse part by log-mass), and an
+ * FP8 variant of the sparse attention products (*_fp8, MXFP8).
  *
  * Sources (page title, section / figure):
  *   RECAP: Reciprocal Sparse Attention and Hierarchical Caching for Efficient Video Diffusion
@@ -63,7 +64,7 @@
 extern "C" {
 #endif
 
-#define RECAP_ABI_VERSION 4 /* 2: *_stats entry points; 3: mask reuse; 4: coarse tail */
+#define RECAP_ABI_VERSION 5 /* 2: *_stats; 3: mask reuse; 4: coarse tail; 5: FP8 */
 #define RECAP_MAX_HEADS 128   /* per-head host arrays are passed by value to the kernels */
 #define RECAP_MAX_BLOCKS 8192 /* M = ceil(N / block) upper bound (top-p sorts a row in LDS) */
 
@@ -99,7 +100,8 @@ enum recap_op {
   RECAP_OP_DENSE_CAPTURE = 4, /* dense refresh that also writes the residual */
   RECAP_OP_TAIL = 5,          /* recap_tail_estimate */
   RECAP_OP_DENSE_TAIL = 6,    /* recap_dense_attn_tail */
-  RECAP_OP_SPARSE_TAIL = 7    /* recap_block_sparse_attn_tail */
+  RECAP_OP_SPARSE_TAIL = 7,   /* recap_block_sparse_attn_tail */
+  RECAP_OP_SPARSE_FP8 = 8     /* recap_block_sparse_attn_fp8 */
 };
 
 /* Version of this ABI (RECAP_ABI_VERSION of the built library). */
@@ -271,6 +273,34 @@ int recap_block_sparse_attn_tail(const recap_desc* d, const void* q, const void*
                                  const int32_t* kept_idx, float sm_scale,
                                  const float* tail_dlse_opt, const float* tail_dout_opt,
                                  void* out, void* ws, size_t ws_bytes, void* stream);
+
+/* FP8 variant of the block-sparse attention products (the RECAP page at thelatestinai.com,
+ * second abstract: FP8 quantisation with fused kernels; the format is not given there). Format
+ * (OCP microscaling, MXFP8): E4M3 elements (1 sign, 4 exponent bits with bias 7, 3 mantissa
+ * bits; largest finite 448) and one E8M0 scale 2^E per block of 32 consecutive elements along
+ * a product's contraction dimension, E = floor(log2(max |x|)) - 7 clamped to [-127, 127]
+ * (-127 for an all-zero block), elements = round-to-nearest-even of x / 2^E.
+ *
+ * recap_block_sparse_attn_fp8: recap_block_sparse_attn (and recap_block_sparse_attn_stats
+ *   when lse_out_opt is given) with Q and K quantised per token in blocks of 32 head dims, V per
+ *   channel in blocks of 32 tokens counted from token 0, the attention weights per row in
+ *   blocks of 32 keys with the block's exponent chosen from its largest weight, and both
+ *   products on the FP8 matrix cores with fp32 accumulation; the row sum adds the rounded
+ *   weights. The inputs stay bf16; the library writes the FP8 copies to the workspace
+ *   (recap_workspace_size(RECAP_OP_SPARSE_FP8)) on every call. Same arguments, layouts and
+ *   errors as recap_block_sparse_attn; the result is within FP8 rounding of attention on the
+ *   quantised Q, K, V.
+ * recap_mx_quantize: the MXFP8 encoding of a bf16 tensor x (q/k/v layout) alone. along_tokens
+ *   = 0: blocks of 32 head dims per token, scales uint8 [B,H,N,D/32]; along_tokens = 1: blocks
+ *   of 32 tokens per channel, scales uint8 [B,H,ceil(N/32),D]. codes: uint8 [B,H,N,D]
+ *   contiguous (E4M3 bit patterns), 16-byte aligned; scale bytes are E + 127. */
+int recap_block_sparse_attn_fp8(const recap_desc* d, const void* q, const void* k, const void* v,
+                                const int32_t* kept_count, const int32_t* kept_idx,
+                                float sm_scale, const void* residual_opt,
+                                const float* res_scale_host, void* out, float* lse_out_opt,
+                                void* ws, size_t ws_bytes, void* stream);
+int recap_mx_quantize(const recap_desc* d, const void* x, int along_tokens, uint8_t* codes,
+                      uint8_t* scales, void* stream);
 
 #ifdef __cplusplus
 }

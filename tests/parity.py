@@ -137,3 +137,58 @@ def check_merged(got, ref, w, spread, lse_tol, extra: int, what: str):
     rel = np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30)
     assert rel <= RTOL_L2, f"{what}: rel-L2 {rel:.3e}"
     return float(err.max()), rel
+
+
+# ---- FP8 (MXFP8) products -------------------------------------------------------------------
+U_E4M3 = 2.0 ** -4  # unit roundoff of E4M3 round-to-nearest (4-bit significand)
+
+
+def fp8_weight_bounds(q, k, v, mask, block: int, sm_scale: float, out_ref, rows=None):
+    """Error bounds of attention whose weights are rounded to E4M3 (relative error <= u each,
+    unbiased, variance <= u^2 / 3), on inputs already quantised (q, k, v dequantised):
+      per element: |dO_d| <= u / (1 - u) * max_j |v_jd - o_d| over the attended keys j (the
+      output stays a convex combination of the attended values with each weight moved by a
+      factor in [1 - u, 1 + u]), plus 1e-3 of that spread for weights in E4M3's subnormal range
+      (below 2^-13 of their 32-key block's largest);
+      expected squared error: (u^2 / 3) * sum_j w_j^2 (v_jd - o_d)^2 (first order, independent
+      roundings). rows: optional (b, h, i) query blocks (default all). Returns (per-element
+      bound [B,H,N,D], zero outside rows; total expected squared error over rows)."""
+    B, H, N, D = q.shape
+    bound = np.zeros((B, H, N, D))
+    exp_sq = 0.0
+    nblk = -(-N // block)
+    if rows is None:
+        rows = [(b, h, i) for b in range(B) for h in range(H) for i in range(nblk)]
+    for b, h, i in rows:
+        lo, hi = i * block, min(N, (i + 1) * block)
+        js = np.nonzero(mask[b, h, i])[0]
+        toks = np.concatenate([np.arange(j * block, min(N, (j + 1) * block)) for j in js])
+        vv = v[b, h, toks]
+        o = out_ref[b, h, lo:hi]
+        spread = np.maximum(vv.max(0)[None, :] - o, o - vv.min(0)[None, :])
+        bound[b, h, lo:hi] = (U_E4M3 / (1 - U_E4M3) + 1e-3) * spread
+        sc = sm_scale * q[b, h, lo:hi] @ k[b, h, toks].T
+        w = np.exp(sc - sc.max(-1, keepdims=True))
+        w /= w.sum(-1, keepdims=True)
+        w2 = w * w
+        var = w2 @ (vv * vv) - 2 * o * (w2 @ vv) + o * o * w2.sum(-1, keepdims=True)
+        exp_sq += float(np.maximum(var, 0).sum()) * U_E4M3 ** 2 / 3
+    return bound, exp_sq
+
+
+def check_fp8_out(got, ref, bound, exp_sq, what: str):
+    """FP8 attention output against the oracle on the quantised inputs: every element within
+    ATOL_OUT (bf16 output rounding and fp32 sums, as for the bf16 path) plus its weight-rounding
+    bound; relative L2 error within RTOL_L2 plus three times the expected relative error of the
+    weight rounding."""
+    got = np.asarray(got, dtype=np.float64)
+    assert np.isfinite(got).all(), f"{what}: non-finite values"
+    err = np.abs(got - ref)
+    bad = err > ATOL_OUT + bound
+    assert not bad.any(), f"{what}: {int(bad.sum())} elements out of bound; worst excess " \
+                          f"{(err - ATOL_OUT - bound).max():.3e}"
+    nref = max(np.linalg.norm(ref), 1e-30)
+    rel = np.linalg.norm(got - ref) / nref
+    lim = RTOL_L2 + 3 * np.sqrt(exp_sq) / nref
+    assert rel <= lim, f"{what}: rel-L2 {rel:.3e} > {lim:.3e}"
+    return float(err.max()), rel, lim

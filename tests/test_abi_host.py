@@ -23,7 +23,7 @@ FAKE = 0x100000  # 16-byte aligned, never dereferenced
 def _declared():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(recap_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(recap_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_symbols_exported():
@@ -36,7 +36,7 @@ def test_header_symbols_exported():
 
 def test_version_and_status_strings():
     lib = _lib.load()
-    assert lib.recap_abi_version() == _lib.ABI_VERSION == 4
+    assert lib.recap_abi_version() == _lib.ABI_VERSION == 5
     for st in list(_lib.STATUS_NAMES) + [-99]:
         s = lib.recap_status_string(st)
         assert s and len(s.decode()) > 1
@@ -75,7 +75,12 @@ def test_workspace_sizes():
     rows = 40 * 75600 * 4
     for op in (_lib.OP_DENSE_TAIL, _lib.OP_SPARSE_TAIL):
         assert ws_size(op, d) == (0, n + 2 * (rows + rows * 128) + nt)
-    assert ws_size(8, d)[0] == -5
+    # FP8 call: Q codes + scales, packed K and V tiles of 66 * D bytes per 64 keys
+    q8 = 40 * 75600 * 128
+    qs = -(-40 * 75600 * 4 // 256) * 256
+    tiles = 40 * (M * 64 // 64) * 66 * 128
+    assert ws_size(_lib.OP_SPARSE_FP8, d) == (0, q8 + qs + 2 * tiles)
+    assert ws_size(9, d)[0] == -5
     assert ws_size(99, d)[0] == -5
     assert _lib.load().recap_workspace_size(0, ctypes.byref(d), None) == -1
 
@@ -235,3 +240,33 @@ def test_tail_validation():
     assert sparse(n=need_t) == -6
     assert sparse() == -7
     assert sparse(dl=_p(FAKE + 8192), do=_p(FAKE + 16384)) == -7
+
+
+@cpu_only
+def test_fp8_validation():
+    lib = _lib.load()
+    d = desc(H=2)
+    _, need = ws_size(_lib.OP_SPARSE_FP8, d)
+    sc = (ctypes.c_float * 2)(0.5, 1.0)
+
+    def fp8(res=None, rs=None, out=_p(FAKE + 4096), lse=None, n=need, s=0.125):
+        return lib.recap_block_sparse_attn_fp8(ctypes.byref(d), _p(), _p(FAKE + 1024),
+                                               _p(FAKE + 2048), _p(), _p(), s, res, rs, out, lse,
+                                               _p(), n, None)
+    assert fp8(out=None) == -1
+    assert fp8(res=_p(FAKE + 8192)) == -1
+    assert fp8(out=_p(FAKE + 1024)) == -5  # out aliases k
+    assert fp8(lse=_p(FAKE + 12290)) == -4
+    assert fp8(s=float("nan")) == -5
+    assert fp8(n=need - 1) == -6
+    assert fp8() == -7
+    assert fp8(res=_p(FAKE + 8192), rs=sc, lse=_p(FAKE + 12288)) == -7
+
+    def quant(x=_p(), mode=0, codes=_p(FAKE + 4096), scales=_p(FAKE + 8192)):
+        return lib.recap_mx_quantize(ctypes.byref(d), x, mode, codes, scales, None)
+    assert quant(codes=None) == -1
+    assert quant(x=_p(FAKE + 2)) == -4
+    assert quant(mode=2) == -5
+    assert quant(scales=_p(FAKE + 4096)) == -5
+    assert quant() == -7
+    assert quant(mode=1) == -7

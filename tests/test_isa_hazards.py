@@ -1,0 +1,229 @@
+"""Register-hazard checks of the kernels' machine code (CPU: hipcc -S for gfx950, no GPU).
+
+1. The compiler inserts the wait states that a vector read of a matrix-core (MFMA) result needs
+   only before instructions it generated itself, not before inline asm. So along every path from
+   each MFMA, the first instruction that reads its result (or the result of an MFMA issued after
+   it) must be compiler-generated. An inline-asm max over scores read straight after their
+   product saw stale registers on the device.
+2. gfx950's scaled FP8 matrix product (v_mfma_scale_f32_32x32x64_f8f6f4) reads its operand
+   registers (bytes and scales) while it runs, not only at issue, and the compiler's register
+   allocation does not model that: with the result registers overlapping an operand, or an
+   operand register rewritten before the product finished, results came out wrong on the
+   device. The FP8 kernel keeps every operand alive until a real vector instruction has read a
+   result of the product (or of one issued after it on the same unit, which finish in order).
+   Checked from each product along every control-flow path: its result registers do not overlap
+   its sources, and no instruction writes a source register before such a read.
+"""
+import os
+import re
+import subprocess
+
+import pytest
+
+from block_sparse_attention_top_amd import build as B
+
+KERNELS = ("attn_mx_kernelILi64", "attn_mx_kernelILi128")
+SOURCES = ("attn_kernels.hip", "attn_fp8.hip", "mask_kernels.hip")
+
+
+def _regs(tok):
+    tok = tok.strip().split()[0] if tok.strip() else ""
+    m = re.match(r"v\[(\d+):(\d+)\]$", tok)
+    if m:
+        return set(range(int(m.group(1)), int(m.group(2)) + 1))
+    m = re.match(r"v(\d+)$", tok)
+    return {int(m.group(1))} if m else set()
+
+
+def _parse(line):
+    s = line.split(";")[0].strip()
+    if not s or s.startswith(".") or s.endswith(":"):
+        return None
+    parts = s.split(None, 1)
+    ops = [o.strip() for o in parts[1].split(",")] if len(parts) > 1 else []
+    return parts[0], ops
+
+
+def _writes(op, ops):
+    if not ops or op.startswith(("v_cmp", "s_", "global_store", "buffer_store", "ds_write")):
+        return set()
+    if op.startswith(("v_", "ds_read", "global_load", "buffer_load")):
+        if op.startswith("global_load_lds") or op.startswith("buffer_load") and "lds" in ops[-1]:
+            return set()
+        return _regs(ops[0])
+    return set()
+
+
+def _reads(op, ops):
+    if not ops:
+        return set()
+    first = 0 if op.startswith(("global_store", "buffer_store", "ds_write", "global_load_lds")) else 1
+    return set().union(*[_regs(o) for o in ops[first:]])
+
+
+def check_listing(lines, pattern):
+    """Returns (number of scaled products in functions matching `pattern`, violation messages).
+
+    From each product every control-flow path is followed (both ways at a conditional branch,
+    across loop back edges) until a real vector instruction reads a result of the product or of
+    one issued after it; a write of one of the product's source registers met before that read,
+    on any path, is a violation."""
+    labels = {}
+    for i, line in enumerate(lines):
+        m = re.match(r"^(\.L\w+):", line)
+        if m:
+            labels[m.group(1)] = i
+    cur, total, bad = None, 0, []
+    for i, line in enumerate(lines):
+        if re.match(r"^_Z\S+:", line):
+            cur = line
+        if not cur or pattern not in cur:
+            continue
+        p = _parse(line)
+        if not p or not p[0].startswith("v_mfma_scale"):
+            continue
+        total += 1
+        op, ops = p
+        dst, srcs = _regs(ops[0]), _regs(ops[1]) | _regs(ops[2])
+        for extra in ops[4:6]:  # the per-lane scale operands are sources too
+            srcs |= _regs(extra)
+        if dst & srcs:
+            bad.append(f"result overlaps a source: {line.strip()}")
+        stack, seen = [(i + 1, frozenset(dst))], set()
+        while stack:
+            j, later = stack.pop()  # `later`: results of this product and of those issued after it
+            while j < len(lines) and j not in seen:
+                seen.add(j)
+                if re.match(r"^_Z\S+:", lines[j]):
+                    bad.append(f"function ends before a result read: {line.strip()}")
+                    break
+                q = _parse(lines[j])
+                j += 1
+                if not q:
+                    continue
+                qop, qops = q
+                if qop.startswith("v_mfma"):
+                    if _regs(qops[0]) & srcs:
+                        bad.append(f"source overwritten in flight: {line.strip()} -> {lines[j - 1].strip()}")
+                        break
+                    later = later | _regs(qops[0])
+                    continue
+                if _reads(qop, qops) & later:
+                    break  # finished: a real vector read of a product result
+                if _writes(qop, qops) & srcs:
+                    bad.append(f"source overwritten in flight: {line.strip()} -> {lines[j - 1].strip()}")
+                    break
+                if qop == "s_endpgm":
+                    break
+                if qop == "s_branch":
+                    j = labels[qops[0]]
+                elif qop.startswith("s_cbranch"):
+                    stack.append((labels[qops[0]], later))
+    return total, bad
+
+
+def asm_first_reads(lines):
+    """(function, product, reader) for every MFMA whose result is first read, on some path, by an
+    instruction inside an inline-asm block."""
+    labels = {}
+    inasm, a = [False] * len(lines), False
+    for i, line in enumerate(lines):
+        m = re.match(r"^(\.L\w+):", line)
+        if m:
+            labels[m.group(1)] = i
+        if ";;#ASMSTART" in line:
+            a = True
+        elif ";;#ASMEND" in line:
+            a = False
+        inasm[i] = a
+    cur, bad = None, []
+    for i, line in enumerate(lines):
+        if re.match(r"^_Z\S+:", line):
+            cur = line.split(":")[0]
+        p = _parse(line)
+        if not cur or not p or not p[0].startswith("v_mfma"):
+            continue
+        stack, seen = [(i + 1, frozenset(_regs(p[1][0])))], set()
+        while stack:
+            j, later = stack.pop()
+            while j < len(lines) and j not in seen:
+                seen.add(j)
+                if re.match(r"^_Z\S+:", lines[j]):
+                    break
+                q = _parse(lines[j])
+                j += 1
+                if not q:
+                    continue
+                qop, qops = q
+                if qop.startswith("v_mfma"):
+                    later = later | _regs(qops[0])
+                    continue
+                if _reads(qop, qops) & later:
+                    if inasm[j - 1]:
+                        bad.append((cur, line.strip(), lines[j - 1].strip()))
+                    break
+                if qop == "s_endpgm":
+                    break
+                if qop == "s_branch":
+                    j = labels[qops[0]]
+                elif qop.startswith("s_cbranch"):
+                    stack.append((labels[qops[0]], later))
+    return bad
+
+
+def _compile_listing(src, tmp_path):
+    try:
+        cc = B.hipcc()
+    except RuntimeError:
+        pytest.skip("hipcc not available")
+    out = tmp_path / (os.path.splitext(src)[0] + ".s")
+    cmd = [cc, *B.COMMON_FLAGS, "--cuda-device-only", "-S", os.path.join(B.CSRC, src), "-o", str(out)]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr
+    return out.read_text().splitlines()
+
+
+def test_asm_first_read_checker():
+    head = "_ZN5recap11attn_kernelILi64ELi2ELi0EEEvNS_10AttnParamsE:\n"
+    mf = "\tv_mfma_f32_32x32x16_bf16 v[50:65], v[34:37], v[66:69], 0\n"
+    asm = "\t;;#ASMSTART\n\tv_max3_f32 v144, v50, v51, v52\n\t;;#ASMEND\n"
+    bad = head + mf + "\ts_cbranch_scc1 .LBB0_2\n\tv_cndmask_b32_e32 v50, v1, v50, vcc\n.LBB0_2:\n" + asm + "\ts_endpgm\n"
+    assert len(asm_first_reads(bad.splitlines())) == 1  # the taken branch reaches the asm first
+    good = head + mf + "\ts_nop 7\n\tv_max_f32_e32 v140, v50, v34\n" + asm + "\ts_endpgm\n"
+    assert asm_first_reads(good.splitlines()) == []
+
+
+@pytest.mark.parametrize("src", SOURCES)
+def test_no_inline_asm_first_read_of_mfma_results(src, tmp_path):
+    lines = _compile_listing(src, tmp_path)
+    bad = asm_first_reads(lines)
+    assert not bad, "\n".join(f"{f}: {p} -> {r}" for f, p, r in bad[:10])
+
+
+def test_checker_flags_known_bad_listing():
+    """The checker itself: a product whose only 'read' is an empty asm before a branch, a source
+    rewritten in flight, and an overlapping result are all flagged; a real read passes."""
+    head = "_ZN5recap14attn_mx_kernelILi64EEEvNS_8MxParamsE:\n"
+    mf = "\tv_mfma_scale_f32_32x32x64_f8f6f4 v[0:15], v[34:41], v[50:57], v[0:15], v59, v65 op_sel_hi:[0,0,0]\n"
+    good = head + mf + "\ts_nop 15\n\tv_mov_b32_e32 v60, v15\n\tv_mov_b32_e32 v34, 0\n\ts_endpgm\n"
+    assert check_listing(good.splitlines(), "attn_mx") == (1, [])
+    loop = (head + ".LBB0_1:\n\tds_read_b128 v[34:37], v100\n" + mf
+            + "\t;;#ASMSTART\n\t;;#ASMEND\n\ts_cbranch_scc1 .LBB0_1\n\tv_mov_b32_e32 v60, v15\n\ts_endpgm\n")
+    assert len(check_listing(loop.splitlines(), "attn_mx")[1]) == 1
+    both = (head + mf + "\ts_cbranch_scc1 .LBB0_2\n\tv_cndmask_b32_e32 v0, v1, v0, vcc\n"
+            + ".LBB0_2:\n\tv_max3_f32 v2, v0, v1, v3\n\tv_mov_b32_e32 v34, 0\n\ts_endpgm\n")
+    assert check_listing(both.splitlines(), "attn_mx") == (1, [])
+    early = head + mf + "\tds_read_b128 v[50:53], v100\n\tv_mov_b32_e32 v60, v15\n"
+    assert len(check_listing(early.splitlines(), "attn_mx")[1]) == 1
+    scale = head + mf + "\tv_lshrrev_b32_e32 v65, 8, v100\n\tv_mov_b32_e32 v60, v15\n"
+    assert len(check_listing(scale.splitlines(), "attn_mx")[1]) == 1
+    overlap = head + mf.replace("v[34:41]", "v[8:15]") + "\tv_mov_b32_e32 v60, v15\n"
+    assert len(check_listing(overlap.splitlines(), "attn_mx")[1]) == 1
+
+
+def test_fp8_kernel_operand_hazards(tmp_path):
+    lines = _compile_listing("attn_fp8.hip", tmp_path)
+    for k in KERNELS:
+        total, bad = check_listing(lines, k)
+        assert total > 0, f"no scaled products found in {k}"
+        assert not bad, f"{k}:\n" + "\n".join(bad)
