@@ -13,7 +13,7 @@ Reported (one JSON line): computed-block TFLOP/s over the step (value), ms per s
 sparse call, sparse-attention TFLOP/s, the roofline of the dominant kernel (and of the sparse
 and mask-prediction kernels), and the CPU oracle timed on a bounded sample of the same work.
 With --tail, RECAP's tail-reconstruction calls are also timed (a "tail" object, outside the
-step and its figures).
+step and its figures); with --fp8, the MXFP8 variant of the sparse calls (an "fp8" object).
 Inputs are resident in HBM before the timed region. Timing uses HIP events on the stream the
 library launches on (torch's current stream).
 """
@@ -33,9 +33,15 @@ sys.path.insert(0, ROOT)
 
 METRIC = "block-sparse attn ms/call + computed-block TFLOP/s (% bf16 MFMA peak), 1 GPU"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0  # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
-ATTN_SRC = os.path.join(ROOT, "block_sparse_attention_top_amd", "csrc", "attn_kernels.hip")
-MASK_SRC = os.path.join(ROOT, "block_sparse_attention_top_amd", "csrc", "mask_kernels.hip")
+CSRC = os.path.join(ROOT, "block_sparse_attention_top_amd", "csrc")
+# the sources each kernel group is compiled from (the key of its counter figures)
+KERNEL_SOURCES = {
+    "attn": [os.path.join(CSRC, f) for f in ("attn_kernels.hip", "attn_device.h", "common.h")],
+    "mask": [os.path.join(CSRC, f) for f in ("mask_kernels.hip", "common.h")],
+    "fp8": [os.path.join(CSRC, f) for f in ("attn_fp8.hip", "attn_device.h", "common.h")],
+}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -43,14 +49,16 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def src_hash(path):
-    """Hash of a kernel source with comments and whitespace removed, so that counter figures
-    recorded for it stay valid across documentation-only edits."""
-    text = open(path).read()
-    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
-    text = re.sub(r"//[^\n]*", " ", text)
-    text = " ".join(text.split())
-    return hashlib.sha256(text.encode()).hexdigest()[:16]
+def src_hash(paths):
+    """Hash of kernel sources with comments and whitespace removed, so that counter figures
+    recorded for them stay valid across documentation-only edits."""
+    h = hashlib.sha256()
+    for path in paths:
+        text = open(path).read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(kernel_key):
@@ -63,8 +71,8 @@ def measured_traffic(kernel_key):
     ent = table.get(kernel_key)
     if not ent:
         return None
-    src = ATTN_SRC if ent.get("source") == "attn" else MASK_SRC
-    if ent.get("source_sha") != src_hash(src):
+    srcs = KERNEL_SOURCES.get(ent.get("source"))
+    if srcs is None or ent.get("source_sha") != src_hash(srcs):
         return None
     return ent.get("bytes_per_launch")
 
@@ -201,6 +209,55 @@ def bench_tail(bsa, cfg, desc, dev_inputs, counts, idxs, s, avg, args, roof):
     }
 
 
+def bench_fp8(bsa, cfg, desc, dev_inputs, counts, idxs, s, res, res_scale, avg, sparse_flops,
+              args, roof):
+    """The MXFP8 variant of the step's sparse calls, timed apart from the step on the same
+    inputs, kept lists and epilogue: recap_block_sparse_attn_fp8, which quantises Q and packs
+    the K / V tiles (E4M3 codes with per-32 power-of-two scales) before the attention kernel.
+    The roofline is the whole call's algorithmic FLOPs against the fp8 MFMA peak."""
+    import numpy as np
+    import torch
+
+    dev = dev_inputs[0][0].device
+    out = torch.empty_like(dev_inputs[0][0])
+    ws = torch.empty(bsa.recap_workspace_size(8, desc), dtype=torch.uint8, device=dev)
+    first = 1 if cfg.refresh_then_sparse else 0
+
+    def run(events):
+        for ci in range(first, len(dev_inputs)):
+            qq, kk, vv = dev_inputs[ci]
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            bsa.recap_block_sparse_attn_fp8(desc, qq, kk, vv, counts[ci], idxs[ci], s, res,
+                                            res_scale if res is not None else None, out,
+                                            workspace=ws)
+            e1.record()
+            if events is not None:
+                events.append((e0, e1))
+
+    log("fp8 sparse calls: warmup 1, timing")
+    run(None)
+    torch.cuda.synchronize()
+    events = []
+    for _ in range(max(1, args.steps // 2)):
+        run(events)
+    torch.cuda.synchronize()
+    ms = [e0.elapsed_time(e1) for e0, e1 in events]
+    t = float(np.median(ms))
+    tflops = float(np.mean(sparse_flops)) / (t * 1e-3) / 1e12
+    return {
+        "ms_sparse_attn_fp8": t,
+        "ms_sparse_attn_fp8_min": float(np.min(ms)),
+        "speedup_vs_bf16_attn": avg["sparse.attn"] / t,
+        "sparse_attn_fp8_tflops": tflops,
+        "n_timed": len(ms),
+        "roofline_fp8": roof("mx_rows + mx_k_tiles + mx_v_tiles + attn_mx_kernel<D=128> (one "
+                             "recap_block_sparse_attn_fp8 call; traffic: attn_mx_kernel)", tflops,
+                             peak=PEAK_FP8_TFLOPS, traffic_key="fp8"),
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -210,6 +267,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="time budget of the CPU-oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--fp8", action="store_true",
+                    help="also time the MXFP8 variant of the sparse calls (reported apart)")
     ap.add_argument("--tail", action="store_true",
                     help="also time the tail-reconstruction calls (reported apart from the step; "
                          "they launch the step's attention kernels with extra outputs, so they "
@@ -342,8 +401,9 @@ def main():
                   + B * H * M * M * 4 + B * H * M * (mean_kept + 1) * 4)  # top-p
     mask_ms = avg["sparse.scores"] + avg["sparse.topp"]
 
-    def roof(kernel, achieved, bound="mfma", traffic_key=None):
-        peak = PEAK_BF16_TFLOPS if bound == "mfma" else PEAK_HBM_GBS
+    def roof(kernel, achieved, bound="mfma", traffic_key=None, peak=None):
+        if peak is None:
+            peak = PEAK_BF16_TFLOPS if bound == "mfma" else PEAK_HBM_GBS
         return {"bound": bound, "achieved": achieved, "peak": peak,
                 "unit": "TFLOP/s" if bound == "mfma" else "GB/s", "frac": achieved / peak,
                 "traffic": measured_traffic(traffic_key) if traffic_key else None,
@@ -408,6 +468,10 @@ def main():
         "roofline_sparse": sparse_roof,
         "roofline_mask": mask_roof,
     }
+    if args.fp8:
+        res = rcap if cfg.refresh_then_sparse else r_dev
+        result["fp8"] = bench_fp8(bsa, cfg, desc, dev_inputs, counts, idxs, s, res, res_scale,
+                                  avg, sparse_flops, args, roof)
     if cfg.refresh_then_sparse and args.tail:
         result["tail"] = bench_tail(bsa, cfg, desc, dev_inputs, counts, idxs, s, avg, args, roof)
     if not args.no_cpu_baseline:
