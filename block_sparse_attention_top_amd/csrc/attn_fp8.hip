@@ -244,6 +244,10 @@ __device__ __forceinline__ void hold(const i32x8& x, float after) {
 __device__ __forceinline__ void hold(uint32_t x, float after) {  // a scale operand
   asm volatile("" ::"v"(x), "v"(after));
 }
+template <int B>
+struct IntC {  // a compile-time int as a value
+  static constexpr int value = B;
+};
 
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_mx_kernel(
@@ -309,7 +313,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const uint32_t* own = kept_bits[pair ? (wave >> 1) : 0];
   UnionSeq seq{kept_bits[0], kept_bits[pair ? 1 : 0], p.M, 0};
 
-  // per-lane DMA source offsets inside a packed tile and LDS read offsets
+  // per-lane DMA source offsets inside a packed tile
   uint32_t koff[LDK], voff[LDK];
 #pragma unroll
   for (int it = 0; it < LDK; ++it) {
@@ -320,14 +324,38 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     voff[it] = opaque((uint32_t)(vr * 64 + (((lane & 3) ^ ((vr >> 2) & 3)) << 4)));
   }
   const uint32_t soff = opaque((uint32_t)(64 * D + (wave * SL + lane) * 16));  // scale lanes
+  const uint32_t kb0 = lds_base(kbuf), vb0 = lds_base(vbuf);
+
+  // per-lane LDS read addresses in stage 0 (stage 1, keys 32..63 and channel groups are
+  // immediate offsets): K row n, chunks (4m + half) ^ ksw and (4m + 2 + half) ^ ksw; V row n,
+  // chunks 2 half ^ vsw and (2 half + 1) ^ vsw; the lane's K and V scale words
   const int ksw = (n / RPB) & (CH - 1), vsw = (n >> 2) & 3;
+  uint32_t kra[D / 64][2];
+#pragma unroll
+  for (int m = 0; m < D / 64; ++m) {
+    kra[m][0] = opaque(kb0 + (uint32_t)(n * D + (((4 * m + half) ^ ksw) << 4)));
+    kra[m][1] = opaque(kb0 + (uint32_t)(n * D + (((4 * m + 2 + half) ^ ksw) << 4)));
+  }
+  const uint32_t vra0 = opaque(vb0 + (uint32_t)(n * 64 + (((2 * half) ^ vsw) << 4)));
+  const uint32_t vra1 = opaque(vb0 + (uint32_t)(n * 64 + (((2 * half + 1) ^ vsw) << 4)));
+  constexpr int SCW = D / 32;  // scale bytes per operand row (one word at D = 128)
+  const uint32_t ksa = opaque(kb0 + (uint32_t)(64 * D + (half * 32 + n) * SCW));
+  const uint32_t vsa = opaque(vb0 + (uint32_t)(64 * D + (half * 32 + n) * SCW));
 
   f32x16 o[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) o[dt] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
+  // Row sums on the matrix cores: an all-ones A operand (E4M3 1.0, scale 2^0) times P^T gives
+  // every register of a lane its query's sum of the rounded, scaled weights of the tile.
+  // (both held in registers for the whole loop: a constant would be rematerialised into
+  // registers the compiler may rewrite while the product still reads them)
+  f32x16 lsum = {};
+  i32x8 ones;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ones[i] = (int)opaque(0x38383838u);
+  const uint32_t one_scale = opaque(127u);
+  float m_run = -INFINITY;
 
-  const uint32_t kb0 = lds_base(kbuf), vb0 = lds_base(vbuf);
   const uint8_t* khead = p.kt + (int64_t)bh * p.ntile * TS;
   const uint8_t* vhead = p.vt + (int64_t)bh * p.ntile * TS;
   auto issue = [&](TileCur t, int buf) {
@@ -346,150 +374,149 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
   };
 
+  // one tile from LDS stage B (a compile-time constant, so its offset is an immediate)
+  auto compute = [&](auto stage, TileCur cur) __attribute__((always_inline)) {
+    constexpr uint32_t SO = decltype(stage)::value * TB;
+    const int key0 = cur.j * p.block + cur.st * 64;
+    // S^T = K Q^T: s0 = keys 0..31 of the tile, s1 = keys 32..63; register r of lane half h
+    // holds key 8 (r / 4) + 4 h + r % 4 (+32 in s1)
+    const uint32_t ksc = D == 128 ? lds_read_u32(ksa + SO) : lds_read_u16(ksa + SO);
+    i32x8 ka[2][D / 64];  // K operands, all in distinct registers until the scores are read
+#pragma unroll
+    for (int m = 0; m < D / 64; ++m) {
+      ka[0][m] = join(lds_read16i(kra[m][0] + SO), lds_read16i(kra[m][1] + SO));
+      ka[1][m] = join(lds_read16i(kra[m][0] + SO + 32 * D), lds_read16i(kra[m][1] + SO + 32 * D));
+    }
+    uint32_t kss[2][D / 64], qss[D / 64];  // per-lane scale operands, held like the bytes
+#pragma unroll
+    for (int m = 0; m < D / 64; ++m) {
+      kss[0][m] = ksc >> (8 * m);
+      kss[1][m] = ksc >> (8 * (D / 64 + m));
+      qss[m] = qsc >> (8 * m);
+    }
+    f32x16 s0 = {}, s1 = {};
+#pragma unroll
+    for (int m = 0; m < D / 64; ++m) {
+      s0 = mx_mfma(ka[0][m], qf[m], s0, kss[0][m], qss[m]);
+      s1 = mx_mfma(ka[1][m], qf[m], s1, kss[1][m], qss[m]);
+    }
+    if (key0 + 64 > p.N) {  // last, partial tile
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kr = 8 * (r >> 2) + 4 * half + (r & 3);
+        if (key0 + kr >= p.N) s0[r] = -INFINITY;
+        if (key0 + 32 + kr >= p.N) s1[r] = -INFINITY;
+      }
+    }
+    // online softmax (base 2, lazy rescale by more than kLazy); the per-block maxima of the
+    // scores (keys 0..31 and 32..63) also set the weights' two MX exponents (fmaxf first: a
+    // compiler-generated read, so the products have finished before the inline-asm max3
+    // reads their results)
+    float lm0 = fmaxf(s0[0], s0[1]), lm1 = fmaxf(s1[0], s1[1]);
+#pragma unroll
+    for (int r = 2; r < 16; r += 2) {
+      lm0 = max3(lm0, s0[r], s0[r + 1]);
+      lm1 = max3(lm1, s1[r], s1[r + 1]);
+    }
+#pragma unroll
+    for (int m = 0; m < D / 64; ++m) {
+      hold(ka[0][m], lm0);
+      hold(ka[1][m], lm1);
+      hold(kss[0][m], lm0);
+      hold(kss[1][m], lm1);
+      hold(qss[m], lm0);
+      hold(qss[m], lm1);
+    }
+    const float c0 = cross_half_max(lm0), c1 = cross_half_max(lm1);
+    const float mt = fmaxf(c0, c1) * p.scale_log2;
+    if (__builtin_amdgcn_ballot_w64(mt > m_run + kLazy) != 0) {
+      const float mn = fmaxf(m_run, mt);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
+      m_run = mn;
+      lsum *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) o[dt] *= alpha;
+    }
+    // block exponents: the block's largest weight 2^(x - e) lands in [128, 256); an all-masked
+    // block (x = -inf) gets the smallest, -127
+    const float f0 = __builtin_floorf(fmaxf(c0 * p.scale_log2 - m_run, -120.f)) - 7.f;
+    const float f1 = __builtin_floorf(fmaxf(c1 * p.scale_log2 - m_run, -120.f)) - 7.f;
+    const float neg0 = -(m_run + f0), neg1 = -(m_run + f1);
+    i32x8 pb;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      float x[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        x[i] = w < 4 ? __builtin_amdgcn_exp2f(__builtin_fmaf(s0[4 * w + i], p.scale_log2, neg0))
+                     : __builtin_amdgcn_exp2f(__builtin_fmaf(s1[4 * (w - 4) + i], p.scale_log2, neg1));
+      // the first conversion keeps the upper half of its old value, which the second one
+      // overwrites: pass a dead register rather than a zero that would need a move
+      const int v = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], __float_as_int(x[0]), false);
+      pb[w] = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], v, true);
+    }
+    // O^T += V^T P^T, row sums += 1 P^T
+    const uint32_t vsc = D == 128 ? lds_read_u32(vsa + SO) : lds_read_u16(vsa + SO);
+    const uint32_t psc = (uint32_t)((int)(half == 0 ? f0 : f1) + 127);  // lane half b: block b
+    i32x8 va[D / 32];  // V operands, distinct registers until the products are read
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+      va[dt] = join(lds_read16i(vra0 + SO + 2048 * dt), lds_read16i(vra1 + SO + 2048 * dt));
+    uint32_t vss[D / 32];
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) vss[dt] = vsc >> (8 * dt);
+    lsum = mx_mfma(ones, pb, lsum, one_scale, psc);
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) o[dt] = mx_mfma(va[dt], pb, o[dt], vss[dt], psc);
+    // A real copy of a result of each product (the compiler may issue them in any order): the
+    // compiler puts the wait states of a vector read of a matrix result before it, so that
+    // product has finished; an empty asm that only names a result register gets no wait.
+    {
+      float done = lsum[15];
+      asm volatile("" : "+v"(done));
+      hold(ones, done);
+      hold(one_scale, done);
+      hold(pb, done);
+      hold(psc, done);
+    }
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+      float done = o[dt][15];
+      asm volatile("" : "+v"(done));
+      hold(va[dt], done);
+      hold(vss[dt], done);
+      hold(pb, done);
+      hold(psc, done);
+    }
+  };
+
   TileCur cur{seq.first(), 0};
   if (cur.j >= 0) {
     TileCur nxt = advance(cur, seq, p.block, p.N);
     issue(cur, 0);
     if (nxt.j >= 0) issue(nxt, 1);
-    int buf = 0;
-    while (true) {
+    // one tile from stage B; false once the last tile is done. Called with B = 0, 1 in turn.
+    auto step = [&](auto stage) __attribute__((always_inline)) -> bool {
+      constexpr int B = decltype(stage)::value;
       const bool has1 = nxt.j >= 0;
       const TileCur nxt2 = advance(nxt, seq, p.block, p.N);
       if (has1) wait_vmem<NPT>(); else wait_vmem<0>();
       lds_barrier();
-      if ((own[cur.j >> 5] >> (cur.j & 31)) & 1u) {
-        const uint32_t kt = kb0 + buf * TB, vt = vb0 + buf * TB;
-        const int key0 = cur.j * p.block + cur.st * 64;
-        // S^T = K Q^T: s0 = keys 0..31 of the tile, s1 = keys 32..63; register r of lane half h
-        // holds key 8 (r / 4) + 4 h + r % 4 (+32 in s1)
-        const uint32_t ksc = D == 128 ? lds_read_u32(kt + 64 * D + (half * 32 + n) * 4)
-                                      : lds_read_u16(kt + 64 * D + (half * 32 + n) * 2);
-        i32x8 ka[2][D / 64];  // K operands, all in distinct registers until the scores are read
-#pragma unroll
-        for (int m = 0; m < D / 64; ++m) {
-          const uint32_t c0 = (uint32_t)(((4 * m + half) ^ ksw) << 4);
-          const uint32_t c1 = (uint32_t)(((4 * m + 2 + half) ^ ksw) << 4);
-          const uint32_t r0 = kt + n * D, r1 = kt + (32 + n) * D;
-          ka[0][m] = join(lds_read16i(r0 + c0), lds_read16i(r0 + c1));
-          ka[1][m] = join(lds_read16i(r1 + c0), lds_read16i(r1 + c1));
-        }
-        uint32_t kss[2][D / 64], qss[D / 64];  // per-lane scale operands, held like the bytes
-#pragma unroll
-        for (int m = 0; m < D / 64; ++m) {
-          kss[0][m] = ksc >> (8 * m);
-          kss[1][m] = ksc >> (8 * (D / 64 + m));
-          qss[m] = qsc >> (8 * m);
-        }
-        f32x16 s0 = {}, s1 = {};
-#pragma unroll
-        for (int m = 0; m < D / 64; ++m) {
-          s0 = mx_mfma(ka[0][m], qf[m], s0, kss[0][m], qss[m]);
-          s1 = mx_mfma(ka[1][m], qf[m], s1, kss[1][m], qss[m]);
-        }
-        if (key0 + 64 > p.N) {  // last, partial tile
-          asm volatile("" ::: "memory");
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int kr = 8 * (r >> 2) + 4 * half + (r & 3);
-            if (key0 + kr >= p.N) s0[r] = -INFINITY;
-            if (key0 + 32 + kr >= p.N) s1[r] = -INFINITY;
-          }
-        }
-        // online softmax (base 2, lazy rescale by more than kLazy); the per-block maxima of
-        // the scores (keys 0..31 and 32..63) also set the weights' two MX exponents
-        // (fmaxf first: a compiler-generated read, so the products have finished before the
-        // inline-asm max3 reads their results)
-        float lm0 = fmaxf(s0[0], s0[1]), lm1 = fmaxf(s1[0], s1[1]);
-#pragma unroll
-        for (int r = 2; r < 16; r += 2) {
-          lm0 = max3(lm0, s0[r], s0[r + 1]);
-          lm1 = max3(lm1, s1[r], s1[r + 1]);
-        }
-#pragma unroll
-        for (int m = 0; m < D / 64; ++m) {
-          hold(ka[0][m], lm0);
-          hold(ka[1][m], lm1);
-          hold(kss[0][m], lm0);
-          hold(kss[1][m], lm1);
-          hold(qss[m], lm0);
-          hold(qss[m], lm1);
-        }
-        const float c0 = cross_half_max(lm0), c1 = cross_half_max(lm1);
-        const float mt = fmaxf(c0, c1) * p.scale_log2;
-        if (__builtin_amdgcn_ballot_w64(mt > m_run + kLazy) != 0) {
-          const float mn = fmaxf(m_run, mt);
-          const float alpha = __builtin_amdgcn_exp2f(m_run - mn);
-          m_run = mn;
-          l_run *= alpha;
-#pragma unroll
-          for (int dt = 0; dt < D / 32; ++dt) o[dt] *= alpha;
-        }
-        // block exponents: the block's largest weight 2^(x - e) lands in [128, 256)
-        const float x0 = c0 * p.scale_log2 - m_run, x1 = c1 * p.scale_log2 - m_run;
-        const int e0 = x0 > -128.f ? max((int)__builtin_floorf(x0) - 7, -127) : -127;
-        const int e1 = x1 > -128.f ? max((int)__builtin_floorf(x1) - 7, -127) : -127;
-        const float neg0 = -(m_run + (float)e0), neg1 = -(m_run + (float)e1);
-        i32x8 pb;
-#pragma unroll
-        for (int w = 0; w < 8; ++w) {
-          float x[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            x[i] = w < 4 ? __builtin_amdgcn_exp2f(__builtin_fmaf(s0[4 * w + i], p.scale_log2, neg0))
-                         : __builtin_amdgcn_exp2f(__builtin_fmaf(s1[4 * (w - 4) + i], p.scale_log2, neg1));
-          int v = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
-          pb[w] = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], v, true);
-        }
-        // row sum of the rounded weights the product uses
-        float ls0 = 0.f, ls1 = 0.f;
-#pragma unroll
-        for (int w = 0; w < 8; ++w) {
-          const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(pb[w], false);
-          const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(pb[w], true);
-          const float t = (lo[0] + lo[1]) + (hi[0] + hi[1]);
-          if (w < 4) ls0 += t; else ls1 += t;
-        }
-        l_run += __builtin_amdgcn_ldexpf(ls0, e0) + __builtin_amdgcn_ldexpf(ls1, e1);
-        // O^T += V^T P^T
-        const uint32_t vsc = D == 128 ? lds_read_u32(vt + 64 * D + (half * 32 + n) * 4)
-                                      : lds_read_u16(vt + 64 * D + (half * 32 + n) * 2);
-        const uint32_t psc = (uint32_t)((half == 0 ? e0 : e1) + 127);  // lane half b: block b
-        i32x8 va[D / 32];  // V operands, distinct registers until the products are read
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
-          const uint32_t r = vt + (32 * dt + n) * 64;
-          va[dt] = join(lds_read16i(r + (uint32_t)(((2 * half) ^ vsw) << 4)),
-                        lds_read16i(r + (uint32_t)(((2 * half + 1) ^ vsw) << 4)));
-        }
-        uint32_t vss[D / 32];
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) vss[dt] = vsc >> (8 * dt);
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) o[dt] = mx_mfma(va[dt], pb, o[dt], vss[dt], psc);
-        // A real copy of a result of each product (the compiler may issue them in any order): the
-        // compiler puts the wait states of a vector read of a matrix result before it, so that
-        // product has finished; an empty asm that only names a result register gets no wait.
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
-          float done = o[dt][15];
-          asm volatile("" : "+v"(done));
-          hold(va[dt], done);
-          hold(vss[dt], done);
-          hold(pb, done);
-          hold(psc, done);
-        }
-      }
-      lds_barrier();  // every wavefront is done with buffer `buf`
-      if (!has1) break;
-      if (nxt2.j >= 0) issue(nxt2, buf);
+      if ((own[cur.j >> 5] >> (cur.j & 31)) & 1u) compute(stage, cur);
+      lds_barrier();  // every wavefront is done with stage B
+      if (!has1) return false;
+      if (nxt2.j >= 0) issue(nxt2, B);
       cur = nxt;
       nxt = nxt2;
-      buf ^= 1;
+      return true;
+    };
+    while (step(IntC<0>{}) && step(IntC<1>{})) {
     }
   }
 
   // epilogue: O = O^T / l (+ c_h R), bf16 in the q layout; optional log-sum-exp
-  const float lt = cross_half_sum(l_run);
+  const float lt = lsum[0];  // the query's whole row sum, in both lane halves
   const float inv = lt > 0.f ? 1.0f / lt : 0.f;
   if (qrow >= p.N) return;
   if (p.lse_out != nullptr && half == 0)
