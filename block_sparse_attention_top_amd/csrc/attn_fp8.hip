@@ -21,9 +21,10 @@
 //                 is scaled per channel and 32-key group, its bytes stored in the slots' key
 //                 order. D/32 instructions per 64 keys.
 // The softmax is the bf16 kernel's (exp2 with the scale folded into one FMA, lazy rescale);
-// the row sum adds the FP8-rounded weights the product uses. Sparse mode only: 128 query rows
-// per work-group (two 64-row query blocks over the union of their kept lists, or one 128-row
-// block), two LDS stages of 8.25 KB K and V tiles (D = 128), DMA'd with 16-byte lanes.
+// the row sum is a fifth product per tile (all-ones A operand) over the FP8-rounded weights the
+// O^T product uses. Sparse mode only: 128 query rows per work-group (two 64-row query blocks
+// over the union of their kept lists, or one 128-row block), LDS stages of 8.25 KB K and V
+// tiles (D = 128) DMA'd with 16-byte lanes, one barrier per tile.
 #include "attn_device.h"
 
 namespace recap {
@@ -248,6 +249,22 @@ template <int B>
 struct IntC {  // a compile-time int as a value
   static constexpr int value = B;
 };
+// Wait until at most n tiles of NPT loads each are still in flight (n <= K, n uniform).
+template <int NPT, int K>
+__device__ __forceinline__ void wait_tiles(int n) {
+  if constexpr (K == 0) {
+    wait_vmem<0>();
+  } else {
+    if (n >= K) wait_vmem<K * NPT>();
+    else wait_tiles<NPT, K - 1>(n);
+  }
+}
+// LDS stages of the FP8 attention loop (2 to 4): tiles in flight ahead of the one computed
+#ifndef RECAP_MX_STAGES
+#define RECAP_MX_STAGES 2
+#endif
+constexpr int kMxStages = RECAP_MX_STAGES;
+static_assert(kMxStages >= 2 && kMxStages <= 4, "2 to 4 LDS stages");
 
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_mx_kernel(
@@ -258,8 +275,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   constexpr int LDK = D / 64;                 // code DMA instructions per wavefront per tile
   constexpr int SL = D / 32;                  // scale DMA lanes per wavefront per tile
   constexpr int NPT = 2 * (LDK + 1);          // DMA instructions per wavefront per tile
-  __shared__ __align__(256) unsigned char kbuf[2 * TB];
-  __shared__ __align__(256) unsigned char vbuf[2 * TB];
+  constexpr int NS = kMxStages;
+  __shared__ __align__(256) unsigned char kbuf[NS * TB];
+  __shared__ __align__(256) unsigned char vbuf[NS * TB];
   __shared__ uint32_t kept_bits[2][kMaxBlocks / 32];
 
   const int lane = threadIdx.x & 63;
@@ -374,6 +392,37 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
   };
 
+  // Operands of the last tile's O^T and row-sum products. They are kept alive until the next
+  // step has passed its barrier, where a compiler-generated copy of each product's result is
+  // made (see hold()): the products drain while the wavefront waits at the barrier.
+  i32x8 pend_va[D / 32], pend_pb;
+  uint32_t pend_vss[D / 32], pend_psc = 0;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) {
+    pend_va[dt] = i32x8{};
+    pend_vss[dt] = 0;
+  }
+  pend_pb = i32x8{};
+  auto retire = [&]() __attribute__((always_inline)) {
+    {
+      float done = lsum[15];
+      asm volatile("" : "+v"(done));
+      hold(ones, done);
+      hold(one_scale, done);
+      hold(pend_pb, done);
+      hold(pend_psc, done);
+    }
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+      float done = o[dt][15];
+      asm volatile("" : "+v"(done));
+      hold(pend_va[dt], done);
+      hold(pend_vss[dt], done);
+      hold(pend_pb, done);
+      hold(pend_psc, done);
+    }
+  };
+
   // one tile from LDS stage B (a compile-time constant, so its offset is an immediate)
   auto compute = [&](auto stage, TileCur cur) __attribute__((always_inline)) {
     constexpr uint32_t SO = decltype(stage)::value * TB;
@@ -469,51 +518,50 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     lsum = mx_mfma(ones, pb, lsum, one_scale, psc);
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) o[dt] = mx_mfma(va[dt], pb, o[dt], vss[dt], psc);
-    // A real copy of a result of each product (the compiler may issue them in any order): the
-    // compiler puts the wait states of a vector read of a matrix result before it, so that
-    // product has finished; an empty asm that only names a result register gets no wait.
-    {
-      float done = lsum[15];
-      asm volatile("" : "+v"(done));
-      hold(ones, done);
-      hold(one_scale, done);
-      hold(pb, done);
-      hold(psc, done);
-    }
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) {
-      float done = o[dt][15];
-      asm volatile("" : "+v"(done));
-      hold(va[dt], done);
-      hold(vss[dt], done);
-      hold(pb, done);
-      hold(psc, done);
+      pend_va[dt] = va[dt];
+      pend_vss[dt] = vss[dt];
     }
+    pend_pb = pb;
+    pend_psc = psc;
   };
 
-  TileCur cur{seq.first(), 0};
-  if (cur.j >= 0) {
-    TileCur nxt = advance(cur, seq, p.block, p.N);
-    issue(cur, 0);
-    if (nxt.j >= 0) issue(nxt, 1);
-    // one tile from stage B; false once the last tile is done. Called with B = 0, 1 in turn.
+  // NS-stage pipeline, one barrier per tile: at the step that computes tile t (stage t mod NS)
+  // the tiles up to t + NS - 2 are in flight, and tile t + NS - 1 is loaded into the stage
+  // that tile t - 1 used, which every wavefront has left once it passes this step's barrier.
+  TileCur q[NS];  // q[0]: the tile of this step; q[1 .. NS - 2]: issued after it
+  q[0] = TileCur{seq.first(), 0};
+  if (q[0].j >= 0) {
+    issue(q[0], 0);
+#pragma unroll
+    for (int i = 1; i < NS - 1; ++i) {
+      q[i] = advance(q[i - 1], seq, p.block, p.N);
+      if (q[i].j >= 0) issue(q[i], i);
+    }
+    // one tile from stage B; false once the last tile is done
     auto step = [&](auto stage) __attribute__((always_inline)) -> bool {
       constexpr int B = decltype(stage)::value;
-      const bool has1 = nxt.j >= 0;
-      const TileCur nxt2 = advance(nxt, seq, p.block, p.N);
-      if (has1) wait_vmem<NPT>(); else wait_vmem<0>();
-      lds_barrier();
-      if ((own[cur.j >> 5] >> (cur.j & 31)) & 1u) compute(stage, cur);
-      lds_barrier();  // every wavefront is done with stage B
-      if (!has1) return false;
-      if (nxt2.j >= 0) issue(nxt2, B);
-      cur = nxt;
-      nxt = nxt2;
+      int inflight = 0;
+#pragma unroll
+      for (int i = 1; i < NS - 1; ++i) inflight += q[i].j >= 0 ? 1 : 0;
+      wait_tiles<NPT, NS - 2>(inflight);  // this wavefront's loads of tile q[0] have landed
+      lds_barrier();                      // ... every wavefront's; all are done with stage B - 1
+      q[NS - 1] = advance(q[NS - 2], seq, p.block, p.N);
+      if (q[NS - 1].j >= 0) issue(q[NS - 1], (B + NS - 1) % NS);
+      retire();  // the previous tile's products have drained while this wavefront waited above
+      if ((own[q[0].j >> 5] >> (q[0].j & 31)) & 1u) compute(stage, q[0]);
+      if (q[1].j < 0) return false;
+#pragma unroll
+      for (int i = 0; i < NS - 1; ++i) q[i] = q[i + 1];
       return true;
     };
-    while (step(IntC<0>{}) && step(IntC<1>{})) {
+    while (step(IntC<0>{}) && step(IntC<1 % NS>{}) && (NS < 3 || step(IntC<2 % NS>{})) &&
+           (NS < 4 || step(IntC<3 % NS>{}))) {
     }
+    retire();
   }
+
 
   // epilogue: O = O^T / l (+ c_h R), bf16 in the q layout; optional log-sum-exp
   const float lt = lsum[0];  // the query's whole row sum, in both lane halves
