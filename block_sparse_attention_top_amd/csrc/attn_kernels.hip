@@ -680,10 +680,13 @@ __global__ __launch_bounds__(256) void tail_keys_kernel(const float* __restrict_
 
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void tail_kernel(TailParams p) {
-  constexpr int NW = 4, QROWS = 128;
-  __shared__ __align__(256) unsigned char kbuf[Tiles<D, NW>::TILE_BYTES];
-  __shared__ __align__(256) unsigned char klbuf[Tiles<D, NW>::TILE_BYTES];
-  __shared__ __align__(256) unsigned char vbuf[Tiles<D, NW>::TILE_BYTES];
+  constexpr int NW = 4, QROWS = 128, TB = Tiles<D, NW>::TILE_BYTES;
+  // K̄ hi and lo: one stage, the next tile's loads issued as soon as this tile's QK^T products
+  // have read it; V̄^T: two stages, the next tile's loads issued at the top of each step.
+  // 64 KB at D = 128, so two work-groups share a CU.
+  __shared__ __align__(256) unsigned char kbuf[TB];
+  __shared__ __align__(256) unsigned char klbuf[TB];
+  __shared__ __align__(256) unsigned char vbuf[2 * TB];
   __shared__ uint32_t kept_bits[2][kMaxBlocks / 32];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -705,8 +708,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
   // kept-block bitmaps of the query blocks of this work-group
   const int nb = QROWS / p.block;  // 2 for block 64, 1 for block 128
-  const int words = (p.M + 31) / 32;
-  for (int w = threadIdx.x; w < nb * words; w += NW * 64) kept_bits[w / words][w % words] = 0u;
+  for (int w = threadIdx.x; w < nb * kMaxBlocks / 32; w += NW * 64)
+    kept_bits[w / (kMaxBlocks / 32)][w % (kMaxBlocks / 32)] = 0u;
   __syncthreads();
   for (int lb = 0; lb < nb; ++lb) {
     const int blk = (qi * QROWS) / p.block + lb;
@@ -731,24 +734,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const bf16_t* klp = p.kb_lo + (int64_t)bh * p.mpad * D;
   const bf16_t* vtp = p.vt + (int64_t)bh * D * p.mpad;
   const int ntile = (p.M + kKeyTile - 1) / kKeyTile;
+  issue_v<D, NW>(vb0, vtp, p.mpad, 0, wave, lc);
+  issue_k<D, NW>(kb0, kp, (int64_t)D, p.M, 0, wave, lane, lc);
+  issue_k<D, NW>(kl0, klp, (int64_t)D, p.M, 0, wave, lane, lc);
   for (int t = 0; t < ntile; ++t) {
     const int key0 = t * kKeyTile;
-    issue_k<D, NW>(kb0, kp, (int64_t)D, p.M, key0, wave, lane, lc);
-    issue_k<D, NW>(kl0, klp, (int64_t)D, p.M, key0, wave, lane, lc);
-    issue_v<D, NW>(vb0, vtp, p.mpad, key0, wave, lc);
+    const uint32_t vt = vb0 + (t & 1) * TB;
+    // this wavefront's loads of tile t (V̄ issued one step ago, K̄ in the previous step's
+    // middle) have landed; the barrier makes them everyone's and frees the other V̄ stage
     wait_vmem<0>();
     lds_barrier();
+    if (t + 1 < ntile) issue_v<D, NW>(vb0 + ((t + 1) & 1) * TB, vtp, p.mpad, key0 + kKeyTile, wave, lc);
     f32x16 s0, s1;
     tile_qk<D, NW>(kb0, qf, lc, s0, s1);
     tile_qk<D, NW, true>(kl0, qf, lc, s0, s1);  // + q . (K̄ - hi)
+    lds_barrier();  // every wavefront has read K̄ of tile t
+    if (t + 1 < ntile) {
+      issue_k<D, NW>(kb0, kp, (int64_t)D, p.M, key0 + kKeyTile, wave, lane, lc);
+      issue_k<D, NW>(kl0, klp, (int64_t)D, p.M, key0 + kKeyTile, wave, lane, lc);
+    }
     // scores in log2 units; kept blocks and pooled keys past M get -inf, the last pooled key
-    // the log2 of its share of a full block
+    // the log2 of its share of a full block. Keys key0 + kr and key0 + 32 + kr are bit kr of
+    // words key0 / 32 and key0 / 32 + 1 of the kept bitmap (key0 is a multiple of 64; a word
+    // past the bitmap's end only holds keys >= M, masked anyway).
+    const uint32_t w0 = own[key0 >> 5], w1 = own[(key0 >> 5) + 1];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int kr = ((r >> 2) << 3) + half * 4 + (r & 3);
       const int j0 = key0 + kr, j1 = key0 + 32 + kr;
-      const bool m0 = j0 >= p.M || ((own[min(j0, p.M - 1) >> 5] >> (j0 & 31)) & 1u);
-      const bool m1 = j1 >= p.M || ((own[min(j1, p.M - 1) >> 5] >> (j1 & 31)) & 1u);
+      const bool m0 = j0 >= p.M || ((w0 >> kr) & 1u);
+      const bool m1 = j1 >= p.M || ((w1 >> kr) & 1u);
       const float x0 = s0[r] * p.scale_log2, x1 = s1[r] * p.scale_log2;
       s0[r] = m0 ? -INFINITY : (j0 == p.M - 1 ? x0 + p.last_bias : x0);
       s1[r] = m1 ? -INFINITY : (j1 == p.M - 1 ? x1 + p.last_bias : x1);
@@ -759,8 +774,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // while every key so far is masked, m = -inf: use +inf so the weights are 0, not NaN
     bf16x8 pf[4];
     sm.l += tile_exp(s0, s1, 1.0f, sm.m == -INFINITY ? INFINITY : sm.m, pf);
-    tile_pv<D, NW>(vb0, pf, lc, o, none, false);
-    lds_barrier();  // every wave is done with the tile buffers
+    tile_pv<D, NW>(vt, pf, lc, o, none, false);
   }
   const float lt = cross_half_sum(sm.l);
   if (qrow >= p.N) return;
