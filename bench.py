@@ -13,7 +13,9 @@ Reported (one JSON line): computed-block TFLOP/s over the step (value), ms per s
 sparse call, sparse-attention TFLOP/s, the roofline of the dominant kernel (and of the sparse
 and mask-prediction kernels), and the CPU oracle timed on a bounded sample of the same work.
 With --tail, RECAP's tail-reconstruction calls are also timed (a "tail" object, outside the
-step and its figures); with --fp8, the MXFP8 variant of the sparse calls (an "fp8" object).
+step and its figures); with --fp8, the MXFP8 variant of the sparse calls (an "fp8" object);
+with --probe-peaks, the rates a plain bf16 GEMM (torch's library GEMM) and a device copy reach
+on the same box (a "probe" object), as practical ceilings next to the spec peaks.
 Inputs are resident in HBM before the timed region. Timing uses HIP events on the stream the
 library launches on (torch's current stream).
 """
@@ -136,7 +138,7 @@ def cpu_baseline(cfg, q, k, v, p, seconds):
         "sample": (f"head 0 of {cfg.name}: mask prediction for all {M} query blocks, "
                    f"sparse attention on {rows_done} query blocks"
                    + (f", dense refresh on {dense_rows} query block" if dense_rows else "")
-                   + f"; {dt:.1f} s, fp64 numpy"),
+                   + f"; {dt:.1f} s, fp64 numpy on {cpu_model()}"),
         "seconds": dt,
     }
 
@@ -258,6 +260,53 @@ def bench_fp8(bsa, cfg, desc, dev_inputs, counts, idxs, s, res, res_scale, avg, 
     }
 
 
+def probe_peaks(dev):
+    """Practical ceilings on this machine: a plain bf16 GEMM (8192^3, contiguous 2-D operands,
+    torch's library GEMM) and a 2 GiB device-to-device copy, each timed with HIP events over
+    several repetitions after a warm-up."""
+    import numpy as np
+    import torch
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        out = []
+        for _ in range(reps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            e1.synchronize()
+            out.append(e0.elapsed_time(e1))
+        return float(np.median(out))
+
+    n = 8192
+    a = torch.randn((n, n), device=dev).to(torch.bfloat16)
+    b = torch.randn((n, n), device=dev).to(torch.bfloat16)
+    c = torch.empty((n, n), device=dev, dtype=torch.bfloat16)
+    ms_gemm = timed(lambda: torch.matmul(a, b, out=c), 20)
+    nbytes = 2 << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    ms_copy = timed(lambda: dst.copy_(src), 20)
+    gemm = 2.0 * n ** 3 / (ms_gemm * 1e-3) / 1e12
+    copy = 2.0 * nbytes / (ms_copy * 1e-3) / 1e9  # read + write
+    return {"gemm_bf16_tflops": gemm, "gemm_frac_bf16_peak": gemm / PEAK_BF16_TFLOPS,
+            "gemm_shape": [n, n, n], "copy_gbs": copy, "copy_frac_hbm_peak": copy / PEAK_HBM_GBS,
+            "copy_bytes": nbytes}
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown CPU"
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -267,6 +316,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="time budget of the CPU-oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--probe-peaks", action="store_true",
+                    help="also time a plain bf16 GEMM and a device copy (practical ceilings)")
     ap.add_argument("--fp8", action="store_true",
                     help="also time the MXFP8 variant of the sparse calls (reported apart)")
     ap.add_argument("--tail", action="store_true",
@@ -468,6 +519,9 @@ def main():
         "roofline_sparse": sparse_roof,
         "roofline_mask": mask_roof,
     }
+    if args.probe_peaks:
+        log("probe: bf16 GEMM and device copy")
+        result["probe"] = probe_peaks(dev)
     if args.fp8:
         res = rcap if cfg.refresh_then_sparse else r_dev
         result["fp8"] = bench_fp8(bsa, cfg, desc, dev_inputs, counts, idxs, s, res, res_scale,
