@@ -430,7 +430,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RECAP_W
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wavefront
   const int n = lane & 31, half = lane >> 5;
   // tile = (b*H + h) * mq + query tile; in the list modes a query tile is one query block
-  const int tile = xcd_remap(blockIdx.x, gridDim.x);
+  // runs of 64 tiles per XCD (all XCDs on one head) rather than one range per XCD: 3% faster
+  // dense capture and sparse calls at 720p
+  const int tile = xcd_runs<64>(blockIdx.x, gridDim.x);
   const int bh = tile / p.mq, qi = tile - bh * p.mq;
   const int b = bh / p.H, h = bh - b * p.H;
   const int64_t base = b * p.st.b + h * p.st.h;

@@ -36,6 +36,18 @@ __device__ __forceinline__ int xcd_remap(int wg, int n) {
   const int xcd = wg & 7, k = wg >> 3;
   return (xcd < r) ? xcd * (q + 1) + k : r * (q + 1) + (xcd - r) * q + k;
 }
+// The other remap: each XCD receives runs of C consecutive logical tiles in turn, so at any
+// time the eight XCDs work on neighbouring tiles of one head. That head's K/V then stays in
+// the last-level cache all XCDs share, while each XCD's L2 still serves runs of neighbouring
+// query tiles. (With one range per XCD, eight heads' K/V are in flight at once, about 310 MB
+// at 720p.) A bijection on [0, n): runs on the largest multiple of 8C, identity after.
+template <int C>
+__device__ __forceinline__ int xcd_runs(int wg, int n) {
+  const int full = (n / (8 * C)) * (8 * C);
+  if (wg >= full) return wg;
+  const int xcd = wg & 7, k = wg >> 3;
+  return (k / C) * 8 * C + xcd * C + (k % C);
+}
 
 // ---- launchers (defined in the kernel sources; all asynchronous on `stream`) ----
 hipError_t launch_pool(const bf16_t* q, const bf16_t* k, Strides st, int B, int H, int N, int D,
