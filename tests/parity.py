@@ -75,6 +75,27 @@ def check_out(got: np.ndarray, ref: np.ndarray, what: str = "output"):
     return err, rel
 
 
+def check_captured(ref_sparse: np.ndarray, residual: np.ndarray, ref_dense: np.ndarray,
+                   what: str = "sparse + captured residual"):
+    """The captured residual R = bf16(O_dense - O_sparse) is the difference of two GPU
+    attention outputs, each held to ATOL_OUT / RTOL_L2 against the oracle, rounded once more to
+    bf16. So ref_sparse + R must lie within the sum of the two outputs' bounds plus R's own
+    rounding (U_BF16 relative) of ref_dense: per element 2 ATOL_OUT + U_BF16 |R|, and in
+    relative L2 2 RTOL_L2 + U_BF16 |R| / |ref_dense|."""
+    got = ref_sparse + residual
+    assert np.isfinite(got).all(), f"{what}: non-finite values"
+    err = np.abs(got - ref_dense)
+    bound = 2 * ATOL_OUT + U_BF16 * np.abs(residual)
+    bad = err > bound
+    assert not bad.any(), f"{what}: {int(bad.sum())} elements out of bound; worst excess " \
+                          f"{(err - bound).max():.3e} (max|err| {err.max():.3e})"
+    nref = max(np.linalg.norm(ref_dense), 1e-30)
+    rel = np.linalg.norm(got - ref_dense) / nref
+    lim = 2 * RTOL_L2 + U_BF16 * np.linalg.norm(residual) / nref
+    assert rel <= lim, f"{what}: rel-L2 {rel:.3e} > {lim:.3e}"
+    return float(err.max()), rel
+
+
 def check_row_stat(got: np.ndarray, ref: np.ndarray, what: str):
     """Per-token row statistic: compared where the oracle computed it (not NaN); -inf (an
     empty kept set) must match exactly."""
