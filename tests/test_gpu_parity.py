@@ -233,6 +233,72 @@ def test_graph_capture_replays(bsa):
     assert not torch.equal(replayed, eager[2])
 
 
+def test_graph_capture_replays_tail_and_fp8(bsa):
+    """RECAP's tail calls (coarse estimate, refresh with discrepancy, sparse call with tail
+    merge) and the FP8 sparse call (with its packers, epilogue and lse) recorded in one HIP
+    graph and replayed several times with eager work in between; every replay must equal the
+    eager result bit for bit, and new inputs must flow through the recorded graph."""
+    cfg = synth.workload("tiny", heads=2, head_dim=128, grid=(1, 1, 2100))
+    s = cfg.head_dim ** -0.5
+    q, k, v = synth.make_qkv(cfg)
+    r = synth.make_residual(cfg)
+    p, c = [0.9, 0.8], [1.0, 0.5]
+    qd, kd, vd, rd = to_dev(q), to_dev(k), to_dev(v), to_dev(r)
+    q1d, k1d, v1d = (to_dev(synth.drifted(x, n, 1)) for x, n in ((q, "q"), (k, "k"), (v, "v")))
+    desc = bsa.make_desc(qd, cfg.block)
+    say(f"[case] graph replay, tail + fp8: N={cfg.seq} M={cfg.num_blocks}")
+    M = cfg.num_blocks
+    probs = torch.empty((1, 2, M, M), dtype=torch.float32, device=DEV)
+    cnt0, cnt1 = (torch.empty((1, 2, M), dtype=torch.int32, device=DEV) for _ in range(2))
+    idx0, idx1 = (torch.empty((1, 2, M, M), dtype=torch.int32, device=DEV) for _ in range(2))
+    od, ot, o8 = (torch.empty_like(qd) for _ in range(3))
+    rows = lambda *tail: torch.empty((1, 2, cfg.seq) + tail, dtype=torch.float32, device=DEV)  # noqa: E731
+    dlse, dout, tlse, tout, lse8 = rows(), rows(128), rows(), rows(128), rows()
+    ws = {op: torch.empty(max(1, bsa.recap_workspace_size(op, desc)), dtype=torch.uint8,
+                          device=DEV) for op in (0, 5, 6, 7, 8)}
+
+    def step():
+        bsa.recap_block_scores(desc, qd, kd, s, probs=probs, workspace=ws[0])
+        bsa.recap_topp_mask(desc, probs, p, kept_count=cnt0, kept_idx=idx0)
+        bsa.recap_dense_attn_tail(desc, qd, kd, vd, cnt0, idx0, s, out=od, tail_dlse=dlse,
+                                  tail_dout=dout, workspace=ws[6])
+        bsa.recap_block_scores(desc, q1d, k1d, s, probs=probs, workspace=ws[0])
+        bsa.recap_topp_mask(desc, probs, p, kept_count=cnt1, kept_idx=idx1)
+        bsa.recap_tail_estimate(desc, q1d, k1d, v1d, cnt1, idx1, s, tail_lse=tlse,
+                                tail_out=tout, workspace=ws[5])
+        bsa.recap_block_sparse_attn_tail(desc, q1d, k1d, v1d, cnt1, idx1, s, tail_dlse=dlse,
+                                         tail_dout=dout, out=ot, workspace=ws[7])
+        bsa.recap_block_sparse_attn_fp8(desc, q1d, k1d, v1d, cnt1, idx1, s, residual=rd,
+                                        res_scale=c, out=o8, workspace=ws[8], lse=lse8)
+
+    results = (od, dlse, dout, tlse, tout, ot, o8, lse8)
+    side = torch.cuda.Stream()  # default priority
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()  # eager on the side stream first (no first-use work inside the capture)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in results]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(3):
+        for t in results:
+            t.fill_(float("nan"))  # eager work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(results, eager)):
+            assert torch.equal(a, b), f"replay {rep}, result {i}"
+    q1d.copy_(to_dev(synth.drifted(q, "q", 2)))
+    g.replay()
+    torch.cuda.synchronize()
+    replayed = [t.clone() for t in (ot, o8)]
+    step()
+    torch.cuda.synchronize()
+    assert torch.equal(replayed[0], ot) and torch.equal(replayed[1], o8)
+    assert not torch.equal(replayed[0], eager[5]) and not torch.equal(replayed[1], eager[6])
+
+
 def _to_blocks(vals, count, idx, m):
     """Candidate-position values -> block space (zeros outside each row's candidates)."""
     out = np.zeros(vals.shape[:-1] + (m,))
