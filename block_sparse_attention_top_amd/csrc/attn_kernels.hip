@@ -318,7 +318,10 @@ __device__ __forceinline__ bool tile_softmax(f32x16& s0, f32x16& s1, int j, int 
   return kept;
 }
 
-// O^T += V^T P^T for one tile (and the kept-block accumulator when `kept`).
+// O^T += V^T P^T for one tile (and the kept-block accumulator when `kept`). The kept-block
+// products form their own sequence behind one wavefront-uniform branch per tile (re-reading
+// their V^T operands from LDS), so that no branch splits the main product sequence and its
+// operand reads can be issued ahead of the products, as in the dense pass.
 template <int D, int NW>
 __device__ __forceinline__ void tile_pv(uint32_t vb, const bf16x8 (&pf)[4],
                                         const LaneConsts<D, NW>& lc, f32x16 (&o)[D / 32],
@@ -329,10 +332,19 @@ __device__ __forceinline__ void tile_pv(uint32_t vb, const bf16x8 (&pf)[4],
   for (int ks = 0; ks < 4; ++ks) {
     const uint32_t a = base ^ (uint32_t)(ks << 5);
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) {
-      const bf16x8 va = lds_read16(a + dt * 4096);
-      o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[ks], o[dt], 0, 0, 0);
-      if (kept) ka.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[ks], ka.o[dt], 0, 0, 0);
+    for (int dt = 0; dt < D / 32; ++dt)
+      o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read16(a + dt * 4096), pf[ks], o[dt],
+                                                      0, 0, 0);
+  }
+  if (kept) {
+    const uint32_t kbase = opaque(vb + lc.v_rd);  // fresh reads, not values held from above
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const uint32_t a = kbase ^ (uint32_t)(ks << 5);
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+        ka.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read16(a + dt * 4096), pf[ks],
+                                                           ka.o[dt], 0, 0, 0);
     }
   }
   mfma_prio_lo();
