@@ -63,15 +63,15 @@ def src_hash(paths):
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel_key):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if the kernel source is
-    unchanged since they were taken; else None."""
+def measured_traffic(kernel_key, workload):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were taken on this
+    workload and the kernel source is unchanged since; else None."""
     try:
         table = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
     ent = table.get(kernel_key)
-    if not ent:
+    if not ent or ent.get("workload") != workload:
         return None
     srcs = KERNEL_SOURCES.get(ent.get("source"))
     if srcs is None or ent.get("source_sha") != src_hash(srcs):
@@ -457,7 +457,7 @@ def main():
             peak = PEAK_BF16_TFLOPS if bound == "mfma" else PEAK_HBM_GBS
         return {"bound": bound, "achieved": achieved, "peak": peak,
                 "unit": "TFLOP/s" if bound == "mfma" else "GB/s", "frac": achieved / peak,
-                "traffic": measured_traffic(traffic_key) if traffic_key else None,
+                "traffic": measured_traffic(traffic_key, cfg.name) if traffic_key else None,
                 "kernel": kernel}
 
     # achieved: algorithmic FLOPs over the HIP-event time of the library call, which also runs

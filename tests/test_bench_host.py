@@ -10,6 +10,7 @@ import pytest
 import torch
 
 import bench
+import synth
 from oracle import oracle as O
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -69,15 +70,16 @@ def test_measured_traffic_needs_matching_source(tmp_path, monkeypatch):
     src = tmp_path / "k.hip"
     src.write_text("kernel body\n")
     monkeypatch.setitem(bench.KERNEL_SOURCES, "t", [str(src)])
-    table = {"x": {"source": "t", "source_sha": bench.src_hash([str(src)]),
+    table = {"x": {"source": "t", "source_sha": bench.src_hash([str(src)]), "workload": "w1",
                    "bytes_per_launch": 123.0}}
     f = tmp_path / "traffic.json"
     f.write_text(json.dumps(table))
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(f))
-    assert bench.measured_traffic("x") == 123.0
-    assert bench.measured_traffic("missing") is None
+    assert bench.measured_traffic("x", "w1") == 123.0
+    assert bench.measured_traffic("x", "w2") is None  # counters taken on another workload
+    assert bench.measured_traffic("missing", "w1") is None
     src.write_text("kernel body changed\n")
-    assert bench.measured_traffic("x") is None
+    assert bench.measured_traffic("x", "w1") is None
 
 
 def test_committed_traffic_table_names_known_sources():
@@ -85,6 +87,7 @@ def test_committed_traffic_table_names_known_sources():
     for key, ent in table.items():
         if isinstance(ent, dict):
             assert ent["source"] in bench.KERNEL_SOURCES, key
+            assert ent["workload"] in synth.WORKLOADS, key
             assert ent["bytes_per_launch"] > 0, key
 
 
