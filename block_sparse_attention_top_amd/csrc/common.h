@@ -31,7 +31,7 @@ struct Strides {
 // across them) receives one contiguous range of logical tiles: neighbouring query blocks of
 // one head then share key/value lines in that XCD's L2. A bijection on [0, n) whatever the
 // dispatch order, so correctness does not depend on it.
-__device__ __forceinline__ int xcd_remap(int wg, int n) {
+__host__ __device__ __forceinline__ int xcd_remap(int wg, int n) {
   const int q = n >> 3, r = n & 7;
   const int xcd = wg & 7, k = wg >> 3;
   return (xcd < r) ? xcd * (q + 1) + k : r * (q + 1) + (xcd - r) * q + k;
@@ -42,7 +42,7 @@ __device__ __forceinline__ int xcd_remap(int wg, int n) {
 // query tiles. (With one range per XCD, eight heads' K/V are in flight at once, about 310 MB
 // at 720p.) A bijection on [0, n): runs on the largest multiple of 8C, identity after.
 template <int C>
-__device__ __forceinline__ int xcd_runs(int wg, int n) {
+__host__ __device__ __forceinline__ int xcd_runs(int wg, int n) {
   const int full = (n / (8 * C)) * (8 * C);
   if (wg >= full) return wg;
   const int xcd = wg & 7, k = wg >> 3;

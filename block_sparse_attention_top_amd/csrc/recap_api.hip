@@ -14,6 +14,7 @@ using namespace recap;
 namespace {
 
 constexpr size_t kAlign = 256;
+constexpr int64_t kMaxStrideN = (int64_t)1 << 24;  // elements
 inline size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 
 int validate_desc(const recap_desc* d) {
@@ -29,6 +30,9 @@ int validate_desc(const recap_desc* d) {
   const int64_t s[3] = {d->stride_b, d->stride_h, d->stride_n};
   for (int i = 0; i < 3; ++i)
     if (s[i] <= 0 || (s[i] % 8) != 0) return RECAP_E_STRIDE;
+  // the attention kernels address the rows of one key tile (up to 128 tokens) as 32-bit byte
+  // offsets from the tile's first row: 128 * stride_n * 2 bytes must stay below 2^32
+  if (d->stride_n >= kMaxStrideN) return RECAP_E_STRIDE;
   // no two (b, h, n) index triples may address the same row: sort the three dimensions by
   // stride and require each stride to clear the full extent of the next-smaller one
   int64_t ext[3] = {d->batch, d->heads, d->seq};

@@ -7,6 +7,8 @@ current HIP stream. There is no CPU or PyTorch fallback: a missing library raise
 from __future__ import annotations
 
 import ctypes
+import functools
+import inspect
 import math
 from typing import Optional, Sequence
 
@@ -14,6 +16,26 @@ import torch
 
 from . import _lib
 from ._lib import RecapDesc, check
+
+
+def _on_stream(fn):
+    """Run an entry point's body with its `stream` argument as torch's current stream, so that
+    every buffer the body allocates (outputs, workspace, temporaries) comes from the caching
+    allocator's pool of that stream. A block freed when the function returns can then be handed
+    out again only to work queued behind the call's kernels on the same stream; allocated on
+    another stream, it could be reused while those kernels still read or write it."""
+    sig = inspect.signature(fn)
+
+    @functools.wraps(fn)
+    def wrapper(*args, **kwargs):
+        stream = sig.bind_partial(*args, **kwargs).arguments.get("stream")
+        if stream is None:
+            return fn(*args, **kwargs)
+        with torch.cuda.stream(stream):
+            return fn(*args, **kwargs)
+
+    wrapper.on_stream = True
+    return wrapper
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -80,6 +102,7 @@ def _like_out(t: torch.Tensor) -> torch.Tensor:
     return torch.empty_strided(t.shape, t.stride(), dtype=t.dtype, device=t.device)
 
 
+@_on_stream
 def recap_block_scores(desc: RecapDesc, q, k, sm_scale: Optional[float] = None, probs=None,
                        workspace=None, stream=None) -> torch.Tensor:
     """fp32 [B,H,M,M] block-pair softmax of mean-pooled Q and K (see include/recap.h)."""
@@ -96,6 +119,7 @@ def recap_block_scores(desc: RecapDesc, q, k, sm_scale: Optional[float] = None, 
     return probs
 
 
+@_on_stream
 def recap_topp_mask(desc: RecapDesc, probs, top_p, kept_count=None, kept_idx=None,
                     want_mask: bool = False, want_mass: bool = False, stream=None):
     """Top-p selection per query block: (count [B,H,M], idx [B,H,M,M], mask|None, mass|None)."""
@@ -128,6 +152,7 @@ def _row_stat(desc: RecapDesc, given: Optional[torch.Tensor], device) -> torch.T
     return given
 
 
+@_on_stream
 def recap_block_sparse_attn(desc: RecapDesc, q, k, v, kept_count, kept_idx,
                             sm_scale: Optional[float] = None, residual=None, res_scale=None,
                             out=None, workspace=None, stream=None, lse=None,
@@ -160,6 +185,7 @@ def recap_block_sparse_attn(desc: RecapDesc, q, k, v, kept_count, kept_idx,
     return out
 
 
+@_on_stream
 def recap_dense_attn(desc: RecapDesc, q, k, v, sm_scale: Optional[float] = None,
                      kept_count=None, kept_idx=None, out=None, residual_out=None,
                      capture: bool = False, workspace=None, stream=None,
@@ -194,6 +220,7 @@ def recap_dense_attn(desc: RecapDesc, q, k, v, sm_scale: Optional[float] = None,
     return (out, residual_out) if capture else out
 
 
+@_on_stream
 def recap_block_sparse_attn_stats(desc: RecapDesc, q, k, v, kept_count, kept_idx,
                                   sm_scale: Optional[float] = None, residual=None,
                                   res_scale=None, out=None, lse=None, workspace=None,
@@ -204,6 +231,7 @@ def recap_block_sparse_attn_stats(desc: RecapDesc, q, k, v, kept_count, kept_idx
                                    res_scale, out, workspace, stream, lse=lse, want_lse=True)
 
 
+@_on_stream
 def recap_dense_attn_stats(desc: RecapDesc, q, k, v, sm_scale: Optional[float] = None,
                            kept_count=None, kept_idx=None, out=None, residual_out=None,
                            capture: bool = False, want_kept_mass: bool = False,
@@ -227,6 +255,7 @@ def _check_means(desc: RecapDesc, *ts) -> None:
             raise ValueError("block means are contiguous fp32 [B, H, M, D]")
 
 
+@_on_stream
 def recap_block_means(desc: RecapDesc, q, k, qbar=None, kbar=None, stream=None):
     """(Q̄, K̄): fp32 [B,H,M,D] block means (recap_block_means)."""
     _same_layout(desc, q, k)
@@ -240,6 +269,7 @@ def recap_block_means(desc: RecapDesc, q, k, qbar=None, kbar=None, stream=None):
     return qbar, kbar
 
 
+@_on_stream
 def recap_scores_from_means(desc: RecapDesc, qbar, kbar, sm_scale: Optional[float] = None,
                             cand_count=None, cand_idx=None, probs=None, stream=None):
     """fp32 [B,H,M,M] block-pair softmax from given means; with candidate lists, each row's
@@ -258,6 +288,7 @@ def recap_scores_from_means(desc: RecapDesc, qbar, kbar, sm_scale: Optional[floa
     return probs
 
 
+@_on_stream
 def recap_topp_mask_cand(desc: RecapDesc, probs, cand_count, cand_idx, top_p, kept_count=None,
                          kept_idx=None, want_mask: bool = False, want_mass: bool = False,
                          stream=None):
@@ -281,6 +312,7 @@ def recap_topp_mask_cand(desc: RecapDesc, probs, cand_count, cand_idx, top_p, ke
     return kept_count, kept_idx, mask, mass
 
 
+@_on_stream
 def recap_mean_drift(desc: RecapDesc, qbar, kbar, qbar_ref, kbar_ref, drift=None, stream=None):
     """fp32 [B,H,2]: relative Frobenius change of Q̄ and of K̄ against a reference step."""
     _check_means(desc, qbar, kbar, qbar_ref, kbar_ref)
@@ -292,6 +324,7 @@ def recap_mean_drift(desc: RecapDesc, qbar, kbar, qbar_ref, kbar_ref, drift=None
     return drift
 
 
+@_on_stream
 def recap_tail_estimate(desc: RecapDesc, q, k, v, kept_count, kept_idx,
                         sm_scale: Optional[float] = None, tail_lse=None, tail_out=None,
                         workspace=None, stream=None):
@@ -319,6 +352,7 @@ def _row_vec(desc: RecapDesc, given: Optional[torch.Tensor], device, what: str):
     return given
 
 
+@_on_stream
 def recap_dense_attn_tail(desc: RecapDesc, q, k, v, kept_count, kept_idx,
                           sm_scale: Optional[float] = None, out=None, tail_dlse=None,
                           tail_dout=None, workspace=None, stream=None):
@@ -338,6 +372,7 @@ def recap_dense_attn_tail(desc: RecapDesc, q, k, v, kept_count, kept_idx,
     return out, tail_dlse, tail_dout
 
 
+@_on_stream
 def recap_block_sparse_attn_tail(desc: RecapDesc, q, k, v, kept_count, kept_idx,
                                  sm_scale: Optional[float] = None, tail_dlse=None,
                                  tail_dout=None, out=None, workspace=None, stream=None):
@@ -360,6 +395,7 @@ def recap_block_sparse_attn_tail(desc: RecapDesc, q, k, v, kept_count, kept_idx,
     return out
 
 
+@_on_stream
 def recap_block_sparse_attn_fp8(desc: RecapDesc, q, k, v, kept_count, kept_idx,
                                 sm_scale: Optional[float] = None, residual=None, res_scale=None,
                                 out=None, workspace=None, stream=None, lse=None,
@@ -385,6 +421,7 @@ def recap_block_sparse_attn_fp8(desc: RecapDesc, q, k, v, kept_count, kept_idx,
     return (out, lse) if lse is not None else out
 
 
+@_on_stream
 def recap_mx_quantize(desc: RecapDesc, x, along_tokens: bool = False, stream=None):
     """MXFP8 encoding of a bf16 [B,H,N,D] view: (codes uint8 [B,H,N,D], scales uint8:
     [B,H,N,D/32] per token, or [B,H,ceil(N/32),D] per 32-token group with along_tokens)."""
@@ -399,6 +436,7 @@ def recap_mx_quantize(desc: RecapDesc, x, along_tokens: bool = False, stream=Non
     return codes, scales
 
 
+@_on_stream
 def sparse_step(desc: RecapDesc, q, k, v, top_p, sm_scale: Optional[float] = None,
                 residual=None, res_scale=None, out=None, stream=None):
     """One corrected sparse attention call: block scores -> top-p -> sparse attention

@@ -33,8 +33,10 @@
  * Conventions shared by every entry point
  *   - Tensors q, k, v, out, residual are bf16 device arrays addressed as
  *       base + b*stride_b + h*stride_h + n*stride_n + d      (element strides, d contiguous),
- *     so both [B,H,N,D] and [B,N,H,D] storage work. Bases must be 16-byte aligned and every
- *     stride a multiple of 8 elements.
+ *     so both [B,H,N,D] and [B,N,H,D] storage work. Bases must be 16-byte aligned, every
+ *     stride a positive multiple of 8 elements, stride_n below 2^24 elements (the kernels
+ *     address one key tile's rows as 32-bit byte offsets), and no two (b, h, n) rows may
+ *     overlap.
  *   - Blocks: b = desc.block; M = ceil(N / b). Block j holds tokens [j*b, min(N,(j+1)*b)); the
  *     same partition is used for queries and keys. The last block may be short: it is pooled
  *     over its valid tokens, padded keys carry no weight, padded query rows are not written.
@@ -84,7 +86,7 @@ enum recap_status {
   RECAP_OK = 0,
   RECAP_E_NULL = -1,      /* a required pointer is NULL */
   RECAP_E_SHAPE = -2,     /* B, H, N, D or block out of the supported set */
-  RECAP_E_STRIDE = -3,    /* a stride is not a positive multiple of 8 elements, or overlaps */
+  RECAP_E_STRIDE = -3,    /* a stride is not a positive multiple of 8, >= 2^24 (stride_n), or overlaps */
   RECAP_E_ALIGN = -4,     /* a base pointer is not 16-byte aligned */
   RECAP_E_VALUE = -5,     /* a scalar or host-array value is out of range (NaN, p not in [0,1]) */
   RECAP_E_WORKSPACE = -6, /* workspace missing or smaller than recap_workspace_size */

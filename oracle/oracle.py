@@ -409,8 +409,8 @@ def merge_attention(o_a, lse_a, o_b, lse_b):
     o_b = np.asarray(o_b, dtype=np.float64)
     la = np.asarray(lse_a, dtype=np.float64)
     lb = np.asarray(lse_b, dtype=np.float64)
-    lse = np.logaddexp(la, lb)
-    with np.errstate(invalid="ignore"):
+    with np.errstate(invalid="ignore"):  # rows left NaN (outside a sample) stay NaN quietly
+        lse = np.logaddexp(la, lb)
         wa = np.where(np.isneginf(la), 0.0, np.exp(la - lse))
         wb = np.where(np.isneginf(lb), 0.0, np.exp(lb - lse))
     out = wa[..., None] * o_a + wb[..., None] * o_b

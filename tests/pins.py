@@ -674,11 +674,6 @@ def check_mx_quantize_invariants():
     for lo in range(0, 100, 32):
         want += brute.mx_quantize_group(row[lo:lo + 32])
     assert np.array_equal(qx[1, 2], np.array(want))
-    row = x[1, 2].tolist()
-    want = []
-    for lo in range(0, 100, 32):
-        want += brute.mx_quantize_group(row[lo:lo + 32])
-    assert np.array_equal(qx[1, 2], np.array(want))
 
 
 def check_attention_mx_definition():
@@ -697,6 +692,28 @@ def check_attention_mx_definition():
     raw = O.masked_attention(q, k, v, 32, s, mask)
     err = np.abs(O.masked_attention_mx(q, k, v, 32, s, mask) - raw).max()
     assert 1e-4 < err < 0.5, err  # FP8 inputs move the output, but boundedly
+
+
+# ----------------------------------------------------------------------------- work counts
+def check_kept_flops_and_sparsity():
+    """Kept FLOPs are 4 D n_i n_j per kept block pair (one QK^T and one PV product per attended
+    (query, key) token pair): every block kept gives the dense count 4 D N^2 per head, one kept
+    pair pairing a full block with the short last block gives 4 D b n_last, and a random mask
+    gives 4 D times the number of attended token pairs counted token by token. Block sparsity
+    is the skipped share of block pairs: 0 with every block kept, 1 - 1/M with one per row."""
+    n, b, d = 200, 64, 16  # blocks of 64, 64, 64, 8
+    m = 4
+    full = np.ones((1, 3, m, m), dtype=bool)
+    assert O.kept_flops(full, n, b, d) == 4.0 * d * n * n * 3
+    one = np.zeros((1, 1, m, m), dtype=bool)
+    one[0, 0, 1, m - 1] = True
+    assert O.kept_flops(one, n, b, d) == 4.0 * d * 64 * 8
+    rnd = np.random.default_rng(11).random((2, 2, m, m)) < 0.4
+    tok_block = np.repeat(np.arange(m), [64, 64, 64, 8])
+    pairs = sum(int(rnd[i, h][tok_block][:, tok_block].sum()) for i in range(2) for h in range(2))
+    assert O.kept_flops(rnd, n, b, d) == 4.0 * d * pairs
+    assert O.block_sparsity(np.full((1, 2, m), m), m) == 0.0
+    assert O.block_sparsity(np.ones((1, 2, m)), m) == 1.0 - 1.0 / m
 
 
 ALL_CHECKS = [
@@ -734,6 +751,7 @@ ALL_CHECKS = [
     check_mx_scale_closed_forms,
     check_mx_quantize_invariants,
     check_attention_mx_definition,
+    check_kept_flops_and_sparsity,
 ]
 
 

@@ -96,6 +96,17 @@ def test_descriptor_validation(field, value, status):
     assert ws_size(_lib.OP_SPARSE, d)[0] == status
 
 
+def test_token_stride_limit():
+    """A token stride of 2^24 elements or more would overflow the 32-bit byte offsets of one
+    key tile's rows (128 rows x stride_n x 2 bytes); such descriptors are rejected. The layout
+    is [N, B, H, D]-like (tokens outermost) and otherwise valid."""
+    D = 128
+    ok = _lib.RecapDesc(1, 128, 100, D, 64, 0, 128 * D, D, (1 << 24) - 8)
+    assert ws_size(_lib.OP_SPARSE, ok)[0] == 0
+    bad = _lib.RecapDesc(1, 128, 100, D, 64, 0, 128 * D, D, 1 << 24)
+    assert ws_size(_lib.OP_SPARSE, bad)[0] == -3
+
+
 def test_layouts_accepted():
     for layout in ("bhnd", "bnhd"):
         assert ws_size(_lib.OP_SPARSE, desc(B=2, H=3, N=1000, layout=layout))[0] == 0

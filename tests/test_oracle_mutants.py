@@ -250,6 +250,19 @@ def _attention_mx_v_wrong_axis(q, k, v, block, sm_scale, mask, rows=None):
                               block, sm_scale, mask, rows=rows)
 
 
+def _kept_flops_full_blocks(count_or_mask, n_tokens, block, head_dim):
+    mask = np.asarray(count_or_mask, dtype=np.float64)
+    return float(4.0 * head_dim * block * block * mask.sum())
+
+
+def _kept_flops_one_product(count_or_mask, n_tokens, block, head_dim):
+    return 0.5 * _REAL["kept_flops"](count_or_mask, n_tokens, block, head_dim)
+
+
+def _sparsity_kept_share(count, m):
+    return float(np.mean(count)) / float(m)
+
+
 MUTANTS = {
     "pool divides by the full block size": ("block_mean_pool", _pool_divides_by_block),
     "pool takes the first token": ("block_mean_pool", _pool_first_token),
@@ -297,6 +310,9 @@ MUTANTS = {
     "MX block exponent offset 8 (overflows E4M3)": ("mx_scale_exponents", _mx_exp_offset(8)),
     "MX block exponent offset 6": ("mx_scale_exponents", _mx_exp_offset(6)),
     "MX blocks of 16": ("mx_quantize", _mx_group16),
+    "kept FLOPs count full blocks": ("kept_flops", _kept_flops_full_blocks),
+    "kept FLOPs count one product": ("kept_flops", _kept_flops_one_product),
+    "sparsity is the kept share": ("block_sparsity", _sparsity_kept_share),
     "FP8 attention quantises V along the head dimension": ("masked_attention_mx",
                                                            _attention_mx_v_wrong_axis),
 }
