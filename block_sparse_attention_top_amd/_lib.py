@@ -37,7 +37,8 @@ class RecapDesc(ctypes.Structure):
 _vp = ctypes.c_void_p
 _dp = ctypes.POINTER(RecapDesc)
 _fp = ctypes.POINTER(ctypes.c_float)
-ABI_VERSION = 5
+ABI_VERSION = 6
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 SIGNATURES = {
     "recap_abi_version": (ctypes.c_int, []),
@@ -45,6 +46,7 @@ SIGNATURES = {
     "recap_workspace_size": (ctypes.c_int, [ctypes.c_int, _dp, ctypes.POINTER(ctypes.c_size_t)]),
     "recap_block_scores": (ctypes.c_int, [_dp, _vp, _vp, ctypes.c_float, _vp, _vp,
                                           ctypes.c_size_t, _vp]),
+    "recap_block_scores_noalloc": (ctypes.c_int, [_dp, _vp, _vp, ctypes.c_float, _vp, _vp]),
     "recap_topp_mask": (ctypes.c_int, [_dp, _vp, _fp, _vp, _vp, _vp, _vp, _vp]),
     "recap_block_sparse_attn": (ctypes.c_int, [_dp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float,
                                                _vp, _fp, _vp, _vp, ctypes.c_size_t, _vp]),

@@ -160,6 +160,42 @@ int check_device() {
   return state == 1 ? RECAP_OK : RECAP_E_DEVICE;
 }
 
+// Fixed device scratch of recap_block_scores_noalloc: the pooled means of one call (2 x fp32
+// [B*H][M][D]). A file-scope device array, so the library never allocates it; each device
+// holds its own copy (at its own address) from the code object's load until the process ends.
+// Host code must not pass `scratch` itself to a kernel (in host code it names a host-side
+// stand-in): the device address comes from hipGetSymbolAddress, once per device.
+__device__ __align__(256) unsigned char scratch[RECAP_NOALLOC_SCRATCH_BYTES];
+
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The current device's address of `scratch`, looked up on the first call on that device with
+// that device current.
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return RECAP_E_DEVICE;
+  }
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      void* addr = nullptr;
+      if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || addr == nullptr) {
+        (void)hipGetLastError();
+        return RECAP_E_DEVICE;
+      }
+      g_scratch[dev].store(addr, std::memory_order_release);
+      p = addr;
+    }
+  }
+  *out = p;
+  return RECAP_OK;
+}
+
 inline Strides strides_of(const recap_desc* d) { return Strides{d->stride_b, d->stride_h, d->stride_n}; }
 
 int launched(hipError_t e) {
@@ -168,6 +204,30 @@ int launched(hipError_t e) {
     return RECAP_E_LAUNCH;
   }
   return RECAP_OK;
+}
+
+int validate_block_scores(const recap_desc* d, const void* q, const void* k, float sm_scale,
+                          const float* probs) {
+  int s = validate_desc(d);
+  if (s != RECAP_OK) return s;
+  if (q == nullptr || k == nullptr || probs == nullptr) return RECAP_E_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(probs)) return RECAP_E_ALIGN;
+  if (!isfinite(sm_scale) || !(sm_scale > 0.f)) return RECAP_E_VALUE;
+  return RECAP_OK;
+}
+
+// Pooling then scores; ws holds the two pooled-mean arrays (2 * pooled_bytes).
+int launch_block_scores(const recap_desc* d, const void* q, const void* k, float sm_scale,
+                        float* probs, void* ws, hipStream_t st) {
+  const int M = num_blocks(d);
+  float* qbar = (float*)ws;
+  float* kbar = (float*)((char*)ws + pooled_bytes(d));
+  hipError_t e = launch_pool((const bf16_t*)q, (const bf16_t*)k, strides_of(d), d->batch,
+                             d->heads, d->seq, d->head_dim, d->block, qbar, kbar, st);
+  if (e == hipSuccess)
+    e = launch_scores(qbar, kbar, d->batch * d->heads, M, d->head_dim,
+                      (float)((double)sm_scale * 1.4426950408889634), probs, st);
+  return launched(e);
 }
 
 }  // namespace
@@ -184,7 +244,7 @@ const char* recap_status_string(int status) {
     case RECAP_E_STRIDE: return "invalid strides (positive multiples of 8, non-overlapping)";
     case RECAP_E_ALIGN: return "a base pointer is not 16-byte aligned (workspace: 256-byte)";
     case RECAP_E_VALUE: return "a scalar or per-head value is out of range";
-    case RECAP_E_WORKSPACE: return "workspace missing or too small";
+    case RECAP_E_WORKSPACE: return "workspace missing or too small (no-alloc calls: the fixed scratch is too small)";
     case RECAP_E_DEVICE: return "no current gfx950 HIP device";
     case RECAP_E_LAUNCH: return "kernel launch failed";
     default: return "unknown status";
@@ -202,24 +262,24 @@ int recap_workspace_size(int op, const recap_desc* d, size_t* bytes) {
 
 int recap_block_scores(const recap_desc* d, const void* q, const void* k, float sm_scale,
                        float* probs, void* ws, size_t ws_bytes, void* stream) {
-  int s = validate_desc(d);
+  int s = validate_block_scores(d, q, k, sm_scale, probs);
   if (s != RECAP_OK) return s;
-  if (q == nullptr || k == nullptr || probs == nullptr) return RECAP_E_NULL;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(probs)) return RECAP_E_ALIGN;
-  if (!isfinite(sm_scale) || !(sm_scale > 0.f)) return RECAP_E_VALUE;
   if ((s = check_workspace(RECAP_OP_BLOCK_SCORES, d, ws, ws_bytes)) != RECAP_OK) return s;
   if ((s = check_device()) != RECAP_OK) return s;
+  return launch_block_scores(d, q, k, sm_scale, probs, ws, (hipStream_t)stream);
+}
 
-  hipStream_t st = (hipStream_t)stream;
-  const int M = num_blocks(d);
-  float* qbar = (float*)ws;
-  float* kbar = (float*)((char*)ws + pooled_bytes(d));
-  hipError_t e = launch_pool((const bf16_t*)q, (const bf16_t*)k, strides_of(d), d->batch,
-                             d->heads, d->seq, d->head_dim, d->block, qbar, kbar, st);
-  if (e == hipSuccess)
-    e = launch_scores(qbar, kbar, d->batch * d->heads, M, d->head_dim,
-                      (float)((double)sm_scale * 1.4426950408889634), probs, st);
-  return launched(e);
+int recap_block_scores_noalloc(const recap_desc* d, const void* q, const void* k,
+                               float sm_scale, float* probs, void* stream) {
+  int s = validate_block_scores(d, q, k, sm_scale, probs);
+  if (s != RECAP_OK) return s;
+  if (workspace_for(RECAP_OP_BLOCK_SCORES, d) > (size_t)RECAP_NOALLOC_SCRATCH_BYTES)
+    return RECAP_E_WORKSPACE;
+  if ((s = check_device()) != RECAP_OK) return s;
+  void* ws = nullptr;
+  if ((s = scratch_address(&ws)) != RECAP_OK) return s;
+  // the pooling kernel writes every mean the score kernel reads: nothing to clear
+  return launch_block_scores(d, q, k, sm_scale, probs, ws, (hipStream_t)stream);
 }
 
 int recap_topp_mask(const recap_desc* d, const float* probs, const float* top_p_host,

@@ -120,6 +120,26 @@ def recap_block_scores(desc: RecapDesc, q, k, sm_scale: Optional[float] = None, 
 
 
 @_on_stream
+def recap_block_scores_noalloc(desc: RecapDesc, q, k, sm_scale: Optional[float] = None,
+                               probs=None, stream=None) -> torch.Tensor:
+    """recap_block_scores with the library's fixed device scratch instead of a workspace
+    (the C call allocates nothing; pass `probs` to allocate nothing here either)."""
+    _same_layout(desc, q, k)
+    M = num_blocks(desc)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(desc.head_dim)
+    if probs is None:
+        probs = torch.empty((desc.batch, desc.heads, M, M), dtype=torch.float32, device=q.device)
+    elif probs.dtype != torch.float32 or tuple(probs.shape) != (desc.batch, desc.heads, M, M) \
+            or not probs.is_contiguous():
+        raise ValueError("probs must be contiguous fp32 [B, H, M, M]")
+    check(_lib.load().recap_block_scores_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k),
+                                                 float(sm_scale), _ptr(probs), _stream(stream)),
+          "recap_block_scores_noalloc")
+    return probs
+
+
+@_on_stream
 def recap_topp_mask(desc: RecapDesc, probs, top_p, kept_count=None, kept_idx=None,
                     want_mask: bool = False, want_mass: bool = False, stream=None):
     """Top-p selection per query block: (count [B,H,M], idx [B,H,M,M], mask|None, mass|None)."""

@@ -66,9 +66,12 @@
 extern "C" {
 #endif
 
-#define RECAP_ABI_VERSION 5 /* 2: *_stats; 3: mask reuse; 4: coarse tail; 5: FP8 */
+#define RECAP_ABI_VERSION 6 /* 2: *_stats; 3: mask reuse; 4: coarse tail; 5: FP8; 6: no-alloc scores */
 #define RECAP_MAX_HEADS 128   /* per-head host arrays are passed by value to the kernels */
 #define RECAP_MAX_BLOCKS 8192 /* M = ceil(N / block) upper bound (top-p sorts a row in LDS) */
+/* Size of the fixed device scratch of recap_block_scores_noalloc (64 MiB per device): the
+ * call needs 2 * B * H * M * D * 4 bytes (each of the two rounded up to 256 bytes). */
+#define RECAP_NOALLOC_SCRATCH_BYTES (64u << 20)
 
 typedef struct recap_desc {
   int32_t batch;    /* B >= 1 */
@@ -126,6 +129,22 @@ int recap_workspace_size(int op, const recap_desc* d, size_t* bytes);
  * recap_workspace_size(RECAP_OP_BLOCK_SCORES) bytes, 256-byte aligned. */
 int recap_block_scores(const recap_desc* d, const void* q, const void* k, float sm_scale,
                        float* probs, void* ws, size_t ws_bytes, void* stream);
+
+/* recap_block_scores for callers that cannot allocate device memory or pass a workspace
+ * (code recorded in a HIP graph, tight serving loops, harnesses that forbid hipMalloc).
+ * Same arguments, kernels and results as recap_block_scores, bit for bit; the pooled means go
+ * to a fixed device scratch array of RECAP_NOALLOC_SCRATCH_BYTES that the library holds on
+ * each device it runs on, from the library's load until the process ends. The call allocates
+ * nothing (no hipMalloc, hipFree or allocating library routine); its first call on a device
+ * looks up that device's scratch address.
+ * Errors: as recap_block_scores, and RECAP_E_WORKSPACE when the call would need more than
+ * RECAP_NOALLOC_SCRATCH_BYTES (2 * B*H*M*D*4 bytes; 48.4 MB at B=1, H=40, M=1182, D=128).
+ * All calls on one device share its scratch, and every call rewrites what it reads: calls
+ * whose execution overlaps on one device (concurrent streams, or host threads on different
+ * streams) race on the scratch and give undefined results. Calls on one stream are ordered
+ * and safe. */
+int recap_block_scores_noalloc(const recap_desc* d, const void* q, const void* k,
+                               float sm_scale, float* probs, void* stream);
 
 /* Mask prediction, part 2: top-p selection per query-block row (thelatestinai.com RECAP page,
  * first and third abstracts; CalibAtt Fig. 5). Key blocks are ordered by probability,

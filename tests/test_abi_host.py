@@ -36,7 +36,7 @@ def test_header_symbols_exported():
 
 def test_version_and_status_strings():
     lib = _lib.load()
-    assert lib.recap_abi_version() == _lib.ABI_VERSION == 5
+    assert lib.recap_abi_version() == _lib.ABI_VERSION == 6
     for st in list(_lib.STATUS_NAMES) + [-99]:
         s = lib.recap_status_string(st)
         assert s and len(s.decode()) > 1
@@ -117,6 +117,26 @@ def test_layouts_accepted():
 
 def _p(x=FAKE):
     return ctypes.c_void_p(x)
+
+
+@cpu_only
+def test_block_scores_noalloc_validation():
+    """The allocation-free variant validates like recap_block_scores and rejects, before any
+    HIP call, a call whose pooled means would not fit the fixed 64 MiB scratch."""
+    lib = _lib.load()
+    call = lambda d, q=_p(), k=_p(), s=0.125, pr=_p(): \
+        lib.recap_block_scores_noalloc(ctypes.byref(d), q, k, s, pr, None)
+    d = desc()
+    assert call(d, q=None) == -1
+    assert call(d, pr=_p(FAKE + 4)) == -4
+    assert call(d, s=float("nan")) == -5
+    assert call(d) == -7  # valid, fits, no device
+    fits = desc(B=1, H=40, N=75600, D=128)  # 2 x 40 x 1182 x 128 x 4 = 48.4 MB
+    assert ws_size(_lib.OP_BLOCK_SCORES, fits)[1] <= _lib.NOALLOC_SCRATCH_BYTES
+    assert call(fits) == -7
+    big = desc(B=1, H=64, N=75600, D=128)  # 77.5 MB of means
+    assert ws_size(_lib.OP_BLOCK_SCORES, big)[1] > _lib.NOALLOC_SCRATCH_BYTES
+    assert call(big) == -6
 
 
 @cpu_only
