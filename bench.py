@@ -9,9 +9,12 @@ workload (Wan2.1-14B-like 720p layer: B=1, H=40, D=128, N=75,600 tokens = 21 x 4
     attention with the fused epilogue O + 1.0 * R using the captured residual.
 Other workloads (--workload) run one sparse call per step (+ epilogue where configured).
 
-Reported (one JSON line): computed-block TFLOP/s over the step (value), ms per step, ms per
-sparse call, sparse-attention TFLOP/s, the roofline of the dominant kernel (and of the sparse
-and mask-prediction kernels), and the CPU oracle timed on a bounded sample of the same work.
+Reported (one JSON line): value = computed-block TFLOP/s of the block-sparse attention call
+(kept-block FLOPs over the mean HIP-event time of recap_block_sparse_attn, the metric's subject),
+ms per sparse call (mask prediction + attention + epilogue) and per step, the roofline of the
+sparse attention kernel (roofline), of the dense refresh (roofline_refresh) and of the
+mask-prediction kernels (roofline_mask), and the CPU oracle timed on a bounded sample of the
+same sparse call (extrapolated to the whole call).
 With --tail, RECAP's tail-reconstruction calls are also timed (a "tail" object, outside the
 step and its figures); with --fp8, the MXFP8 variant of the sparse calls (an "fp8" object);
 with --probe-peaks, the rates a plain bf16 GEMM (torch's library GEMM) and a device copy reach
@@ -94,52 +97,69 @@ def kept_token_pairs(count, idx, N, block):
     return float((per_row * n.view(1, 1, M)).sum().item())
 
 
-def cpu_baseline(cfg, q, k, v, p, seconds):
-    """The oracle as it stands on a bounded sample of the same work (head 0): full mask
-    prediction for the head, then sparse attention on query blocks spread over the sequence
-    until the time budget is spent, plus the dense refresh on one query block when the
-    workload refreshes. Returns the JSON object."""
+def host_threads():
+    """Host cores for the oracle: the CPUs this process may run on (sched_getaffinity), capped
+    by OMP_NUM_THREADS when the environment sets it (the host share of one GPU on a shared
+    box). Returns (threads used, affinity CPU count)."""
+    aff = len(os.sched_getaffinity(0))
+    cap = os.environ.get("OMP_NUM_THREADS")
+    n = min(aff, int(cap)) if cap and cap.isdigit() and int(cap) > 0 else aff
+    return n, aff
+
+
+def cpu_baseline(cfg, q, k, v, p, seconds, call_flops):
+    """The oracle as it stands (fp64 numpy, never tuned for this), timed on the host on a
+    bounded sample of one sparse call of the same workload, head 0:
+      * mask prediction (block scores, top-p) of the head in full: t_mask;
+      * sparse attention and the residual epilogue on query blocks spread over the sequence
+        until the time budget is spent: kept FLOPs F_s in t_att.
+    value = F_s / t_att, the oracle's computed-block rate (the unit of the GPU value). The
+    whole call is extrapolated as H * t_mask + call_flops * t_att / F_s and labelled so."""
     import numpy as np
-    from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_limits
 
     import synth
     from oracle import oracle as O
 
+    threads, aff = host_threads()
     s = cfg.head_dim ** -0.5
-    q64, k64, v64 = (synth.to_f64(x[:, :1]) for x in (q, k, v))
-    M, blk, N, D = cfg.num_blocks, cfg.block, cfg.seq, cfg.head_dim
-    nblk = np.full(M, blk, dtype=np.float64)
-    nblk[-1] = N - (M - 1) * blk
-    t0 = time.perf_counter()
-    probs = O.block_scores(q64, k64, blk, s)
-    sel = O.topp_select(probs, p[:1])
-    mask = sel["mask"]
-    flops = 0.0
-    rows_done = 0
-    dense_rows = 0
-    if cfg.refresh_then_sparse:
-        O.dense_attention(q64, k64, v64, s, rows=[(0, 0, M // 2)], block=blk)
-        flops += 4.0 * D * nblk[M // 2] * N
-        dense_rows = 1
-    order = np.argsort((np.arange(M) * 0.6180339887) % 1.0)  # spread over the sequence
-    for i in order:
-        O.masked_attention(q64, k64, v64, blk, s, mask, rows=[(0, 0, int(i))])
-        flops += 4.0 * D * nblk[i] * float((mask[0, 0, i] * nblk).sum())
-        rows_done += 1
-        if time.perf_counter() - t0 > seconds:
-            break
-    dt = time.perf_counter() - t0
-    threads = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
+    M, blk, N, H = cfg.num_blocks, cfg.block, cfg.seq, cfg.heads
+    with threadpool_limits(limits=threads):
+        q64, k64, v64 = (synth.to_f64(x[:, :1]) for x in (q, k, v))
+        r64 = synth.to_f64(synth.random_bf16((1, 1, N, cfg.head_dim), 4, 0.05))
+        t0 = time.perf_counter()
+        probs = O.block_scores(q64, k64, blk, s)
+        mask = O.topp_select(probs, p[:1])["mask"]
+        t_mask = time.perf_counter() - t0
+        order = np.argsort((np.arange(M) * 0.6180339887) % 1.0)  # spread over the sequence
+        done = []
+        t1 = time.perf_counter()
+        for i in order:
+            o = O.masked_attention(q64, k64, v64, blk, s, mask, rows=[(0, 0, int(i))])
+            lo, hi = int(i) * blk, min(N, (int(i) + 1) * blk)
+            O.residual_epilogue(o[:, :, lo:hi], r64[:, :, lo:hi], [1.0])
+            done.append(int(i))
+            if time.perf_counter() - t1 > seconds:
+                break
+        t_att = time.perf_counter() - t1
+    sampled = np.zeros_like(mask)
+    sampled[0, 0, done] = mask[0, 0, done]
+    flops = O.kept_flops(sampled, N, blk, cfg.head_dim)
+    rows_done = len(done)
+    call_s = H * t_mask + call_flops * t_att / flops
     return {
-        "value": flops / dt / 1e12,
+        "value": flops / t_att / 1e12,
         "unit": "TFLOP/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": (f"head 0 of {cfg.name}: mask prediction for all {M} query blocks, "
-                   f"sparse attention on {rows_done} query blocks"
-                   + (f", dense refresh on {dense_rows} query block" if dense_rows else "")
-                   + f"; {dt:.1f} s, fp64 numpy on {cpu_model()}"),
-        "seconds": dt,
+        "sample": (f"head 0 of {cfg.name}: mask prediction for all {M} query blocks "
+                   f"({t_mask:.1f} s), then sparse attention + epilogue on {rows_done} of {M} "
+                   f"query blocks ({t_att:.1f} s); value = computed-block FLOPs of those blocks "
+                   f"/ their time; fp64 numpy on {threads} threads "
+                   f"({aff} CPUs in the affinity mask) of {cpu_model()}"),
+        "extrapolated": {"ms_per_sparse_call": call_s * 1e3,
+                         "rule": "H x head-0 mask time + call FLOPs x attention s/FLOP"},
+        "seconds": t_mask + t_att,
     }
 
 
@@ -440,10 +460,11 @@ def main():
         sparse_flops.append(4.0 * D * kept_token_pairs(counts[ci], idxs[ci], N, blk))
         sparsity.append(1.0 - counts[ci].double().mean().item() / M)
     step_flops = sum(sparse_flops) + (dense_flops if cfg.refresh_then_sparse else 0.0)
-    value = step_flops / (ms_step * 1e-3) / 1e12
+    step_tflops = step_flops / (ms_step * 1e-3) / 1e12
     sp_attn_ms = avg["sparse.attn"]
     sp_call_ms = avg["sparse.scores"] + avg["sparse.topp"] + sp_attn_ms
     sp_tflops = float(np.mean(sparse_flops)) / (sp_attn_ms * 1e-3) / 1e12
+    value = sp_tflops  # the metric: computed-block TFLOP/s of the block-sparse attention call
 
     # mask-prediction algorithmic bytes per call (pool, scores, top-p)
     mean_kept = float(np.mean([counts[ci].double().mean().item() for ci in range(ncalls)]))
@@ -461,20 +482,20 @@ def main():
                 "kernel": kernel}
 
     # achieved: algorithmic FLOPs over the HIP-event time of the library call, which also runs
-    # the V^T pack (0.27 ms) and, for the refresh, the residual fallback pass (0.13 ms when no
-    # block is flagged); traffic: the attention kernel's own counters
-    sparse_roof = roof("attn_kernel<D=128, 4 wavefronts, sparse, paired 64-row blocks> "
-                       "(timed as one recap_block_sparse_attn call)", sp_tflops,
-                       traffic_key="attn_sparse")
+    # the V^T pack (0.27 ms at 720p) and, for the refresh, the residual fallback pass (0.13 ms
+    # when no block is flagged); traffic: the attention kernel's own counters
+    sparse_roof = roof("attn_kernel<D=128, 4 wavefronts, sparse> (block-sparse attention with "
+                       "the fused epilogue; timed as one recap_block_sparse_attn call)",
+                       sp_tflops, traffic_key="attn_sparse")
     if cfg.refresh_then_sparse:
         dense_ms = avg["refresh.attn"]
         dense_tflops = dense_flops / (dense_ms * 1e-3) / 1e12
-        main_roof = roof("attn_kernel<D=128, 4 wavefronts, dense + residual capture> "
-                         "(timed as one recap_dense_attn call)", dense_tflops,
-                         traffic_key="attn_capture")
+        refresh_roof = roof("attn_kernel<D=128, 4 wavefronts, dense + residual capture> "
+                            "(timed as one recap_dense_attn call)", dense_tflops,
+                            traffic_key="attn_capture")
     else:
         dense_ms = None
-        main_roof = sparse_roof
+        refresh_roof = None
     mask_roof = roof("pool + score + topp kernels (one call's mask prediction)",
                      mask_bytes / (mask_ms * 1e-3) / 1e9, bound="hbm", traffic_key="mask")
 
@@ -505,6 +526,7 @@ def main():
         },
         "ms_per_sparse_call": sp_call_ms,
         "ms_sparse_attn": sp_attn_ms,
+        "step_tflops": step_tflops,
         "ms_mask_prediction": mask_ms,
         "ms_refresh_call": (avg["refresh.scores"] + avg["refresh.topp"] + dense_ms)
         if dense_ms is not None else None,
@@ -515,8 +537,8 @@ def main():
         "per_op_ms": avg,
         "per_op_ms_dist": {k: dist(v) for k, v in per.items()},
         "per_call_ms_dist": {k: dist(v) for k, v in calls.items() if v},
-        "roofline": main_roof,
-        "roofline_sparse": sparse_roof,
+        "roofline": sparse_roof,
+        "roofline_refresh": refresh_roof,
         "roofline_mask": mask_roof,
     }
     if args.probe_peaks:
@@ -530,7 +552,8 @@ def main():
         result["tail"] = bench_tail(bsa, cfg, desc, dev_inputs, counts, idxs, s, avg, args, roof)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle on a bounded sample)")
-        cb = cpu_baseline(cfg, q, k, v, p, args.cpu_seconds)
+        qs, ks, vs = inputs[1] if cfg.refresh_then_sparse else inputs[0]
+        cb = cpu_baseline(cfg, qs, ks, vs, p, args.cpu_seconds, float(np.mean(sparse_flops)))
         result["cpu_baseline"] = {kk: vv for kk, vv in cb.items() if kk != "seconds"}
     print(json.dumps(result), flush=True)
 

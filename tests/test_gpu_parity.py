@@ -504,6 +504,8 @@ def _check_head(probs_g, mask_g, cnt_g, idx_g, q64, k64, v64, cfg, p_h, s, rows,
         for i in rows:
             lo, hi = i * cfg.block, min(cfg.seq, (i + 1) * cfg.block)
             parity.check_out(out_g[:, :, lo:hi], ref[:, :, lo:hi], f"head {h} block {i}")
+        if len(rows) == cfg.num_blocks:
+            parity.check_out(out_g, ref, f"head {h} whole")
 
 
 def _head(x, h):
@@ -528,9 +530,9 @@ def test_full_size_sparse(bsa, name, heads):
     out = bsa.recap_block_sparse_attn(desc, qd, kd, vd, count, idx, s, rd,
                                       c.tolist() if rd is not None else None)
     torch.cuda.synchronize()
-    say(f"[check] {name}: oracle on heads {heads}")
+    say(f"[check] {name}: oracle on every query block of heads {heads}")
     for h in heads:
-        rows = _sample_rows(cfg.num_blocks, 6, h)
+        rows = list(range(cfg.num_blocks))
         extra = None
         if r is not None:
             r64 = _head(r, h)
@@ -590,8 +592,9 @@ def test_full_size_refresh_then_sparse(bsa):
     out, count1, idx1 = bsa.sparse_step(desc, q1d, k1d, v1d, p.tolist(), s, residual=rcap,
                                         res_scale=c.tolist())
     torch.cuda.synchronize()
+    say(f"[check] drifted step 1: oracle on every query block of heads {heads}")
     for h in heads:
-        rows = _sample_rows(cfg.num_blocks, 3, 200 + h)
+        rows = list(range(cfg.num_blocks))
         m_h = O.mask_from_lists(count1[:, h:h + 1].cpu().numpy(), idx1[:, h:h + 1].cpu().numpy(),
                                 cfg.num_blocks)
         q64, k64, v64 = _head(q1, h), _head(k1, h), _head(v1, h)
@@ -601,3 +604,4 @@ def test_full_size_refresh_then_sparse(bsa):
         for i in rows:
             lo, hi = i * cfg.block, min(cfg.seq, (i + 1) * cfg.block)
             parity.check_out(got[:, :, lo:hi], ref[:, :, lo:hi], f"step1 h{h} b{i}")
+        parity.check_out(got, ref, f"step1 h{h} whole head")
