@@ -127,6 +127,68 @@ def coarse_tail_row(qt, k, v, n_tokens, block, tail_blocks, sm_scale):
     return mx + math.log(tot), out
 
 
+def block_variance(k, n_tokens, block, dim):
+    """[M][D] per-dimension key variance inside each block (population form), plain floats."""
+    kb = pool(k, n_tokens, block, dim)
+    out = []
+    for j in range(len(kb)):
+        lo, hi = j * block, min(n_tokens, (j + 1) * block)
+        row = []
+        for d in range(dim):
+            acc = 0.0
+            for t in range(lo, hi):
+                acc += (k[t][d] - kb[j][d]) ** 2
+            row.append(acc / (hi - lo))
+        out.append(row)
+    return out
+
+
+def pooled_covariance(k, v, n_tokens, block, dim):
+    """[D][D] pooled within-block value-key covariance, C[a][c] over value dim a, key dim c."""
+    kb = pool(k, n_tokens, block, dim)
+    vb = pool(v, n_tokens, block, dim)
+    c = [[0.0] * dim for _ in range(dim)]
+    for t in range(n_tokens):
+        j = t // block
+        for a in range(dim):
+            for e in range(dim):
+                c[a][e] += (v[t][a] - vb[j][a]) * (k[t][e] - kb[j][e])
+    return [[x / n_tokens for x in row] for row in c]
+
+
+def coarse_tail_moments_row(qt, k, v, n_tokens, block, tail_blocks, sm_scale):
+    """The block-mean estimate with both moment refinements, with plain floats: block
+    log-mass ln n_j + s q . K̄_j + (s^2/2) sum_d q_d^2 Var_j(k_d); output the mass-weighted
+    block means plus s C q with the pooled covariance C."""
+    dim = len(v[0])
+    if not tail_blocks:
+        return -math.inf, [0.0] * dim
+    kb = pool(k, n_tokens, block, dim)
+    vb = pool(v, n_tokens, block, dim)
+    var = block_variance(k, n_tokens, block, dim)
+    cov = pooled_covariance(k, v, n_tokens, block, dim)
+    logm = []
+    for j in tail_blocks:
+        nj = min(n_tokens, (j + 1) * block) - j * block
+        dot = 0.0
+        quad = 0.0
+        for d in range(dim):
+            dot += qt[d] * kb[j][d]
+            quad += qt[d] * qt[d] * var[j][d]
+        logm.append(math.log(nj) + sm_scale * dot + 0.5 * sm_scale * sm_scale * quad)
+    mx = max(logm)
+    w = [math.exp(x - mx) for x in logm]
+    tot = sum(w)
+    out = [0.0] * dim
+    for wi, j in zip(w, tail_blocks):
+        for d in range(dim):
+            out[d] += wi / tot * vb[j][d]
+    for a in range(dim):
+        for e in range(dim):
+            out[a] += sm_scale * cov[a][e] * qt[e]
+    return mx + math.log(tot), out
+
+
 def e4m3_value(code: int) -> float:
     """Value of an 8-bit OCP E4M3 code from its bit fields (sign, exponent with bias 7, 3-bit
     mantissa; exponent field 0 is subnormal; S.1111.111 is NaN)."""

@@ -27,8 +27,12 @@ Readings where the pages are silent (all listed in the design notes):
   * the residual epilogue adds c_h * R to the sparse output, R = O_dense - O_sparse captured
     at a dense refresh on the same kept set;
   * the coarse tail (RECAP §3.2) uses each query token against the block means of the omitted
-    key blocks, a block's mass being its token count times exp(s * q . K̄_j); its moment
-    refinements are left out (formulas absent), and the cached discrepancy is added unscaled.
+    key blocks, a block's mass being its token count times exp(s * q . K̄_j); with the moment
+    refinements (moments=True) the block log-mass gains the second-order term
+    (s^2 / 2) sum_d q_d^2 Var_j(k_d) (per-dimension key variance within the block, population
+    form: the diagonal reading of "key variance"), and the output gains the first-order value
+    compensation s * C q with C the pooled within-block value-key covariance of the head (one
+    matrix shared by every block); the cached discrepancy is added unscaled.
 """
 from __future__ import annotations
 
@@ -323,7 +327,39 @@ def _row_blocks(mask, rows, B, H, M):
     return rows
 
 
-def coarse_tail(q, k, v, block: int, sm_scale: float, mask, rows=None):
+def block_key_variance(k, block: int) -> np.ndarray:
+    """Per-dimension variance of the keys inside each block, population form over the block's
+    valid tokens: Var_j(k_d) = (1/n_j) sum_{u in j} (k_{u,d} - K̄_{j,d})^2 ([RECAP] §3.2: key
+    variance for the second-order log-mass refinement). k: [B, H, N, D] -> [B, H, M, D]."""
+    k = np.asarray(k, dtype=np.float64)
+    starts, ends = block_partition(k.shape[2], block)
+    kb = block_mean_pool(k, block)
+    out = np.empty(k.shape[:2] + (len(starts), k.shape[3]))
+    for j, (a, b) in enumerate(zip(starts, ends)):
+        dev = k[:, :, a:b] - kb[:, :, j:j + 1]
+        out[:, :, j] = (dev * dev).mean(axis=2)
+    return out
+
+
+def pooled_value_key_covariance(k, v, block: int) -> np.ndarray:
+    """Pooled within-block value-key covariance of each head ([RECAP] §3.2 and §2: the pooled
+    value-key covariance of PISA's shared first-order value compensation):
+        C = (1/N) sum_j sum_{u in j} (v_u - V̄_j) (k_u - K̄_j)^T,
+    rows indexed by the value dimension, columns by the key dimension; one matrix per (b, h),
+    shared by every block. k, v: [B, H, N, D] -> [B, H, D, D]."""
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    starts, ends = block_partition(k.shape[2], block)
+    kb, vb = block_mean_pool(k, block), block_mean_pool(v, block)
+    acc = np.zeros(k.shape[:2] + (v.shape[3], k.shape[3]))
+    for j, (a, b) in enumerate(zip(starts, ends)):
+        dk = k[:, :, a:b] - kb[:, :, j:j + 1]
+        dv = v[:, :, a:b] - vb[:, :, j:j + 1]
+        acc += np.einsum("bhnv,bhnk->bhvk", dv, dk)
+    return acc / float(k.shape[2])
+
+
+def coarse_tail(q, k, v, block: int, sm_scale: float, mask, rows=None, moments: bool = False):
     """Zeroth-order estimate of the attention over each query's omitted key blocks, from block
     means ([RECAP] §3.2: block means give first estimates of the omitted tail's value and
     normalising mass; the coarse log-mass is the log of the summed block masses, the coarse
@@ -335,9 +371,19 @@ def coarse_tail(q, k, v, block: int, sm_scale: float, mask, rows=None):
     token count (the last block may be short). Then
         lse_bar_t = ln sum_j n_j exp(s * Q_t . K̄_j)
         o_bar_t   = sum_j n_j exp(s * Q_t . K̄_j) V̄_j / sum_j n_j exp(s * Q_t . K̄_j).
-    The key-variance (COBS) and value-key-covariance (PISA) refinements named on the page are
-    not applied: their formulas are not on the pages. A query block that keeps every key block
-    has no tail: lse_bar = -inf, o_bar = 0.
+    With moments=True, the two moment refinements the page names (key variance refines the
+    log-mass at second order, COBS; pooled value-key covariance refines the value at first
+    order, PISA), in the reading written out here: writing each key as K̄_j + e_u,
+        ln sum_{u in j} exp(s Q_t . k_u) = ln n_j + s Q_t . K̄_j + ln mean_u exp(s Q_t . e_u)
+    and the last term's second-order (cumulant) approximation with the per-dimension variances
+    (the diagonal of the block's key covariance: "key variance") is
+        (s^2 / 2) sum_d Q_{t,d}^2 Var_j(k_d)                          (`block_key_variance`);
+    the block's attention output, to first order in e_u, is V̄_j + s C_j Q_t with C_j the
+    block's value-key covariance; C_j is replaced by the pooled C of the head
+    (`pooled_value_key_covariance`), shared by every block, so the weighted output gains
+    s C Q_t whatever the weights:
+        o_bar_t = sum_j w_tj V̄_j / sum_j w_tj + s C Q_t.
+    A query block that keeps every key block has no tail: lse_bar = -inf, o_bar = 0.
     q, k, v: [B, H, N, D]; mask: bool [B, H, M, M]. Returns (lse_bar float64 [B, H, N],
     o_bar float64 [B, H, N, D]), NaN outside `rows` (an iterable of (b, h, i)).
     """
@@ -348,6 +394,10 @@ def coarse_tail(q, k, v, block: int, sm_scale: float, mask, rows=None):
     kb = block_mean_pool(k, block)
     vb = block_mean_pool(v, block)
     n = (ends - starts).astype(np.float64)
+    s = float(sm_scale)
+    if moments:
+        var = block_key_variance(k, block)
+        cov = pooled_value_key_covariance(k, v, block)
     lse = np.full((B, H, N), np.nan)
     out = np.full((B, H, N, D), np.nan)
     for b, h, i in _row_blocks(mask, rows, B, H, M):
@@ -357,12 +407,17 @@ def coarse_tail(q, k, v, block: int, sm_scale: float, mask, rows=None):
             lse[b, h, qs] = -np.inf
             out[b, h, qs] = 0.0
             continue
-        logw = float(sm_scale) * (q[b, h, qs] @ kb[b, h, js].T) + np.log(n[js])[None, :]
+        qt = q[b, h, qs]
+        logw = s * (qt @ kb[b, h, js].T) + np.log(n[js])[None, :]
+        if moments:
+            logw = logw + 0.5 * s * s * ((qt * qt) @ var[b, h, js].T)
         mx = logw.max(axis=-1, keepdims=True)
         w = np.exp(logw - mx)
         tot = w.sum(axis=-1)
         lse[b, h, qs] = mx[:, 0] + np.log(tot)
         out[b, h, qs] = (w @ vb[b, h, js]) / tot[:, None]
+        if moments:
+            out[b, h, qs] += s * (qt @ cov[b, h].T)
     return lse, out
 
 

@@ -589,6 +589,155 @@ def check_tail_empty_and_merge():
     assert np.array_equal(out, ob)
 
 
+# ----------------------------------------------------------------- coarse tail: moment refinements
+def check_moment_stats():
+    """Block key variance and the pooled value-key covariance against numpy's population
+    variance and covariance (ddof 0 / bias=True) per block, the pooled one weighted by n_j / N
+    over a ragged partition; and a two-token block k = K̄ +- d, v = V̄ +- w, where the variance is
+    d^2 per dimension and the covariance is exactly w d^T."""
+    n, b, d = 70, 16, 3  # blocks of 16 x 4 and 6
+    k = _rand((1, 2, n, d), 600)
+    v = _rand((1, 2, n, d), 601)
+    var = O.block_key_variance(k, b)
+    cov = O.pooled_value_key_covariance(k, v, b)
+    st, en = O.block_partition(n, b)
+    want = np.zeros((d, d))
+    for j, (a, e) in enumerate(zip(st, en)):
+        assert np.allclose(var[0, 1, j], np.var(k[0, 1, a:e], axis=0), rtol=0, atol=1e-13)
+        both = np.cov(np.concatenate([v[0, 1, a:e], k[0, 1, a:e]], axis=1).T, bias=True)
+        want += (e - a) / n * both[:d, d:]
+    assert np.allclose(cov[0, 1], want, rtol=0, atol=1e-13)
+    kd, vw = np.array([0.5, -1.0, 2.0]), np.array([3.0, 0.25, -1.5])
+    k2 = np.stack([1.0 + kd, 1.0 - kd])[None, None]
+    v2 = np.stack([-2.0 + vw, -2.0 - vw])[None, None]
+    assert np.allclose(O.block_key_variance(k2, 2)[0, 0, 0], kd * kd, rtol=0, atol=1e-15)
+    assert np.allclose(O.pooled_value_key_covariance(k2, v2, 2)[0, 0], np.outer(vw, kd),
+                       rtol=0, atol=1e-15)
+
+
+def _two_key_case(kd, vw, q_rows):
+    """One block of two keys K̄ +- kd with values V̄ +- vw, omitted by its only query block."""
+    kbar, vbar = np.array([0.3, -0.2, 0.1]), np.array([1.0, -1.0, 0.5])
+    k = np.stack([kbar + kd, kbar - kd])[None, None]
+    v = np.stack([vbar + vw, vbar - vw])[None, None]
+    q = np.asarray(q_rows, dtype=np.float64)[None, None]
+    return q, k, v, np.zeros((1, 1, 1, 1), bool), kbar, vbar
+
+
+def check_tail_moments_two_key_block():
+    """Two keys K̄ +- d in one omitted block: the exact log-mass is ln 2 + s q.K̄ + ln cosh(x)
+    with x = s q.d, the exact output V̄ + w tanh(x). With d along one dimension the refined
+    log-mass is ln 2 + s q.K̄ + x^2 / 2 (the second-order term of ln cosh) and the refined
+    output V̄ + w x (the first-order term of tanh), so they miss the exact values by at most
+    x^4 / 12 and |w| |x|^3 / 3. With d along two dimensions the refined log-mass takes the
+    per-dimension variances only: ln 2 + s q.K̄ + (s^2 / 2)(q_0^2 d_0^2 + q_1^2 d_1^2)."""
+    s = 0.4
+    kd, vw = np.array([0.9, 0.0, 0.0]), np.array([0.5, -0.25, 1.0])
+    q, k, v, mask, kbar, vbar = _two_key_case(kd, vw, [[1.2, -0.7, 0.4], [-0.5, 2.0, 1.0]])
+    lse, out = O.coarse_tail(q, k, v, 2, s, mask, moments=True)
+    for t in range(2):
+        x = s * q[0, 0, t] @ kd
+        base = math.log(2.0) + s * q[0, 0, t] @ kbar
+        assert abs(lse[0, 0, t] - (base + x * x / 2)) < 1e-14
+        assert abs(lse[0, 0, t] - (base + math.log(math.cosh(x)))) <= x ** 4 / 12 + 1e-15
+        assert np.allclose(out[0, 0, t], vbar + vw * x, rtol=0, atol=1e-14)
+        assert np.all(np.abs(out[0, 0, t] - (vbar + vw * math.tanh(x)))
+                      <= np.abs(vw) * abs(x) ** 3 / 3 + 1e-15)
+    kd2 = np.array([0.9, -0.6, 0.0])
+    q, k, v, mask, kbar, _ = _two_key_case(kd2, vw, [[1.2, -0.7, 0.4], [0.3, 0.3, 0.3]])
+    lse, _ = O.coarse_tail(q, k, v, 2, s, mask, moments=True)
+    qt = q[0, 0, 0]
+    want = math.log(2.0) + s * qt @ kbar + 0.5 * s * s * (qt[0] ** 2 * 0.81 + qt[1] ** 2 * 0.36)
+    assert abs(lse[0, 0, 0] - want) < 1e-14
+
+
+def check_tail_moments_vanish_and_brute():
+    """Keys and values constant over each block: no variance, no covariance, so the refined
+    tail equals the zeroth-order one and the exact tail. On a ragged random case the refined
+    tail agrees with the scalar brute force."""
+    n, b, d = 200, 32, 8
+    q, k, v, mask = _tail_case(n, b, d, 610)
+    kb, vb = O.block_mean_pool(k, b), O.block_mean_pool(v, b)
+    st, en = O.block_partition(n, b)
+    for j in range(len(st)):
+        k[:, :, st[j]:en[j]] = kb[:, :, j:j + 1]
+        v[:, :, st[j]:en[j]] = vb[:, :, j:j + 1]
+    l1, o1 = O.coarse_tail(q, k, v, b, 0.9, mask, moments=True)
+    l0, o0 = O.coarse_tail(q, k, v, b, 0.9, mask)
+    el, eo = O.exact_tail(q, k, v, b, 0.9, mask)
+    assert np.allclose(l1, l0, rtol=0, atol=1e-13) and np.allclose(o1, o0, rtol=0, atol=1e-13)
+    assert np.allclose(l1, el, rtol=0, atol=1e-12) and np.allclose(o1, eo, rtol=0, atol=1e-12)
+    n, b, d = 70, 16, 5
+    q, k, v, mask = _tail_case(n, b, d, 620, heads=1)
+    s = 0.6
+    cl, co = O.coarse_tail(q, k, v, b, s, mask, moments=True)
+    qs, ks, vs = q[0, 0].tolist(), k[0, 0].tolist(), v[0, 0].tolist()
+    for t in range(0, n, 3):
+        tail = [j for j in range(5) if not mask[0, 0, t // b, j]]
+        bl, bo = brute.coarse_tail_moments_row(qs[t], ks, vs, n, b, tail, s)
+        assert abs(cl[0, 0, t] - bl) < 1e-12, (t, cl[0, 0, t], bl)
+        assert np.allclose(co[0, 0, t], bo, rtol=0, atol=1e-12)
+
+
+def check_tail_moments_order():
+    """The refinements raise the order of the estimate in the score scale s. Keys K̄_j + e_u and
+    values V̄_j + W e_u with the same symmetric, axis-aligned deviations e_u in every block (so
+    every block's value-key covariance is the pooled one and its key covariance is diagonal):
+    halving s divides the zeroth-order log-mass error
+    by about 4 (it is O(s^2)) and the refined one by about 16 (O(s^4): the third cumulant of
+    symmetric deviations vanishes); the zeroth-order output error by about 2 (O(s)) and the
+    refined one by about 4 (O(s^2))."""
+    n, b, d = 128, 16, 4
+    rng = np.random.default_rng(630)
+    # each token deviates along one axis (+- a_d e_d, twice each): mean zero, symmetric, and a
+    # diagonal key covariance, so the per-dimension variances hold the whole second cumulant
+    amp = rng.uniform(0.5, 1.5, size=d)
+    dev = np.concatenate([np.diag(sg * amp) for sg in (1.0, -1.0, 1.0, -1.0)])
+    W = rng.normal(size=(d, d))
+    kbar = rng.normal(size=(n // b, d))
+    vbar = rng.normal(size=(n // b, d))
+    k = np.concatenate([kbar[j] + dev for j in range(n // b)])[None, None]
+    v = np.concatenate([vbar[j] + dev @ W.T for j in range(n // b)])[None, None]
+    q = rng.normal(size=(1, 1, n, d))
+    mask = np.zeros((1, 1, n // b, n // b), bool)
+    mask[0, 0, :, 0] = True
+
+    def errs(s):
+        el, eo = O.exact_tail(q, k, v, b, s, mask)
+        out = []
+        for mom in (False, True):
+            cl, co = O.coarse_tail(q, k, v, b, s, mask, moments=mom)
+            out.append((np.abs(cl - el).max(), np.abs(co - eo).max()))
+        return out
+
+    e1, e2 = errs(0.02), errs(0.01)
+    (l0a, o0a), (l1a, o1a) = e1
+    (l0b, o0b), (l1b, o1b) = e2
+    assert 3.5 < l0a / l0b < 4.5, l0a / l0b
+    assert l1a / l1b > 12.0, l1a / l1b
+    assert 1.7 < o0a / o0b < 2.3, o0a / o0b
+    assert o1a / o1b > 3.5, o1a / o1b
+    assert l1a < 0.1 * l0a and o1a < 0.1 * o0a
+
+
+def check_tail_moments_shifts():
+    """A vector c added to every key leaves the variances and the covariance unchanged and
+    moves the refined log-mass by s * q_t . c; one added to every value moves the refined
+    output by c."""
+    n, b, d = 130, 32, 6
+    q, k, v, mask = _tail_case(n, b, d, 640)
+    c = _rand((d,), 641, 0.5)
+    s = 0.8
+    l0, o0 = O.coarse_tail(q, k, v, b, s, mask, moments=True)
+    l1, o1 = O.coarse_tail(q, k + c, v, b, s, mask, moments=True)
+    assert np.allclose(l1 - l0, s * q @ c, rtol=0, atol=1e-11)
+    assert np.allclose(o1, o0, rtol=0, atol=1e-11)
+    l2, o2 = O.coarse_tail(q, k, v + c, b, s, mask, moments=True)
+    tail = np.isfinite(l0)
+    assert np.allclose(l2, l0, rtol=0, atol=1e-12)
+    assert np.allclose(o2[tail], (o0 + c)[tail], rtol=0, atol=1e-11)
+
+
 # ----------------------------------------------------------------------------- FP8 (MX)
 def _e4m3_grid():
     return np.array(sorted({brute.e4m3_value(c) for c in range(256)
@@ -747,6 +896,11 @@ ALL_CHECKS = [
     check_tail_partition_identity,
     check_tail_refresh_identity,
     check_tail_empty_and_merge,
+    check_moment_stats,
+    check_tail_moments_two_key_block,
+    check_tail_moments_vanish_and_brute,
+    check_tail_moments_order,
+    check_tail_moments_shifts,
     check_e4m3_rounding_vs_brute,
     check_mx_scale_closed_forms,
     check_mx_quantize_invariants,

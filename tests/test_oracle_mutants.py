@@ -158,7 +158,7 @@ def _drift_swapped(qbar, kbar, qref, kref):
 
 
 def _coarse_variant(no_count=False, full_count=False, pooled_query=False, with_kept=False):
-    def f(q, k, v, block, sm_scale, mask, rows=None):
+    def f(q, k, v, block, sm_scale, mask, rows=None, moments=False):  # zeroth order only
         q = np.asarray(q, dtype=np.float64)
         B, H, N, D = q.shape
         st, en = O.block_partition(N, block)
@@ -263,6 +263,57 @@ def _sparsity_kept_share(count, m):
     return float(np.mean(count)) / float(m)
 
 
+def _moments_variant(half=0.5, s_power=2, full_quad=False, transposed=False, comp_scale=True,
+                     sample_var=False, raw_cov=False):
+    """coarse_tail with moments, written out with one planted slip in a refinement."""
+    def f(q, k, v, block, sm_scale, mask, rows=None, moments=False):
+        if not moments:
+            return _REAL["coarse_tail"](q, k, v, block, sm_scale, mask, rows)
+        q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
+        B, H, N, D = q.shape
+        st, en = O.block_partition(N, block)
+        M = len(st)
+        kb, vb = O.block_mean_pool(k, block), O.block_mean_pool(v, block)
+        n = (en - st).astype(np.float64)
+        var = np.empty((B, H, M, D))
+        cov = np.zeros((B, H, D, D))
+        sig = [None] * M
+        for j in range(M):
+            dk = k[:, :, st[j]:en[j]] - kb[:, :, j:j + 1]
+            dv = v[:, :, st[j]:en[j]] - (0.0 if raw_cov else vb[:, :, j:j + 1])
+            var[:, :, j] = (dk * dk).sum(2) / (max(n[j] - 1, 1) if sample_var else n[j])
+            sig[j] = np.einsum("bhnd,bhne->bhde", dk, dk) / n[j]
+            cov += np.einsum("bhnv,bhnk->bhvk", dv, dk if not raw_cov else k[:, :, st[j]:en[j]])
+        cov /= N
+        if transposed:
+            cov = np.swapaxes(cov, -1, -2)
+        s = float(sm_scale)
+        lse, out = np.full((B, H, N), np.nan), np.full((B, H, N, D), np.nan)
+        for b in range(B):
+            for h in range(H):
+                for i in range(M):
+                    qs = slice(st[i], en[i])
+                    js = np.nonzero(~np.asarray(mask[b, h, i], dtype=bool))[0]
+                    if len(js) == 0:
+                        lse[b, h, qs], out[b, h, qs] = -np.inf, 0.0
+                        continue
+                    qt = q[b, h, qs]
+                    lw = s * (qt @ kb[b, h, js].T) + np.log(n[js])[None, :]
+                    if full_quad:
+                        quad = np.stack([np.einsum("td,de,te->t", qt, sig[j][b, h], qt)
+                                         for j in js], axis=1)
+                    else:
+                        quad = (qt * qt) @ var[b, h, js].T
+                    lw = lw + half * s ** s_power * quad
+                    mx = lw.max(-1, keepdims=True)
+                    w = np.exp(lw - mx)
+                    lse[b, h, qs] = mx[:, 0] + np.log(w.sum(-1))
+                    out[b, h, qs] = (w @ vb[b, h, js]) / w.sum(-1)[:, None]
+                    out[b, h, qs] += (s if comp_scale else 1.0) * (qt @ cov[b, h].T)
+        return lse, out
+    return f
+
+
 MUTANTS = {
     "pool divides by the full block size": ("block_mean_pool", _pool_divides_by_block),
     "pool takes the first token": ("block_mean_pool", _pool_first_token),
@@ -310,6 +361,15 @@ MUTANTS = {
     "MX block exponent offset 8 (overflows E4M3)": ("mx_scale_exponents", _mx_exp_offset(8)),
     "MX block exponent offset 6": ("mx_scale_exponents", _mx_exp_offset(6)),
     "MX blocks of 16": ("mx_quantize", _mx_group16),
+    "variance term without the 1/2": ("coarse_tail", _moments_variant(half=1.0)),
+    "variance term scaled by s, not s^2": ("coarse_tail", _moments_variant(s_power=1)),
+    "full key covariance instead of per-dimension variance": ("coarse_tail",
+                                                              _moments_variant(full_quad=True)),
+    "sample (n - 1) key variance": ("coarse_tail", _moments_variant(sample_var=True)),
+    "value compensation with the transposed covariance": ("coarse_tail",
+                                                           _moments_variant(transposed=True)),
+    "value compensation without the scale": ("coarse_tail", _moments_variant(comp_scale=False)),
+    "covariance of raw, uncentred tokens": ("coarse_tail", _moments_variant(raw_cov=True)),
     "kept FLOPs count full blocks": ("kept_flops", _kept_flops_full_blocks),
     "kept FLOPs count one product": ("kept_flops", _kept_flops_one_product),
     "sparsity is the kept share": ("block_sparsity", _sparsity_kept_share),
