@@ -165,10 +165,14 @@ def cpu_baseline(cfg, q, k, v, p, seconds, call_flops):
 
 def bench_tail(bsa, cfg, desc, dev_inputs, counts, idxs, s, avg, args, roof):
     """RECAP's tail reconstruction timed apart from the step, on the same inputs and kept
-    lists: the refresh with the discrepancy (recap_dense_attn_tail on X_0), each drifted sparse
-    call merged with the fresh coarse tail plus that discrepancy (recap_block_sparse_attn_tail
-    on X_1..), and the coarse estimate alone (recap_tail_estimate on X_1). The roofline is the
-    estimate's: 4 D FLOPs per (query token, omitted key block) pair over its call time."""
+    lists, zeroth order and with the moment refinements: the refresh with the discrepancy
+    (recap_dense_attn_tail on X_0), each drifted sparse call merged with the fresh coarse tail
+    plus that discrepancy (recap_block_sparse_attn_tail on X_1..), and the coarse estimate alone
+    (recap_tail_estimate on X_1). The roofline is the zeroth-order estimate's: 4 D FLOPs per
+    (query token, omitted key block) pair over its call time. Accuracy at the drifted step X_1
+    (the refresh's kept lists reused, as RECAP reuses them between refreshes): relative L2 and
+    largest error against the dense output on X_1 of the plain sparse output, of the merge with
+    the coarse tail alone and of the merge with coarse tail + discrepancy."""
     import numpy as np
     import torch
 
@@ -182,7 +186,7 @@ def bench_tail(bsa, cfg, desc, dev_inputs, counts, idxs, s, avg, args, roof):
     ws_m = torch.empty(bsa.recap_workspace_size(7, desc), dtype=torch.uint8, device=dev)
     ws_e = torch.empty(bsa.recap_workspace_size(5, desc), dtype=torch.uint8, device=dev)
 
-    def run(events):
+    def run(events, mom):
         def timed(name, fn):
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
@@ -193,42 +197,69 @@ def bench_tail(bsa, cfg, desc, dev_inputs, counts, idxs, s, avg, args, roof):
                 events.append((name, e0, e1))
         q0, k0, v0 = dev_inputs[0]
         timed("refresh", lambda: bsa.recap_dense_attn_tail(desc, q0, k0, v0, counts[0], idxs[0], s,
-                                                           out, d_lse, d_o, ws_m))
+                                                           out, d_lse, d_o, ws_m, moments=mom))
         for ci in range(1, len(dev_inputs)):
             qq, kk, vv = dev_inputs[ci]
             timed("sparse", lambda: bsa.recap_block_sparse_attn_tail(
-                desc, qq, kk, vv, counts[ci], idxs[ci], s, d_lse, d_o, out, ws_m))
+                desc, qq, kk, vv, counts[ci], idxs[ci], s, d_lse, d_o, out, ws_m, moments=mom))
         q1, k1, v1 = dev_inputs[1]
         timed("estimate", lambda: bsa.recap_tail_estimate(desc, q1, k1, v1, counts[1], idxs[1],
-                                                          s, t_lse, t_out, ws_e))
+                                                          s, t_lse, t_out, ws_e, moments=mom))
 
-    log("tail reconstruction: warmup 1, timing")
-    run(None)
+    res = {}
+    for mom in (False, True):
+        tag = "moments" if mom else "zeroth"
+        log(f"tail reconstruction ({tag}): warmup 1, timing")
+        run(None, mom)
+        torch.cuda.synchronize()
+        events = []
+        for _ in range(max(1, args.steps // 2)):
+            run(events, mom)
+        torch.cuda.synchronize()
+        per = {}
+        for name, e0, e1 in events:
+            per.setdefault(name, []).append(e0.elapsed_time(e1))
+        t = {k: float(np.median(v)) for k, v in per.items()}
+        res[tag] = {"ms_refresh_call_with_discrepancy": t["refresh"],
+                    "ms_sparse_call_with_tail": t["sparse"], "ms_tail_estimate": t["estimate"],
+                    "refresh_overhead_ms": t["refresh"] - avg["refresh.attn"],
+                    "sparse_overhead_ms": t["sparse"] - avg["sparse.attn"],
+                    "n_timed": {k: len(v) for k, v in per.items()}}
+        if not mom:
+            # omitted (query token, key block) pairs of the estimate's kept lists
+            starts = torch.arange(M, device=dev) * blk
+            n_q = (torch.clamp(starts + blk, max=N) - starts).double()
+            omitted = ((M - counts[1].double()) * n_q).sum().item()
+            est_tflops = 4.0 * D * omitted / (t["estimate"] * 1e-3) / 1e12
+            res["roofline_estimate"] = roof(
+                "pool + tail_keys + pack + tail_kernel (one zeroth-order recap_tail_estimate "
+                "call; algorithmic FLOPs on omitted pairs only)", est_tflops, traffic_key="tail")
+
+    # accuracy at the drifted step X_1 with the refresh's kept lists and discrepancy
+    log("tail reconstruction: accuracy at the drifted step")
+    q0, k0, v0 = dev_inputs[0]
+    q1, k1, v1 = dev_inputs[1]
+    c0, i0 = counts[0], idxs[0]
+    ref = bsa.recap_dense_attn(desc, q1, k1, v1, s).float()
+    nref = ref.norm().item()
+
+    def err(x):
+        e = x.float() - ref
+        return {"rel_l2": e.norm().item() / nref, "max_abs": e.abs().max().item()}
+
+    acc = {"reference": "dense attention on X_1 (recap_dense_attn)",
+           "kept_lists": "the refresh's (X_0) lists reused at X_1",
+           "sparse_only": err(bsa.recap_block_sparse_attn(desc, q1, k1, v1, c0, i0, s))}
+    for mom in (False, True):
+        tag = "moments" if mom else "zeroth"
+        bsa.recap_dense_attn_tail(desc, q0, k0, v0, c0, i0, s, out, d_lse, d_o, ws_m, moments=mom)
+        acc[f"coarse_tail_{tag}"] = err(bsa.recap_block_sparse_attn_tail(
+            desc, q1, k1, v1, c0, i0, s, None, None, None, ws_m, moments=mom))
+        acc[f"coarse_tail_plus_discrepancy_{tag}"] = err(bsa.recap_block_sparse_attn_tail(
+            desc, q1, k1, v1, c0, i0, s, d_lse, d_o, None, ws_m, moments=mom))
     torch.cuda.synchronize()
-    events = []
-    for _ in range(max(1, args.steps // 2)):
-        run(events)
-    torch.cuda.synchronize()
-    per = {}
-    for name, e0, e1 in events:
-        per.setdefault(name, []).append(e0.elapsed_time(e1))
-    t = {k: float(np.median(v)) for k, v in per.items()}
-    # omitted (query token, key block) pairs of the estimate's kept lists
-    starts = torch.arange(M, device=dev) * blk
-    n_q = (torch.clamp(starts + blk, max=N) - starts).double()
-    omitted = ((M - counts[1].double()) * n_q).sum().item()
-    est_tflops = 4.0 * D * omitted / (t["estimate"] * 1e-3) / 1e12
-    return {
-        "ms_refresh_call_with_discrepancy": t["refresh"],
-        "ms_sparse_call_with_tail": t["sparse"],
-        "ms_tail_estimate": t["estimate"],
-        "refresh_overhead_ms": t["refresh"] - avg["refresh.attn"],
-        "sparse_overhead_ms": t["sparse"] - avg["sparse.attn"],
-        "n_timed": {k: len(v) for k, v in per.items()},
-        "roofline_estimate": roof("pool + tail_keys + pack + tail_kernel (one recap_tail_estimate "
-                                  "call; algorithmic FLOPs on omitted pairs only)", est_tflops,
-                                  traffic_key="tail"),
-    }
+    res["accuracy_at_drifted_step"] = acc
+    return res
 
 
 def bench_fp8(bsa, cfg, desc, dev_inputs, counts, idxs, s, res, res_scale, avg, sparse_flops,

@@ -37,7 +37,8 @@ class RecapDesc(ctypes.Structure):
 _vp = ctypes.c_void_p
 _dp = ctypes.POINTER(RecapDesc)
 _fp = ctypes.POINTER(ctypes.c_float)
-ABI_VERSION = 6
+ABI_VERSION = 7
+TAIL_MOMENTS = 1
 NOALLOC_SCRATCH_BYTES = 64 << 20
 
 SIGNATURES = {
@@ -62,13 +63,14 @@ SIGNATURES = {
                                                _vp]),
     "recap_topp_mask_cand": (ctypes.c_int, [_dp, _vp, _vp, _vp, _fp, _vp, _vp, _vp, _vp, _vp]),
     "recap_mean_drift": (ctypes.c_int, [_dp, _vp, _vp, _vp, _vp, _vp, _vp]),
-    "recap_tail_estimate": (ctypes.c_int, [_dp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float, _vp,
-                                           _vp, _vp, ctypes.c_size_t, _vp]),
-    "recap_dense_attn_tail": (ctypes.c_int, [_dp, _vp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp,
-                                             _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+    "recap_tail_estimate": (ctypes.c_int, [_dp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float,
+                                           ctypes.c_int, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+    "recap_dense_attn_tail": (ctypes.c_int, [_dp, _vp, _vp, _vp, ctypes.c_float, ctypes.c_int,
+                                             _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
+                                             _vp]),
     "recap_block_sparse_attn_tail": (ctypes.c_int, [_dp, _vp, _vp, _vp, _vp, _vp,
-                                                    ctypes.c_float, _vp, _vp, _vp, _vp,
-                                                    ctypes.c_size_t, _vp]),
+                                                    ctypes.c_float, ctypes.c_int, _vp, _vp, _vp,
+                                                    _vp, ctypes.c_size_t, _vp]),
     "recap_block_sparse_attn_fp8": (ctypes.c_int, [_dp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float,
                                                    _vp, _fp, _vp, _vp, _vp, ctypes.c_size_t,
                                                    _vp]),

@@ -8,6 +8,7 @@ namespace recap {
 
 typedef const __attribute__((address_space(4))) int32_t* cptr_i32;
 typedef const __attribute__((address_space(4))) uint8_t* cptr_u8;
+typedef const __attribute__((address_space(4))) uint32_t* cptr_u32;
 
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -33,7 +34,9 @@ __device__ __forceinline__ void load_lds16(const void* base_uniform, uint32_t vo
       "global_load_lds_dwordx4 %2, %3\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
-      : "s"(lds_dst_uniform), "v"(voff), "s"(base_uniform)
+      // readfirstlane: a no-op for a value the compiler keeps in a scalar register, and a
+      // move back to one where it has merged uniform values into a vector register
+      : "s"(__builtin_amdgcn_readfirstlane(lds_dst_uniform)), "v"(voff), "s"(base_uniform)
       : "memory");
 }
 // 16-byte LDS read at a byte address

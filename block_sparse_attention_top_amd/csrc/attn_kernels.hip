@@ -671,13 +671,19 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RECAP_W
 // Pooled keys as a pair of bf16 values, hi = bf16(K̄) and lo = bf16(K̄ - hi) (about 16
 // significant bits, so the pooled scores are as accurate as the token scores, whose bf16
 // operands are exact), pooled values as bf16. Element e of [B*H][mpad][D]; rows >= M are zero.
+// With the moment refinements, also the per-dimension key variances scaled by s/2 (the factor
+// that makes their product with q^2 the second-order log-mass term once the scores are scaled
+// by s), bf16, in the same layout.
 template <int D>
 __global__ __launch_bounds__(256) void tail_keys_kernel(const float* __restrict__ kbar,
-                                                        const float* __restrict__ vbar, int M,
-                                                        int mpad, int64_t total,
+                                                        const float* __restrict__ vbar,
+                                                        const float* __restrict__ var,
+                                                        float var_scale, int M, int mpad,
+                                                        int64_t total,
                                                         bf16_t* __restrict__ kb_hi,
                                                         bf16_t* __restrict__ kb_lo,
-                                                        bf16_t* __restrict__ vb16) {
+                                                        bf16_t* __restrict__ vb16,
+                                                        bf16_t* __restrict__ sv16) {
   for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total;
        e += (int64_t)gridDim.x * 256) {
     const int64_t bh = e / ((int64_t)mpad * D);
@@ -689,19 +695,163 @@ __global__ __launch_bounds__(256) void tail_keys_kernel(const float* __restrict_
     kb_hi[e] = hi;
     kb_lo[e] = (bf16_t)(kx - (float)hi);
     vb16[e] = (bf16_t)(j < M ? vbar[src] : 0.f);
+    if (var != nullptr) sv16[e] = (bf16_t)(j < M ? var_scale * var[src] : 0.f);
   }
 }
 
+// Kept lists -> one bitmap row per query block (bit j set: key block j kept), wbits words with
+// the last one zero, so that a 64-key tile's two words can always be read.
+__global__ __launch_bounds__(64) void kept_bits_kernel(const int32_t* __restrict__ count,
+                                                       const int32_t* __restrict__ idx, int M,
+                                                       int wbits, uint32_t* __restrict__ bits) {
+  __shared__ uint32_t w[kMaxBlocks / 32 + 1];
+  const int64_t row = blockIdx.x;
+  for (int i = threadIdx.x; i < wbits; i += 64) w[i] = 0u;
+  __syncthreads();
+  const int cnt = min(max(count[row], 0), M);
+  for (int c = threadIdx.x; c < cnt; c += 64) {
+    const int jj = min(max(idx[row * M + c], 0), M - 1);
+    atomicOr(&w[jj >> 5], 1u << (jj & 31));
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < wbits; i += 64) bits[row * wbits + i] = w[i];
+}
+
+// ------------------------------------------------------------------------------------------
+// Moment statistics of the key and value blocks for the refined coarse tail (paperpeel.com
+// RECAP Sec. 3.2: key variance refines the block log-mass at second order, the pooled
+// value-key covariance refines the value at first order). Work-group = (b*h, slice of
+// kStatSlice key blocks). Per block, thread (d, part) takes dimension d over a part of the
+// block's tokens: it sums the squared deviations of the keys from the block mean (fp32, then
+// a reduction over the parts in LDS: the per-dimension variance, population form) and writes
+// the centred keys and values, bf16, transposed into LDS ([dim][token], rows padded by 16
+// bytes). The four wavefronts then add the block's (v - V̄)(k - K̄)^T to a D x D accumulator
+// with bf16 MFMA 32x32x16 (A: value rows, B: key rows, contraction over the tokens; wave w
+// owns value rows 32w.. at D = 128, one 32 x 32 tile at D = 64). The slice's sum is written
+// as one fp32 partial; tail_cov_reduce_kernel adds the slices.
+// ------------------------------------------------------------------------------------------
+template <int D, int BLK>
+__global__ __launch_bounds__(256) void tail_stats_kernel(const bf16_t* __restrict__ k,
+                                                         const bf16_t* __restrict__ v,
+                                                         Strides st, int H, int N, int M,
+                                                         int nslice,
+                                                         const float* __restrict__ kbar,
+                                                         const float* __restrict__ vbar,
+                                                         float* __restrict__ var,
+                                                         float* __restrict__ cov_part) {
+  constexpr int PARTS = 256 / D;      // token parts per dimension
+  constexpr int TP = BLK / PARTS;     // tokens per thread
+  constexpr int RS = BLK + 8;         // LDS row stride (bf16 elements)
+  constexpr int TILES = D == 128 ? 4 : 1;  // 32 x 32 output tiles per wavefront
+  __shared__ __align__(16) bf16_t kt[D * RS];
+  __shared__ __align__(16) bf16_t vt[D * RS];
+  __shared__ float vpart[PARTS][D];
+  const int bh = blockIdx.x / nslice, slice = blockIdx.x - bh * nslice;
+  const int b = bh / H, h = bh - b * H;
+  const bf16_t* kp = k + b * st.b + h * st.h;
+  const bf16_t* vp = v + b * st.b + h * st.h;
+  const int d = threadIdx.x % D, part = threadIdx.x / D;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 31, half = lane >> 5;
+  // output tiles of this wavefront: (row tile, column tile)
+  const int rt = D == 128 ? wave : wave >> 1;
+  f32x16 acc[TILES];
+#pragma unroll
+  for (int c = 0; c < TILES; ++c) acc[c] = f32x16{};
+  const int j0 = slice * kStatSlice, j1 = min(M, j0 + kStatSlice);
+  for (int j = j0; j < j1; ++j) {
+    const int t0 = j * BLK, nj = min(BLK, N - t0);
+    const float km = kbar[((int64_t)bh * M + j) * D + d];
+    const float vm = vbar[((int64_t)bh * M + j) * D + d];
+    float sq = 0.f;
+#pragma unroll
+    for (int g = 0; g < TP / 8; ++g) {
+      bf16x8 kw, vw;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int u = part * TP + g * 8 + e;
+        float kx = 0.f, vx = 0.f;
+        if (u < nj) {
+          kx = (float)kp[(int64_t)(t0 + u) * st.n + d] - km;
+          vx = (float)vp[(int64_t)(t0 + u) * st.n + d] - vm;
+        }
+        sq += kx * kx;
+        kw[e] = (bf16_t)kx;
+        vw[e] = (bf16_t)vx;
+      }
+      *reinterpret_cast<bf16x8*>(&kt[d * RS + part * TP + g * 8]) = kw;
+      *reinterpret_cast<bf16x8*>(&vt[d * RS + part * TP + g * 8]) = vw;
+    }
+    vpart[part][d] = sq;
+    __syncthreads();
+    if (part == 0) {
+      float tot = 0.f;
+#pragma unroll
+      for (int q = 0; q < PARTS; ++q) tot += vpart[q][d];
+      var[((int64_t)bh * M + j) * D + d] = tot / (float)nj;
+    }
+#pragma unroll
+    for (int ks = 0; ks < BLK / 16; ++ks) {
+      const int u0 = ks * 16 + half * 8;
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&vt[(rt * 32 + n) * RS + u0]);
+#pragma unroll
+      for (int c = 0; c < TILES; ++c) {
+        const int ct = D == 128 ? c : (wave & 1);
+        const bf16x8 bb = *reinterpret_cast<const bf16x8*>(&kt[(ct * 32 + n) * RS + u0]);
+        acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bb, acc[c], 0, 0, 0);
+      }
+    }
+    __syncthreads();  // LDS rows and vpart are rewritten by the next block
+  }
+  float* dst = cov_part + ((int64_t)bh * nslice + slice) * D * D;
+#pragma unroll
+  for (int c = 0; c < TILES; ++c) {
+    const int ct = D == 128 ? c : (wave & 1);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = rt * 32 + ((r >> 2) << 3) + half * 4 + (r & 3);  // value dimension
+      dst[row * D + ct * 32 + n] = acc[c][r];
+    }
+  }
+}
+
+// x = scale * (sum over the slices of cov_part[bh][slice][r][c]), written as a bf16 pair:
+// cov16[e] = bf16(x) and cov16[total + e] = bf16(x - bf16(x)) (about 16 significant bits)
 template <int D>
+__global__ __launch_bounds__(256) void tail_cov_reduce_kernel(const float* __restrict__ cov_part,
+                                                              int nslice, float scale,
+                                                              int64_t total,
+                                                              bf16_t* __restrict__ cov16) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= total) return;
+  const int64_t bh = e / (D * D), rc = e - bh * (D * D);
+  const float* src = cov_part + bh * nslice * D * D + rc;
+  float acc = 0.f;
+  for (int sl = 0; sl < nslice; ++sl) acc += src[(int64_t)sl * D * D];
+  const float x = scale * acc;
+  const bf16_t hi = (bf16_t)x;
+  cov16[e] = hi;
+  cov16[total + e] = (bf16_t)(x - (float)hi);
+}
+
+// MOM: the moment refinements. The block log-mass gains (s^2/2) sum_d q_d^2 Var_j(k_d): one
+// more product per tile, of bf16(q^2) (held in registers like the Q fragments) with the
+// scaled variances (an LDS tile loaded with the pooled keys), added to the same score
+// accumulators; the output gains s C q, computed after the loop as C Q^T from two (D = 128) or
+// one (D = 64) 64-row tiles of the scaled covariance loaded into the pooled-key buffers.
+// Kept blocks come from bitmap rows in global memory (two words per tile, read through the
+// scalar cache), which leaves LDS to the tiles: 80 KB with the variance tile at D = 128, two
+// work-groups per CU.
+template <int D, bool MOM>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void tail_kernel(TailParams p) {
   constexpr int NW = 4, QROWS = 128, TB = Tiles<D, NW>::TILE_BYTES;
-  // K̄ hi and lo: one stage, the next tile's loads issued as soon as this tile's QK^T products
-  // have read it; V̄^T: two stages, the next tile's loads issued at the top of each step.
-  // 64 KB at D = 128, so two work-groups share a CU.
+  // K̄ hi and lo (and the variance tile): one stage, the next tile's loads issued as soon as
+  // this tile's QK^T products have read it; V̄^T: two stages, the next tile's loads issued at
+  // the top of each step.
   __shared__ __align__(256) unsigned char kbuf[TB];
   __shared__ __align__(256) unsigned char klbuf[TB];
   __shared__ __align__(256) unsigned char vbuf[2 * TB];
-  __shared__ uint32_t kept_bits[2][kMaxBlocks / 32];
+  __shared__ __align__(256) unsigned char sbuf[MOM ? TB : 256];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 31, half = lane >> 5;
@@ -713,30 +863,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   LaneConsts<D, NW> lc;
   lc.init(lane, wave, (int64_t)D, p.mpad);
   bf16x8 qf[D / 16];
+  bf16x8 q2f[MOM ? D / 16 : 1];
   {
     const bf16_t* src = p.q + base + (int64_t)min(qrow, p.N - 1) * p.st.n + half * 8;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(src + ks * 16);
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) asm volatile("" ::"v"(qf[ks]));
-  }
-  // kept-block bitmaps of the query blocks of this work-group
-  const int nb = QROWS / p.block;  // 2 for block 64, 1 for block 128
-  for (int w = threadIdx.x; w < nb * kMaxBlocks / 32; w += NW * 64)
-    kept_bits[w / (kMaxBlocks / 32)][w % (kMaxBlocks / 32)] = 0u;
-  __syncthreads();
-  for (int lb = 0; lb < nb; ++lb) {
-    const int blk = (qi * QROWS) / p.block + lb;
-    if (blk >= p.M) break;
-    const int64_t row = (int64_t)bh * p.M + blk;
-    const int cnt = min(max(p.count[row], 0), p.M);
-    for (int c = threadIdx.x; c < cnt; c += NW * 64) {
-      const int jj = min(max(p.idx[row * p.M + c], 0), p.M - 1);
-      atomicOr(&kept_bits[lb][jj >> 5], 1u << (jj & 31));
+    if constexpr (MOM) {
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x = (float)qf[ks][e];
+          q2f[ks][e] = (bf16_t)(x * x);
+        }
     }
   }
-  __syncthreads();
-  const uint32_t* own = kept_bits[(wave * 32) / p.block];
+  // this wavefront's kept-block bitmap row (its query block; rows past the last block clamp)
+  const int blk = min((qi * QROWS + wave * 32) / p.block, p.M - 1);
+  const cptr_u32 own = (cptr_u32)(p.bits + ((int64_t)bh * p.M + blk) * p.wbits);
 
   f32x16 o[D / 32];
 #pragma unroll
@@ -744,13 +890,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   SoftmaxState sm{-INFINITY, 0.f};
   KeptAcc<D> none;
   const uint32_t kb0 = lds_base(kbuf), kl0 = lds_base(klbuf), vb0 = lds_base(vbuf);
+  const uint32_t sb0 = MOM ? lds_base(sbuf) : 0u;
   const bf16_t* kp = p.kb + (int64_t)bh * p.mpad * D;
   const bf16_t* klp = p.kb_lo + (int64_t)bh * p.mpad * D;
+  const bf16_t* svp = MOM ? p.sv + (int64_t)bh * p.mpad * D : nullptr;
   const bf16_t* vtp = p.vt + (int64_t)bh * D * p.mpad;
   const int ntile = (p.M + kKeyTile - 1) / kKeyTile;
   issue_v<D, NW>(vb0, vtp, p.mpad, 0, wave, lc);
   issue_k<D, NW>(kb0, kp, (int64_t)D, p.M, 0, wave, lane, lc);
   issue_k<D, NW>(kl0, klp, (int64_t)D, p.M, 0, wave, lane, lc);
+  if constexpr (MOM) issue_k<D, NW>(sb0, svp, (int64_t)D, p.M, 0, wave, lane, lc);
   for (int t = 0; t < ntile; ++t) {
     const int key0 = t * kKeyTile;
     const uint32_t vt = vb0 + (t & 1) * TB;
@@ -762,15 +911,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     f32x16 s0, s1;
     tile_qk<D, NW>(kb0, qf, lc, s0, s1);
     tile_qk<D, NW, true>(kl0, qf, lc, s0, s1);  // + q . (K̄ - hi)
+    if constexpr (MOM) tile_qk<D, NW, true>(sb0, q2f, lc, s0, s1);  // + q^2 . (s/2) Var
     lds_barrier();  // every wavefront has read K̄ of tile t
     if (t + 1 < ntile) {
       issue_k<D, NW>(kb0, kp, (int64_t)D, p.M, key0 + kKeyTile, wave, lane, lc);
       issue_k<D, NW>(kl0, klp, (int64_t)D, p.M, key0 + kKeyTile, wave, lane, lc);
+      if constexpr (MOM) issue_k<D, NW>(sb0, svp, (int64_t)D, p.M, key0 + kKeyTile, wave, lane, lc);
     }
     // scores in log2 units; kept blocks and pooled keys past M get -inf, the last pooled key
     // the log2 of its share of a full block. Keys key0 + kr and key0 + 32 + kr are bit kr of
-    // words key0 / 32 and key0 / 32 + 1 of the kept bitmap (key0 is a multiple of 64; a word
-    // past the bitmap's end only holds keys >= M, masked anyway).
+    // words key0 / 32 and key0 / 32 + 1 of the kept bitmap (key0 is a multiple of 64; the
+    // row's last word is zero, and every bit past M is masked anyway).
     const uint32_t w0 = own[key0 >> 5], w1 = own[(key0 >> 5) + 1];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -791,10 +942,49 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     tile_pv<D, NW>(vt, pf, lc, o, none, false);
   }
   const float lt = cross_half_sum(sm.l);
+  const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+  if constexpr (MOM) {
+    // value compensation s C q: C (scaled by s/N) as a bf16 pair hi + lo, in 64-row tiles, in
+    // the pooled-key and variance buffers (no wavefront reads them after the last tile's
+    // second barrier) and, at D = 128, in the V̄ stage the last tile did not use (every
+    // wavefront finished reading it before the last tile's first barrier)
+    const bf16_t* cp = p.cov + (int64_t)bh * D * D;
+    const bf16_t* cpl = cp + (int64_t)p.BH * D * D;
+    const uint32_t free_v = vb0 + (((ntile - 1) & 1) ^ 1) * TB;
+    issue_k<D, NW>(kb0, cp, (int64_t)D, D, 0, wave, lane, lc);
+    issue_k<D, NW>(kl0, cpl, (int64_t)D, D, 0, wave, lane, lc);
+    if (D == 128) {
+      issue_k<D, NW>(sb0, cp, (int64_t)D, D, 64, wave, lane, lc);
+      issue_k<D, NW>(free_v, cpl, (int64_t)D, D, 64, wave, lane, lc);
+    }
+    wait_vmem<0>();
+    lds_barrier();
+    f32x16 c0, c1;
+    tile_qk<D, NW>(kb0, qf, lc, c0, c1);
+    tile_qk<D, NW, true>(kl0, qf, lc, c0, c1);
+    if (lt > 0.f) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        o[0][r] = o[0][r] * inv + c0[r];
+        o[1][r] = o[1][r] * inv + c1[r];
+      }
+    }
+    if constexpr (D == 128) {
+      tile_qk<D, NW>(sb0, qf, lc, c0, c1);
+      tile_qk<D, NW, true>(free_v, qf, lc, c0, c1);
+      if (lt > 0.f) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          o[2][r] = o[2][r] * inv + c0[r];
+          o[3][r] = o[3][r] * inv + c1[r];
+        }
+      }
+    }
+  }
   if (qrow >= p.N) return;
   const int64_t srow = (int64_t)bh * p.N + qrow;
   if (half == 0) p.tail_lse[srow] = lt > 0.f ? (sm.m + log2f(lt)) * kLn2 + p.ln_block : -INFINITY;
-  const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+  const float scale_out = MOM ? (lt > 0.f ? 1.0f : 0.f) : inv;  // MOM: already normalised
   float* to = p.tail_o + srow * D;
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) {
@@ -802,7 +992,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int g = 0; g < 4; ++g) {
       f32x4 x;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) x[e] = o[dt][g * 4 + e] * inv;
+      for (int e = 0; e < 4; ++e) x[e] = o[dt][g * 4 + e] * scale_out;
       *reinterpret_cast<f32x4*>(to + dt * 32 + g * 8 + half * 4) = x;
     }
   }
@@ -859,26 +1049,72 @@ __global__ __launch_bounds__(256) void tail_combine_kernel(int mode, int H, int 
 }
 
 // ------------------------------------------------------------------------------------------
-hipError_t launch_tail_keys(const float* kbar, const float* vbar, int BH, int M, int D, int mpad,
-                            bf16_t* kb_hi, bf16_t* kb_lo, bf16_t* vb16, hipStream_t stream) {
+hipError_t launch_tail_keys(const float* kbar, const float* vbar, const float* var,
+                            float var_scale, int BH, int M, int D, int mpad, bf16_t* kb_hi,
+                            bf16_t* kb_lo, bf16_t* vb16, bf16_t* sv16, hipStream_t stream) {
   const int64_t total = (int64_t)BH * mpad * D;
   const int grid = (int)(total < 65536LL * 256 ? (total + 255) / 256 : 65536);
   if (D == 128)
-    tail_keys_kernel<128><<<grid, 256, 0, stream>>>(kbar, vbar, M, mpad, total, kb_hi, kb_lo,
-                                                    vb16);
+    tail_keys_kernel<128><<<grid, 256, 0, stream>>>(kbar, vbar, var, var_scale, M, mpad, total,
+                                                    kb_hi, kb_lo, vb16, sv16);
   else
-    tail_keys_kernel<64><<<grid, 256, 0, stream>>>(kbar, vbar, M, mpad, total, kb_hi, kb_lo,
-                                                   vb16);
+    tail_keys_kernel<64><<<grid, 256, 0, stream>>>(kbar, vbar, var, var_scale, M, mpad, total,
+                                                   kb_hi, kb_lo, vb16, sv16);
+  return hipGetLastError();
+}
+
+hipError_t launch_kept_bits(const int32_t* count, const int32_t* idx, int rows, int M, int wbits,
+                            uint32_t* bits, hipStream_t stream) {
+  kept_bits_kernel<<<rows, 64, 0, stream>>>(count, idx, M, wbits, bits);
+  return hipGetLastError();
+}
+
+hipError_t launch_tail_stats(const bf16_t* k, const bf16_t* v, Strides st, int B, int H, int N,
+                             int D, int block, const float* kbar, const float* vbar, float* var,
+                             float* cov_part, float cov_scale, bf16_t* cov16,
+                             hipStream_t stream) {
+  const int M = (N + block - 1) / block;
+  const int nslice = (M + kStatSlice - 1) / kStatSlice;
+  const int grid = B * H * nslice;
+  if (D == 128) {
+    if (block == 64)
+      tail_stats_kernel<128, 64><<<grid, 256, 0, stream>>>(k, v, st, H, N, M, nslice, kbar,
+                                                           vbar, var, cov_part);
+    else
+      tail_stats_kernel<128, 128><<<grid, 256, 0, stream>>>(k, v, st, H, N, M, nslice, kbar,
+                                                            vbar, var, cov_part);
+  } else {
+    if (block == 64)
+      tail_stats_kernel<64, 64><<<grid, 256, 0, stream>>>(k, v, st, H, N, M, nslice, kbar, vbar,
+                                                          var, cov_part);
+    else
+      tail_stats_kernel<64, 128><<<grid, 256, 0, stream>>>(k, v, st, H, N, M, nslice, kbar,
+                                                           vbar, var, cov_part);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t total = (int64_t)B * H * D * D;
+  const int rgrid = (int)((total + 255) / 256);
+  if (D == 128)
+    tail_cov_reduce_kernel<128><<<rgrid, 256, 0, stream>>>(cov_part, nslice, cov_scale, total,
+                                                           cov16);
+  else
+    tail_cov_reduce_kernel<64><<<rgrid, 256, 0, stream>>>(cov_part, nslice, cov_scale, total,
+                                                          cov16);
   return hipGetLastError();
 }
 
 hipError_t launch_tail(TailParams p, int B, int D, hipStream_t stream) {
   p.mq = (p.N + 127) / 128;
   const int grid = B * p.H * p.mq;
-  if (D == 128)
-    tail_kernel<128><<<grid, 256, 0, stream>>>(p);
-  else
-    tail_kernel<64><<<grid, 256, 0, stream>>>(p);
+  const bool mom = p.sv != nullptr;
+  if (D == 128) {
+    if (mom) tail_kernel<128, true><<<grid, 256, 0, stream>>>(p);
+    else tail_kernel<128, false><<<grid, 256, 0, stream>>>(p);
+  } else {
+    if (mom) tail_kernel<64, true><<<grid, 256, 0, stream>>>(p);
+    else tail_kernel<64, false><<<grid, 256, 0, stream>>>(p);
+  }
   return hipGetLastError();
 }
 

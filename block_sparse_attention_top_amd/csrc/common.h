@@ -105,14 +105,32 @@ struct TailParams {
   float scale_log2;
   float last_bias;     // added to the log2-unit score of pooled key M-1: log2(n_last / block)
   float ln_block;      // ln(block): each pooled key stands for `block` tokens
-  const int32_t* count;
-  const int32_t* idx;
+  const uint32_t* bits; // kept-block bitmaps [B*H][M][wbits] (bit j of row i: j kept)
+  int wbits;            // words per bitmap row: ceil(M / 32) + 1 (the last one zero)
   float* tail_lse;     // [B*H][N]
   float* tail_o;       // [B*H][N][D]
+  // moment refinements (null when off)
+  const bf16_t* sv;    // (s/2) * per-dimension key variance, bf16 [B*H][mpad][D], rows >= M 0
+  const bf16_t* cov;   // (s/N) * pooled value-key covariance as a bf16 pair: hi [B*H][D][D]
+                       // (row: value dim), then lo in the same layout
+  int BH;              // B * H (offset of the lo half of cov)
 };
-hipError_t launch_tail_keys(const float* kbar, const float* vbar, int BH, int M, int D, int mpad,
-                            bf16_t* kb_hi, bf16_t* kb_lo, bf16_t* vb16, hipStream_t stream);
+hipError_t launch_tail_keys(const float* kbar, const float* vbar, const float* var,
+                            float var_scale, int BH, int M, int D, int mpad, bf16_t* kb_hi,
+                            bf16_t* kb_lo, bf16_t* vb16, bf16_t* sv16, hipStream_t stream);
 hipError_t launch_tail(TailParams p, int B, int D, hipStream_t stream);
+// Kept lists -> bitmaps [B*H*M][wbits] (wbits = ceil(M/32) + 1 words, the last one zero).
+hipError_t launch_kept_bits(const int32_t* count, const int32_t* idx, int rows, int M, int wbits,
+                            uint32_t* bits, hipStream_t stream);
+// Moment statistics of the key/value blocks: per-dimension key variance var [B*H][M][D] and
+// the pooled within-block value-key covariance, as per-slice partial sums
+// cov_part [B*H][nslice][D][D], reduced to cov16 = cov_scale * sum as a bf16 pair (hi
+// [B*H][D][D], then lo).
+constexpr int kStatSlice = 32;  // key blocks per slice of the covariance sums
+hipError_t launch_tail_stats(const bf16_t* k, const bf16_t* v, Strides st, int B, int H, int N,
+                             int D, int block, const float* kbar, const float* vbar, float* var,
+                             float* cov_part, float cov_scale, bf16_t* cov16,
+                             hipStream_t stream);
 // mode 0: d = exact - coarse (d_lse [B*H][N], d_o [B*H][N][D], fp32);
 // mode 1: out (bf16, q layout) = merge of the fp32 sparse output (log-mass lse_s) with the
 // tail (coarse + d, d optional)

@@ -82,9 +82,24 @@ size_t row_bytes(const recap_desc* d) {
 size_t row_d_bytes(const recap_desc* d) {
   return align_up((size_t)d->batch * d->heads * d->seq * d->head_dim * sizeof(float));
 }
-// K̄, V̄ (fp32), K̄ hi and lo, V̄ (bf16), packed V̄^T (bf16)
+// kept-block bitmaps of the coarse tail: wbits words per query block (the last one zero)
+inline int bit_words(const recap_desc* d) { return (num_blocks(d) + 31) / 32 + 1; }
+size_t bits_bytes(const recap_desc* d) {
+  return align_up((size_t)d->batch * d->heads * num_blocks(d) * bit_words(d) * 4);
+}
+// moment refinements: per-slice covariance partial sums (fp32) and the reduced covariance (bf16)
+inline int stat_slices(const recap_desc* d) { return (num_blocks(d) + kStatSlice - 1) / kStatSlice; }
+size_t cov_part_bytes(const recap_desc* d) {
+  return align_up((size_t)d->batch * d->heads * stat_slices(d) * d->head_dim * d->head_dim * 4);
+}
+size_t cov16_bytes(const recap_desc* d) {  // hi and lo halves
+  return align_up((size_t)d->batch * d->heads * d->head_dim * d->head_dim * 2 * 2);
+}
+// K̄, V̄ (fp32), K̄ hi and lo, V̄ (bf16), packed V̄^T (bf16), the kept bitmaps, and for the
+// moment refinements the key variances (fp32), their scaled bf16 copy and the covariance
 size_t tail_estimate_bytes(const recap_desc* d) {
-  return 2 * pooled_bytes(d) + 4 * pooled16_bytes(d);
+  return 2 * pooled_bytes(d) + 4 * pooled16_bytes(d) + bits_bytes(d) + pooled_bytes(d) +
+         pooled16_bytes(d) + cov_part_bytes(d) + cov16_bytes(d);
 }
 // V^T; one attention part (log-sum-exp, fp32 output); the coarse tail (same); the estimate
 size_t tail_merge_bytes(const recap_desc* d) {
@@ -549,8 +564,8 @@ constexpr double kLog2eD = 1.4426950408889634;
 // Coarse tail over each query block's omitted key blocks (log-mass c_lse [B*H][N], output c_o
 // [B*H][N][D], fp32) from the block means of k and v; tws: tail_estimate_bytes(d) of workspace.
 hipError_t coarse_tail(const recap_desc* d, const void* q, const void* k, const void* v,
-                       const int32_t* count, const int32_t* idx, float sm_scale, float* c_lse,
-                       float* c_o, void* tws, hipStream_t st) {
+                       const int32_t* count, const int32_t* idx, float sm_scale, bool moments,
+                       float* c_lse, float* c_o, void* tws, hipStream_t st) {
   const int M = num_blocks(d), mpad = pooled_pad(d), H = d->heads, D = d->head_dim;
   char* w = (char*)tws;
   float* kbar = (float*)w;
@@ -560,10 +575,23 @@ hipError_t coarse_tail(const recap_desc* d, const void* q, const void* k, const 
   bf16_t* kb_lo = (bf16_t*)(w16 + pooled16_bytes(d));
   bf16_t* vb16 = (bf16_t*)(w16 + 2 * pooled16_bytes(d));
   bf16_t* vt = (bf16_t*)(w16 + 3 * pooled16_bytes(d));
+  char* wm = w16 + 4 * pooled16_bytes(d);
+  uint32_t* bits = (uint32_t*)wm;
+  float* var = (float*)(wm + bits_bytes(d));
+  bf16_t* sv16 = (bf16_t*)(wm + bits_bytes(d) + pooled_bytes(d));
+  float* cov_part = (float*)(wm + bits_bytes(d) + pooled_bytes(d) + pooled16_bytes(d));
+  bf16_t* cov16 = (bf16_t*)((char*)cov_part + cov_part_bytes(d));
   hipError_t e = launch_pool((const bf16_t*)k, (const bf16_t*)v, strides_of(d), d->batch, H,
                              d->seq, D, d->block, kbar, vbar, st);
+  if (e == hipSuccess && moments)
+    e = launch_tail_stats((const bf16_t*)k, (const bf16_t*)v, strides_of(d), d->batch, H,
+                          d->seq, D, d->block, kbar, vbar, var, cov_part,
+                          (float)((double)sm_scale / d->seq), cov16, st);
   if (e == hipSuccess)
-    e = launch_tail_keys(kbar, vbar, d->batch * H, M, D, mpad, kb_hi, kb_lo, vb16, st);
+    e = launch_tail_keys(kbar, vbar, moments ? var : nullptr, 0.5f * sm_scale, d->batch * H, M,
+                         D, mpad, kb_hi, kb_lo, vb16, sv16, st);
+  if (e == hipSuccess)
+    e = launch_kept_bits(count, idx, d->batch * H * M, M, bit_words(d), bits, st);
   if (e == hipSuccess) {
     const Strides ps{(int64_t)H * mpad * D, (int64_t)mpad * D, (int64_t)D};
     e = launch_pack_vt(vb16, ps, d->batch, H, M, D, mpad, vt, st);
@@ -585,17 +613,20 @@ hipError_t coarse_tail(const recap_desc* d, const void* q, const void* k, const 
   const int n_last = d->seq - (M - 1) * d->block;
   p.last_bias = (float)log2((double)n_last / d->block);
   p.ln_block = (float)log((double)d->block);
-  p.count = count;
-  p.idx = idx;
+  p.bits = bits;
+  p.wbits = bit_words(d);
   p.tail_lse = c_lse;
   p.tail_o = c_o;
+  p.sv = moments ? sv16 : nullptr;
+  p.cov = moments ? cov16 : nullptr;
+  p.BH = d->batch * H;
   return launch_tail(p, d->batch, D, st);
 }
 
-// Shared validation of the tail entry points: q, k, v, kept lists, scale, workspace, device.
+// Shared validation of the tail entry points: q, k, v, kept lists, scale, flags, workspace.
 int check_tail_args(int op, const recap_desc* d, const void* q, const void* k, const void* v,
-                    const int32_t* count, const int32_t* idx, float sm_scale, const void* ws,
-                    size_t ws_bytes) {
+                    const int32_t* count, const int32_t* idx, float sm_scale, int flags,
+                    const void* ws, size_t ws_bytes) {
   int s = validate_desc(d);
   if (s != RECAP_OK) return s;
   if (q == nullptr || k == nullptr || v == nullptr || count == nullptr || idx == nullptr)
@@ -603,6 +634,7 @@ int check_tail_args(int op, const recap_desc* d, const void* q, const void* k, c
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(count) || !aligned16(idx))
     return RECAP_E_ALIGN;
   if (!isfinite(sm_scale) || !(sm_scale > 0.f)) return RECAP_E_VALUE;
+  if ((flags & ~RECAP_TAIL_MOMENTS) != 0) return RECAP_E_VALUE;
   return check_workspace(op, d, ws, ws_bytes);
 }
 
@@ -652,25 +684,26 @@ extern "C" {
 
 int recap_tail_estimate(const recap_desc* d, const void* q, const void* k, const void* v,
                         const int32_t* kept_count, const int32_t* kept_idx, float sm_scale,
-                        float* tail_lse, float* tail_out, void* ws, size_t ws_bytes,
+                        int flags, float* tail_lse, float* tail_out, void* ws, size_t ws_bytes,
                         void* stream) {
-  int s = check_tail_args(RECAP_OP_TAIL, d, q, k, v, kept_count, kept_idx, sm_scale, ws,
+  int s = check_tail_args(RECAP_OP_TAIL, d, q, k, v, kept_count, kept_idx, sm_scale, flags, ws,
                           ws_bytes);
   if (s != RECAP_OK) return s;
   if (tail_lse == nullptr || tail_out == nullptr) return RECAP_E_NULL;
   if (!aligned16(tail_lse) || !aligned16(tail_out)) return RECAP_E_ALIGN;
   if ((void*)tail_lse == (void*)tail_out) return RECAP_E_VALUE;
   if ((s = check_device()) != RECAP_OK) return s;
-  return launched(coarse_tail(d, q, k, v, kept_count, kept_idx, sm_scale, tail_lse, tail_out,
-                              ws, (hipStream_t)stream));
+  return launched(coarse_tail(d, q, k, v, kept_count, kept_idx, sm_scale,
+                              (flags & RECAP_TAIL_MOMENTS) != 0, tail_lse, tail_out, ws,
+                              (hipStream_t)stream));
 }
 
 int recap_dense_attn_tail(const recap_desc* d, const void* q, const void* k, const void* v,
-                          float sm_scale, const int32_t* kept_count, const int32_t* kept_idx,
-                          void* out, float* tail_dlse, float* tail_dout, void* ws,
-                          size_t ws_bytes, void* stream) {
-  int s = check_tail_args(RECAP_OP_DENSE_TAIL, d, q, k, v, kept_count, kept_idx, sm_scale, ws,
-                          ws_bytes);
+                          float sm_scale, int flags, const int32_t* kept_count,
+                          const int32_t* kept_idx, void* out, float* tail_dlse,
+                          float* tail_dout, void* ws, size_t ws_bytes, void* stream) {
+  int s = check_tail_args(RECAP_OP_DENSE_TAIL, d, q, k, v, kept_count, kept_idx, sm_scale,
+                          flags, ws, ws_bytes);
   if (s != RECAP_OK) return s;
   if (out == nullptr || tail_dlse == nullptr || tail_dout == nullptr) return RECAP_E_NULL;
   if (!aligned16(out) || !aligned16(tail_dlse) || !aligned16(tail_dout)) return RECAP_E_ALIGN;
@@ -693,7 +726,8 @@ int recap_dense_attn_tail(const recap_desc* d, const void* q, const void* k, con
   p.tail_o = t.a_o;
   e = launch_attention(p, d->batch, d->head_dim, kDenseTail, st);
   if (e == hipSuccess)
-    e = coarse_tail(d, q, k, v, kept_count, kept_idx, sm_scale, t.c_lse, t.c_o, t.est, st);
+    e = coarse_tail(d, q, k, v, kept_count, kept_idx, sm_scale,
+                    (flags & RECAP_TAIL_MOMENTS) != 0, t.c_lse, t.c_o, t.est, st);
   if (e == hipSuccess)
     e = launch_tail_combine(0, d->batch, d->heads, d->seq, d->head_dim, strides_of(d), t.a_lse,
                             t.a_o, t.c_lse, t.c_o, nullptr, nullptr, tail_dlse, tail_dout,
@@ -703,11 +737,11 @@ int recap_dense_attn_tail(const recap_desc* d, const void* q, const void* k, con
 
 int recap_block_sparse_attn_tail(const recap_desc* d, const void* q, const void* k,
                                  const void* v, const int32_t* kept_count,
-                                 const int32_t* kept_idx, float sm_scale,
+                                 const int32_t* kept_idx, float sm_scale, int flags,
                                  const float* tail_dlse_opt, const float* tail_dout_opt,
                                  void* out, void* ws, size_t ws_bytes, void* stream) {
-  int s = check_tail_args(RECAP_OP_SPARSE_TAIL, d, q, k, v, kept_count, kept_idx, sm_scale, ws,
-                          ws_bytes);
+  int s = check_tail_args(RECAP_OP_SPARSE_TAIL, d, q, k, v, kept_count, kept_idx, sm_scale,
+                          flags, ws, ws_bytes);
   if (s != RECAP_OK) return s;
   if (out == nullptr) return RECAP_E_NULL;
   if ((tail_dlse_opt == nullptr) != (tail_dout_opt == nullptr)) return RECAP_E_NULL;
@@ -731,7 +765,8 @@ int recap_block_sparse_attn_tail(const recap_desc* d, const void* q, const void*
   p.lse_out = t.a_lse;
   e = launch_attention(p, d->batch, d->head_dim, kSparse, st);
   if (e == hipSuccess)
-    e = coarse_tail(d, q, k, v, kept_count, kept_idx, sm_scale, t.c_lse, t.c_o, t.est, st);
+    e = coarse_tail(d, q, k, v, kept_count, kept_idx, sm_scale,
+                    (flags & RECAP_TAIL_MOMENTS) != 0, t.c_lse, t.c_o, t.est, st);
   if (e == hipSuccess)
     e = launch_tail_combine(1, d->batch, d->heads, d->seq, d->head_dim, strides_of(d), t.a_lse,
                             t.a_o, t.c_lse, t.c_o, tail_dlse_opt, tail_dout_opt, nullptr,

@@ -347,9 +347,10 @@ def recap_mean_drift(desc: RecapDesc, qbar, kbar, qbar_ref, kbar_ref, drift=None
 @_on_stream
 def recap_tail_estimate(desc: RecapDesc, q, k, v, kept_count, kept_idx,
                         sm_scale: Optional[float] = None, tail_lse=None, tail_out=None,
-                        workspace=None, stream=None):
+                        workspace=None, stream=None, moments: bool = False):
     """Coarse tail from block means over each query block's omitted key blocks: (tail_lse fp32
-    [B,H,N], tail_out fp32 [B,H,N,D] contiguous)."""
+    [B,H,N], tail_out fp32 [B,H,N,D] contiguous). moments: the key-variance and value-key
+    covariance refinements (RECAP_TAIL_MOMENTS)."""
     _same_layout(desc, q, k, v)
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(desc.head_dim)
@@ -358,7 +359,8 @@ def recap_tail_estimate(desc: RecapDesc, q, k, v, kept_count, kept_idx,
     ws, nbytes = _workspace(_lib.OP_TAIL, desc, q.device, workspace)
     check(_lib.load().recap_tail_estimate(
         ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(kept_count), _ptr(kept_idx),
-        float(sm_scale), _ptr(tail_lse), _ptr(tail_out), _ptr(ws), nbytes, _stream(stream)),
+        float(sm_scale), _lib.TAIL_MOMENTS if moments else 0, _ptr(tail_lse), _ptr(tail_out),
+        _ptr(ws), nbytes, _stream(stream)),
         "recap_tail_estimate")
     return tail_lse, tail_out
 
@@ -375,9 +377,9 @@ def _row_vec(desc: RecapDesc, given: Optional[torch.Tensor], device, what: str):
 @_on_stream
 def recap_dense_attn_tail(desc: RecapDesc, q, k, v, kept_count, kept_idx,
                           sm_scale: Optional[float] = None, out=None, tail_dlse=None,
-                          tail_dout=None, workspace=None, stream=None):
+                          tail_dout=None, workspace=None, stream=None, moments: bool = False):
     """Dense refresh that also writes the tail discrepancy on the kept set: (out bf16,
-    tail_dlse fp32 [B,H,N], tail_dout fp32 [B,H,N,D])."""
+    tail_dlse fp32 [B,H,N], tail_dout fp32 [B,H,N,D]); moments as recap_tail_estimate."""
     _same_layout(desc, q, k, v, out)
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(desc.head_dim)
@@ -386,18 +388,21 @@ def recap_dense_attn_tail(desc: RecapDesc, q, k, v, kept_count, kept_idx,
     tail_dlse = _row_stat(desc, tail_dlse, q.device)
     ws, nbytes = _workspace(_lib.OP_DENSE_TAIL, desc, q.device, workspace)
     check(_lib.load().recap_dense_attn_tail(
-        ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), float(sm_scale), _ptr(kept_count),
-        _ptr(kept_idx), _ptr(out), _ptr(tail_dlse), _ptr(tail_dout), _ptr(ws), nbytes,
-        _stream(stream)), "recap_dense_attn_tail")
+        ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), float(sm_scale),
+        _lib.TAIL_MOMENTS if moments else 0, _ptr(kept_count), _ptr(kept_idx), _ptr(out),
+        _ptr(tail_dlse), _ptr(tail_dout), _ptr(ws), nbytes, _stream(stream)),
+        "recap_dense_attn_tail")
     return out, tail_dlse, tail_dout
 
 
 @_on_stream
 def recap_block_sparse_attn_tail(desc: RecapDesc, q, k, v, kept_count, kept_idx,
                                  sm_scale: Optional[float] = None, tail_dlse=None,
-                                 tail_dout=None, out=None, workspace=None, stream=None):
+                                 tail_dout=None, out=None, workspace=None, stream=None,
+                                 moments: bool = False):
     """Block-sparse attention merged by log-mass with the fresh coarse tail plus the cached
-    discrepancy (both or neither of tail_dlse, tail_dout); bf16 out in q's layout."""
+    discrepancy (both or neither of tail_dlse, tail_dout); bf16 out in q's layout; moments as
+    recap_tail_estimate (the refresh that cached the discrepancy must use the same)."""
     _same_layout(desc, q, k, v, out)
     if (tail_dlse is None) != (tail_dout is None):
         raise ValueError("tail_dlse and tail_dout go together")
@@ -410,8 +415,8 @@ def recap_block_sparse_attn_tail(desc: RecapDesc, q, k, v, kept_count, kept_idx,
     ws, nbytes = _workspace(_lib.OP_SPARSE_TAIL, desc, q.device, workspace)
     check(_lib.load().recap_block_sparse_attn_tail(
         ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(kept_count), _ptr(kept_idx),
-        float(sm_scale), _ptr(tail_dlse), _ptr(tail_dout), _ptr(out), _ptr(ws), nbytes,
-        _stream(stream)), "recap_block_sparse_attn_tail")
+        float(sm_scale), _lib.TAIL_MOMENTS if moments else 0, _ptr(tail_dlse), _ptr(tail_dout),
+        _ptr(out), _ptr(ws), nbytes, _stream(stream)), "recap_block_sparse_attn_tail")
     return out
 
 

@@ -66,7 +66,8 @@
 extern "C" {
 #endif
 
-#define RECAP_ABI_VERSION 6 /* 2: *_stats; 3: mask reuse; 4: coarse tail; 5: FP8; 6: no-alloc scores */
+#define RECAP_ABI_VERSION 7 /* 2: *_stats; 3: mask reuse; 4: coarse tail; 5: FP8; 6: no-alloc scores;
+                             7: tail flags (moment refinements) */
 #define RECAP_MAX_HEADS 128   /* per-head host arrays are passed by value to the kernels */
 #define RECAP_MAX_BLOCKS 8192 /* M = ceil(N / block) upper bound (top-p sorts a row in LDS) */
 /* Size of the fixed device scratch of recap_block_scores_noalloc (64 MiB per device): the
@@ -253,8 +254,22 @@ int recap_mean_drift(const recap_desc* d, const float* qbar, const float* kbar,
  * means, plus the discrepancy d the estimate leaves, taken exactly at a dense refresh and
  * cached; at a sparse step the tail is estimated again and d added (y = coarse + d, whose
  * error d_h - d_t vanishes at the refresh step), and the result is merged with the sparse
- * attention by log-mass. Zeroth order: the page's key-variance and value-key-covariance
- * refinements of the estimate are not applied (their formulas are not on the pages).
+ * attention by log-mass. `flags` selects the estimate: 0 for the zeroth-order block-mean one,
+ * RECAP_TAIL_MOMENTS for the page's two moment refinements (key variance refines the
+ * log-mass at second order, after COBS; the pooled value-key covariance refines the value at
+ * first order, after PISA's shared first-order value compensation; Sec. 3.2 and Sec. 2). The
+ * page gives no formulas; the reading implemented (cumulant expansion about the block mean):
+ *   block log-mass  ln n_j + sm_scale Q_t.K̄_j + (sm_scale^2 / 2) sum_d Q_{t,d}^2 Var_j(k_d)
+ *     with Var_j the per-dimension variance of the block's keys (population form, the diagonal
+ *     of the block's key covariance);
+ *   output          sum_j w_tj V̄_j / sum_j w_tj + sm_scale C Q_t
+ *     with C = (1/N) sum_j sum_{u in j} (v_u - V̄_j)(k_u - K̄_j)^T the pooled within-block
+ *     value-key covariance of the head (rows: value dimension), one matrix for every block.
+ * On the GPU the variance term is one more product per pooled-key tile, of bf16(Q^2) with
+ * bf16((sm_scale / 2) Var) (relative error within 2^-8 of the term), and C Q is a bf16 product
+ * of bf16((sm_scale / N) C) with Q (fp32 statistics and sums). Other flag bits:
+ * RECAP_E_VALUE. A refresh and the sparse steps that use its discrepancy must pass the same
+ * flags.
  *
  * Coarse tail of query token t in query block i, over the key blocks j outside i's kept set,
  * with n_j the token count of block j and K̄_j, V̄_j block means (fp32 pooling; K̄ then held
@@ -281,17 +296,18 @@ int recap_mean_drift(const recap_desc* d, const float* qbar, const float* kbar,
  *   ws: RECAP_OP_SPARSE_TAIL. With the refresh's inputs and kept lists it reproduces the
  *   dense output (up to rounding).
  * Kept lists as for recap_block_sparse_attn (indices clamped into [0, M)). */
+#define RECAP_TAIL_MOMENTS 1 /* flags of the tail entry points: the moment refinements */
 int recap_tail_estimate(const recap_desc* d, const void* q, const void* k, const void* v,
                         const int32_t* kept_count, const int32_t* kept_idx, float sm_scale,
-                        float* tail_lse, float* tail_out, void* ws, size_t ws_bytes,
+                        int flags, float* tail_lse, float* tail_out, void* ws, size_t ws_bytes,
                         void* stream);
 int recap_dense_attn_tail(const recap_desc* d, const void* q, const void* k, const void* v,
-                          float sm_scale, const int32_t* kept_count, const int32_t* kept_idx,
-                          void* out, float* tail_dlse, float* tail_dout, void* ws,
-                          size_t ws_bytes, void* stream);
+                          float sm_scale, int flags, const int32_t* kept_count,
+                          const int32_t* kept_idx, void* out, float* tail_dlse,
+                          float* tail_dout, void* ws, size_t ws_bytes, void* stream);
 int recap_block_sparse_attn_tail(const recap_desc* d, const void* q, const void* k,
                                  const void* v, const int32_t* kept_count,
-                                 const int32_t* kept_idx, float sm_scale,
+                                 const int32_t* kept_idx, float sm_scale, int flags,
                                  const float* tail_dlse_opt, const float* tail_dout_opt,
                                  void* out, void* ws, size_t ws_bytes, void* stream);
 

@@ -128,6 +128,19 @@ def coarse_lse_atol(q, kbar, sm_scale) -> float:
     return ATOL_STAT + score_rounding_bound(q, kbar, sm_scale)
 
 
+def variance_lse_atol(q, var, sm_scale) -> float:
+    """Moment-refined coarse log-mass: the second-order term (s^2 / 2) sum_d q_d^2 Var_jd is
+    formed on the GPU as a bf16 product of bf16(q^2) and bf16((s / 2) Var) with fp32 sums, so
+    each factor carries a relative error of at most U_BF16 and every block's term at most
+    (2 U_BF16 + U_BF16^2) of itself (plus fp32 sums); ln of the summed masses moves by at most
+    the largest such change. Returns that bound over all (t, j)."""
+    worst = 0.0
+    for b in range(q.shape[0]):
+        for h in range(q.shape[1]):
+            worst = max(worst, float(((q[b, h] * q[b, h]) @ var[b, h].T).max()))
+    return 0.5 * float(sm_scale) ** 2 * (2 * U_BF16 + U_BF16 ** 2 + 64 * U_F32) * worst
+
+
 def check_rows_within(got: np.ndarray, ref: np.ndarray, atol, what: str):
     """Per-token values (finite reference) within a per-row or scalar bound."""
     got = np.asarray(got, dtype=np.float64)
@@ -143,14 +156,15 @@ def check_rows_within(got: np.ndarray, ref: np.ndarray, atol, what: str):
 def check_merged(got, ref, w, spread, lse_tol, extra: int, what: str):
     """A log-mass merge out = bf16(w O_s + (1 - w) o_T) of attention-like parts, against the
     oracle's merge. Per row: ATOL_OUT for the convex combination of parts that each meet the
-    attention-output rule (final rounding included), plus ATOL_OUT * (1 - w) for each of
-    `extra` further tail terms whose errors do not cancel (a coarse tail taken at another step
-    than the one it is combined with), plus the weight error: w (1 - w) * (log-mass error
-    lse_tol) * max_d |O_s - o_T| (`spread`). Relative L2 error within RTOL_L2.
-    got, ref: [B,H,N,D]; w, spread: [B,H,N] from the oracle."""
+    attention-output rule, plus the final bf16 rounding of the merged value (U_BF16 |out|; the
+    parts are fp32), plus ATOL_OUT * (1 - w) for each of `extra` further tail terms whose errors
+    do not cancel (a coarse tail taken at another step than the one it is combined with), plus
+    the weight error: w (1 - w) * (log-mass error lse_tol) * max_d |O_s - o_T| (`spread`).
+    Relative L2 error within RTOL_L2. got, ref: [B,H,N,D]; w, spread: [B,H,N] from the oracle."""
     got = np.asarray(got, dtype=np.float64)
     assert np.isfinite(got).all(), f"{what}: non-finite values"
-    bound = ATOL_OUT * (1.0 + extra * (1.0 - w)) + w * (1.0 - w) * lse_tol * spread
+    bound = ATOL_OUT * (1.0 + extra * (1.0 - w)) + w * (1.0 - w) * lse_tol * spread \
+        + U_BF16 * np.abs(ref).max(axis=-1)
     err = np.abs(got - ref).max(axis=-1)
     bad = err > bound
     assert not bad.any(), f"{what}: {int(bad.sum())} rows out of bound; worst excess " \

@@ -36,7 +36,7 @@ def test_header_symbols_exported():
 
 def test_version_and_status_strings():
     lib = _lib.load()
-    assert lib.recap_abi_version() == _lib.ABI_VERSION == 6
+    assert lib.recap_abi_version() == _lib.ABI_VERSION == 7
     for st in list(_lib.STATUS_NAMES) + [-99]:
         s = lib.recap_status_string(st)
         assert s and len(s.decode()) > 1
@@ -67,11 +67,16 @@ def test_workspace_sizes():
     st, n2 = ws_size(_lib.OP_DENSE_CAPTURE, d)
     flags = -(-40 * M // 256) * 256  # one byte per query block, 256-byte aligned
     assert st == 0 and n2 == n + 40 * M * 64 * 128 * 4 + flags
-    # coarse tail: K̄, V̄ fp32, then K̄ hi, K̄ lo, V̄, V̄^T bf16 over M padded to 1216 pooled keys
+    # coarse tail: K̄, V̄ fp32, then K̄ hi, K̄ lo, V̄, V̄^T bf16 over M padded to 1216 pooled keys,
+    # the kept bitmaps (ceil(M / 32) + 1 = 38 words per query block), and for the moment
+    # refinements the key variances (fp32 and a bf16 copy), 37 slices of covariance partial
+    # sums (fp32 D x D) and the covariance (a bf16 pair, D x D each), each 256-byte aligned
     pooled = 40 * M * 128 * 4
     p16 = 40 * 1216 * 128 * 2
+    bits = -(-40 * M * 38 * 4 // 256) * 256
+    mom = pooled + p16 + 40 * 37 * 128 * 128 * 4 + 2 * 40 * 128 * 128 * 2
     st, nt = ws_size(_lib.OP_TAIL, d)
-    assert st == 0 and nt == 2 * pooled + 4 * p16
+    assert st == 0 and nt == 2 * pooled + 4 * p16 + bits + mom
     rows = 40 * 75600 * 4
     for op in (_lib.OP_DENSE_TAIL, _lib.OP_SPARSE_TAIL):
         assert ws_size(op, d) == (0, n + 2 * (rows + rows * 128) + nt)
@@ -239,9 +244,11 @@ def test_tail_validation():
     _, need_m = ws_size(_lib.OP_SPARSE_TAIL, d)
     q, k, v = _p(), _p(FAKE + 1024), _p(FAKE + 2048)
 
-    def est(cnt=_p(), lse=_p(FAKE + 8192), to=_p(FAKE + 16384), n=need_t, s=0.125):
-        return lib.recap_tail_estimate(ctypes.byref(d), q, k, v, cnt, _p(), s, lse, to, _p(), n,
-                                       None)
+    def est(cnt=_p(), lse=_p(FAKE + 8192), to=_p(FAKE + 16384), n=need_t, s=0.125, fl=0):
+        return lib.recap_tail_estimate(ctypes.byref(d), q, k, v, cnt, _p(), s, fl, lse, to, _p(),
+                                       n, None)
+    assert est(fl=2) == -5 and est(fl=-1) == -5  # unknown flag bits
+    assert est(fl=_lib.TAIL_MOMENTS) == -7
     assert est(cnt=None) == -1
     assert est(lse=None) == -1
     assert est(to=_p(FAKE + 16388)) == -4
@@ -250,9 +257,10 @@ def test_tail_validation():
     assert est(n=need_t - 1) == -6
     assert est() == -7
 
-    def dense(out=_p(FAKE + 4096), dl=_p(FAKE + 8192), do=_p(FAKE + 16384), n=need_m):
-        return lib.recap_dense_attn_tail(ctypes.byref(d), q, k, v, 0.125, _p(), _p(), out, dl, do,
-                                         _p(), n, None)
+    def dense(out=_p(FAKE + 4096), dl=_p(FAKE + 8192), do=_p(FAKE + 16384), n=need_m, fl=0):
+        return lib.recap_dense_attn_tail(ctypes.byref(d), q, k, v, 0.125, fl, _p(), _p(), out,
+                                         dl, do, _p(), n, None)
+    assert dense(fl=4) == -5 and dense(fl=1) == -7
     assert dense(dl=None) == -1
     assert dense(do=None) == -1
     assert dense(do=_p(FAKE + 4096)) == -5  # discrepancy aliases out
@@ -261,9 +269,10 @@ def test_tail_validation():
     assert dense(n=need_m - 256) == -6
     assert dense() == -7
 
-    def sparse(dl=None, do=None, out=_p(FAKE + 4096), n=need_m):
-        return lib.recap_block_sparse_attn_tail(ctypes.byref(d), q, k, v, _p(), _p(), 0.125, dl,
-                                                do, out, _p(), n, None)
+    def sparse(dl=None, do=None, out=_p(FAKE + 4096), n=need_m, fl=0):
+        return lib.recap_block_sparse_attn_tail(ctypes.byref(d), q, k, v, _p(), _p(), 0.125, fl,
+                                                dl, do, out, _p(), n, None)
+    assert sparse(fl=3) == -5 and sparse(fl=1) == -7
     assert sparse(dl=_p(FAKE + 8192)) == -1  # both or neither
     assert sparse(do=_p(FAKE + 16384)) == -1
     assert sparse(out=None) == -1

@@ -265,7 +265,7 @@ def test_graph_capture_replays_tail_and_fp8(bsa):
         bsa.recap_block_scores(desc, q1d, k1d, s, probs=probs, workspace=ws[0])
         bsa.recap_topp_mask(desc, probs, p, kept_count=cnt1, kept_idx=idx1)
         bsa.recap_tail_estimate(desc, q1d, k1d, v1d, cnt1, idx1, s, tail_lse=tlse,
-                                tail_out=tout, workspace=ws[5])
+                                tail_out=tout, workspace=ws[5], moments=True)
         bsa.recap_block_sparse_attn_tail(desc, q1d, k1d, v1d, cnt1, idx1, s, tail_dlse=dlse,
                                          tail_dout=dout, out=ot, workspace=ws[7])
         bsa.recap_block_sparse_attn_fp8(desc, q1d, k1d, v1d, cnt1, idx1, s, residual=rd,

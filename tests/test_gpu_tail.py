@@ -58,8 +58,9 @@ TAIL = {
 }
 
 
+@pytest.mark.parametrize("mom", [False, True], ids=["zeroth", "moments"])
 @pytest.mark.parametrize("case", list(TAIL))
-def test_tail_case(bsa, case):
+def test_tail_case(bsa, case, mom):
     kw = dict(TAIL[case])
     seq = kw.pop("seq", None)
     layout = kw.pop("layout", "bhnd")
@@ -74,16 +75,18 @@ def test_tail_case(bsa, case):
     p = p_def if top_p is None else np.broadcast_to(np.asarray(top_p, float), (cfg.heads,))
     s = cfg.head_dim ** -0.5
     say(f"[test] tail {case}: B={cfg.batch} H={cfg.heads} D={cfg.head_dim} N={N} "
-        f"block={cfg.block} layout={layout} p={np.round(p, 3).tolist()}")
+        f"block={cfg.block} layout={layout} p={np.round(p, 3).tolist()} moments={mom}")
     qd, kd, vd, q2d, k2d, v2d = (to_dev(x, layout) for x in (q, k, v, q2, k2, v2))
     desc = bsa.make_desc(qd, cfg.block)
     probs = bsa.recap_block_scores(desc, qd, kd, s)
     count, idx, _, _ = bsa.recap_topp_mask(desc, probs, p.tolist())
-    c_lse, c_o = bsa.recap_tail_estimate(desc, qd, kd, vd, count, idx, s)
-    out_d, d_lse, d_o = bsa.recap_dense_attn_tail(desc, qd, kd, vd, count, idx, s)
-    out_h = bsa.recap_block_sparse_attn_tail(desc, qd, kd, vd, count, idx, s, d_lse, d_o)
-    out_c = bsa.recap_block_sparse_attn_tail(desc, qd, kd, vd, count, idx, s)
-    out_2 = bsa.recap_block_sparse_attn_tail(desc, q2d, k2d, v2d, count, idx, s, d_lse, d_o)
+    c_lse, c_o = bsa.recap_tail_estimate(desc, qd, kd, vd, count, idx, s, moments=mom)
+    out_d, d_lse, d_o = bsa.recap_dense_attn_tail(desc, qd, kd, vd, count, idx, s, moments=mom)
+    out_h = bsa.recap_block_sparse_attn_tail(desc, qd, kd, vd, count, idx, s, d_lse, d_o,
+                                             moments=mom)
+    out_c = bsa.recap_block_sparse_attn_tail(desc, qd, kd, vd, count, idx, s, moments=mom)
+    out_2 = bsa.recap_block_sparse_attn_tail(desc, q2d, k2d, v2d, count, idx, s, d_lse, d_o,
+                                             moments=mom)
     od_cap, _ = bsa.recap_dense_attn(desc, qd, kd, vd, s, count, idx, capture=True)
     o_sp = bsa.recap_block_sparse_attn(desc, qd, kd, vd, count, idx, s)
     torch.cuda.synchronize()
@@ -94,7 +97,7 @@ def test_tail_case(bsa, case):
     gmask = O.mask_from_lists(cnt, ix, M)
     q64, k64, v64 = (synth.to_f64(x) for x in (q, k, v))
     q2_64, k2_64, v2_64 = (synth.to_f64(x) for x in (q2, k2, v2))
-    cl, co = O.coarse_tail(q64, k64, v64, cfg.block, s, gmask)
+    cl, co = O.coarse_tail(q64, k64, v64, cfg.block, s, gmask, moments=mom)
     el, eo = O.exact_tail(q64, k64, v64, cfg.block, s, gmask)
     dl, do = O.tail_discrepancy(el, eo, cl, co)
     ref_d = O.dense_attention(q64, k64, v64, s, block=cfg.block)
@@ -107,6 +110,8 @@ def test_tail_case(bsa, case):
     _check_inf_pattern(g_cl, cl, "coarse lse")
     kbar = O.block_mean_pool(k64, cfg.block)
     tol_c = parity.coarse_lse_atol(q64, kbar, s)
+    if mom:
+        tol_c += parity.variance_lse_atol(q64, O.block_key_variance(k64, cfg.block), s)
     parity.check_rows_within(g_cl, cl, tol_c, "coarse lse")
     parity.check_out(c_o.cpu().numpy().astype(np.float64), co, "coarse output")
 
@@ -133,7 +138,11 @@ def test_tail_case(bsa, case):
                         0, "coarse-only merge")
     o_s2 = O.masked_attention(q2_64, k2_64, v2_64, cfg.block, s, gmask)
     l_s2 = O.attention_lse(q2_64, k2_64, cfg.block, s, gmask)
-    cl2, co2 = O.coarse_tail(q2_64, k2_64, v2_64, cfg.block, s, gmask)
+    cl2, co2 = O.coarse_tail(q2_64, k2_64, v2_64, cfg.block, s, gmask, moments=mom)
+    if mom:  # the drifted step's own variance term
+        tol_c = max(tol_c, parity.coarse_lse_atol(q2_64, O.block_mean_pool(k2_64, cfg.block), s)
+                    + parity.variance_lse_atol(q2_64, O.block_key_variance(k2_64, cfg.block), s))
+        lse_tol = 2 * parity.ATOL_STAT + 2 * tol_c
     # the coarse tails of this step and of the refresh both enter (their errors do not cancel)
     w2, spread2 = _merge_weights(o_s2, l_s2, cl2 + dl, co2 + do)
     parity.check_merged(f64(out_2), O.tail_reconstruction(o_s2, l_s2, cl2, co2, dl, do), w2,
@@ -149,10 +158,12 @@ def _rows_of(blocks, block, n):
     return [(0, 0, i) for i in blocks], [(i * block, min(n, (i + 1) * block)) for i in blocks]
 
 
-def test_full_size_tail(bsa):
+@pytest.mark.parametrize("mom", [False, True], ids=["zeroth", "moments"])
+def test_full_size_tail(bsa, mom):
     """Wan2.1-14B 720p layer (B=1, H=40, D=128, N=75,600, block 64): refresh with the tail
     discrepancy, the reconstruction at the refresh inputs, and a drifted step that reuses the
-    refresh's kept lists and discrepancy; sampled heads and query blocks against the oracle."""
+    refresh's kept lists and discrepancy; sampled heads and query blocks against the oracle;
+    with and without the moment refinements."""
     cfg = synth.WORKLOADS["wan14b_720p"]
     heads = [0, 21]
     say("[test] full-size tail wan14b_720p: generating inputs")
@@ -167,10 +178,12 @@ def test_full_size_tail(bsa):
     probs = bsa.recap_block_scores(desc, qd, kd, s)
     count, idx, _, _ = bsa.recap_topp_mask(desc, probs, p.tolist())
     del probs
-    c_lse, c_o = bsa.recap_tail_estimate(desc, qd, kd, vd, count, idx, s)
-    out_d, d_lse, d_o = bsa.recap_dense_attn_tail(desc, qd, kd, vd, count, idx, s)
-    out_h = bsa.recap_block_sparse_attn_tail(desc, qd, kd, vd, count, idx, s, d_lse, d_o)
-    out_1 = bsa.recap_block_sparse_attn_tail(desc, q1d, k1d, v1d, count, idx, s, d_lse, d_o)
+    c_lse, c_o = bsa.recap_tail_estimate(desc, qd, kd, vd, count, idx, s, moments=mom)
+    out_d, d_lse, d_o = bsa.recap_dense_attn_tail(desc, qd, kd, vd, count, idx, s, moments=mom)
+    out_h = bsa.recap_block_sparse_attn_tail(desc, qd, kd, vd, count, idx, s, d_lse, d_o,
+                                             moments=mom)
+    out_1 = bsa.recap_block_sparse_attn_tail(desc, q1d, k1d, v1d, count, idx, s, d_lse, d_o,
+                                             moments=mom)
     torch.cuda.synchronize()
     for h in heads:
         blocks = sorted({0, M - 1} | set(np.random.default_rng(300 + h).choice(M, 2, False).tolist()))
@@ -179,13 +192,15 @@ def test_full_size_tail(bsa):
         cnt, ix = count[:, h:h + 1].cpu().numpy(), idx[:, h:h + 1].cpu().numpy()
         m_h = O.mask_from_lists(cnt, ix, M)
         q64, k64, v64 = (synth.to_f64(x[:, h:h + 1]) for x in (q, k, v))
-        cl, co = O.coarse_tail(q64, k64, v64, blk, s, m_h, rows=sel)
+        cl, co = O.coarse_tail(q64, k64, v64, blk, s, m_h, rows=sel, moments=mom)
         el, eo = O.exact_tail(q64, k64, v64, blk, s, m_h, rows=sel)
         dl, do = O.tail_discrepancy(el, eo, cl, co)
         ref_d = O.dense_attention(q64, k64, v64, s, rows=sel, block=blk)
         lse_d = O.attention_lse(q64, k64, blk, s, rows=sel)
         q_rows = np.concatenate([q64[:, :, lo:hi] for lo, hi in spans], axis=2)
         tol_c = parity.coarse_lse_atol(q_rows, O.block_mean_pool(k64, blk), s)
+        if mom:
+            tol_c += parity.variance_lse_atol(q_rows, O.block_key_variance(k64, blk), s)
         g = {name: t[:, h:h + 1].cpu().numpy().astype(np.float64)
              for name, t in (("cl", c_lse), ("co", c_o), ("dl", d_lse), ("do", d_o))}
         g.update({name: f64(t[:, h:h + 1]) for name, t in (("out_d", out_d), ("out_h", out_h),
@@ -193,7 +208,11 @@ def test_full_size_tail(bsa):
         q1_64, k1_64, v1_64 = (synth.to_f64(x[:, h:h + 1]) for x in (q1, k1, v1))
         o_s1 = O.masked_attention(q1_64, k1_64, v1_64, blk, s, m_h, rows=sel)
         l_s1 = O.attention_lse(q1_64, k1_64, blk, s, m_h, rows=sel)
-        cl1, co1 = O.coarse_tail(q1_64, k1_64, v1_64, blk, s, m_h, rows=sel)
+        cl1, co1 = O.coarse_tail(q1_64, k1_64, v1_64, blk, s, m_h, rows=sel, moments=mom)
+        if mom:
+            q1_rows = np.concatenate([q1_64[:, :, lo:hi] for lo, hi in spans], axis=2)
+            tol_c = max(tol_c, parity.coarse_lse_atol(q1_rows, O.block_mean_pool(k1_64, blk), s)
+                        + parity.variance_lse_atol(q1_rows, O.block_key_variance(k1_64, blk), s))
         ref_1 = O.tail_reconstruction(o_s1, l_s1, cl1, co1, dl, do)
         w1, spread1 = _merge_weights(o_s1, l_s1, cl1 + dl, co1 + do)
         with np.errstate(invalid="ignore"):
