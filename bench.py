@@ -262,6 +262,109 @@ def bench_tail(bsa, cfg, desc, dev_inputs, counts, idxs, s, avg, args, roof):
     return res
 
 
+def bench_reuse(bsa, cfg, desc, x0, x1, p, s, args, tau):
+    """Mask reuse across steps (NEXT-3), on a reference step X_0 and a drifted step X_1 of the
+    same layer, timed apart from the step:
+      * fresh: the full mask prediction at X_1 (recap_block_scores + recap_topp_mask);
+      * gate: block means at X_1 and their relative drift against X_0's (recap_block_means +
+        recap_mean_drift); when the largest drift is below tau the step reuses X_0's kept
+        lists and skips scores and top-p (Temporal Mask Reuse in the head-wise adaptive
+        abstract: skip mask prediction on low query-key drift);
+      * candidates: block means at X_1, scores over candidate lists taken at X_0 with a looser
+        threshold p_c = 1 - (1 - p) / 4 (recap_scores_from_means with the lists), then top-p
+        at p over each row's candidate distribution (recap_topp_mask_cand) (GSRS abstract:
+        search restricted to an early candidate set).
+    Agreement with the fresh mask at X_1: share of equal block pairs, and the fresh block
+    probability mass the reused / restricted kept sets carry (against p)."""
+    import numpy as np
+    import torch
+
+    B, H, M = cfg.batch, cfg.heads, cfg.num_blocks
+    dev = x0[0].device
+    (q0, k0), (q1, k1) = x0, x1
+    plist = p.tolist()
+    pc = [min(1.0, 1.0 - (1.0 - float(v)) / 4.0) for v in plist]
+    means = lambda q, k: bsa.recap_block_means(desc, q, k)  # noqa: E731
+    qb0, kb0 = means(q0, k0)
+    pr0 = bsa.recap_scores_from_means(desc, qb0, kb0, s)
+    c0, i0, _, _ = bsa.recap_topp_mask(desc, pr0, plist)
+    cc, ci, _, _ = bsa.recap_topp_mask(desc, pr0, pc)
+    del pr0
+    probs = torch.empty((B, H, M, M), dtype=torch.float32, device=dev)
+    ws = torch.empty(bsa.recap_workspace_size(0, desc), dtype=torch.uint8, device=dev)
+    qb1 = torch.empty_like(qb0)
+    kb1 = torch.empty_like(kb0)
+    drift = torch.empty((B, H, 2), dtype=torch.float32, device=dev)
+    c1, i1 = torch.empty_like(c0), torch.empty_like(i0)
+    ccand, icand = torch.empty_like(c0), torch.empty_like(i0)
+
+    legs = {
+        "fresh": lambda: (bsa.recap_block_scores(desc, q1, k1, s, probs, ws),
+                          bsa.recap_topp_mask(desc, probs, plist, c1, i1)),
+        "gate": lambda: (bsa.recap_block_means(desc, q1, k1, qb1, kb1),
+                         bsa.recap_mean_drift(desc, qb1, kb1, qb0, kb0, drift)),
+        "candidates": lambda: (bsa.recap_block_means(desc, q1, k1, qb1, kb1),
+                               bsa.recap_scores_from_means(desc, qb1, kb1, s, cc, ci, probs),
+                               bsa.recap_topp_mask_cand(desc, probs, cc, ci, plist, ccand,
+                                                        icand)),
+    }
+    ms = {}
+    for name, fn in legs.items():
+        fn()
+        torch.cuda.synchronize()
+        ev = []
+        for _ in range(max(3, args.steps)):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            ev.append((e0, e1))
+        torch.cuda.synchronize()
+        ms[name] = float(np.median([a.elapsed_time(b) for a, b in ev]))
+    # the gate's decision needs the drift on the host: one synchronisation per gated step
+    # (wall time of the gate's launches, its kernels and the read of the largest drift, after a
+    # warm-up of the reduction)
+    legs["gate"]()
+    float(drift.max().item())
+    t0 = time.perf_counter()
+    legs["gate"]()
+    dmax = float(drift.max().item())
+    ms["gate_with_host_decision"] = (time.perf_counter() - t0) * 1e3
+    # masks: fresh (c1, i1 from the last fresh run), reused (c0, i0), restricted (ccand, icand)
+    legs["fresh"]()
+    legs["candidates"]()
+    bsa.recap_block_scores(desc, q1, k1, s, probs, ws)
+    torch.cuda.synchronize()
+
+    def mask_of(cnt, idx):
+        cols = torch.arange(M, device=dev).view(1, 1, 1, M)
+        valid = cols < cnt.unsqueeze(-1).long()
+        m = torch.zeros((B, H, M, M), dtype=torch.bool, device=dev)
+        m.scatter_(-1, torch.where(valid, idx.long(), torch.zeros_like(idx.long())), valid)
+        return m
+
+    fresh = mask_of(c1, i1)
+    ptens = torch.tensor(plist, device=dev, dtype=torch.float64).view(1, H, 1)
+
+    def agreement(m):
+        mass = (probs.double() * m).sum(-1)
+        return {"equal_block_pairs": float((m == fresh).double().mean().item()),
+                "mean_fresh_mass_kept": float(mass.mean().item()),
+                "rows_below_p": float((mass < ptens - 1e-4).double().mean().item()),
+                "kept_blocks_per_row": float(m.sum(-1).double().mean().item())}
+
+    res = {"threshold_tau": tau, "max_relative_drift": dmax, "reuse_chosen": dmax < tau,
+           "candidate_threshold": pc[0] if len(set(pc)) == 1 else "1 - (1 - p_h) / 4",
+           "ms": ms,
+           "ms_saved_by_reuse": ms["fresh"] - ms["gate"],
+           "ms_saved_by_candidates": ms["fresh"] - ms["candidates"],
+           "fresh": {"kept_blocks_per_row": float(fresh.sum(-1).double().mean().item())},
+           "reused_mask": agreement(mask_of(c0, i0)),
+           "candidate_mask": agreement(mask_of(ccand, icand))}
+    return res
+
+
 def bench_fp8(bsa, cfg, desc, dev_inputs, counts, idxs, s, res, res_scale, avg, sparse_flops,
               args, roof):
     """The MXFP8 variant of the step's sparse calls, timed apart from the step on the same
@@ -371,6 +474,11 @@ def main():
                     help="also time a plain bf16 GEMM and a device copy (practical ceilings)")
     ap.add_argument("--fp8", action="store_true",
                     help="also time the MXFP8 variant of the sparse calls (reported apart)")
+    ap.add_argument("--reuse", action="store_true",
+                    help="also time mask reuse across steps: the drift gate and the candidate-"
+                         "restricted search, against fresh mask prediction (reported apart)")
+    ap.add_argument("--reuse-tau", type=float, default=0.05,
+                    help="drift threshold of the mask-reuse gate (relative Frobenius change)")
     ap.add_argument("--tail", action="store_true",
                     help="also time the tail-reconstruction calls (reported apart from the step; "
                          "they launch the step's attention kernels with extra outputs, so they "
@@ -579,6 +687,14 @@ def main():
         res = rcap if cfg.refresh_then_sparse else r_dev
         result["fp8"] = bench_fp8(bsa, cfg, desc, dev_inputs, counts, idxs, s, res, res_scale,
                                   avg, sparse_flops, args, roof)
+    if args.reuse:
+        log("mask reuse: gate and candidate search against fresh mask prediction")
+        if cfg.refresh_then_sparse:
+            x1 = dev_inputs[1]
+        else:
+            x1 = tuple(synth.drifted(t, n, 1).to(dev) for t, n in ((q, "q"), (k, "k")))
+        result["reuse"] = bench_reuse(bsa, cfg, desc, dev_inputs[0][:2], x1[:2], p, s, args,
+                                      args.reuse_tau)
     if cfg.refresh_then_sparse and args.tail:
         result["tail"] = bench_tail(bsa, cfg, desc, dev_inputs, counts, idxs, s, avg, args, roof)
     if not args.no_cpu_baseline:

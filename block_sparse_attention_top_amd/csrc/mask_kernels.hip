@@ -707,26 +707,33 @@ __global__ __launch_bounds__(256) void score_cand_kernel(const float* __restrict
 
 // ------------------------------------------------------------------------------------------
 // Drift of the block means between two steps, per (b, h): ||X̄ - X̄_ref||_F / ||X̄_ref||_F for
-// X = Q and X = K, sums in fp64 over the M x D means (one work-group per (b, h)); a caller
-// reuses the mask of the reference step while both stay under its threshold.
+// X = Q and X = K, sums in fp64 over the M x D means (one 1024-thread work-group per (b, h),
+// 16-byte loads; a fixed reduction order, so the result is deterministic); a caller reuses
+// the mask of the reference step while both stay under its threshold.
 // ------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void mean_drift_kernel(const float* __restrict__ qbar,
-                                                         const float* __restrict__ kbar,
-                                                         const float* __restrict__ qref,
-                                                         const float* __restrict__ kref,
-                                                         int64_t per_head,
-                                                         float* __restrict__ drift) {
-  __shared__ double red[4][4];
+__global__ __launch_bounds__(1024) void mean_drift_kernel(const float* __restrict__ qbar,
+                                                          const float* __restrict__ kbar,
+                                                          const float* __restrict__ qref,
+                                                          const float* __restrict__ kref,
+                                                          int64_t per_head,
+                                                          float* __restrict__ drift) {
+  __shared__ double red[16][4];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t off = (int64_t)blockIdx.x * per_head;
+  const int64_t off = (int64_t)blockIdx.x * per_head;  // per_head = M * D, a multiple of 64
   double dq = 0.0, rq = 0.0, dk = 0.0, rk = 0.0;
-  for (int64_t t = threadIdx.x; t < per_head; t += 256) {
-    const double a = qbar[off + t], ar = qref[off + t];
-    const double b = kbar[off + t], br = kref[off + t];
-    dq += (a - ar) * (a - ar);
-    rq += ar * ar;
-    dk += (b - br) * (b - br);
-    rk += br * br;
+  for (int64_t t = threadIdx.x * 4; t < per_head; t += 1024 * 4) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(qbar + off + t);
+    const f32x4 ar = *reinterpret_cast<const f32x4*>(qref + off + t);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(kbar + off + t);
+    const f32x4 br = *reinterpret_cast<const f32x4*>(kref + off + t);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const double x = (double)a[e] - (double)ar[e], y = (double)b[e] - (double)br[e];
+      dq += x * x;
+      rq += (double)ar[e] * (double)ar[e];
+      dk += y * y;
+      rk += (double)br[e] * (double)br[e];
+    }
   }
   double v[4] = {dq, rq, dk, rk};
 #pragma unroll
@@ -738,7 +745,7 @@ __global__ __launch_bounds__(256) void mean_drift_kernel(const float* __restrict
   __syncthreads();
   if (threadIdx.x == 0) {
     double t[4] = {0.0, 0.0, 0.0, 0.0};
-    for (int w = 0; w < 4; ++w)
+    for (int w = 0; w < 16; ++w)
       for (int c = 0; c < 4; ++c) t[c] += red[w][c];
     drift[2 * blockIdx.x] = (float)(t[1] > 0.0 ? sqrt(t[0] / t[1]) : (t[0] > 0.0 ? INFINITY : 0.0));
     drift[2 * blockIdx.x + 1] =
@@ -865,7 +872,7 @@ hipError_t launch_scores_cand(const float* qbar, const float* kbar, int BH, int 
 hipError_t launch_mean_drift(const float* qbar, const float* kbar, const float* qref,
                              const float* kref, int BH, int M, int D, float* drift,
                              hipStream_t stream) {
-  mean_drift_kernel<<<BH, 256, 0, stream>>>(qbar, kbar, qref, kref, (int64_t)M * D, drift);
+  mean_drift_kernel<<<BH, 1024, 0, stream>>>(qbar, kbar, qref, kref, (int64_t)M * D, drift);
   return hipGetLastError();
 }
 

@@ -46,6 +46,8 @@ int validate_desc(const recap_desc* d) {
   int64_t span = d->head_dim;  // elements covered by the dimensions below
   for (int i = 0; i < 3; ++i) {
     if (ext[i] > 1 && st[i] < span) return RECAP_E_STRIDE;
+    // the whole tensor must be addressable with 64-bit element offsets
+    if (ext[i] > 1 && st[i] > (INT64_MAX - span) / (ext[i] - 1)) return RECAP_E_STRIDE;
     span = st[i] * (ext[i] - 1) + span;
   }
   return RECAP_OK;

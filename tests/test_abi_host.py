@@ -112,6 +112,15 @@ def test_token_stride_limit():
     assert ws_size(_lib.OP_SPARSE, bad)[0] == -3
 
 
+def test_strides_beyond_64_bit_offsets_rejected():
+    """Strides whose tensor extent does not fit 64-bit element offsets are RECAP_E_STRIDE (the
+    overlap check itself must not overflow: the sanitizer build runs this arithmetic too)."""
+    d = _lib.RecapDesc(3, 5, 1000, 128, 128, 0, 1 << 62, 1 << 62, 128)
+    assert ws_size(_lib.OP_SPARSE, d)[0] == -3
+    d = _lib.RecapDesc(3, 5, 1000, 128, 128, 0, (1 << 63) - 8, 128 * 1000, 128)
+    assert ws_size(_lib.OP_SPARSE, d)[0] == -3
+
+
 def test_layouts_accepted():
     for layout in ("bhnd", "bnhd"):
         assert ws_size(_lib.OP_SPARSE, desc(B=2, H=3, N=1000, layout=layout))[0] == 0
