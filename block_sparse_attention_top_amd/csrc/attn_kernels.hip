@@ -721,14 +721,15 @@ __global__ __launch_bounds__(64) void kept_bits_kernel(const int32_t* __restrict
 // Moment statistics of the key and value blocks for the refined coarse tail (paperpeel.com
 // RECAP Sec. 3.2: key variance refines the block log-mass at second order, the pooled
 // value-key covariance refines the value at first order). Work-group = (b*h, slice of
-// kStatSlice key blocks). Per block, thread (d, part) takes dimension d over a part of the
-// block's tokens: it sums the squared deviations of the keys from the block mean (fp32, then
-// a reduction over the parts in LDS: the per-dimension variance, population form) and writes
-// the centred keys and values, bf16, transposed into LDS ([dim][token], rows padded by 16
+// kStatSlice key blocks). Per block, thread (token pair tp, 8-dim chunk c) loads 16 bytes of K
+// and of V for two adjacent tokens per pass (coalesced rows), subtracts the block means (fp32),
+// adds the squared key deviations to eight per-thread sums (reduced over the token pairs in
+// LDS: the per-dimension variance, population form) and writes the centred keys and values,
+// bf16, transposed into LDS ([dim][token], two tokens per 4-byte write, rows padded by 16
 // bytes). The four wavefronts then add the block's (v - V̄)(k - K̄)^T to a D x D accumulator
 // with bf16 MFMA 32x32x16 (A: value rows, B: key rows, contraction over the tokens; wave w
 // owns value rows 32w.. at D = 128, one 32 x 32 tile at D = 64). The slice's sum is written
-// as one fp32 partial; tail_cov_reduce_kernel adds the slices.
+// as one fp32 partial; tail_cov_reduce_kernel adds the slices in a fixed order.
 // ------------------------------------------------------------------------------------------
 template <int D, int BLK>
 __global__ __launch_bounds__(256) void tail_stats_kernel(const bf16_t* __restrict__ k,
@@ -739,78 +740,96 @@ __global__ __launch_bounds__(256) void tail_stats_kernel(const bf16_t* __restric
                                                          const float* __restrict__ vbar,
                                                          float* __restrict__ var,
                                                          float* __restrict__ cov_part) {
-  constexpr int PARTS = 256 / D;      // token parts per dimension
-  constexpr int TP = BLK / PARTS;     // tokens per thread
-  constexpr int RS = BLK + 8;         // LDS row stride (bf16 elements)
+  constexpr int CH = D / 8;              // 16-byte chunks per token row
+  constexpr int TPW = 256 / CH;          // token pairs per pass
+  constexpr int PASSES = BLK / (2 * TPW);
+  constexpr int RS = BLK + 8;            // LDS row stride (bf16 elements)
   constexpr int TILES = D == 128 ? 4 : 1;  // 32 x 32 output tiles per wavefront
   __shared__ __align__(16) bf16_t kt[D * RS];
   __shared__ __align__(16) bf16_t vt[D * RS];
-  __shared__ float vpart[PARTS][D];
+  __shared__ float vred[TPW][D];
   const int bh = blockIdx.x / nslice, slice = blockIdx.x - bh * nslice;
   const int b = bh / H, h = bh - b * H;
   const bf16_t* kp = k + b * st.b + h * st.h;
   const bf16_t* vp = v + b * st.b + h * st.h;
-  const int d = threadIdx.x % D, part = threadIdx.x / D;
+  const int c = threadIdx.x % CH, tp = threadIdx.x / CH;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 31, half = lane >> 5;
-  // output tiles of this wavefront: (row tile, column tile)
-  const int rt = D == 128 ? wave : wave >> 1;
+  const int rt = D == 128 ? wave : wave >> 1;  // this wavefront's row tile of the output
   f32x16 acc[TILES];
 #pragma unroll
-  for (int c = 0; c < TILES; ++c) acc[c] = f32x16{};
+  for (int t = 0; t < TILES; ++t) acc[t] = f32x16{};
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
   const int j0 = slice * kStatSlice, j1 = min(M, j0 + kStatSlice);
   for (int j = j0; j < j1; ++j) {
     const int t0 = j * BLK, nj = min(BLK, N - t0);
-    const float km = kbar[((int64_t)bh * M + j) * D + d];
-    const float vm = vbar[((int64_t)bh * M + j) * D + d];
-    float sq = 0.f;
+    const float* kmp = kbar + ((int64_t)bh * M + j) * D + c * 8;
+    const float* vmp = vbar + ((int64_t)bh * M + j) * D + c * 8;
+    float km[8], vm[8], sq[8];
 #pragma unroll
-    for (int g = 0; g < TP / 8; ++g) {
-      bf16x8 kw, vw;
+    for (int e = 0; e < 8; ++e) {
+      km[e] = kmp[e];
+      vm[e] = vmp[e];
+      sq[e] = 0.f;
+    }
+#pragma unroll
+    for (int ps = 0; ps < PASSES; ++ps) {
+      const int u0 = ps * 2 * TPW + 2 * tp;  // this thread's first token of the pass
+      bf16x8 kx[2], vx[2];
+#pragma unroll
+      for (int w = 0; w < 2; ++w) {
+        const int u = u0 + w;
+        if (u < nj) {
+          kx[w] = *reinterpret_cast<const bf16x8*>(kp + (int64_t)(t0 + u) * st.n + c * 8);
+          vx[w] = *reinterpret_cast<const bf16x8*>(vp + (int64_t)(t0 + u) * st.n + c * 8);
+        }
+      }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int u = part * TP + g * 8 + e;
-        float kx = 0.f, vx = 0.f;
-        if (u < nj) {
-          kx = (float)kp[(int64_t)(t0 + u) * st.n + d] - km;
-          vx = (float)vp[(int64_t)(t0 + u) * st.n + d] - vm;
+        bf16x2 kw, vw;
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+          const bool ok = u0 + w < nj;
+          const float kd = ok ? (float)kx[w][e] - km[e] : 0.f;
+          const float vd = ok ? (float)vx[w][e] - vm[e] : 0.f;
+          sq[e] += kd * kd;
+          kw[w] = (bf16_t)kd;
+          vw[w] = (bf16_t)vd;
         }
-        sq += kx * kx;
-        kw[e] = (bf16_t)kx;
-        vw[e] = (bf16_t)vx;
+        *reinterpret_cast<bf16x2*>(&kt[(c * 8 + e) * RS + u0]) = kw;
+        *reinterpret_cast<bf16x2*>(&vt[(c * 8 + e) * RS + u0]) = vw;
       }
-      *reinterpret_cast<bf16x8*>(&kt[d * RS + part * TP + g * 8]) = kw;
-      *reinterpret_cast<bf16x8*>(&vt[d * RS + part * TP + g * 8]) = vw;
     }
-    vpart[part][d] = sq;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) vred[tp][c * 8 + e] = sq[e];
     __syncthreads();
-    if (part == 0) {
+    if (threadIdx.x < D) {
       float tot = 0.f;
 #pragma unroll
-      for (int q = 0; q < PARTS; ++q) tot += vpart[q][d];
-      var[((int64_t)bh * M + j) * D + d] = tot / (float)nj;
+      for (int q = 0; q < TPW; ++q) tot += vred[q][threadIdx.x];
+      var[((int64_t)bh * M + j) * D + threadIdx.x] = tot / (float)nj;
     }
 #pragma unroll
     for (int ks = 0; ks < BLK / 16; ++ks) {
       const int u0 = ks * 16 + half * 8;
       const bf16x8 a = *reinterpret_cast<const bf16x8*>(&vt[(rt * 32 + n) * RS + u0]);
 #pragma unroll
-      for (int c = 0; c < TILES; ++c) {
-        const int ct = D == 128 ? c : (wave & 1);
+      for (int t = 0; t < TILES; ++t) {
+        const int ct = D == 128 ? t : (wave & 1);
         const bf16x8 bb = *reinterpret_cast<const bf16x8*>(&kt[(ct * 32 + n) * RS + u0]);
-        acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bb, acc[c], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bb, acc[t], 0, 0, 0);
       }
     }
-    __syncthreads();  // LDS rows and vpart are rewritten by the next block
+    __syncthreads();  // LDS rows and vred are rewritten by the next block
   }
   float* dst = cov_part + ((int64_t)bh * nslice + slice) * D * D;
 #pragma unroll
-  for (int c = 0; c < TILES; ++c) {
-    const int ct = D == 128 ? c : (wave & 1);
+  for (int t = 0; t < TILES; ++t) {
+    const int ct = D == 128 ? t : (wave & 1);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int row = rt * 32 + ((r >> 2) << 3) + half * 4 + (r & 3);  // value dimension
-      dst[row * D + ct * 32 + n] = acc[c][r];
+      dst[row * D + ct * 32 + n] = acc[t][r];
     }
   }
 }

@@ -239,10 +239,16 @@ constexpr int kStripVals = 20;
 
 __host__ __device__ constexpr int strip_stride(int M) { return ((M + 15) / 16) * 16 + 4; }
 
-template <int D>
+// CAND: scores restricted to candidate lists (the reduced search of the GSRS abstract on the
+// RECAP page at thelatestinai.com). The strip's logits are computed the same way; each row is
+// then normalised over its candidates only, gathered from the LDS strip at the listed blocks,
+// and written at the candidate positions.
+template <int D, bool CAND>
 __global__ __launch_bounds__(256) void score_strip_kernel(const float* __restrict__ qbar,
                                                           const float* __restrict__ kbar, int M,
                                                           float scale_log2,
+                                                          const int32_t* __restrict__ ccount,
+                                                          const int32_t* __restrict__ cidx,
                                                           float* __restrict__ probs) {
   extern __shared__ float srow[];  // [kStripRows][strip_stride(M)]
   constexpr int KS = D / 4;        // contraction steps; lane group g covers D indices [g*KS, ..)
@@ -309,12 +315,17 @@ __global__ __launch_bounds__(256) void score_strip_kernel(const float* __restric
     const int qrow = st * kStripRows + r;
     if (qrow >= M) break;  // uniform per wavefront
     const float* x = srow + r * stride;
+    const int64_t grow = (int64_t)bh * M + qrow;
+    const int n = CAND ? min(max(ccount[grow], 0), M) : M;  // values of the row
+    if (CAND && n == 0) continue;  // no candidates: nothing to write (uniform per wavefront)
+    const int32_t* crow = CAND ? cidx + grow * M : nullptr;
     float e[kStripVals];
     float mx = -INFINITY;
 #pragma unroll
     for (int i = 0; i < kStripVals; ++i) {
       const int j = i * 64 + lane;
-      e[i] = j < M ? x[j] : -INFINITY;
+      if (CAND) e[i] = j < n ? x[min(max(crow[j], 0), M - 1)] : -INFINITY;
+      else e[i] = j < M ? x[j] : -INFINITY;
       mx = fmaxf(mx, e[i]);
     }
     mx = wave_max_f(mx);
@@ -329,7 +340,7 @@ __global__ __launch_bounds__(256) void score_strip_kernel(const float* __restric
 #pragma unroll
     for (int i = 0; i < kStripVals; ++i) {
       const int j = i * 64 + lane;
-      if (j < M) prow[j] = e[i] * inv;
+      if (j < n) prow[j] = e[i] * inv;
     }
   }
 }
@@ -790,13 +801,17 @@ hipError_t launch_scores(const float* qbar, const float* kbar, int BH, int M, in
     constexpr int kMaxLds = kStripRows * strip_stride(kStripMaxM) * sizeof(float);
     static std::atomic<uint32_t> lds128{0u}, lds64{0u};
     if (D == 128) {
-      const hipError_t e = allow_lds_once((const void*)score_strip_kernel<128>, kMaxLds, lds128);
+      const hipError_t e =
+          allow_lds_once((const void*)score_strip_kernel<128, false>, kMaxLds, lds128);
       if (e != hipSuccess) return e;
-      score_strip_kernel<128><<<sgrid, 256, lds, stream>>>(qbar, kbar, M, scale_log2, probs);
+      score_strip_kernel<128, false><<<sgrid, 256, lds, stream>>>(qbar, kbar, M, scale_log2,
+                                                                  nullptr, nullptr, probs);
     } else {
-      const hipError_t e = allow_lds_once((const void*)score_strip_kernel<64>, kMaxLds, lds64);
+      const hipError_t e =
+          allow_lds_once((const void*)score_strip_kernel<64, false>, kMaxLds, lds64);
       if (e != hipSuccess) return e;
-      score_strip_kernel<64><<<sgrid, 256, lds, stream>>>(qbar, kbar, M, scale_log2, probs);
+      score_strip_kernel<64, false><<<sgrid, 256, lds, stream>>>(qbar, kbar, M, scale_log2,
+                                                                 nullptr, nullptr, probs);
     }
     return hipGetLastError();
   }
@@ -858,6 +873,26 @@ hipError_t launch_topp(const float* probs, int B, int H, int M, const HeadScalar
 hipError_t launch_scores_cand(const float* qbar, const float* kbar, int BH, int M, int D,
                               float scale_log2, const int32_t* ccount, const int32_t* cidx,
                               float* probs, hipStream_t stream) {
+  if (M <= kStripMaxM) {  // the one-pass strip kernel, normalising over the candidates
+    const size_t lds = (size_t)kStripRows * strip_stride(M) * sizeof(float);
+    const int sgrid = BH * ((M + kStripRows - 1) / kStripRows);
+    constexpr int kMaxLds = kStripRows * strip_stride(kStripMaxM) * sizeof(float);
+    static std::atomic<uint32_t> lds128{0u}, lds64{0u};
+    if (D == 128) {
+      const hipError_t e =
+          allow_lds_once((const void*)score_strip_kernel<128, true>, kMaxLds, lds128);
+      if (e != hipSuccess) return e;
+      score_strip_kernel<128, true><<<sgrid, 256, lds, stream>>>(qbar, kbar, M, scale_log2,
+                                                                 ccount, cidx, probs);
+    } else {
+      const hipError_t e =
+          allow_lds_once((const void*)score_strip_kernel<64, true>, kMaxLds, lds64);
+      if (e != hipSuccess) return e;
+      score_strip_kernel<64, true><<<sgrid, 256, lds, stream>>>(qbar, kbar, M, scale_log2,
+                                                                ccount, cidx, probs);
+    }
+    return hipGetLastError();
+  }
   const int rows = BH * M;
   const int grid = (rows + 3) / 4;
   if (D == 128)
