@@ -54,6 +54,10 @@ __device__ __forceinline__ uint32_t opaque(uint32_t x) {
   asm volatile("" : "+v"(x));
   return x;
 }
+__device__ __forceinline__ float opaque_f(float x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
 
 // ------------------------------------------------------------------------------------------
 // Block sequences walked by one attention phase. first()/next() return a key-block index or

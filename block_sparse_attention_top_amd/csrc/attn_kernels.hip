@@ -39,6 +39,7 @@
 //   RECAP_PAIR      sparse calls with 64-row blocks run two query blocks per work-group
 //   RECAP_PRIO      raise the wavefront priority around MFMA bursts
 //   RECAP_WPE       wavefronts per SIMD targeted by register allocation
+//   RECAP_PIPE      software-pipelined tile loop (next tile's QK^T under this tile's softmax)
 #ifndef RECAP_STAGES4
 #define RECAP_STAGES4 2
 #endif
@@ -50,6 +51,9 @@
 #endif
 #ifndef RECAP_WPE  // wavefronts per SIMD the register allocation targets
 #define RECAP_WPE 2
+#endif
+#ifndef RECAP_PIPE  // two-stage phases without capture overlap QK^T(t+1) with tile t's weights
+#define RECAP_PIPE 1
 #endif
 
 namespace recap {
@@ -69,8 +73,10 @@ __device__ __forceinline__ void mfma_prio_lo() {
 __device__ __forceinline__ int swap23(int p) { return (p & 3) | ((p & 4) << 1) | ((p & 8) >> 1); }
 
 // ------------------------------------------------------------------------------------------
-// V -> packed V^T [B*H][D][npad] (npad = M * block, zero past N), keys permuted inside each
-// 16-key group as described above. One work-group per (b*h, 64-key tile), staged through LDS.
+// V -> packed V^T tiles [B*H][npad / 64][D][64] (npad = M * block, zero past N): each 64-key
+// tile's V^T is one contiguous 16 KB block, so a gathered tile is one sequential read rather
+// than D rows of 128 bytes spread over the head. Keys are permuted inside each 16-key group as
+// described above. One work-group per (b*h, 64-key tile), staged through LDS.
 // ------------------------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void pack_vt_kernel(const bf16_t* __restrict__ v, Strides st,
@@ -91,7 +97,7 @@ __global__ __launch_bounds__(256) void pack_vt_kernel(const bf16_t* __restrict__
     for (int e = 0; e < 8; ++e) tile[key][c * 8 + e] = x[e];
   }
   __syncthreads();
-  bf16_t* dst = vt + (int64_t)bh * D * npad + key0;
+  bf16_t* dst = vt + (int64_t)bh * D * npad + (int64_t)key0 * D;
   for (int s = threadIdx.x; s < D * 8; s += 256) {
     const int d = s >> 3, c = s & 7;
     bf16x8 y;
@@ -100,7 +106,7 @@ __global__ __launch_bounds__(256) void pack_vt_kernel(const bf16_t* __restrict__
       const int pos = c * 8 + e;
       y[e] = tile[(pos & ~15) | swap23(pos & 15)][d];
     }
-    *reinterpret_cast<bf16x8*>(dst + (int64_t)d * npad + c * 8) = y;
+    *reinterpret_cast<bf16x8*>(dst + d * 64 + c * 8) = y;
   }
 }
 
@@ -116,7 +122,7 @@ struct Tiles {
 // Per-lane constants of the inner loop, computed once per work-group.
 //  K tile in LDS: row `key` (0..63) holds its 16-byte chunks XOR-swizzled, chunk c stored at
 //  position c ^ (key & (CH-1)). V^T tile: row d (0..D-1) of 64 keys, chunk c stored at
-//  c ^ ((d >> 1) & 7). Both make the 16-byte MFMA-fragment reads bank-conflict free, and
+//  c ^ ((d >> 1) & 7); in global memory the tile is D contiguous rows of 128 bytes. Both make the 16-byte MFMA-fragment reads bank-conflict free, and
 //  both reduce to "lane base XOR (ks << 5)" plus an immediate offset per 32-row tile.
 template <int D, int NW>
 struct LaneConsts {
@@ -129,7 +135,7 @@ struct LaneConsts {
   uint32_t k_rd, v_rd;   // LDS read offsets (bytes) within a tile buffer
   uint32_t k_voff[KP];   // K DMA source offsets (bytes)
   uint32_t v_voff[VP];   // V^T DMA source offsets (bytes)
-  __device__ void init(int lane, int wave, int64_t sn, int npad) {
+  __device__ void init(int lane, int wave, int64_t sn) {
     constexpr int CH = Tiles<D, NW>::CH, ROWB = Tiles<D, NW>::ROWB, KROWS = Tiles<D, NW>::KROWS;
     const int n = lane & 31, half = lane >> 5;
     k_rd = opaque(n * ROWB + ((half ^ (n & (CH - 1))) << 4));
@@ -145,7 +151,7 @@ struct LaneConsts {
     for (int r = 0; r < VP; ++r) {
       const int x = LD >= 2 ? r : wave * LD + r;
       const int c = (lane & 7) ^ ((x * 4 + (lane >> 4)) & 7);
-      v_voff[r] = opaque((uint32_t)((lane >> 3) * npad * 2 + c * 16));
+      v_voff[r] = opaque((uint32_t)((lane >> 3) * 128 + c * 16));
     }
   }
   __device__ uint32_t kv(int x, int it) const { return k_voff[LD >= 4 ? (x & 3) : it]; }
@@ -186,16 +192,17 @@ __device__ __forceinline__ void issue_k(uint32_t kbuf, const bf16_t* kp, int64_t
   }
 }
 
+// Issue the global -> LDS loads of one packed V^T tile (keys [key0, key0 + 64), key0 a
+// multiple of 64): 16 KB at vtp + key0 * D, 1 KB per instruction.
 template <int D, int NW>
-__device__ __forceinline__ void issue_v(uint32_t vbuf, const bf16_t* vtp, int npad,
-                                        int key0, int wave, const LaneConsts<D, NW>& lc) {
+__device__ __forceinline__ void issue_v(uint32_t vbuf, const bf16_t* vtp, int key0, int wave,
+                                        const LaneConsts<D, NW>& lc) {
   constexpr int LD = Tiles<D, NW>::LD;
-  const char* tile_base = (const char*)(vtp + key0);
-  const uint32_t row_bytes = (uint32_t)npad * 2;
+  const char* tile_base = (const char*)(vtp + (int64_t)key0 * D);
 #pragma unroll
   for (int it = 0; it < LD; ++it) {
     const int x = wave * LD + it;
-    load_lds16(tile_base, (uint32_t)(x * 8 * row_bytes + lc.vv(x, it)), vbuf + x * 1024);
+    load_lds16(tile_base, (uint32_t)(x * 1024 + lc.vv(x, it)), vbuf + x * 1024);
   }
 }
 
@@ -303,6 +310,38 @@ __device__ __forceinline__ float tile_exp(const f32x16& s0, const f32x16& s1, fl
   return acc;
 }
 
+// The next tile's S^T = K Q^T (into n0, n1, from K tile kb) fused with this tile's weights
+// (tile_exp on s0, s1): the two are independent, so the products run on the matrix cores while
+// the vector ALUs compute the exponentials. The scheduling groups interleave them: after each
+// product, a sixteenth of the weight computation.
+template <int D, int NW>
+__device__ __forceinline__ float tile_qk_exp(uint32_t kb, const bf16x8 (&qf)[D / 16],
+                                             const LaneConsts<D, NW>& lc, f32x16& n0,
+                                             f32x16& n1, const f32x16& s0, const f32x16& s1,
+                                             float scale_log2, float m, bf16x8 (&pf)[4]) {
+  constexpr int ROWB = Tiles<D, NW>::ROWB;
+  constexpr int KS = D / 16;
+  constexpr int VALU_PER = (96 + 2 * KS - 1) / (2 * KS);  // tile_exp: 96 vector instructions
+  n0 = f32x16{};
+  n1 = f32x16{};
+  const uint32_t base = opaque(kb + lc.k_rd);
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const uint32_t a = base ^ (uint32_t)(ks << 5);
+    const bf16x8 ka = lds_read16(a);
+    const bf16x8 kb2 = lds_read16(a + 32 * ROWB);
+    n0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], n0, 0, 0, 0);
+    n1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb2, qf[ks], n1, 0, 0, 0);
+  }
+  const float acc = tile_exp(s0, s1, scale_log2, m, pf);
+#pragma unroll
+  for (int ks = 0; ks < 2 * KS; ++ks) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                 // one product
+    __builtin_amdgcn_sched_group_barrier(0x002 | 0x400, VALU_PER, 0);  // vector + transcendental
+  }
+  return acc;
+}
+
 // Online softmax of one tile in the base-2 domain with lazy rescale; returns the bf16 P^T
 // operands and whether the tile also feeds the kept-block accumulator.
 template <int D, bool CAP>
@@ -350,6 +389,76 @@ __device__ __forceinline__ void tile_pv(uint32_t vb, const bf16x8 (&pf)[4],
   mfma_prio_lo();
 }
 
+// Software-pipelined two-stage phase (no capture): step t computes tile t's weights and PV
+// product while the next tile's QK^T runs on the matrix cores (tile_qk_exp). K runs one tile
+// ahead of V: at the start of step t (one barrier), K(t+1) and V(t) have landed, K(t+2) goes
+// into the buffer K(t) used and V(t+1) into the one V(t-1) used. SKIP as in attend_phase.
+template <int D, int NW, bool SKIP, class Seq>
+__device__ __forceinline__ void attend_phase_pipe(Seq& seq, unsigned char* kbuf,
+                                                  unsigned char* vbuf, const bf16_t* kp,
+                                                  const bf16_t* vtp, int64_t sn, int N,
+                                                  int block, float scale_log2,
+                                                  const bf16x8 (&qf)[D / 16],
+                                                  f32x16 (&o)[D / 32], SoftmaxState& sm,
+                                                  int wave, int lane, const LaneConsts<D, NW>& lc,
+                                                  KeptAcc<D>& ka, const uint32_t* own) {
+  constexpr int LD = Tiles<D, NW>::LD, TB = Tiles<D, NW>::TILE_BYTES;
+  const int half = lane >> 5;
+  TileCur cur{seq.first(), 0};
+  if (cur.j < 0) return;
+  const uint32_t kb0 = lds_base(kbuf), vb0 = lds_base(vbuf);
+  auto key0_of = [&](TileCur t) { return t.j * block + t.st * kKeyTile; };
+  auto active_for = [&](TileCur t) {
+    return t.j >= 0 && (!SKIP || ((own[t.j >> 5] >> (t.j & 31)) & 1u));
+  };
+  TileCur nxt = advance(cur, seq, block, N);
+  issue_k<D, NW>(kb0, kp, sn, N, key0_of(cur), wave, lane, lc);
+  issue_v<D, NW>(vb0, vtp, key0_of(cur), wave, lc);
+  if (nxt.j >= 0) {
+    issue_k<D, NW>(kb0 + TB, kp, sn, N, key0_of(nxt), wave, lane, lc);
+    wait_vmem<2 * LD>();  // K(0) landed; V(0), K(1) may be in flight
+  } else {
+    wait_vmem<LD>();
+  }
+  lds_barrier();
+  f32x16 sa0, sa1, sb0, sb1;
+  bool act = active_for(cur);
+  if (act) tile_qk<D, NW>(kb0, qf, lc, sa0, sa1);
+  int b = 0;  // K(cur + 1) is in K buffer b ^ 1, V(cur) in V buffer b
+  auto step = [&](f32x16& s0, f32x16& s1, f32x16& n0, f32x16& n1) -> bool {
+    const TileCur nxt2 = advance(nxt, seq, block, N);
+    const bool has1 = nxt.j >= 0;
+    wait_vmem<0>();  // V(cur) and K(nxt) landed
+    lds_barrier();   // every wave is past the previous step: K buffer b, V buffer b ^ 1 free
+    if (nxt2.j >= 0) issue_k<D, NW>(kb0 + b * TB, kp, sn, N, key0_of(nxt2), wave, lane, lc);
+    if (has1) issue_v<D, NW>(vb0 + (b ^ 1) * TB, vtp, key0_of(nxt), wave, lc);
+    const bool act1 = active_for(nxt);
+    if (act) {
+      mask_tail(s0, s1, key0_of(cur), N, half);  // finite max: a tile has a valid key
+      raise_max<D, false>(tile_rowmax(s0, s1, scale_log2), sm, o, ka);
+      bf16x8 pf[4];
+      // (the plain arm takes the max through an opaque copy: identical arms would let the
+      // compiler hoist the exponentials out of the fused block, away from the products)
+      const float acc =
+          act1 ? tile_qk_exp<D, NW>(kb0 + (b ^ 1) * TB, qf, lc, n0, n1, s0, s1, scale_log2,
+                                    sm.m, pf)
+               : tile_exp(s0, s1, scale_log2, opaque_f(sm.m), pf);
+      sm.l += acc;
+      tile_pv<D, NW>(vb0 + b * TB, pf, lc, o, ka, false);
+    } else if (act1) {
+      tile_qk<D, NW>(kb0 + (b ^ 1) * TB, qf, lc, n0, n1);
+    }
+    act = act1;
+    cur = nxt;
+    nxt = nxt2;
+    b ^= 1;
+    return has1;
+  };
+  // two steps per trip, so that the current and next score tiles swap registers by name
+  while (step(sa0, sa1, sb0, sb1) && step(sb0, sb1, sa0, sa1)) {
+  }
+}
+
 // One attention phase over a block sequence, continuing the online-softmax state (m, l, o).
 // STAGES = 1: one K and one V^T buffer; K(t+1) loads during softmax + PV of tile t and
 //             V^T(t+1) during the QK^T of tile t+1 (four barriers per tile).
@@ -360,11 +469,16 @@ __device__ __forceinline__ void tile_pv(uint32_t vb, const bf16x8 (&pf)[4],
 template <int D, int NW, int STAGES, bool CAP, bool SKIP = false, class Seq>
 __device__ __forceinline__ void attend_phase(Seq& seq, unsigned char* kbuf, unsigned char* vbuf,
                                              const bf16_t* kp, const bf16_t* vtp, int64_t sn,
-                                             int N, int block, int npad, float scale_log2,
+                                             int N, int block, float scale_log2,
                                              const bf16x8 (&qf)[D / 16], f32x16 (&o)[D / 32],
                                              SoftmaxState& sm, int wave, int lane,
                                              const LaneConsts<D, NW>& lc, KeptAcc<D>& ka,
                                              const uint32_t* own = nullptr) {
+  if constexpr (RECAP_PIPE && STAGES == 2 && !CAP) {
+    attend_phase_pipe<D, NW, SKIP>(seq, kbuf, vbuf, kp, vtp, sn, N, block, scale_log2, qf, o,
+                                   sm, wave, lane, lc, ka, own);
+    return;
+  }
   constexpr int LD = Tiles<D, NW>::LD, TB = Tiles<D, NW>::TILE_BYTES;
   const int half = lane >> 5;
   TileCur cur{seq.first(), 0};
@@ -373,7 +487,7 @@ __device__ __forceinline__ void attend_phase(Seq& seq, unsigned char* kbuf, unsi
   auto issue_both = [&](TileCur t, int buf) {
     const int key0 = t.j * block + t.st * kKeyTile;
     issue_k<D, NW>(kb0 + buf * TB, kp, sn, N, key0, wave, lane, lc);
-    issue_v<D, NW>(vb0 + buf * TB, vtp, npad, key0, wave, lc);
+    issue_v<D, NW>(vb0 + buf * TB, vtp, key0, wave, lc);
   };
   auto active_for = [&](int j) { return !SKIP || ((own[j >> 5] >> (j & 31)) & 1u); };
 
@@ -425,7 +539,7 @@ __device__ __forceinline__ void attend_phase(Seq& seq, unsigned char* kbuf, unsi
       if (active) tile_pv<D, NW>(vb0, pf, lc, o, ka, kept);
       lds_barrier();  // every wave is done reading the V buffer
       if (!has_next) break;
-      issue_v<D, NW>(vb0, vtp, npad, nxt.j * block + nxt.st * kKeyTile, wave, lc);
+      issue_v<D, NW>(vb0, vtp, nxt.j * block + nxt.st * kKeyTile, wave, lc);
       cur = nxt;
     }
   }
@@ -452,17 +566,27 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RECAP_W
   const bf16_t* vtp = p.vt + (int64_t)bh * D * p.npad;
   const int qrow = qi * QROWS + wave * 32 + n;
   LaneConsts<D, NW> lc;
-  lc.init(lane, wave, p.st.n, p.npad);
+  lc.init(lane, wave, p.st.n);
 
   bf16x8 qf[D / 16];
   {
     const bf16_t* src = p.q + base + (int64_t)min(qrow, p.N - 1) * p.st.n + half * 8;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(src + ks * 16);
-    // consume the fragments here, so the compiler's waits for these loads sit before the loop
-    // (the tile loads in the loop are invisible to its wait-count bookkeeping)
+  }
+  // The epilogue's residual rows, requested with Q (they are read once, at the end): the
+  // work-group then does not wait for them after its last tile.
+  const bool has_res = MODE == kSparse && p.res != nullptr && p.o32_out == nullptr;
+  // (not with the pipelined loop, whose second score tile needs these registers)
+  constexpr bool PREFETCH_RES = MODE == kSparse && !RECAP_PIPE;
+  bf16x4 rpre[D / 32][4];
+  if (PREFETCH_RES && has_res) {
+    const bf16_t* rsrc = p.res + base + (int64_t)min(qrow, p.N - 1) * p.st.n;
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) asm volatile("" ::"v"(qf[ks]));
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        rpre[dt][g] = *reinterpret_cast<const bf16x4*>(rsrc + dt * 32 + g * 8 + half * 4);
   }
   f32x16 o[D / 32];
 #pragma unroll
@@ -481,19 +605,37 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RECAP_W
   int qb = 0;  // this wavefront's query block (capture mode)
   const bool pair = PAIRABLE && p.block == 64;
   if (CAP || pair) {
-    // kept-block bitmaps of the query blocks covered by this work-group
+    // kept-block bitmaps of the query blocks covered by this work-group. The counts and the
+    // first NW * 64 entries of each list are requested together (and with Q above), so the
+    // prologue waits for one round trip, not one per count and list; entries past a count are
+    // read but unused (a list row always holds M entries).
     const int nb = QROWS / p.block;  // 2 for block 64, 1 for block 128
+    const int wpr = (p.M + 31) / 32;
+    const int blk0 = (qi * QROWS) / p.block;
     qb = (qi * QROWS + wave * 32) / p.block;
-    for (int w = threadIdx.x; w < nb * ((p.M + 31) / 32); w += NW * 64)
-      kept_bits[w / ((p.M + 31) / 32)][w % ((p.M + 31) / 32)] = 0u;
+    // unconditional loads at clamped (in-bounds) addresses, conditions applied afterwards: a
+    // load behind a branch gets its wait at the branch's end
+    int cnt[BLKS], first[BLKS];
+#pragma unroll
+    for (int lb = 0; lb < BLKS; ++lb) {
+      const int64_t row = (int64_t)bh * p.M + min(blk0 + lb, p.M - 1);
+      cnt[lb] = p.count[row];
+      first[lb] = p.idx[row * p.M + min((int)threadIdx.x, p.M - 1)];
+    }
+#pragma unroll
+    for (int lb = 0; lb < BLKS; ++lb)
+      cnt[lb] = (lb < nb && blk0 + lb < p.M) ? min(max(cnt[lb], 0), p.M) : 0;
+    for (int w = threadIdx.x; w < nb * wpr; w += NW * 64) kept_bits[w / wpr][w % wpr] = 0u;
     if (threadIdx.x < BLKS) blk_flag[threadIdx.x] = 0;
     __syncthreads();
-    for (int lb = 0; lb < nb; ++lb) {
-      const int blk = (qi * QROWS) / p.block + lb;
-      if (blk >= p.M) break;
-      const int64_t row = (int64_t)bh * p.M + blk;
-      const int cnt = min(max(p.count[row], 0), p.M);
-      for (int c = threadIdx.x; c < cnt; c += NW * 64) {
+#pragma unroll
+    for (int lb = 0; lb < BLKS; ++lb) {
+      if ((int)threadIdx.x < cnt[lb]) {
+        const int jj = min(max(first[lb], 0), p.M - 1);
+        atomicOr(&kept_bits[lb][jj >> 5], 1u << (jj & 31));
+      }
+      const int64_t row = (int64_t)bh * p.M + min(blk0 + lb, p.M - 1);
+      for (int c = threadIdx.x + NW * 64; c < cnt[lb]; c += NW * 64) {
         const int jj = min(max(p.idx[row * p.M + c], 0), p.M - 1);
         atomicOr(&kept_bits[lb][jj >> 5], 1u << (jj & 31));
       }
@@ -505,24 +647,36 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RECAP_W
     for (int dt = 0; dt < D / 32; ++dt) ka.o[dt] = f32x16{};
   }
 
+  // consume the Q fragments (and the residual rows) here, so the compiler's waits for these
+  // loads sit before the loop (the tile loads in the loop are invisible to its wait-count
+  // bookkeeping)
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) asm volatile("" ::"v"(qf[ks]));
+  if (PREFETCH_RES && has_res) {
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) asm volatile("" ::"v"(rpre[dt][g]));
+  }
+
   int nlist = 0;
   if (PAIRABLE && pair) {
     UnionSeq seq{kept_bits[0], kept_bits[1], p.M, 0};
-    attend_phase<D, NW, STAGES, false, true>(seq, kbuf, vbuf, kp, vtp, p.st.n, p.N, p.block, p.npad,
+    attend_phase<D, NW, STAGES, false, true>(seq, kbuf, vbuf, kp, vtp, p.st.n, p.N, p.block,
                                      p.scale_log2, qf, o, sm, wave, lane, lc, ka,
                                      kept_bits[(wave * 32) / p.block]);
   } else if (MODE == kDense || CAP) {
     // staggered start at the diagonal: neighbouring work-groups stream the same K/V tiles at
     // nearly the same time, which keeps them in L2
     AllSeq seq{0, p.M, min((qi * QROWS) / p.block, p.M - 1)};
-    attend_phase<D, NW, STAGES, CAP>(seq, kbuf, vbuf, kp, vtp, p.st.n, p.N, p.block, p.npad,
+    attend_phase<D, NW, STAGES, CAP>(seq, kbuf, vbuf, kp, vtp, p.st.n, p.N, p.block,
                              p.scale_log2, qf, o, sm, wave, lane, lc, ka);
   } else {
     const int32_t* lst = p.idx + (int64_t)tile * p.M;  // one query block per work-group here
     nlist = min(max(((cptr_i32)p.count)[tile], 0), p.M);
     if (MODE == kCaptureR && ((cptr_u8)p.flags)[tile] == 0) return;  // done in the dense pass
     ListSeq seq{lst, nlist, 0, p.M};
-    attend_phase<D, NW, STAGES, false>(seq, kbuf, vbuf, kp, vtp, p.st.n, p.N, p.block, p.npad,
+    attend_phase<D, NW, STAGES, false>(seq, kbuf, vbuf, kp, vtp, p.st.n, p.N, p.block,
                                p.scale_log2, qf, o, sm, wave, lane, lc, ka);
   }
 
@@ -626,8 +780,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RECAP_W
   }
 
   bf16_t* dst = p.out + orow;
-  const bool has_res = MODE == kSparse && p.res != nullptr;
-  const bf16_t* rsrc = has_res ? p.res + orow : nullptr;
   const float c = p.res_scale.v[h];
   float* dst32 = (MODE == kSparse && p.o32_out != nullptr)
                      ? p.o32_out + ((int64_t)bh * p.N + qrow) * D : nullptr;
@@ -644,7 +796,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RECAP_W
         continue;
       }
       if (has_res) {
-        const bf16x4 r4 = *reinterpret_cast<const bf16x4*>(rsrc + d0);
+        bf16x4 r4;
+        if constexpr (PREFETCH_RES) r4 = rpre[dt][g];
+        else r4 = *reinterpret_cast<const bf16x4*>(p.res + orow + d0);
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] += c * (float)r4[e];
       }
@@ -661,8 +815,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RECAP_W
 // omitted interactions, block means give initial estimates of the normalisation mass and the
 // value). For query token t of query block i, over the pooled key blocks j outside i's kept
 // set: weights n_j * exp(s * q_t . K̄_j), values V̄_j. The coarse log-mass is ln of the summed
-// weights, the coarse output the weighted mean of the V̄_j. Zeroth order: the key-variance and
-// value-key-covariance refinements the page names are not applied.
+// weights, the coarse output the weighted mean of the V̄_j. With the moment refinements (MOM)
+// each weight's exponent also gets (s^2 / 2) * sum_d q_d^2 var_jd from the block's key
+// variances, and the output gets s * C q_t from the pooled within-block value-key covariance C.
 // Same tile math as attn_kernel (4 wavefronts, 128 query rows, 64 pooled keys per tile, one
 // LDS stage: a row has only ceil(M / 64) tiles), with the pooled scores from the hi + lo key
 // pair. Kept blocks and pooled keys past M get score -inf; the last pooled key's weight
@@ -880,7 +1035,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int64_t base = b * p.st.b + h * p.st.h;
   const int qrow = qi * QROWS + wave * 32 + n;
   LaneConsts<D, NW> lc;
-  lc.init(lane, wave, (int64_t)D, p.mpad);
+  lc.init(lane, wave, (int64_t)D);
   bf16x8 qf[D / 16];
   bf16x8 q2f[MOM ? D / 16 : 1];
   {
@@ -915,7 +1070,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const bf16_t* svp = MOM ? p.sv + (int64_t)bh * p.mpad * D : nullptr;
   const bf16_t* vtp = p.vt + (int64_t)bh * D * p.mpad;
   const int ntile = (p.M + kKeyTile - 1) / kKeyTile;
-  issue_v<D, NW>(vb0, vtp, p.mpad, 0, wave, lc);
+  issue_v<D, NW>(vb0, vtp, 0, wave, lc);
   issue_k<D, NW>(kb0, kp, (int64_t)D, p.M, 0, wave, lane, lc);
   issue_k<D, NW>(kl0, klp, (int64_t)D, p.M, 0, wave, lane, lc);
   if constexpr (MOM) issue_k<D, NW>(sb0, svp, (int64_t)D, p.M, 0, wave, lane, lc);
@@ -926,7 +1081,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // middle) have landed; the barrier makes them everyone's and frees the other V̄ stage
     wait_vmem<0>();
     lds_barrier();
-    if (t + 1 < ntile) issue_v<D, NW>(vb0 + ((t + 1) & 1) * TB, vtp, p.mpad, key0 + kKeyTile, wave, lc);
+    if (t + 1 < ntile) issue_v<D, NW>(vb0 + ((t + 1) & 1) * TB, vtp, key0 + kKeyTile, wave, lc);
     f32x16 s0, s1;
     tile_qk<D, NW>(kb0, qf, lc, s0, s1);
     tile_qk<D, NW, true>(kl0, qf, lc, s0, s1);  // + q . (K̄ - hi)
