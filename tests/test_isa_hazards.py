@@ -14,9 +14,12 @@
    Checked from each product along every control-flow path: its result registers do not overlap
    its sources, and no instruction writes a source register before such a read.
 3. Not a hazard but a scheduling check: no basic-block boundary falls inside a run of matrix
-   products (consecutive MFMAs a few instructions apart). A branch there keeps the scheduler
-   from issuing the next products' LDS operand reads ahead of the products; the residual
-   capture pass, with a branch around each kept-block product, ran 5% slower that way.
+   products (consecutive MFMAs a few instructions apart) that keeps accumulating into the same
+   registers across it. A branch there keeps the scheduler from issuing the next products' LDS
+   operand reads ahead of the products; the residual capture pass, with a branch around each
+   kept-block product, ran 5% slower that way. A boundary between two different runs (one
+   tile's score products and another tile's output products, which the software-pipelined
+   loop chooses per wavefront) is not a split.
 """
 import os
 import re
@@ -233,18 +236,30 @@ def test_fp8_kernel_operand_hazards(tmp_path):
         assert not bad, f"{k}:\n" + "\n".join(bad)
 
 
+def _mfma_dst(t):
+    """Destination register range of an MFMA line ('v[0:15]'), or None."""
+    m = re.match(r"^v_mfma\w*\s+([av]\[\d+:\d+\]|[av]\d+)", t)
+    return m.group(1) if m else None
+
+
 def mfma_run_splits(lines, gap=40):
-    """(function, line) of each label between two MFMAs at most `gap` lines apart."""
-    bad, func, last = [], None, None
+    """(function, line) of each label inside a product run: between two MFMAs at most `gap`
+    lines apart, the later of which accumulates into a range an MFMA of the same run (before
+    the label) wrote."""
+    bad, func, last, run = [], None, None, set()
     for i, line in enumerate(lines):
         t = line.strip()
         m = re.match(r"^(_Z\w+):", t)
         if m:
-            func, last = m.group(1), None
+            func, last, run = m.group(1), None, set()
             continue
         if t.startswith("v_mfma"):
-            if last is not None and i - last[0] <= gap and last[1] is not None:
+            dst = _mfma_dst(t)
+            if last is None or i - last[0] > gap:
+                run = set()
+            elif last[1] is not None and dst in run:
                 bad.append((func, last[1]))
+            run.add(dst)
             last = (i, None)
         elif re.match(r"^\.LBB\w+:", t) and last is not None:
             last = (last[0], i)
@@ -259,6 +274,10 @@ def test_mfma_run_split_checker():
     straight = head + mf + "\tds_read_b128 v[64:67], v80\n" + mf + "\ts_cbranch_vccnz .LBB1_3\n" \
         + mf + mf + ".LBB1_3:\n\ts_endpgm\n"
     assert mfma_run_splits(straight.splitlines()) == []
+    # a label between one run's last product and another run's first is not a split
+    other = mf.replace("v[0:15], v[64:67], v[68:71], v[0:15]", "v[16:31], v[64:67], v[68:71], 0")
+    joined = head + mf + mf + "\ts_cbranch_vccnz .LBB1_4\n.LBB1_4:\n" + other + other + "\ts_endpgm\n"
+    assert mfma_run_splits(joined.splitlines()) == []
 
 
 @pytest.mark.parametrize("src", ("attn_kernels.hip", "attn_fp8.hip"))
