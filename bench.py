@@ -232,7 +232,7 @@ def bench_tail(bsa, cfg, desc, dev_inputs, counts, idxs, s, avg, args, roof):
             omitted = ((M - counts[1].double()) * n_q).sum().item()
             est_tflops = 4.0 * D * omitted / (t["estimate"] * 1e-3) / 1e12
             res["roofline_estimate"] = roof(
-                "pool + tail_keys + pack + tail_kernel (one zeroth-order recap_tail_estimate "
+                "pool + tail_keys + kept_bits + tail_kernel (one zeroth-order recap_tail_estimate "
                 "call; algorithmic FLOPs on omitted pairs only)", est_tflops, traffic_key="tail")
 
     # accuracy at the drifted step X_1 with the refresh's kept lists and discrepancy
@@ -620,9 +620,9 @@ def main():
                 "traffic": measured_traffic(traffic_key, cfg.name) if traffic_key else None,
                 "kernel": kernel}
 
-    # achieved: algorithmic FLOPs over the HIP-event time of the library call, which also runs
-    # the V^T pack (0.27 ms at 720p) and, for the refresh, the residual fallback pass (0.13 ms
-    # when no block is flagged); traffic: the attention kernel's own counters
+    # achieved: algorithmic FLOPs over the HIP-event time of the library call (the sparse call
+    # is one launch; the refresh also runs the residual fallback pass, 0.13 ms when no block is
+    # flagged); traffic: the attention kernel's own counters
     sparse_roof = roof("attn_kernel<D=128, 4 wavefronts, sparse> (block-sparse attention with "
                        "the fused epilogue; timed as one recap_block_sparse_attn call)",
                        sp_tflops, traffic_key="attn_sparse")

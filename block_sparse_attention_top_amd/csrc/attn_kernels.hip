@@ -69,47 +69,6 @@ __device__ __forceinline__ void mfma_prio_lo() {
 #endif
 }
 
-// Key order inside each 16-key group of packed V^T: position pos holds key swap23(pos).
-__device__ __forceinline__ int swap23(int p) { return (p & 3) | ((p & 4) << 1) | ((p & 8) >> 1); }
-
-// ------------------------------------------------------------------------------------------
-// V -> packed V^T tiles [B*H][npad / 64][D][64] (npad = M * block, zero past N): each 64-key
-// tile's V^T is one contiguous 16 KB block, so a gathered tile is one sequential read rather
-// than D rows of 128 bytes spread over the head. Keys are permuted inside each 16-key group as
-// described above. One work-group per (b*h, 64-key tile), staged through LDS.
-// ------------------------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(256) void pack_vt_kernel(const bf16_t* __restrict__ v, Strides st,
-                                                      int H, int N, int npad,
-                                                      bf16_t* __restrict__ vt) {
-  constexpr int CH = D / 8;
-  __shared__ bf16_t tile[64][D + 2];
-  const int ntile = npad / 64;
-  const int bh = blockIdx.x / ntile, kt = blockIdx.x - bh * ntile;
-  const int b = bh / H, h = bh - b * H;
-  const bf16_t* src = v + b * st.b + h * st.h;
-  const int key0 = kt * 64;
-  for (int s = threadIdx.x; s < 64 * CH; s += 256) {
-    const int key = s / CH, c = s - key * CH;
-    bf16x8 x = {};
-    if (key0 + key < N) x = *reinterpret_cast<const bf16x8*>(src + (int64_t)(key0 + key) * st.n + c * 8);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) tile[key][c * 8 + e] = x[e];
-  }
-  __syncthreads();
-  bf16_t* dst = vt + (int64_t)bh * D * npad + (int64_t)key0 * D;
-  for (int s = threadIdx.x; s < D * 8; s += 256) {
-    const int d = s >> 3, c = s & 7;
-    bf16x8 y;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int pos = c * 8 + e;
-      y[e] = tile[(pos & ~15) | swap23(pos & 15)][d];
-    }
-    *reinterpret_cast<bf16x8*>(dst + d * 64 + c * 8) = y;
-  }
-}
-
 template <int D, int NW>
 struct Tiles {
   static constexpr int CH = D / 8;       // 16-byte chunks in a K row
@@ -121,25 +80,42 @@ struct Tiles {
 
 // Per-lane constants of the inner loop, computed once per work-group.
 //  K tile in LDS: row `key` (0..63) holds its 16-byte chunks XOR-swizzled, chunk c stored at
-//  position c ^ (key & (CH-1)). V^T tile: row d (0..D-1) of 64 keys, chunk c stored at
-//  c ^ ((d >> 1) & 7); in global memory the tile is D contiguous rows of 128 bytes. Both make the 16-byte MFMA-fragment reads bank-conflict free, and
-//  both reduce to "lane base XOR (ks << 5)" plus an immediate offset per 32-row tile.
+//  position c ^ (key & (CH-1)), which makes the 16-byte K fragment reads bank-conflict free
+//  and reduces them to "lane base XOR (ks << 5)" plus an immediate offset per 32-row tile.
+//  V tile in LDS: row-major like K (row `key` holds V[key][0..D)), chunk c stored at position
+//  c ^ vsw(key) (vsw below). The PV products read it with LDS transpose reads: within each
+//  group of 16 lanes, ds_read_b64_tr_b16 hands lane i element i % 4 of the 8-byte chunks that
+//  lanes i / 4 + {0, 4, 8, 12} of the group address. Lane s of group g addresses V[row][d0..d0+4)
+//  with row = 4 (g / 2) + s / 4 and d0 = 16 (g % 2) + 4 (s % 4) (plus the k-step and d tile), so
+//  lane l receives four consecutive keys at d = l % 32; two reads (keys +0 and +8) give the
+//  A operand of the 32x32x16 product: keys 4h + [0, 4) and 8 + 4h + [0, 4) for lane half h,
+//  which is the order of the P^T operand taken from the S^T accumulators.
+template <int D>
+__host__ __device__ constexpr int vsw(int key) {
+  // 16-byte chunk swizzle of V rows: the 8 rows of one transpose read (4 consecutive keys per
+  // lane half) land on distinct 64-byte bank groups
+  return D == 128 ? ((key & 3) << 2) : (((key >> 1) & 1) << 2);
+}
 template <int D, int NW>
 struct LaneConsts {
   static constexpr int LD = Tiles<D, NW>::LD;
-  // K offsets repeat with the instruction index mod 4, V^T offsets mod 2. With enough
-  // instructions per wavefront that index is a compile-time constant; otherwise the
-  // wavefront's own instructions are folded in at init (never a run-time register index).
+  // K offsets repeat with the instruction index mod 4. With enough instructions per wavefront
+  // that index is a compile-time constant; otherwise the wavefront's own instructions are
+  // folded in at init (never a run-time register index).
   static constexpr int KP = LD >= 4 ? 4 : LD;
-  static constexpr int VP = LD >= 2 ? 2 : LD;
   uint32_t k_rd, v_rd;   // LDS read offsets (bytes) within a tile buffer
   uint32_t k_voff[KP];   // K DMA source offsets (bytes)
-  uint32_t v_voff[VP];   // V^T DMA source offsets (bytes)
+  uint32_t v_voff;       // V DMA source offset (bytes; the same for every instruction)
   __device__ void init(int lane, int wave, int64_t sn) {
     constexpr int CH = Tiles<D, NW>::CH, ROWB = Tiles<D, NW>::ROWB, KROWS = Tiles<D, NW>::KROWS;
     const int n = lane & 31, half = lane >> 5;
     k_rd = opaque(n * ROWB + ((half ^ (n & (CH - 1))) << 4));
-    v_rd = opaque(n * 128 + ((half ^ ((n >> 1) & 7)) << 4));
+    {
+      const int g = lane >> 4, sl = lane & 15, t = sl >> 2;
+      const int row = 4 * (g >> 1) + t;
+      const int chunk = 2 * (g & 1) + ((sl & 3) >> 1);  // + 4 * dt, applied by XOR at the read
+      v_rd = opaque((uint32_t)(row * ROWB + ((chunk ^ vsw<D>(row)) << 4) + (sl & 1) * 8));
+    }
 #pragma unroll
     for (int r = 0; r < KP; ++r) {
       const int x = LD >= 4 ? r : wave * LD + r;
@@ -147,15 +123,11 @@ struct LaneConsts {
       const int c = (lane % CH) ^ (key & (CH - 1));
       k_voff[r] = opaque((uint32_t)((lane / CH) * sn * 2 + c * 16));
     }
-#pragma unroll
-    for (int r = 0; r < VP; ++r) {
-      const int x = LD >= 2 ? r : wave * LD + r;
-      const int c = (lane & 7) ^ ((x * 4 + (lane >> 4)) & 7);
-      v_voff[r] = opaque((uint32_t)((lane >> 3) * 128 + c * 16));
-    }
+    // rows of one V instruction are x * KROWS + lane / CH, and KROWS is a multiple of the
+    // swizzle's period, so the source chunk depends on the lane only
+    v_voff = opaque((uint32_t)((lane / CH) * sn * 2 + (((lane % CH) ^ vsw<D>(lane / CH)) * 16)));
   }
   __device__ uint32_t kv(int x, int it) const { return k_voff[LD >= 4 ? (x & 3) : it]; }
-  __device__ uint32_t vv(int x, int it) const { return v_voff[LD >= 2 ? (x & 1) : it]; }
 };
 
 // Issue the global -> LDS loads of one 64-key K tile: rows [key0, key0 + 64) of this head.
@@ -192,17 +164,34 @@ __device__ __forceinline__ void issue_k(uint32_t kbuf, const bf16_t* kp, int64_t
   }
 }
 
-// Issue the global -> LDS loads of one packed V^T tile (keys [key0, key0 + 64), key0 a
-// multiple of 64): 16 KB at vtp + key0 * D, 1 KB per instruction.
+// Issue the global -> LDS loads of one 64-key V tile (rows [key0, key0 + 64) of this head,
+// row-major, swizzled by vsw): the same DMA pattern as K, rows past N clamped to row N-1 (their
+// weights are zero).
 template <int D, int NW>
-__device__ __forceinline__ void issue_v(uint32_t vbuf, const bf16_t* vtp, int key0, int wave,
+__device__ __forceinline__ void issue_v(uint32_t vbuf, const bf16_t* vp, int64_t sn, int N,
+                                        int key0, int wave, int lane,
                                         const LaneConsts<D, NW>& lc) {
-  constexpr int LD = Tiles<D, NW>::LD;
-  const char* tile_base = (const char*)(vtp + (int64_t)key0 * D);
+  constexpr int CH = Tiles<D, NW>::CH, LD = Tiles<D, NW>::LD, KROWS = Tiles<D, NW>::KROWS;
+  const char* tile_base = (const char*)(vp + (int64_t)key0 * sn);
+  const uint32_t row_bytes = (uint32_t)(sn * 2);
+  if (key0 + 64 <= N) {
 #pragma unroll
-  for (int it = 0; it < LD; ++it) {
-    const int x = wave * LD + it;
-    load_lds16(tile_base, (uint32_t)(x * 1024 + lc.vv(x, it)), vbuf + x * 1024);
+    for (int it = 0; it < LD; ++it) {
+      const int x = wave * LD + it;
+      load_lds16(tile_base, (uint32_t)(x * KROWS * row_bytes + lc.v_voff), vbuf + x * 1024);
+    }
+  } else {
+    asm volatile("" ::: "memory");  // the rare last tile: keep its address math out of the loop
+    const int last = N - 1 - key0;
+    const int ln = (int)opaque((uint32_t)lane);
+#pragma unroll
+    for (int it = 0; it < LD; ++it) {
+      const int slot0 = (wave * LD + it) * 64;
+      const int slot = slot0 + ln;
+      const int key = slot / CH;
+      const int c = (slot % CH) ^ vsw<D>(key);
+      load_lds16(tile_base, (uint32_t)(min(key, last) * row_bytes + c * 16), vbuf + slot0 * 16);
+    }
   }
 }
 
@@ -357,6 +346,20 @@ __device__ __forceinline__ bool tile_softmax(f32x16& s0, f32x16& s1, int j, int 
   return kept;
 }
 
+// The A operand (V^T: 32 channels x 16 keys) of k-step ks and channel tile dt: two transpose
+// reads of the row-major V tile (keys 4h + [0, 4) and 8 + 4h + [0, 4) of the k-step).
+template <int D>
+__device__ __forceinline__ bf16x8 v_operand(uint32_t base, int ks, int dt) {
+  constexpr int ROWB = D * 2;
+  typedef __attribute__((ext_vector_type(4))) short i16x4;
+  typedef __attribute__((ext_vector_type(8))) short i16x8;
+  typedef __attribute__((address_space(3))) i16x4* lds_i16x4;
+  const uint32_t a = (base ^ (uint32_t)(dt << 6)) + ks * 16 * ROWB;
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4)(size_t)a);
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4)(size_t)(a + 8 * ROWB));
+  return __builtin_bit_cast(bf16x8, (i16x8)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 // O^T += V^T P^T for one tile (and the kept-block accumulator when `kept`). The kept-block
 // products form their own sequence behind one wavefront-uniform branch per tile (re-reading
 // their V^T operands from LDS), so that no branch splits the main product sequence and its
@@ -369,20 +372,18 @@ __device__ __forceinline__ void tile_pv(uint32_t vb, const bf16x8 (&pf)[4],
   mfma_prio_hi();
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
-    const uint32_t a = base ^ (uint32_t)(ks << 5);
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
-      o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read16(a + dt * 4096), pf[ks], o[dt],
+      o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_operand<D>(base, ks, dt), pf[ks], o[dt],
                                                       0, 0, 0);
   }
   if (kept) {
     const uint32_t kbase = opaque(vb + lc.v_rd);  // fresh reads, not values held from above
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      const uint32_t a = kbase ^ (uint32_t)(ks << 5);
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
-        ka.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read16(a + dt * 4096), pf[ks],
+        ka.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_operand<D>(kbase, ks, dt), pf[ks],
                                                            ka.o[dt], 0, 0, 0);
     }
   }
@@ -396,7 +397,7 @@ __device__ __forceinline__ void tile_pv(uint32_t vb, const bf16x8 (&pf)[4],
 template <int D, int NW, bool SKIP, class Seq>
 __device__ __forceinline__ void attend_phase_pipe(Seq& seq, unsigned char* kbuf,
                                                   unsigned char* vbuf, const bf16_t* kp,
-                                                  const bf16_t* vtp, int64_t sn, int N,
+                                                  const bf16_t* vp, int64_t sn, int N,
                                                   int block, float scale_log2,
                                                   const bf16x8 (&qf)[D / 16],
                                                   f32x16 (&o)[D / 32], SoftmaxState& sm,
@@ -413,7 +414,7 @@ __device__ __forceinline__ void attend_phase_pipe(Seq& seq, unsigned char* kbuf,
   };
   TileCur nxt = advance(cur, seq, block, N);
   issue_k<D, NW>(kb0, kp, sn, N, key0_of(cur), wave, lane, lc);
-  issue_v<D, NW>(vb0, vtp, key0_of(cur), wave, lc);
+  issue_v<D, NW>(vb0, vp, sn, N, key0_of(cur), wave, lane, lc);
   if (nxt.j >= 0) {
     issue_k<D, NW>(kb0 + TB, kp, sn, N, key0_of(nxt), wave, lane, lc);
     wait_vmem<2 * LD>();  // K(0) landed; V(0), K(1) may be in flight
@@ -431,7 +432,7 @@ __device__ __forceinline__ void attend_phase_pipe(Seq& seq, unsigned char* kbuf,
     wait_vmem<0>();  // V(cur) and K(nxt) landed
     lds_barrier();   // every wave is past the previous step: K buffer b, V buffer b ^ 1 free
     if (nxt2.j >= 0) issue_k<D, NW>(kb0 + b * TB, kp, sn, N, key0_of(nxt2), wave, lane, lc);
-    if (has1) issue_v<D, NW>(vb0 + (b ^ 1) * TB, vtp, key0_of(nxt), wave, lc);
+    if (has1) issue_v<D, NW>(vb0 + (b ^ 1) * TB, vp, sn, N, key0_of(nxt), wave, lane, lc);
     const bool act1 = active_for(nxt);
     if (act) {
       mask_tail(s0, s1, key0_of(cur), N, half);  // finite max: a tile has a valid key
@@ -468,14 +469,14 @@ __device__ __forceinline__ void attend_phase_pipe(Seq& seq, unsigned char* kbuf,
 //       computes only the tiles of its own block's kept set (bitmap `own`).
 template <int D, int NW, int STAGES, bool CAP, bool SKIP = false, class Seq>
 __device__ __forceinline__ void attend_phase(Seq& seq, unsigned char* kbuf, unsigned char* vbuf,
-                                             const bf16_t* kp, const bf16_t* vtp, int64_t sn,
+                                             const bf16_t* kp, const bf16_t* vp, int64_t sn,
                                              int N, int block, float scale_log2,
                                              const bf16x8 (&qf)[D / 16], f32x16 (&o)[D / 32],
                                              SoftmaxState& sm, int wave, int lane,
                                              const LaneConsts<D, NW>& lc, KeptAcc<D>& ka,
                                              const uint32_t* own = nullptr) {
   if constexpr (RECAP_PIPE && STAGES == 2 && !CAP) {
-    attend_phase_pipe<D, NW, SKIP>(seq, kbuf, vbuf, kp, vtp, sn, N, block, scale_log2, qf, o,
+    attend_phase_pipe<D, NW, SKIP>(seq, kbuf, vbuf, kp, vp, sn, N, block, scale_log2, qf, o,
                                    sm, wave, lane, lc, ka, own);
     return;
   }
@@ -487,7 +488,7 @@ __device__ __forceinline__ void attend_phase(Seq& seq, unsigned char* kbuf, unsi
   auto issue_both = [&](TileCur t, int buf) {
     const int key0 = t.j * block + t.st * kKeyTile;
     issue_k<D, NW>(kb0 + buf * TB, kp, sn, N, key0, wave, lane, lc);
-    issue_v<D, NW>(vb0 + buf * TB, vtp, key0, wave, lc);
+    issue_v<D, NW>(vb0 + buf * TB, vp, sn, N, key0, wave, lane, lc);
   };
   auto active_for = [&](int j) { return !SKIP || ((own[j >> 5] >> (j & 31)) & 1u); };
 
@@ -539,7 +540,7 @@ __device__ __forceinline__ void attend_phase(Seq& seq, unsigned char* kbuf, unsi
       if (active) tile_pv<D, NW>(vb0, pf, lc, o, ka, kept);
       lds_barrier();  // every wave is done reading the V buffer
       if (!has_next) break;
-      issue_v<D, NW>(vb0, vtp, nxt.j * block + nxt.st * kKeyTile, wave, lc);
+      issue_v<D, NW>(vb0, vp, sn, N, nxt.j * block + nxt.st * kKeyTile, wave, lane, lc);
       cur = nxt;
     }
   }
@@ -563,7 +564,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RECAP_W
   const int b = bh / p.H, h = bh - b * p.H;
   const int64_t base = b * p.st.b + h * p.st.h;
   const bf16_t* kp = p.k + base;
-  const bf16_t* vtp = p.vt + (int64_t)bh * D * p.npad;
+  const bf16_t* vp = p.v + base;
   const int qrow = qi * QROWS + wave * 32 + n;
   LaneConsts<D, NW> lc;
   lc.init(lane, wave, p.st.n);
@@ -662,21 +663,21 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RECAP_W
   int nlist = 0;
   if (PAIRABLE && pair) {
     UnionSeq seq{kept_bits[0], kept_bits[1], p.M, 0};
-    attend_phase<D, NW, STAGES, false, true>(seq, kbuf, vbuf, kp, vtp, p.st.n, p.N, p.block,
+    attend_phase<D, NW, STAGES, false, true>(seq, kbuf, vbuf, kp, vp, p.st.n, p.N, p.block,
                                      p.scale_log2, qf, o, sm, wave, lane, lc, ka,
                                      kept_bits[(wave * 32) / p.block]);
   } else if (MODE == kDense || CAP) {
     // staggered start at the diagonal: neighbouring work-groups stream the same K/V tiles at
     // nearly the same time, which keeps them in L2
     AllSeq seq{0, p.M, min((qi * QROWS) / p.block, p.M - 1)};
-    attend_phase<D, NW, STAGES, CAP>(seq, kbuf, vbuf, kp, vtp, p.st.n, p.N, p.block,
+    attend_phase<D, NW, STAGES, CAP>(seq, kbuf, vbuf, kp, vp, p.st.n, p.N, p.block,
                              p.scale_log2, qf, o, sm, wave, lane, lc, ka);
   } else {
     const int32_t* lst = p.idx + (int64_t)tile * p.M;  // one query block per work-group here
     nlist = min(max(((cptr_i32)p.count)[tile], 0), p.M);
     if (MODE == kCaptureR && ((cptr_u8)p.flags)[tile] == 0) return;  // done in the dense pass
     ListSeq seq{lst, nlist, 0, p.M};
-    attend_phase<D, NW, STAGES, false>(seq, kbuf, vbuf, kp, vtp, p.st.n, p.N, p.block,
+    attend_phase<D, NW, STAGES, false>(seq, kbuf, vbuf, kp, vp, p.st.n, p.N, p.block,
                                p.scale_log2, qf, o, sm, wave, lane, lc, ka);
   }
 
@@ -1068,9 +1069,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const bf16_t* kp = p.kb + (int64_t)bh * p.mpad * D;
   const bf16_t* klp = p.kb_lo + (int64_t)bh * p.mpad * D;
   const bf16_t* svp = MOM ? p.sv + (int64_t)bh * p.mpad * D : nullptr;
-  const bf16_t* vtp = p.vt + (int64_t)bh * D * p.mpad;
+  const bf16_t* vbp = p.vb + (int64_t)bh * p.mpad * D;  // rows >= M are zero
   const int ntile = (p.M + kKeyTile - 1) / kKeyTile;
-  issue_v<D, NW>(vb0, vtp, 0, wave, lc);
+  issue_v<D, NW>(vb0, vbp, (int64_t)D, p.mpad, 0, wave, lane, lc);
   issue_k<D, NW>(kb0, kp, (int64_t)D, p.M, 0, wave, lane, lc);
   issue_k<D, NW>(kl0, klp, (int64_t)D, p.M, 0, wave, lane, lc);
   if constexpr (MOM) issue_k<D, NW>(sb0, svp, (int64_t)D, p.M, 0, wave, lane, lc);
@@ -1081,7 +1082,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // middle) have landed; the barrier makes them everyone's and frees the other V̄ stage
     wait_vmem<0>();
     lds_barrier();
-    if (t + 1 < ntile) issue_v<D, NW>(vb0 + ((t + 1) & 1) * TB, vtp, key0 + kKeyTile, wave, lc);
+    if (t + 1 < ntile)
+      issue_v<D, NW>(vb0 + ((t + 1) & 1) * TB, vbp, (int64_t)D, p.mpad, key0 + kKeyTile, wave, lane, lc);
     f32x16 s0, s1;
     tile_qk<D, NW>(kb0, qf, lc, s0, s1);
     tile_qk<D, NW, true>(kl0, qf, lc, s0, s1);  // + q . (K̄ - hi)
@@ -1309,15 +1311,6 @@ hipError_t launch_tail_combine(int mode, int B, int H, int N, int D, Strides st,
 }
 
 // ------------------------------------------------------------------------------------------
-hipError_t launch_pack_vt(const bf16_t* v, Strides st, int B, int H, int N, int D, int npad,
-                          bf16_t* vt, hipStream_t stream) {
-  const int grid = B * H * (npad / 64);
-  if (D == 128)
-    pack_vt_kernel<128><<<grid, 256, 0, stream>>>(v, st, H, N, npad, vt);
-  else
-    pack_vt_kernel<64><<<grid, 256, 0, stream>>>(v, st, H, N, npad, vt);
-  return hipGetLastError();
-}
 
 template <int D, int NW>
 static void launch_mode(const AttnParams& p, int grid, AttnMode mode, hipStream_t stream) {

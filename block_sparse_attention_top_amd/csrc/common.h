@@ -63,15 +63,13 @@ hipError_t launch_scores_cand(const float* qbar, const float* kbar, int BH, int 
 hipError_t launch_mean_drift(const float* qbar, const float* kbar, const float* qref,
                              const float* kref, int BH, int M, int D, float* drift,
                              hipStream_t stream);
-hipError_t launch_pack_vt(const bf16_t* v, Strides st, int B, int H, int N, int D, int npad,
-                          bf16_t* vt, hipStream_t stream);
 
 enum AttnMode { kSparse = 0, kDense = 1, kCaptureR = 2, kDenseCapture = 3, kDenseTail = 4 };
 
 struct AttnParams {
   const bf16_t* q;
   const bf16_t* k;
-  const bf16_t* vt;  // packed V^T [B*H][D][npad]
+  const bf16_t* v;   // V, bf16, the layout and strides of q and k
   Strides st;
   int H, N, M, block, npad;
   int mq;  // query tiles per (b, h); set by launch_attention
@@ -100,7 +98,7 @@ struct TailParams {
   Strides st;          // q strides
   const bf16_t* kb;    // pooled keys, bf16 [B*H][mpad][D] (rows >= M zero): hi part
   const bf16_t* kb_lo; // bf16(K̄ - hi), same layout
-  const bf16_t* vt;    // pooled values, packed V^T [B*H][D][mpad]
+  const bf16_t* vb;    // pooled values, bf16 [B*H][mpad][D] (rows >= M zero)
   int H, N, M, block, mpad, mq;
   float scale_log2;
   float last_bias;     // added to the log2-unit score of pooled key M-1: log2(n_last / block)

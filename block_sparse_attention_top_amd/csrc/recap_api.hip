@@ -60,10 +60,6 @@ inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 size_t pooled_bytes(const recap_desc* d) {
   return align_up((size_t)d->batch * d->heads * num_blocks(d) * d->head_dim * sizeof(float));
 }
-size_t vt_bytes(const recap_desc* d) {
-  const size_t npad = (size_t)num_blocks(d) * d->block;
-  return align_up((size_t)d->batch * d->heads * d->head_dim * npad * 2);
-}
 size_t snapshot_bytes(const recap_desc* d) {
   const size_t npad = (size_t)num_blocks(d) * d->block;
   return align_up((size_t)d->batch * d->heads * npad * d->head_dim * sizeof(float));
@@ -97,15 +93,15 @@ size_t cov_part_bytes(const recap_desc* d) {
 size_t cov16_bytes(const recap_desc* d) {  // hi and lo halves
   return align_up((size_t)d->batch * d->heads * d->head_dim * d->head_dim * 2 * 2);
 }
-// K̄, V̄ (fp32), K̄ hi and lo, V̄ (bf16), packed V̄^T (bf16), the kept bitmaps, and for the
-// moment refinements the key variances (fp32), their scaled bf16 copy and the covariance
+// K̄, V̄ (fp32), K̄ hi and lo, V̄ (bf16), the kept bitmaps, and for the moment refinements the
+// key variances (fp32), their scaled bf16 copy and the covariance
 size_t tail_estimate_bytes(const recap_desc* d) {
-  return 2 * pooled_bytes(d) + 4 * pooled16_bytes(d) + bits_bytes(d) + pooled_bytes(d) +
+  return 2 * pooled_bytes(d) + 3 * pooled16_bytes(d) + bits_bytes(d) + pooled_bytes(d) +
          pooled16_bytes(d) + cov_part_bytes(d) + cov16_bytes(d);
 }
-// V^T; one attention part (log-sum-exp, fp32 output); the coarse tail (same); the estimate
+// one attention part (log-sum-exp, fp32 output); the coarse tail (same); the estimate
 size_t tail_merge_bytes(const recap_desc* d) {
-  return vt_bytes(d) + 2 * (row_bytes(d) + row_d_bytes(d)) + tail_estimate_bytes(d);
+  return 2 * (row_bytes(d) + row_d_bytes(d)) + tail_estimate_bytes(d);
 }
 
 // FP8 sparse call: Q codes [B*H][N][D] and scales [B*H][N][D/32], packed K and V tiles
@@ -131,8 +127,8 @@ size_t workspace_for(int op, const recap_desc* d) {
     case RECAP_OP_BLOCK_SCORES: return 2 * pooled_bytes(d);
     case RECAP_OP_TOPP: return 0;
     case RECAP_OP_SPARSE:
-    case RECAP_OP_DENSE: return vt_bytes(d);
-    case RECAP_OP_DENSE_CAPTURE: return vt_bytes(d) + snapshot_bytes(d) + flag_bytes(d);
+    case RECAP_OP_DENSE: return 0;
+    case RECAP_OP_DENSE_CAPTURE: return snapshot_bytes(d) + flag_bytes(d);
     case RECAP_OP_TAIL: return tail_estimate_bytes(d);
     case RECAP_OP_DENSE_TAIL:
     case RECAP_OP_SPARSE_TAIL: return tail_merge_bytes(d);
@@ -358,13 +354,9 @@ int sparse_impl(const recap_desc* d, const void* q, const void* k, const void* v
   hipStream_t st = (hipStream_t)stream;
   const int M = num_blocks(d);
   const int npad = M * d->block;
-  bf16_t* vt = (bf16_t*)ws;
-  hipError_t e = launch_pack_vt((const bf16_t*)v, strides_of(d), d->batch, d->heads, d->seq,
-                                d->head_dim, npad, vt, st);
-  if (e != hipSuccess) return launched(e);
   p.q = (const bf16_t*)q;
   p.k = (const bf16_t*)k;
-  p.vt = vt;
+  p.v = (const bf16_t*)v;
   p.st = strides_of(d);
   p.H = d->heads;
   p.N = d->seq;
@@ -408,15 +400,11 @@ int dense_impl(const recap_desc* d, const void* q, const void* k, const void* v,
   hipStream_t st = (hipStream_t)stream;
   const int M = num_blocks(d);
   const int npad = M * d->block;
-  bf16_t* vt = (bf16_t*)ws;
-  hipError_t e = launch_pack_vt((const bf16_t*)v, strides_of(d), d->batch, d->heads, d->seq,
-                                d->head_dim, npad, vt, st);
-  if (e != hipSuccess) return launched(e);
   AttnParams p;
   memset(&p, 0, sizeof(p));
   p.q = (const bf16_t*)q;
   p.k = (const bf16_t*)k;
-  p.vt = vt;
+  p.v = (const bf16_t*)v;
   p.st = strides_of(d);
   p.H = d->heads;
   p.N = d->seq;
@@ -428,13 +416,13 @@ int dense_impl(const recap_desc* d, const void* q, const void* k, const void* v,
   p.idx = kept_idx_opt;
   p.out = (bf16_t*)out;
   p.res_out = (bf16_t*)residual_out_opt;
-  p.od_ws = capture ? (float*)((char*)ws + vt_bytes(d)) : nullptr;
-  p.flags = capture ? (uint8_t*)ws + vt_bytes(d) + snapshot_bytes(d) : nullptr;
+  p.od_ws = capture ? (float*)ws : nullptr;
+  p.flags = capture ? (uint8_t*)ws + snapshot_bytes(d) : nullptr;
   p.lse_out = lse_out;
   p.kmass_out = kmass_out;
   // capture: the dense pass also accumulates the kept blocks and writes R; the residual pass
   // only recomputes query blocks the dense pass flagged (kept mass underflow), others exit
-  e = launch_attention(p, d->batch, d->head_dim, capture ? kDenseCapture : kDense, st);
+  hipError_t e = launch_attention(p, d->batch, d->head_dim, capture ? kDenseCapture : kDense, st);
   if (e == hipSuccess && residual_out_opt != nullptr)
     e = launch_attention(p, d->batch, d->head_dim, kCaptureR, st);
   return launched(e);
@@ -576,8 +564,7 @@ hipError_t coarse_tail(const recap_desc* d, const void* q, const void* k, const 
   bf16_t* kb_hi = (bf16_t*)w16;
   bf16_t* kb_lo = (bf16_t*)(w16 + pooled16_bytes(d));
   bf16_t* vb16 = (bf16_t*)(w16 + 2 * pooled16_bytes(d));
-  bf16_t* vt = (bf16_t*)(w16 + 3 * pooled16_bytes(d));
-  char* wm = w16 + 4 * pooled16_bytes(d);
+  char* wm = w16 + 3 * pooled16_bytes(d);
   uint32_t* bits = (uint32_t*)wm;
   float* var = (float*)(wm + bits_bytes(d));
   bf16_t* sv16 = (bf16_t*)(wm + bits_bytes(d) + pooled_bytes(d));
@@ -594,10 +581,6 @@ hipError_t coarse_tail(const recap_desc* d, const void* q, const void* k, const 
                          D, mpad, kb_hi, kb_lo, vb16, sv16, st);
   if (e == hipSuccess)
     e = launch_kept_bits(count, idx, d->batch * H * M, M, bit_words(d), bits, st);
-  if (e == hipSuccess) {
-    const Strides ps{(int64_t)H * mpad * D, (int64_t)mpad * D, (int64_t)D};
-    e = launch_pack_vt(vb16, ps, d->batch, H, M, D, mpad, vt, st);
-  }
   if (e != hipSuccess) return e;
   TailParams p;
   memset(&p, 0, sizeof(p));
@@ -605,7 +588,7 @@ hipError_t coarse_tail(const recap_desc* d, const void* q, const void* k, const 
   p.st = strides_of(d);
   p.kb = kb_hi;
   p.kb_lo = kb_lo;
-  p.vt = vt;
+  p.vb = vb16;
   p.H = H;
   p.N = d->seq;
   p.M = M;
@@ -642,15 +625,12 @@ int check_tail_args(int op, const recap_desc* d, const void* q, const void* k, c
 
 // Workspace carving shared by the dense and sparse tail calls (tail_merge_bytes).
 struct TailWs {
-  bf16_t* vt;
   float *a_lse, *a_o, *c_lse, *c_o;
   void* est;
 };
 TailWs carve_tail_ws(const recap_desc* d, void* ws) {
   char* w = (char*)ws;
   TailWs t;
-  t.vt = (bf16_t*)w;
-  w += vt_bytes(d);
   t.a_lse = (float*)w;
   w += row_bytes(d);
   t.a_o = (float*)w;
@@ -664,11 +644,11 @@ TailWs carve_tail_ws(const recap_desc* d, void* ws) {
 }
 
 void fill_attn(AttnParams& p, const recap_desc* d, const void* q, const void* k,
-               const bf16_t* vt, float sm_scale, const int32_t* count, const int32_t* idx) {
+               const void* v, float sm_scale, const int32_t* count, const int32_t* idx) {
   memset(&p, 0, sizeof(p));
   p.q = (const bf16_t*)q;
   p.k = (const bf16_t*)k;
-  p.vt = vt;
+  p.v = (const bf16_t*)v;
   p.st = strides_of(d);
   p.H = d->heads;
   p.N = d->seq;
@@ -716,17 +696,14 @@ int recap_dense_attn_tail(const recap_desc* d, const void* q, const void* k, con
 
   hipStream_t st = (hipStream_t)stream;
   const TailWs t = carve_tail_ws(d, ws);
-  hipError_t e = launch_pack_vt((const bf16_t*)v, strides_of(d), d->batch, d->heads, d->seq,
-                                d->head_dim, num_blocks(d) * d->block, t.vt, st);
-  if (e != hipSuccess) return launched(e);
   // dense pass with the kept-block accumulator: the exact tail is the dense sums minus the
   // kept ones (no residual, so no snapshot or flags)
   AttnParams p;
-  fill_attn(p, d, q, k, t.vt, sm_scale, kept_count, kept_idx);
+  fill_attn(p, d, q, k, v, sm_scale, kept_count, kept_idx);
   p.out = (bf16_t*)out;
   p.tail_lse = t.a_lse;
   p.tail_o = t.a_o;
-  e = launch_attention(p, d->batch, d->head_dim, kDenseTail, st);
+  hipError_t e = launch_attention(p, d->batch, d->head_dim, kDenseTail, st);
   if (e == hipSuccess)
     e = coarse_tail(d, q, k, v, kept_count, kept_idx, sm_scale,
                     (flags & RECAP_TAIL_MOMENTS) != 0, t.c_lse, t.c_o, t.est, st);
@@ -757,15 +734,12 @@ int recap_block_sparse_attn_tail(const recap_desc* d, const void* q, const void*
 
   hipStream_t st = (hipStream_t)stream;
   const TailWs t = carve_tail_ws(d, ws);
-  hipError_t e = launch_pack_vt((const bf16_t*)v, strides_of(d), d->batch, d->heads, d->seq,
-                                d->head_dim, num_blocks(d) * d->block, t.vt, st);
-  if (e != hipSuccess) return launched(e);
   AttnParams p;
-  fill_attn(p, d, q, k, t.vt, sm_scale, kept_count, kept_idx);
+  fill_attn(p, d, q, k, v, sm_scale, kept_count, kept_idx);
   p.out = (bf16_t*)out;  // not written: the fp32 output goes to the merge
   p.o32_out = t.a_o;
   p.lse_out = t.a_lse;
-  e = launch_attention(p, d->batch, d->head_dim, kSparse, st);
+  hipError_t e = launch_attention(p, d->batch, d->head_dim, kSparse, st);
   if (e == hipSuccess)
     e = coarse_tail(d, q, k, v, kept_count, kept_idx, sm_scale,
                     (flags & RECAP_TAIL_MOMENTS) != 0, t.c_lse, t.c_o, t.est, st);

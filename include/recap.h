@@ -117,8 +117,9 @@ int recap_abi_version(void);
 const char* recap_status_string(int status);
 
 /* Bytes of device workspace that entry point `op` needs for descriptor `d`, written to
- * *bytes. Returns RECAP_OK, RECAP_E_NULL or the descriptor's validation error. Pure host
- * computation: makes no HIP call. */
+ * *bytes; zero (top-p, sparse and plain dense attention) means the call uses none and ws
+ * may be NULL. Returns RECAP_OK, RECAP_E_NULL or the descriptor's validation error. Pure
+ * host computation: makes no HIP call. */
 int recap_workspace_size(int op, const recap_desc* d, size_t* bytes);
 
 /* Mask prediction, part 1 (RECAP Sec. 3.2 block means; first abstract of the RECAP page at

@@ -95,7 +95,9 @@ int main() {
     recap_desc e = desc(1, 128, 8192 * 128, 128, 128);
     for (int op = RECAP_OP_BLOCK_SCORES; op <= RECAP_OP_SPARSE_FP8; ++op) {
       EXPECT(recap_workspace_size(op, &e, &n), RECAP_OK);
-      if (op != RECAP_OP_TOPP && n == 0) ++failures;
+      // top-p, sparse and plain dense attention need no workspace; every other op does
+      const bool none = op == RECAP_OP_TOPP || op == RECAP_OP_SPARSE || op == RECAP_OP_DENSE;
+      if (none != (n == 0)) ++failures;
     }
     recap_desc f = desc(1024, 128, 8192 * 64, 64, 64);  // B * H * M = 2^30: accepted
     EXPECT(recap_workspace_size(RECAP_OP_SPARSE, &f, &n), RECAP_OK);

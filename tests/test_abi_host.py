@@ -62,12 +62,13 @@ def test_workspace_sizes():
     st, n = ws_size(_lib.OP_BLOCK_SCORES, d)
     assert st == 0 and n == 2 * M * 40 * 128 * 4
     assert ws_size(_lib.OP_TOPP, d) == (0, 0)
-    st, n = ws_size(_lib.OP_SPARSE, d)
-    assert st == 0 and n == 40 * 128 * M * 64 * 2
+    # sparse and plain dense attention read q, k, v as given: no workspace
+    assert ws_size(_lib.OP_SPARSE, d) == (0, 0)
+    assert ws_size(_lib.OP_DENSE, d) == (0, 0)
     st, n2 = ws_size(_lib.OP_DENSE_CAPTURE, d)
     flags = -(-40 * M // 256) * 256  # one byte per query block, 256-byte aligned
-    assert st == 0 and n2 == n + 40 * M * 64 * 128 * 4 + flags
-    # coarse tail: K̄, V̄ fp32, then K̄ hi, K̄ lo, V̄, V̄^T bf16 over M padded to 1216 pooled keys,
+    assert st == 0 and n2 == 40 * M * 64 * 128 * 4 + flags
+    # coarse tail: K̄, V̄ fp32, then K̄ hi, K̄ lo, V̄ bf16 over M padded to 1216 pooled keys,
     # the kept bitmaps (ceil(M / 32) + 1 = 38 words per query block), and for the moment
     # refinements the key variances (fp32 and a bf16 copy), 37 slices of covariance partial
     # sums (fp32 D x D) and the covariance (a bf16 pair, D x D each), each 256-byte aligned
@@ -76,10 +77,10 @@ def test_workspace_sizes():
     bits = -(-40 * M * 38 * 4 // 256) * 256
     mom = pooled + p16 + 40 * 37 * 128 * 128 * 4 + 2 * 40 * 128 * 128 * 2
     st, nt = ws_size(_lib.OP_TAIL, d)
-    assert st == 0 and nt == 2 * pooled + 4 * p16 + bits + mom
+    assert st == 0 and nt == 2 * pooled + 3 * p16 + bits + mom
     rows = 40 * 75600 * 4
     for op in (_lib.OP_DENSE_TAIL, _lib.OP_SPARSE_TAIL):
-        assert ws_size(op, d) == (0, n + 2 * (rows + rows * 128) + nt)
+        assert ws_size(op, d) == (0, 2 * (rows + rows * 128) + nt)
     # FP8 call: Q codes + scales, packed K and V tiles of 66 * D bytes per 64 keys
     q8 = 40 * 75600 * 128
     qs = -(-40 * 75600 * 4 // 256) * 256
@@ -202,7 +203,7 @@ def test_sparse_and_dense_validation():
     assert sparse(out=None) == -1
     assert sparse(out=_p(FAKE)) == -5  # out aliases q
     assert sparse(res=_p(FAKE + 8192), rs=(ctypes.c_float * 2)(0.5, float("inf"))) == -5
-    assert sparse(n=need - 256) == -6
+    assert need == 0 and sparse(ws=None, n=0) == -7  # no workspace needed
     assert sparse(s=-1.0) == -5
     assert sparse(res=_p(FAKE + 8192), rs=sc) == -7
 
