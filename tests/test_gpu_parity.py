@@ -544,6 +544,63 @@ def test_full_size_sparse(bsa, name, heads):
                     out_g=f64(out[:, h:h + 1]), extra=extra)
 
 
+@pytest.mark.parametrize("name,heads", [("wan14b_720p", [0, 21]), ("hunyuan_720p", [0, 23])])
+def test_full_size_mask_reuse(bsa, name, heads):
+    """Mask reuse at the full workloads, as the benchmark's reuse leg runs it: block means at a
+    reference step X_0 and the drifted step X_1 and their drift, candidate lists from X_0 at the
+    looser threshold 1 - (1 - p) / 4, scores from X_1's means over the candidates and top-p at p
+    over each row's candidate distribution; each against the oracle on whole heads."""
+    cfg = synth.WORKLOADS[name]
+    say(f"[test] full-size mask reuse {name}: generating inputs")
+    q0, k0, _ = synth.make_qkv(cfg)
+    q1, k1 = synth.drifted(q0, "q", 1), synth.drifted(k0, "k", 1)
+    p, _ = synth.head_params(cfg)
+    pc = np.minimum(1.0, 1.0 - (1.0 - p) / 4.0)
+    s, M = cfg.head_dim ** -0.5, cfg.num_blocks
+    q0d, k0d, q1d, k1d = (to_dev(x) for x in (q0, k0, q1, k1))
+    desc = bsa.make_desc(q0d, cfg.block)
+    say(f"[gpu] {name}: means, candidates at X_0, drift, restricted scores and top-p at X_1")
+    qb0, kb0 = bsa.recap_block_means(desc, q0d, k0d)
+    pr0 = bsa.recap_scores_from_means(desc, qb0, kb0, s)
+    cc, ci, cmask, _ = bsa.recap_topp_mask(desc, pr0, pc.tolist(), want_mask=True)
+    qb1, kb1 = bsa.recap_block_means(desc, q1d, k1d)
+    dr = bsa.recap_mean_drift(desc, qb1, kb1, qb0, kb0)
+    pr1 = bsa.recap_scores_from_means(desc, qb1, kb1, s, cc, ci)
+    kc, ki, km, kmass = bsa.recap_topp_mask_cand(desc, pr1, cc, ci, p.tolist(), want_mask=True,
+                                                 want_mass=True)
+    torch.cuda.synchronize()
+    say(f"[check] {name}: oracle on every query block of heads {heads}")
+    for h in heads:
+        q064, k064, q164, k164 = (_head(x, h) for x in (q0, k0, q1, k1))
+        means0 = O.block_mean_pool(q064, cfg.block), O.block_mean_pool(k064, cfg.block)
+        means1 = O.block_mean_pool(q164, cfg.block), O.block_mean_pool(k164, cfg.block)
+        # fp32 sums of at most `block` bf16 values: each mean within block * 2^-24 * max|x|
+        for got, ref, x in ((qb1, means1[0], q164), (kb1, means1[1], k164)):
+            tol = cfg.block * 2.0 ** -24 * np.abs(x).max()
+            assert np.abs(got[:, h:h + 1].cpu().numpy() - ref).max() <= tol, (name, h)
+        ref_dr = O.mean_drift(*means1, *means0)
+        got_dr = dr[:, h:h + 1].cpu().numpy().astype(np.float64)
+        assert np.all(ref_dr > 0) and np.abs(got_dr / ref_dr - 1).max() < 1e-3, (got_dr, ref_dr)
+        # candidate lists at X_0: the mask rule at the looser threshold
+        ref0 = O.block_scores(q064, k064, cfg.block, s)
+        parity.check_probs(pr0[:, h:h + 1].cpu().numpy().astype(np.float64), ref0)
+        c_m = cmask[:, h:h + 1].cpu().numpy().astype(bool)
+        cnt, idx = cc[:, h:h + 1].cpu().numpy(), ci[:, h:h + 1].cpu().numpy()
+        parity.check_lists(cnt, idx, M, c_m)
+        parity.check_mask(c_m, ref0, O.topp_select(ref0, pc[h:h + 1])["mask"], pc[h:h + 1])
+        # X_1: scores over the GPU's candidate lists and top-p over them
+        cand = O.mask_from_lists(cnt, idx, M)
+        ref_c = O.candidate_scores(q164, k164, cfg.block, s, cand)
+        parity.check_probs(_to_blocks(pr1[:, h:h + 1].cpu().numpy().astype(np.float64), cnt,
+                                      idx, M), ref_c)
+        gmask = km[:, h:h + 1].cpu().numpy().astype(bool)
+        assert not (gmask & ~cand).any(), "kept blocks must be candidates"
+        parity.check_lists(kc[:, h:h + 1].cpu().numpy(), ki[:, h:h + 1].cpu().numpy(), M, gmask)
+        parity.check_mask(gmask, ref_c, O.topp_select_candidates(ref_c, cand, p[h:h + 1])["mask"],
+                          p[h:h + 1])
+        assert np.abs(kmass[:, h:h + 1].cpu().numpy() - (ref_c * gmask).sum(-1)).max() <= 2e-5
+
+
 def test_full_size_refresh_then_sparse(bsa):
     """Wan2.1-14B 720p layer: dense refresh with residual capture, then a drifted sparse step
     that reuses the captured residual at scale 1."""
