@@ -648,7 +648,13 @@ def test_full_size_refresh_then_sparse(bsa):
     q1d, k1d, v1d = (to_dev(x) for x in (q1, k1, v1))
     out, count1, idx1 = bsa.sparse_step(desc, q1d, k1d, v1d, p.tolist(), s, residual=rcap,
                                         res_scale=c.tolist())
+    # the statistics entry point on the same lists: the same output bit for bit, plus the
+    # log-sum-exp over each query's kept keys
+    out_st, lse1 = bsa.recap_block_sparse_attn_stats(desc, q1d, k1d, v1d, count1, idx1, s,
+                                                     rcap, c.tolist())
     torch.cuda.synchronize()
+    assert torch.equal(out_st, out)
+    del out_st
     say(f"[check] drifted step 1: oracle on every query block of heads {heads}")
     for h in heads:
         rows = list(range(cfg.num_blocks))
@@ -662,3 +668,7 @@ def test_full_size_refresh_then_sparse(bsa):
             lo, hi = i * cfg.block, min(cfg.seq, (i + 1) * cfg.block)
             parity.check_out(got[:, :, lo:hi], ref[:, :, lo:hi], f"step1 h{h} b{i}")
         parity.check_out(got, ref, f"step1 h{h} whole head")
+        sel = [(0, 0, i) for i in _sample_rows(cfg.num_blocks, 6, 200 + h)]
+        parity.check_row_stat(lse1[:, h:h + 1].cpu().numpy(),
+                              O.attention_lse(q64, k64, cfg.block, s, mask=m_h, rows=sel),
+                              f"sparse lse step1 h{h}")
