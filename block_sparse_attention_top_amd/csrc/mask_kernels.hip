@@ -584,9 +584,26 @@ __global__ __launch_bounds__(256) void topp_wave_kernel(const float* __restrict_
       z0 = max(z0, u[i]);
     }
     uint32_t vmin = wave_min_u(a0), vmax = wave_max_u(z0);
+    // fp32 masses at the bracket ends, mass(>= vmin) and mass(>= vmax + 1); they only place the
+    // next split point
+    float m_lo = (float)total, m_hi = 0.f;
+    const float tf = (float)target;
+    int pass = 0;
     // invariant: mass(>= vmin) >= target > mass(>= vmax + 1)
     while (vmin < vmax) {
-      const uint32_t mid = vmin + ((vmax - vmin + 1u) >> 1);  // vmin < mid <= vmax
+      // split where the mass, taken as linear in the value between the bracket ends, reaches
+      // the target (about 7 passes on the 720p rows against 10 for halving the bit range); any
+      // split in (vmin, vmax] keeps the invariant, and after 16 passes plain halving bounds the
+      // count
+      uint32_t mid;
+      if (pass < 16) {
+        const float fl = __uint_as_float(vmin), fh = __uint_as_float(vmax);
+        const float frac = fminf(fmaxf((m_lo - tf) / fmaxf(m_lo - m_hi, 1e-30f), 0.f), 1.f);
+        mid = min(max(__float_as_uint(fl + frac * (fh - fl)), vmin + 1u), vmax);
+      } else {
+        mid = vmin + ((vmax - vmin + 1u) >> 1);  // vmin < mid <= vmax
+      }
+      ++pass;
       // one pass: mass of values >= mid (fp32), smallest value >= mid, largest value < mid
       float acc = 0.f;
       uint32_t a = 0xffffffffu, z = 0u;
@@ -597,12 +614,18 @@ __global__ __launch_bounds__(256) void topp_wave_kernel(const float* __restrict_
         a = min(a, ge ? u[i] : 0xffffffffu);
         z = max(z, ge ? 0u : u[i]);
       }
-      const double d = (double)wave_sum_f(acc) - target;
+      const float accs = wave_sum_f(acc);
+      const double d = (double)accs - target;
       const bool up = d > slack ? true : d < -slack ? false : mass_at_least(mid) >= target;
       // values outside [vmin, vmax] lie below vmin or above vmax, so the smallest value >= mid
       // is inside the bracket (vmax is a candidate), and so is the largest value < mid (vmin)
-      if (up) vmin = wave_min_u(a);  // mass(>= mid) >= target: the answer is >= mid
-      else vmax = wave_max_u(z);      // mass(>= mid) < target: the answer is < mid
+      if (up) {  // mass(>= mid) >= target: the answer is >= mid
+        vmin = wave_min_u(a);
+        m_lo = accs;
+      } else {  // mass(>= mid) < target: the answer is < mid
+        vmax = wave_max_u(z);
+        m_hi = accs;
+      }
     }
     const uint32_t T = vmin;
     const float vstar = __uint_as_float(T);
