@@ -228,8 +228,9 @@ __device__ __forceinline__ float wave_max_f(float x) {
 // The strip's scaled logits are computed once into LDS with the fp32 MFMA 16x16x4, as
 // S^T = K̄ Q̄^T so that lane l owns query block l % 16 and four consecutive key blocks of each
 // 16-key tile (the contraction over D is split as D index = (l / 16) * D/4 + step, identically
-// for both operands). Then each wavefront takes four rows: row max and sum from LDS, and the
-// normalised row written with consecutive lanes on consecutive key blocks.
+// for both operands). Eight wavefronts share a strip: each multiplies every eighth key tile,
+// then normalises two rows: row max and sum from LDS, and the normalised row written with
+// consecutive lanes on consecutive key blocks.
 // ------------------------------------------------------------------------------------------
 constexpr int kStripRows = 16;
 // Rows of up to kStripMaxM blocks run in one pass: 16 rows x 1268 fp32 of LDS (79.25 KB, two
@@ -238,13 +239,15 @@ constexpr int kStripMaxM = 1264;
 constexpr int kStripVals = 20;
 
 __host__ __device__ constexpr int strip_stride(int M) { return ((M + 15) / 16) * 16 + 4; }
+// wavefronts per strip work-group: 16 per CU with two work-groups, which the registers allow
+constexpr int kStripWaves = 8;
 
 // CAND: scores restricted to candidate lists (the reduced search of the GSRS abstract on the
 // RECAP page at thelatestinai.com). The strip's logits are computed the same way; each row is
 // then normalised over its candidates only, gathered from the LDS strip at the listed blocks,
 // and written at the candidate positions.
 template <int D, bool CAND>
-__global__ __launch_bounds__(256) void score_strip_kernel(const float* __restrict__ qbar,
+__global__ __launch_bounds__(kStripWaves * 64) void score_strip_kernel(const float* __restrict__ qbar,
                                                           const float* __restrict__ kbar, int M,
                                                           float scale_log2,
                                                           const int32_t* __restrict__ ccount,
@@ -288,11 +291,11 @@ __global__ __launch_bounds__(256) void score_strip_kernel(const float* __restric
   };
   float kn[KS];
   if (wave < nkt) load_k(wave, kn);
-  for (int kt = wave; kt < nkt; kt += 4) {
+  for (int kt = wave; kt < nkt; kt += kStripWaves) {
     float kv[KS];
 #pragma unroll
     for (int s = 0; s < KS; ++s) kv[s] = kn[s];
-    if (kt + 4 < nkt) load_k(kt + 4, kn);
+    if (kt + kStripWaves < nkt) load_k(kt + kStripWaves, kn);
     f32x4 a0 = {}, a1 = {};
 #pragma unroll
     for (int s = 0; s < KS; s += 2) {
@@ -309,9 +312,9 @@ __global__ __launch_bounds__(256) void score_strip_kernel(const float* __restric
     *reinterpret_cast<f32x4*>(srow + col * stride + kt * 16 + grp * 4) = x;
   }
   __syncthreads();
-  // each wavefront normalises four rows; a row (M <= 64 * kStripVals) sits in registers
-  for (int rr = 0; rr < kStripRows / 4; ++rr) {
-    const int r = wave * (kStripRows / 4) + rr;
+  // each wavefront normalises kStripRows / kStripWaves rows; a row (M <= 64 * kStripVals) sits in registers
+  for (int rr = 0; rr < kStripRows / kStripWaves; ++rr) {
+    const int r = wave * (kStripRows / kStripWaves) + rr;
     const int qrow = st * kStripRows + r;
     if (qrow >= M) break;  // uniform per wavefront
     const float* x = srow + r * stride;
@@ -827,13 +830,13 @@ hipError_t launch_scores(const float* qbar, const float* kbar, int BH, int M, in
       const hipError_t e =
           allow_lds_once((const void*)score_strip_kernel<128, false>, kMaxLds, lds128);
       if (e != hipSuccess) return e;
-      score_strip_kernel<128, false><<<sgrid, 256, lds, stream>>>(qbar, kbar, M, scale_log2,
+      score_strip_kernel<128, false><<<sgrid, kStripWaves * 64, lds, stream>>>(qbar, kbar, M, scale_log2,
                                                                   nullptr, nullptr, probs);
     } else {
       const hipError_t e =
           allow_lds_once((const void*)score_strip_kernel<64, false>, kMaxLds, lds64);
       if (e != hipSuccess) return e;
-      score_strip_kernel<64, false><<<sgrid, 256, lds, stream>>>(qbar, kbar, M, scale_log2,
+      score_strip_kernel<64, false><<<sgrid, kStripWaves * 64, lds, stream>>>(qbar, kbar, M, scale_log2,
                                                                  nullptr, nullptr, probs);
     }
     return hipGetLastError();
@@ -905,13 +908,13 @@ hipError_t launch_scores_cand(const float* qbar, const float* kbar, int BH, int 
       const hipError_t e =
           allow_lds_once((const void*)score_strip_kernel<128, true>, kMaxLds, lds128);
       if (e != hipSuccess) return e;
-      score_strip_kernel<128, true><<<sgrid, 256, lds, stream>>>(qbar, kbar, M, scale_log2,
+      score_strip_kernel<128, true><<<sgrid, kStripWaves * 64, lds, stream>>>(qbar, kbar, M, scale_log2,
                                                                  ccount, cidx, probs);
     } else {
       const hipError_t e =
           allow_lds_once((const void*)score_strip_kernel<64, true>, kMaxLds, lds64);
       if (e != hipSuccess) return e;
-      score_strip_kernel<64, true><<<sgrid, 256, lds, stream>>>(qbar, kbar, M, scale_log2,
+      score_strip_kernel<64, true><<<sgrid, kStripWaves * 64, lds, stream>>>(qbar, kbar, M, scale_log2,
                                                                 ccount, cidx, probs);
     }
     return hipGetLastError();
