@@ -24,14 +24,13 @@
 //                in registers for the whole kernel (column = query). Lane (n, half) of the
 //                result owns query n and 16 keys of each 32-key tile, so the row max needs a
 //                single cross-half exchange and the row sum stays per lane until the end.
-//   O^T += V^T P^T  A = V^T tile from LDS (row = head dim), B = P^T taken straight from the
-//                S^T registers after bf16 rounding. The 16-key contraction step pairs lane
-//                half 0 with keys {0-3, 8-11} and half 1 with {4-7, 12-15}, which is what
-//                the S^T accumulator already holds; V^T is packed with the same key order so
-//                each A fragment is one 16-byte LDS read.
-// K and V^T tiles go global -> LDS directly (global_load_lds, 16 bytes per lane) into two
-// separate buffers: the load of the next K tile overlaps softmax + PV of the current tile,
-// the load of the next V^T tile overlaps the next QK^T.
+//   O^T += V^T P^T  A = V^T (row = head dim), read from the row-major V tile in LDS with
+//                transpose reads, B = P^T taken straight from the S^T registers after bf16
+//                rounding. The 16-key contraction step pairs lane half 0 with keys
+//                {0-3, 8-11} and half 1 with {4-7, 12-15}, which is what the S^T
+//                accumulator already holds.
+// K and V tiles go global -> LDS directly (global_load_lds, 16 bytes per lane) into separate
+// buffers, loaded while earlier tiles are multiplied (see the phase drivers below).
 #include "attn_device.h"
 
 // Build-time pipeline choices (defaults are the measured best on MI355X):

@@ -3,8 +3,9 @@
 1. The compiler inserts the wait states that a vector read of a matrix-core (MFMA) result needs
    only before instructions it generated itself, not before inline asm. So along every path from
    each MFMA, the first instruction that reads its result (or the result of an MFMA issued after
-   it) must be compiler-generated. An inline-asm max over scores read straight after their
-   product saw stale registers on the device.
+   it) must be compiler-generated, and no inline asm may overwrite such a register first; a
+   compiler-generated write ends that register's result. An inline-asm max over scores read
+   straight after their product saw stale registers on the device.
 2. gfx950's scaled FP8 matrix product (v_mfma_scale_f32_32x32x64_f8f6f4) reads its operand
    registers (bytes and scales) while it runs, not only at issue, and the compiler's register
    allocation does not model that: with the result registers overlapping an operand, or an
@@ -169,6 +170,15 @@ def asm_first_reads(lines):
                     if inasm[j - 1]:
                         bad.append((cur, line.strip(), lines[j - 1].strip()))
                     break
+                killed = _writes(qop, qops) & later
+                if killed:
+                    if inasm[j - 1]:  # an asm write over a result in flight: no wait states
+                        bad.append((cur, line.strip(), lines[j - 1].strip()))
+                        break
+                    # a compiler-generated write (with its wait states) ends the result's life
+                    later = later - killed
+                    if not later:
+                        break
                 if qop == "s_endpgm":
                     break
                 if qop == "s_branch":
@@ -198,6 +208,15 @@ def test_asm_first_read_checker():
     assert len(asm_first_reads(bad.splitlines())) == 1  # the taken branch reaches the asm first
     good = head + mf + "\ts_nop 7\n\tv_max_f32_e32 v140, v50, v34\n" + asm + "\ts_endpgm\n"
     assert asm_first_reads(good.splitlines()) == []
+    # registers the compiler has overwritten no longer hold the product: the asm reads its own
+    # value there, but one register still holding a result makes the read a violation
+    dead = (head + mf + "\tv_mov_b32_e32 v50, 0\n\tv_mov_b32_e32 v51, 0\n\tv_mov_b32_e32 v52, 0\n"
+            + asm + "\ts_endpgm\n")
+    assert asm_first_reads(dead.splitlines()) == []
+    part = head + mf + "\tv_mov_b32_e32 v50, 0\n" + asm + "\ts_endpgm\n"
+    assert len(asm_first_reads(part.splitlines())) == 1
+    clobber = head + mf + "\t;;#ASMSTART\n\tv_mov_b32 v50, 0\n\t;;#ASMEND\n\ts_endpgm\n"
+    assert len(asm_first_reads(clobber.splitlines())) == 1
 
 
 @pytest.mark.parametrize("src", SOURCES)
