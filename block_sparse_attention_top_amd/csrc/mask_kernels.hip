@@ -7,6 +7,7 @@
 // every query block. Pooling and top-p are bound by HBM bandwidth and latency; the scores are
 // a small fp32 contraction done on the fp32 matrix cores.
 #include <atomic>
+#include <type_traits>
 
 #include "common.h"
 
@@ -14,8 +15,10 @@ namespace recap {
 
 // ------------------------------------------------------------------------------------------
 // Pooling: one wavefront per (tensor, b, h, block). Lanes stride over the block's rows with
-// 16-byte loads (CH lanes cover one row, G rows in flight per load), accumulate in fp32,
-// reduce across the row groups with lane shuffles and write the fp32 mean row.
+// 16-byte loads (CH lanes cover one row, G rows per load), all of a lane's loads issued before
+// the first is summed, and non-temporal (Q and K are read once here: 8-9% faster than cached
+// loads issued four at a time); then fp32 sums in row order, a reduction across the row groups
+// with lane shuffles, and the fp32 mean row.
 // ------------------------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void pool_kernel(const bf16_t* __restrict__ q,
@@ -40,12 +43,27 @@ __global__ __launch_bounds__(256) void pool_kernel(const bf16_t* __restrict__ q,
   float acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-#pragma unroll 4
-  for (int t = t0 + g; t < t1; t += G) {
-    const bf16x8 x = *reinterpret_cast<const bf16x8*>(src + (int64_t)t * st.n + c * 8);
+  // NIT loads per lane cover the block (NIT * G >= t1 - t0); past the block's last row the
+  // address is clamped to it and the value left out of the sum
+  auto pool_rows = [&](auto nit) {
+    constexpr int NIT = decltype(nit)::value;
+    bf16x8 xs[NIT];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] += (float)x[e];
-  }
+    for (int it = 0; it < NIT; ++it) {
+      const int t = min(t0 + g + it * G, t1 - 1);
+      xs[it] = __builtin_nontemporal_load(
+          reinterpret_cast<const bf16x8*>(src + (int64_t)t * st.n + c * 8));
+    }
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      if (t0 + g + it * G < t1) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += (float)xs[it][e];
+      }
+    }
+  };
+  if (t1 - t0 <= 64) pool_rows(std::integral_constant<int, 64 / G>{});
+  else pool_rows(std::integral_constant<int, 128 / G>{});  // block <= 128 (validated)
 #pragma unroll
   for (int off = CH; off < 64; off <<= 1) {
 #pragma unroll
@@ -793,6 +811,7 @@ __global__ __launch_bounds__(1024) void mean_drift_kernel(const float* __restric
 // ------------------------------------------------------------------------------------------
 hipError_t launch_pool(const bf16_t* q, const bf16_t* k, Strides st, int B, int H, int N, int D,
                        int block, float* qbar, float* kbar, hipStream_t stream) {
+  if (block < 1 || block > 128) return hipErrorInvalidValue;  // the kernel's loads cover 128 rows
   const int M = (N + block - 1) / block;
   const int rows = B * H * M;
   const int grid = (2 * rows + 3) / 4;
