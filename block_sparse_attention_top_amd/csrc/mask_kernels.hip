@@ -585,9 +585,21 @@ __global__ __launch_bounds__(256) void topp_wave_kernel(const float* __restrict_
   auto valid = [&](int i) { return i * 64 + lane < n; };
 
   bool kept[VPL];
-  double kmass;
-  const double total = mass_at_least(0u);
-  if (p >= 1.0f || total < (double)p) {
+  double kmass;  // mass of the kept set (output only)
+  // the row total in fp32. An fp32 sum here (VPL terms per lane, then six reduction levels)
+  // is within (VPL + 6) * 2^-24 * total of its exact value, so `slack` is more than twice that
+  // bound: a comparison with p decided by more than `slack` is exact, closer ones go to fp64
+  float t32 = 0.f;
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) t32 += val[i];
+  double total = (double)wave_sum_f(t32);
+  const double slack = (double)(VPL + 8) * 0x1p-23 * total;
+  bool all = p >= 1.0f;
+  if (!all && total - (double)p <= slack) {
+    total = mass_at_least(0u);  // within the error bound of p (or below): decide in fp64
+    all = total < (double)p;
+  }
+  if (all) {
     // p >= 1, or rounding left the total below p: every block is kept
 #pragma unroll
     for (int i = 0; i < VPL; ++i) kept[i] = valid(i);
@@ -596,7 +608,6 @@ __global__ __launch_bounds__(256) void topp_wave_kernel(const float* __restrict_
     // largest t with mass(>= t) >= p (p = 0 behaves like the smallest positive mass, so v* is
     // the maximum and exactly one block is kept)
     const double target = p > 0.f ? (double)p : 1e-300;
-    const double slack = (double)(VPL + 8) * 0x1p-23 * total;  // > twice the fp32 error bound
     // bracket [vmin, vmax]: the values between lo and hi; start with the whole row
     uint32_t a0 = 0xffffffffu, z0 = 0u;
 #pragma unroll
@@ -650,15 +661,28 @@ __global__ __launch_bounds__(256) void topp_wave_kernel(const float* __restrict_
     }
     const uint32_t T = vmin;
     const float vstar = __uint_as_float(T);
-    double c = 0.0;
+    int nties = 0;  // blocks holding v*
 #pragma unroll
     for (int i = 0; i < VPL; ++i)
-      if (u[i] > T) c += (double)val[i];
-    c = wave_sum(c);
-    // ties at v*, ascending index: position (i, lane) is index i*64 + lane
+      nties += (int)__builtin_popcountll(__builtin_amdgcn_ballot_w64(u[i] == T && valid(i)));
     int need = 0;  // number of tie blocks to keep
-    {
-      double cc = c;
+    if (nties == 1) {
+      // mass(> v*) < p <= mass(>= v*) holds exactly (the search's invariant): the one block
+      // at v* is kept, and the kept mass is only reported (fp32 sum)
+      need = 1;
+      float c32 = 0.f;
+#pragma unroll
+      for (int i = 0; i < VPL; ++i)
+        if (u[i] > T) c32 += val[i];
+      kmass = (double)wave_sum_f(c32) + (double)vstar;
+    } else {
+      // ties at v*, ascending index: position (i, lane) is index i*64 + lane; the running
+      // mass from mass(> v*) in fp64
+      double c = 0.0;
+#pragma unroll
+      for (int i = 0; i < VPL; ++i)
+        if (u[i] > T) c += (double)val[i];
+      double cc = wave_sum(c);
       bool done = false;
       for (int i = 0; i < VPL && !done; ++i) {
         uint64_t m = __builtin_amdgcn_ballot_w64(u[i] == T && valid(i));

@@ -152,10 +152,12 @@ int recap_block_scores_noalloc(const recap_desc* d, const void* q, const void* k
  * first and third abstracts; CalibAtt Fig. 5). Key blocks are ordered by probability,
  * descending, equal values by lower index first; k* is the smallest k whose running mass
  * reaches p_h (inclusive), or M when p_h >= 1 or when no prefix reaches p_h; the first k*
- * ordered blocks are kept. The running mass is accumulated in fp64 on the fp32 probs.
- * probs: fp32 device [B,H,M,M]. top_p_host: host array of H values in [0, 1].
+ * ordered blocks are kept. The selection is the one an fp64 running mass over the fp32 probs
+ * gives (fp32 sums decide where they are farther from p than their error bound, fp64 sums
+ * elsewhere). probs: fp32 device [B,H,M,M]. top_p_host: host array of H values in [0, 1].
  * kept_count, kept_idx: int32 device outputs (kept indices ascending). mask_opt (uint8
- * [B,H,M,M]) and kept_mass_opt (fp32 [B,H,M], mass of the kept set) may be NULL. */
+ * [B,H,M,M]) and kept_mass_opt (fp32 [B,H,M], mass of the kept set, summed in fp32 or fp64
+ * in an unspecified order) may be NULL. */
 int recap_topp_mask(const recap_desc* d, const float* probs, const float* top_p_host,
                     int32_t* kept_count, int32_t* kept_idx, uint8_t* mask_opt,
                     float* kept_mass_opt, void* stream);
