@@ -456,6 +456,35 @@ def test_topp_exact_ties(bsa, m):
         assert np.allclose(mass.cpu().numpy(), ref["mass"], rtol=1e-6, atol=1e-7)
 
 
+
+@pytest.mark.parametrize("m", [100, 1182])
+def test_topp_total_near_p(bsa, m):
+    """Rows whose total lies within the fp32 sums' error bound of p, where the selection takes
+    the total in fp64: 20 dyadic blocks 2^-1 .. 2^-20 at random places (total 1 - 2^-20, exact
+    in fp32), the rest zero. p equal to the total keeps the 20 blocks; p 2^-21 above it keeps
+    every block (no prefix reaches p); p 2^-20 below it keeps 19 (the running mass reaches p
+    exactly one block early)."""
+    say(f"[test] top-p with the row total near p, M={m}")
+    H = 3
+    g = np.random.default_rng(1000 + m)
+    probs = np.zeros((1, H, m, m), dtype=np.float32)
+    for h in range(H):
+        for r in range(m):
+            probs[0, h, r, g.choice(m, size=20, replace=False)] = 0.5 ** (1 + np.arange(20))
+    p = [1.0 - 2.0 ** -20, 1.0 - 2.0 ** -21, 1.0 - 2.0 ** -19]
+    desc = bsa.RecapDesc(1, H, m * 64, 64, 64, 0, H * m * 64 * 64, m * 64 * 64, 64)
+    count, idx, mask, mass = bsa.recap_topp_mask(desc, torch.from_numpy(probs).to(DEV), p,
+                                                 want_mask=True, want_mass=True)
+    torch.cuda.synchronize()
+    ref = O.topp_select(probs.astype(np.float64), np.array(p, dtype=np.float32).astype(np.float64))
+    cnt = count.cpu().numpy()
+    assert (cnt[0, 0] == 20).all() and (cnt[0, 1] == m).all() and (cnt[0, 2] == 19).all()
+    gm = mask.cpu().numpy().astype(bool)
+    assert np.array_equal(gm, ref["mask"])
+    assert np.array_equal(cnt, ref["count"])
+    parity.check_lists(cnt, idx.cpu().numpy(), m, gm)
+    assert np.allclose(mass.cpu().numpy(), ref["mass"], rtol=1e-6, atol=1e-7)
+
 def test_deterministic_poison_and_guards(bsa):
     say("[test] determinism, NaN poison, guard bands")
     cfg = synth.workload("tiny", heads=2, head_dim=128, grid=(1, 1, 1333))
