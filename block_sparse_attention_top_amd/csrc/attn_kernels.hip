@@ -39,6 +39,7 @@
 //   RECAP_PRIO      raise the wavefront priority around MFMA bursts
 //   RECAP_WPE       wavefronts per SIMD targeted by register allocation
 //   RECAP_PIPE      software-pipelined tile loop (next tile's QK^T under this tile's softmax)
+//   RECAP_LAST_ORDER  paired sparse walks take the last head's pairs longest list first
 #ifndef RECAP_STAGES4
 #define RECAP_STAGES4 2
 #endif
@@ -53,6 +54,9 @@
 #endif
 #ifndef RECAP_PIPE  // two-stage phases without capture overlap QK^T(t+1) with tile t's weights
 #define RECAP_PIPE 1
+#endif
+#ifndef RECAP_LAST_ORDER
+#define RECAP_LAST_ORDER 1
 #endif
 
 namespace recap {
@@ -545,6 +549,49 @@ __device__ __forceinline__ void attend_phase(Seq& seq, unsigned char* kbuf, unsi
   }
 }
 
+// The grid ends on the last (b, h): work-groups of unequal walks (paired kept lists of 20 to
+// 420 tiles at 720p) leave the launch's last wave of work-groups unbalanced. For that head only,
+// the work-group at position r of the head's pairs takes the pair of rank r by descending kept
+// count (the two query blocks' counts summed; ties by index), so the longest walks start first
+// and the launch ends on short ones (a dispatch model of the 720p lists: 3.0% -> 2.1%
+// imbalance). Every work-group of that head ranks the pairs in LDS scratch (the K stage, not yet
+// in use): each thread holds up to kOrderCand candidate pairs and compares each key, read once
+// (the same address across the work-group), against all of them. Each rank belongs to exactly
+// one pair.
+constexpr int kOrderCand = 4;
+template <int NT>
+__device__ int last_head_pair(int r, int mq, int M, const int32_t* counts, int* keys) {
+  for (int j = threadIdx.x; j < mq; j += NT) {
+    const int c0 = min(max(counts[2 * j], 0), M);
+    const int c1 = 2 * j + 1 < M ? min(max(counts[2 * j + 1], 0), M) : 0;
+    keys[j] = c0 + c1;
+  }
+  if (threadIdx.x == 0) keys[mq] = 0;
+  __syncthreads();
+  int kc[kOrderCand], rk[kOrderCand];
+#pragma unroll
+  for (int c = 0; c < kOrderCand; ++c) {
+    const int j = threadIdx.x + c * NT;
+    kc[c] = j < mq ? keys[j] : 0;
+    rk[c] = 0;
+  }
+  for (int i = 0; i < mq; ++i) {
+    const int ki = keys[i];
+#pragma unroll
+    for (int c = 0; c < kOrderCand; ++c)
+      rk[c] += (ki > kc[c] || (ki == kc[c] && i < (int)threadIdx.x + c * NT)) ? 1 : 0;
+  }
+#pragma unroll
+  for (int c = 0; c < kOrderCand; ++c) {
+    const int j = threadIdx.x + c * NT;
+    if (j < mq && rk[c] == r) keys[mq] = j;
+  }
+  __syncthreads();
+  const int q = __builtin_amdgcn_readfirstlane(keys[mq]);
+  __syncthreads();  // the scratch is the K stage: every lane has read before the first DMA
+  return q;
+}
+
 template <int D, int NW, int MODE>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RECAP_WPE, RECAP_WPE))) void attn_kernel(AttnParams p) {
   constexpr int STAGES = NW == 4 ? RECAP_STAGES4 : 1;
@@ -558,8 +605,20 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RECAP_W
   // tile = (b*H + h) * mq + query tile; in the list modes a query tile is one query block
   // runs of 64 tiles per XCD (all XCDs on one head) rather than one range per XCD: 3% faster
   // dense capture and sparse calls at 720p
-  const int tile = xcd_runs<64>(blockIdx.x, gridDim.x);
-  const int bh = tile / p.mq, qi = tile - bh * p.mq;
+  const int tile0 = xcd_runs<64>(blockIdx.x, gridDim.x);
+  const int bh = tile0 / p.mq;
+  int qi = tile0 - bh * p.mq;
+  if constexpr (MODE == kSparse && NW == 4 && RECAP_LAST_ORDER) {
+    // paired 64-row blocks only: single-block walks (block 128) are too short to repay the
+    // ranking
+    if (p.block == 64 && RECAP_PAIR && bh == (int)gridDim.x / p.mq - 1 &&
+        p.mq <= kOrderCand * NW * 64) {
+      static_assert(Tiles<D, NW>::TILE_BYTES >= (kOrderCand * NW * 64 + 1) * 4, "rank scratch");
+      qi = last_head_pair<NW * 64>(qi, p.mq, p.M, p.count + (int64_t)bh * p.M,
+                                   reinterpret_cast<int*>(kbuf));
+    }
+  }
+  const int tile = bh * p.mq + qi;
   const int b = bh / p.H, h = bh - b * p.H;
   const int64_t base = b * p.st.b + h * p.st.h;
   const bf16_t* kp = p.k + base;
