@@ -603,9 +603,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RECAP_W
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wavefront
   const int n = lane & 31, half = lane >> 5;
   // tile = (b*H + h) * mq + query tile; in the list modes a query tile is one query block
-  // runs of 64 tiles per XCD (all XCDs on one head) rather than one range per XCD: 3% faster
-  // dense capture and sparse calls at 720p
-  const int tile0 = xcd_runs<64>(blockIdx.x, gridDim.x);
+  // (or a pair). Runs of tiles per XCD, the XCDs in turn (all on one head), rather than one
+  // range per XCD: 3% faster dense capture and sparse calls at 720p. Paired sparse walks take
+  // runs of 8 pairs: with 256 pairs per head (480p) runs of 64 gave every head's same four
+  // stretches of frames to the same four XCDs, and the middle frames, whose kept lists are
+  // longer, loaded XCDs 1, 2, 5, 6 with up to 1.19x the mean work (Wan-14B 480p sparse call
+  // 3.14 -> 2.71 ms with runs of 8, 720p -0.9%); single-block walks (block 128) keep 64.
+  const bool short_runs = MODE == kSparse && NW == 4 && RECAP_PAIR && p.block == 64;
+  const int tile0 = short_runs ? xcd_runs<8>(blockIdx.x, gridDim.x)
+                               : xcd_runs<64>(blockIdx.x, gridDim.x);
   const int bh = tile0 / p.mq;
   int qi = tile0 - bh * p.mq;
   if constexpr (MODE == kSparse && NW == 4 && RECAP_LAST_ORDER) {

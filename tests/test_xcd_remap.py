@@ -42,6 +42,7 @@ int main() {
     bad |= check("xcd_remap", [](int w, int m) { return xcd_remap(w, m); }, n);
     bad |= check("xcd_runs<64>", [](int w, int m) { return xcd_runs<64>(w, m); }, n);
     bad |= check("xcd_runs<16>", [](int w, int m) { return xcd_runs<16>(w, m); }, n);
+    bad |= check("xcd_runs<8>", [](int w, int m) { return xcd_runs<8>(w, m); }, n);
     bad |= check("xcd_runs<1>", [](int w, int m) { return xcd_runs<1>(w, m); }, n);
   }
   printf(bad ? "FAIL\n" : "OK\n");
