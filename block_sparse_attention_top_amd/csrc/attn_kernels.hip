@@ -39,7 +39,6 @@
 //   RECAP_PRIO      raise the wavefront priority around MFMA bursts
 //   RECAP_WPE       wavefronts per SIMD targeted by register allocation
 //   RECAP_PIPE      software-pipelined tile loop (next tile's QK^T under this tile's softmax)
-//   RECAP_LAST_ORDER  paired sparse walks take the last head's pairs longest list first
 #ifndef RECAP_STAGES4
 #define RECAP_STAGES4 2
 #endif
@@ -54,9 +53,6 @@
 #endif
 #ifndef RECAP_PIPE  // two-stage phases without capture overlap QK^T(t+1) with tile t's weights
 #define RECAP_PIPE 1
-#endif
-#ifndef RECAP_LAST_ORDER
-#define RECAP_LAST_ORDER 1
 #endif
 
 namespace recap {
@@ -549,47 +545,44 @@ __device__ __forceinline__ void attend_phase(Seq& seq, unsigned char* kbuf, unsi
   }
 }
 
-// The grid ends on the last (b, h): work-groups of unequal walks (paired kept lists of 20 to
-// 420 tiles at 720p) leave the launch's last wave of work-groups unbalanced. For that head only,
-// the work-group at position r of the head's pairs takes the pair of rank r by descending kept
-// count (the two query blocks' counts summed; ties by index), so the longest walks start first
-// and the launch ends on short ones (a dispatch model of the 720p lists: 3.0% -> 2.1%
-// imbalance). Every work-group of that head ranks the pairs in LDS scratch (the K stage, not yet
-// in use): each thread holds up to kOrderCand candidate pairs and compares each key, read once
-// (the same address across the work-group), against all of them. Each rank belongs to exactly
-// one pair.
-constexpr int kOrderCand = 4;
-template <int NT>
-__device__ int last_head_pair(int r, int mq, int M, const int32_t* counts, int* keys) {
-  for (int j = threadIdx.x; j < mq; j += NT) {
-    const int c0 = min(max(counts[2 * j], 0), M);
-    const int c1 = 2 * j + 1 < M ? min(max(counts[2 * j + 1], 0), M) : 0;
-    keys[j] = c0 + c1;
+// The end of the grid: work-groups of unequal walks (paired kept lists of 20 to 420 tiles at
+// 720p) leave the launch's last waves of work-groups unbalanced, all the more where a launch is
+// only a few waves of work-groups long (480p). The last G tiles of a paired sparse grid
+// therefore run longest walk first: end_order_kernel sorts them by the two query blocks' kept
+// counts summed (descending, ties by tile index) into a table in the call's workspace, and the
+// work-group at position r of that group takes the tile of rank r (a dispatch model of the kept
+// lists: 720p 2.9% -> 1.7% imbalance, Wan-14B 480p 9.5% -> 4.5%, Wan-1.3B 480p 23% -> 10%).
+// One work-group of kEndOrderTiles threads: a bitonic sort of (key, index) words in LDS.
+__global__ __launch_bounds__(kEndOrderTiles) void end_order_kernel(const int32_t* __restrict__ counts,
+                                                                   int M, int mq, int n, int G,
+                                                                   int32_t* __restrict__ order) {
+  __shared__ uint32_t key[kEndOrderTiles];
+  const int j = threadIdx.x;
+  uint32_t w = 0xffffffffu;  // padding sorts last
+  if (j < G) {
+    const int t = n - G + j, bh = t / mq, pq = t - bh * mq;
+    const int32_t* c = counts + (int64_t)bh * M;
+    const int c0 = min(max(c[2 * pq], 0), M);
+    const int c1 = 2 * pq + 1 < M ? min(max(c[2 * pq + 1], 0), M) : 0;
+    // ascending words: longer walks first (c0 + c1 <= 2 * kMaxBlocks < 32768), then index
+    w = ((uint32_t)(32767 - (c0 + c1)) << 10) | (uint32_t)j;
   }
-  if (threadIdx.x == 0) keys[mq] = 0;
+  key[j] = w;
   __syncthreads();
-  int kc[kOrderCand], rk[kOrderCand];
-#pragma unroll
-  for (int c = 0; c < kOrderCand; ++c) {
-    const int j = threadIdx.x + c * NT;
-    kc[c] = j < mq ? keys[j] : 0;
-    rk[c] = 0;
+  for (int k = 2; k <= kEndOrderTiles; k <<= 1) {
+    for (int st = k >> 1; st > 0; st >>= 1) {
+      const int l = j ^ st;
+      if (l > j) {
+        const uint32_t a = key[j], b = key[l];
+        if ((a > b) == ((j & k) == 0)) {
+          key[j] = b;
+          key[l] = a;
+        }
+      }
+      __syncthreads();
+    }
   }
-  for (int i = 0; i < mq; ++i) {
-    const int ki = keys[i];
-#pragma unroll
-    for (int c = 0; c < kOrderCand; ++c)
-      rk[c] += (ki > kc[c] || (ki == kc[c] && i < (int)threadIdx.x + c * NT)) ? 1 : 0;
-  }
-#pragma unroll
-  for (int c = 0; c < kOrderCand; ++c) {
-    const int j = threadIdx.x + c * NT;
-    if (j < mq && rk[c] == r) keys[mq] = j;
-  }
-  __syncthreads();
-  const int q = __builtin_amdgcn_readfirstlane(keys[mq]);
-  __syncthreads();  // the scratch is the K stage: every lane has read before the first DMA
-  return q;
+  if (j < G) order[j] = (int32_t)(key[j] & (kEndOrderTiles - 1));
 }
 
 template <int D, int NW, int MODE>
@@ -610,21 +603,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RECAP_W
   // longer, loaded XCDs 1, 2, 5, 6 with up to 1.19x the mean work (Wan-14B 480p sparse call
   // 3.14 -> 2.71 ms with runs of 8, 720p -0.9%); single-block walks (block 128) keep 64.
   const bool short_runs = MODE == kSparse && NW == 4 && RECAP_PAIR && p.block == 64;
-  const int tile0 = short_runs ? xcd_runs<8>(blockIdx.x, gridDim.x)
-                               : xcd_runs<64>(blockIdx.x, gridDim.x);
-  const int bh = tile0 / p.mq;
-  int qi = tile0 - bh * p.mq;
-  if constexpr (MODE == kSparse && NW == 4 && RECAP_LAST_ORDER) {
-    // paired 64-row blocks only: single-block walks (block 128) are too short to repay the
-    // ranking
-    if (p.block == 64 && RECAP_PAIR && bh == (int)gridDim.x / p.mq - 1 &&
-        p.mq <= kOrderCand * NW * 64) {
-      static_assert(Tiles<D, NW>::TILE_BYTES >= (kOrderCand * NW * 64 + 1) * 4, "rank scratch");
-      qi = last_head_pair<NW * 64>(qi, p.mq, p.M, p.count + (int64_t)bh * p.M,
-                                   reinterpret_cast<int*>(kbuf));
-    }
+  int tile = short_runs ? xcd_runs<8>(blockIdx.x, gridDim.x) : xcd_runs<64>(blockIdx.x, gridDim.x);
+  if (MODE == kSparse && p.end_order != nullptr) {  // the grid's last tiles, longest walk first
+    const int g0 = (int)gridDim.x - p.end_order_g;
+    if (tile >= g0) tile = g0 + min(max(((cptr_i32)p.end_order)[tile - g0], 0), p.end_order_g - 1);
   }
-  const int tile = bh * p.mq + qi;
+  const int bh = tile / p.mq, qi = tile - bh * p.mq;
   const int b = bh / p.H, h = bh - b * p.H;
   const int64_t base = b * p.st.b + h * p.st.h;
   const bf16_t* kp = p.k + base;
@@ -1387,6 +1371,19 @@ static void launch_mode(const AttnParams& p, int grid, AttnMode mode, hipStream_
   }
   if (mode == kSparse) attn_kernel<D, NW, kSparse><<<grid, NW * 64, 0, stream>>>(p);
   if (mode == kCaptureR) attn_kernel<D, NW, kCaptureR><<<grid, NW * 64, 0, stream>>>(p);
+}
+
+int sparse_end_order_tiles(int B, int H, int M, int block) {
+  if (!(RECAP_PAIR && block == 64)) return 0;  // paired walks only: single-block walks are short
+  const int64_t n = (int64_t)B * H * ((M + 1) / 2);
+  return (int)(n < kEndOrderTiles ? n : kEndOrderTiles);
+}
+
+hipError_t launch_end_order(const int32_t* counts, int B, int H, int M, int G, int32_t* order,
+                            hipStream_t stream) {
+  const int mq = (M + 1) / 2;
+  end_order_kernel<<<1, kEndOrderTiles, 0, stream>>>(counts, M, mq, B * H * mq, G, order);
+  return hipGetLastError();
 }
 
 // Dense work-groups always cover 128 query rows (4 wavefronts sharing every K/V tile); the

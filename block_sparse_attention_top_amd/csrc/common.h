@@ -87,9 +87,18 @@ struct AttnParams {
   float* tail_lse;  // kDenseTail: [B*H][N] log-mass of the keys outside the kept set
   float* tail_o;    // kDenseTail: [B*H][N][D] attention output over those keys
   HeadScalars res_scale;
+  const int32_t* end_order;  // optional (sparse mode): ranks of the grid's last end_order_g tiles
+  int end_order_g;
 };
 
 hipError_t launch_attention(AttnParams p, int B, int D, AttnMode mode, hipStream_t stream);
+
+// The last tiles of a paired sparse grid run longest walk first: number of tiles ordered (0 when
+// the call does not order), and the one-work-group kernel that writes their order (int32 [G]).
+constexpr int kEndOrderTiles = 1024;
+int sparse_end_order_tiles(int B, int H, int M, int block);
+hipError_t launch_end_order(const int32_t* counts, int B, int H, int M, int G, int32_t* order,
+                            hipStream_t stream);
 
 // Coarse tail of the attention-level reconstruction: attention over the pooled key blocks
 // outside each query block's kept set (block means stand for their tokens).

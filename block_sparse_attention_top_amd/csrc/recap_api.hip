@@ -54,6 +54,11 @@ int validate_desc(const recap_desc* d) {
 }
 
 inline int num_blocks(const recap_desc* d) { return (d->seq + d->block - 1) / d->block; }
+// Sparse calls with paired 64-token blocks: the order of the grid's last tiles (int32 each).
+size_t end_order_bytes(const recap_desc* d) {
+  const int g = sparse_end_order_tiles(d->batch, d->heads, num_blocks(d), d->block);
+  return g > 0 ? align_up((size_t)g * sizeof(int32_t)) : 0;
+}
 
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -126,7 +131,7 @@ size_t workspace_for(int op, const recap_desc* d) {
   switch (op) {
     case RECAP_OP_BLOCK_SCORES: return 2 * pooled_bytes(d);
     case RECAP_OP_TOPP: return 0;
-    case RECAP_OP_SPARSE:
+    case RECAP_OP_SPARSE: return end_order_bytes(d);
     case RECAP_OP_DENSE: return 0;
     case RECAP_OP_DENSE_CAPTURE: return snapshot_bytes(d) + flag_bytes(d);
     case RECAP_OP_TAIL: return tail_estimate_bytes(d);
@@ -369,6 +374,14 @@ int sparse_impl(const recap_desc* d, const void* q, const void* k, const void* v
   p.res = (const bf16_t*)residual_opt;
   p.out = (bf16_t*)out;
   p.lse_out = lse_out;
+  // the grid's last tiles run longest walk first (their order written to the workspace)
+  const int g = sparse_end_order_tiles(d->batch, d->heads, M, d->block);
+  if (g > 0) {
+    hipError_t e = launch_end_order(kept_count, d->batch, d->heads, M, g, (int32_t*)ws, st);
+    if (e != hipSuccess) return launched(e);
+    p.end_order = (const int32_t*)ws;
+    p.end_order_g = g;
+  }
   return launched(launch_attention(p, d->batch, d->head_dim, kSparse, st));
 }
 

@@ -117,9 +117,10 @@ int recap_abi_version(void);
 const char* recap_status_string(int status);
 
 /* Bytes of device workspace that entry point `op` needs for descriptor `d`, written to
- * *bytes; zero (top-p, sparse and plain dense attention) means the call uses none and ws
- * may be NULL. Returns RECAP_OK, RECAP_E_NULL or the descriptor's validation error. Pure
- * host computation: makes no HIP call. */
+ * *bytes; zero (top-p, plain dense attention, sparse attention with 128-token blocks) means
+ * the call uses none and ws may be NULL. Sparse attention with 64-token blocks needs at most
+ * 4 KB. Returns RECAP_OK, RECAP_E_NULL or the descriptor's validation error. Pure host
+ * computation: makes no HIP call. */
 int recap_workspace_size(int op, const recap_desc* d, size_t* bytes);
 
 /* Mask prediction, part 1 (RECAP Sec. 3.2 block means; first abstract of the RECAP page at
@@ -171,7 +172,10 @@ int recap_topp_mask(const recap_desc* d, const float* probs, const float* top_p_
  * [0, M) are clamped; a row with count 0 outputs zeros before the epilogue).
  * residual_opt: bf16 device tensor in the q/out layout, or NULL. res_scale_host: host array
  * of H finite scales c_h, required iff residual_opt is not NULL. out: bf16 device tensor,
- * must not alias q, k, v or the residual. ws: recap_workspace_size(RECAP_OP_SPARSE) bytes. */
+ * must not alias q, k, v or the residual. ws: recap_workspace_size(RECAP_OP_SPARSE) bytes
+ * (with 64-token blocks, pairs of query blocks share work-groups and the call first writes
+ * there the order in which the launch's last work-groups take their pairs: the longest kept
+ * lists first, so that the launch does not end on long walks). */
 int recap_block_sparse_attn(const recap_desc* d, const void* q, const void* k, const void* v,
                             const int32_t* kept_count, const int32_t* kept_idx, float sm_scale,
                             const void* residual_opt, const float* res_scale_host, void* out,

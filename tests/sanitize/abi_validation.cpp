@@ -95,7 +95,8 @@ int main() {
     recap_desc e = desc(1, 128, 8192 * 128, 128, 128);
     for (int op = RECAP_OP_BLOCK_SCORES; op <= RECAP_OP_SPARSE_FP8; ++op) {
       EXPECT(recap_workspace_size(op, &e, &n), RECAP_OK);
-      // top-p, sparse and plain dense attention need no workspace; every other op does
+      // top-p, sparse (128-token blocks: no end-order table) and plain dense attention need
+      // no workspace; every other op does
       const bool none = op == RECAP_OP_TOPP || op == RECAP_OP_SPARSE || op == RECAP_OP_DENSE;
       if (none != (n == 0)) ++failures;
     }

@@ -62,8 +62,11 @@ def test_workspace_sizes():
     st, n = ws_size(_lib.OP_BLOCK_SCORES, d)
     assert st == 0 and n == 2 * M * 40 * 128 * 4
     assert ws_size(_lib.OP_TOPP, d) == (0, 0)
-    # sparse and plain dense attention read q, k, v as given: no workspace
-    assert ws_size(_lib.OP_SPARSE, d) == (0, 0)
+    # sparse and plain dense attention read q, k, v as given; paired sparse walks (64-token
+    # blocks) keep the order of the grid's last min(tiles, 1024) tiles (int32 each, 256-aligned)
+    assert ws_size(_lib.OP_SPARSE, d) == (0, 1024 * 4)
+    assert ws_size(_lib.OP_SPARSE, desc(H=2, N=4096)) == (0, 256)  # 2 x 32 pairs
+    assert ws_size(_lib.OP_SPARSE, desc(H=24, N=118800, D=128, block=128)) == (0, 0)
     assert ws_size(_lib.OP_DENSE, d) == (0, 0)
     st, n2 = ws_size(_lib.OP_DENSE_CAPTURE, d)
     flags = -(-40 * M // 256) * 256  # one byte per query block, 256-byte aligned
@@ -203,7 +206,8 @@ def test_sparse_and_dense_validation():
     assert sparse(out=None) == -1
     assert sparse(out=_p(FAKE)) == -5  # out aliases q
     assert sparse(res=_p(FAKE + 8192), rs=(ctypes.c_float * 2)(0.5, float("inf"))) == -5
-    assert need == 0 and sparse(ws=None, n=0) == -7  # no workspace needed
+    assert need == 256 and sparse(ws=None, n=0) == -6  # the end-order table is required
+    assert sparse(n=need - 1) == -6
     assert sparse(s=-1.0) == -5
     assert sparse(res=_p(FAKE + 8192), rs=sc) == -7
 
