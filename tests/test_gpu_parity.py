@@ -511,6 +511,34 @@ def test_deterministic_poison_and_guards(bsa):
     assert torch.equal(p1, p2)
 
 
+def test_sparse_grid_order_across_batches(bsa):
+    """Paired sparse walks run the grid's last min(tiles, 1024) tiles in an order computed on the
+    device from the kept counts. With B = 2 the grid has 2*4*151 = 1208 paired tiles, so the
+    ordered group starts inside batch 0 and crosses into batch 1 (and ends on a pair with one
+    query block, M = 301); each batch alone has 604 tiles, all ordered. The output of every
+    query row depends only on its own lists, so both launches must agree bit for bit."""
+    say("[test] sparse grid order: B=2 call against two B=1 calls")
+    cfg = synth.workload("tiny", batch=2, heads=4, head_dim=64, grid=(1, 1, 19240))
+    q, k, v = synth.make_qkv(cfg)
+    r = synth.make_residual(cfg)
+    qd, kd, vd, rd = (to_dev(x) for x in (q, k, v, r))
+    desc = bsa.make_desc(qd, cfg.block)
+    assert -(-cfg.seq // cfg.block) == 301
+    p = [0.9, 0.8, 0.95, 0.7]
+    c = [0.5, 1.0, 0.25, 0.0]
+    _, count, idx = bsa.sparse_step(desc, qd, kd, vd, p)
+    out = bsa.recap_block_sparse_attn(desc, qd, kd, vd, count, idx, None, rd, c)
+    lens = count.sum(dim=-1)
+    assert int(lens.min()) < int(lens.max())  # unequal walks: the order matters
+    for b in range(2):
+        sl = slice(b, b + 1)
+        d1 = bsa.make_desc(qd[sl], cfg.block)
+        o1 = bsa.recap_block_sparse_attn(d1, qd[sl], kd[sl], vd[sl], count[sl].contiguous(),
+                                         idx[sl].contiguous(), None, rd[sl], c)
+        torch.cuda.synchronize()
+        assert torch.equal(o1[0], out[b]), f"batch {b} differs"
+
+
 # ------------------------------------------------------------------------- full-size workloads
 def _sample_rows(m, n, seed):
     g = np.random.default_rng(seed)
