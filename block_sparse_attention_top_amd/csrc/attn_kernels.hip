@@ -39,6 +39,9 @@
 //   RECAP_PRIO      raise the wavefront priority around MFMA bursts
 //   RECAP_WPE       wavefronts per SIMD targeted by register allocation
 //   RECAP_PIPE      software-pipelined tile loop (next tile's QK^T under this tile's softmax)
+//   RECAP_RES_LATE  pipelined sparse loop: the epilogue's residual rows go global -> LDS into
+//                   the K buffers at the start of the last tile step (no K tile is read after
+//                   it), so their latency hides under that step's work
 #ifndef RECAP_STAGES4
 #define RECAP_STAGES4 2
 #endif
@@ -53,6 +56,9 @@
 #endif
 #ifndef RECAP_PIPE  // two-stage phases without capture overlap QK^T(t+1) with tile t's weights
 #define RECAP_PIPE 1
+#endif
+#ifndef RECAP_RES_LATE
+#define RECAP_RES_LATE 1
 #endif
 
 namespace recap {
@@ -393,7 +399,7 @@ __device__ __forceinline__ void tile_pv(uint32_t vb, const bf16x8 (&pf)[4],
 // product while the next tile's QK^T runs on the matrix cores (tile_qk_exp). K runs one tile
 // ahead of V: at the start of step t (one barrier), K(t+1) and V(t) have landed, K(t+2) goes
 // into the buffer K(t) used and V(t+1) into the one V(t-1) used. SKIP as in attend_phase.
-template <int D, int NW, bool SKIP, class Seq>
+template <int D, int NW, bool SKIP, class Seq, class Hook>
 __device__ __forceinline__ void attend_phase_pipe(Seq& seq, unsigned char* kbuf,
                                                   unsigned char* vbuf, const bf16_t* kp,
                                                   const bf16_t* vp, int64_t sn, int N,
@@ -401,11 +407,15 @@ __device__ __forceinline__ void attend_phase_pipe(Seq& seq, unsigned char* kbuf,
                                                   const bf16x8 (&qf)[D / 16],
                                                   f32x16 (&o)[D / 32], SoftmaxState& sm,
                                                   int wave, int lane, const LaneConsts<D, NW>& lc,
-                                                  KeptAcc<D>& ka, const uint32_t* own) {
+                                                  KeptAcc<D>& ka, const uint32_t* own,
+                                                  Hook& last_step) {
   constexpr int LD = Tiles<D, NW>::LD, TB = Tiles<D, NW>::TILE_BYTES;
   const int half = lane >> 5;
   TileCur cur{seq.first(), 0};
-  if (cur.j < 0) return;
+  if (cur.j < 0) {
+    last_step();
+    return;
+  }
   const uint32_t kb0 = lds_base(kbuf), vb0 = lds_base(vbuf);
   auto key0_of = [&](TileCur t) { return t.j * block + t.st * kKeyTile; };
   auto active_for = [&](TileCur t) {
@@ -430,6 +440,8 @@ __device__ __forceinline__ void attend_phase_pipe(Seq& seq, unsigned char* kbuf,
     const bool has1 = nxt.j >= 0;
     wait_vmem<0>();  // V(cur) and K(nxt) landed
     lds_barrier();   // every wave is past the previous step: K buffer b, V buffer b ^ 1 free
+    // the last tile: its scores are computed, so no wavefront reads a K buffer any more
+    if (!has1) last_step();
     if (nxt2.j >= 0) issue_k<D, NW>(kb0 + b * TB, kp, sn, N, key0_of(nxt2), wave, lane, lc);
     if (has1) issue_v<D, NW>(vb0 + (b ^ 1) * TB, vp, sn, N, key0_of(nxt), wave, lane, lc);
     const bool act1 = active_for(nxt);
@@ -466,17 +478,22 @@ __device__ __forceinline__ void attend_phase_pipe(Seq& seq, unsigned char* kbuf,
 //             every tile has a full tile of compute to land (two barriers per tile).
 // SKIP: the work-group streams the union of two query blocks' kept sets; each wavefront
 //       computes only the tiles of its own block's kept set (bitmap `own`).
-template <int D, int NW, int STAGES, bool CAP, bool SKIP = false, class Seq>
+struct NoHook {
+  __device__ void operator()() const {}
+};
+
+template <int D, int NW, int STAGES, bool CAP, bool SKIP = false, class Seq, class Hook = NoHook>
 __device__ __forceinline__ void attend_phase(Seq& seq, unsigned char* kbuf, unsigned char* vbuf,
                                              const bf16_t* kp, const bf16_t* vp, int64_t sn,
                                              int N, int block, float scale_log2,
                                              const bf16x8 (&qf)[D / 16], f32x16 (&o)[D / 32],
                                              SoftmaxState& sm, int wave, int lane,
                                              const LaneConsts<D, NW>& lc, KeptAcc<D>& ka,
-                                             const uint32_t* own = nullptr) {
+                                             const uint32_t* own = nullptr,
+                                             Hook last_step = Hook{}) {
   if constexpr (RECAP_PIPE && STAGES == 2 && !CAP) {
     attend_phase_pipe<D, NW, SKIP>(seq, kbuf, vbuf, kp, vp, sn, N, block, scale_log2, qf, o,
-                                   sm, wave, lane, lc, ka, own);
+                                   sm, wave, lane, lc, ka, own, last_step);
     return;
   }
   constexpr int LD = Tiles<D, NW>::LD, TB = Tiles<D, NW>::TILE_BYTES;
@@ -628,6 +645,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RECAP_W
   const bool has_res = MODE == kSparse && p.res != nullptr && p.o32_out == nullptr;
   // (not with the pipelined loop, whose second score tile needs these registers)
   constexpr bool PREFETCH_RES = MODE == kSparse && !RECAP_PIPE;
+  // pipelined sparse loop: the residual rows go to LDS during the last tile step (rows of
+  // D * 2 bytes, 16-byte chunk c of row r at position c ^ (r mod CH): conflict-free reads)
+  constexpr bool LATE_RES = MODE == kSparse && RECAP_PIPE && RECAP_RES_LATE && STAGES == 2;
+  constexpr int RES_WAVE_BYTES = 32 * D * 2;  // one wavefront's rows
+  static_assert(!LATE_RES || NW * RES_WAVE_BYTES <= STAGES * Tiles<D, NW>::TILE_BYTES,
+                "residual rows must fit in the K buffers");
   bf16x4 rpre[D / 32][4];
   if (PREFETCH_RES && has_res) {
     const bf16_t* rsrc = p.res + base + (int64_t)min(qrow, p.N - 1) * p.st.n;
@@ -709,11 +732,29 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RECAP_W
   }
 
   int nlist = 0;
+  auto last_step = [&]() {
+    if constexpr (LATE_RES) {
+      if (has_res) {
+        constexpr int CH = D / 8;  // 16-byte chunks per row
+        const int r0 = min(qi * QROWS + wave * 32, p.N - 1);  // the wavefront's first row
+        const char* rbase = (const char*)(p.res + base + (int64_t)r0 * p.st.n);
+        const uint32_t dst = lds_base(kbuf) + wave * RES_WAVE_BYTES;
+        const int ln = (int)opaque((uint32_t)lane);
+#pragma unroll
+        for (int x = 0; x < RES_WAVE_BYTES / 1024; ++x) {
+          const int slot = x * 64 + ln, row = slot / CH, pos = slot % CH;
+          const int c = pos ^ (row & (CH - 1));
+          const int rr = min(r0 + row, p.N - 1) - r0;  // rows past N read row N - 1 (unused)
+          load_lds16(rbase, (uint32_t)(rr * (uint32_t)(p.st.n * 2) + c * 16), dst + x * 1024);
+        }
+      }
+    }
+  };
   if (PAIRABLE && pair) {
     UnionSeq seq{kept_bits[0], kept_bits[1], p.M, 0};
     attend_phase<D, NW, STAGES, false, true>(seq, kbuf, vbuf, kp, vp, p.st.n, p.N, p.block,
                                      p.scale_log2, qf, o, sm, wave, lane, lc, ka,
-                                     kept_bits[(wave * 32) / p.block]);
+                                     kept_bits[(wave * 32) / p.block], last_step);
   } else if (MODE == kDense || CAP) {
     // staggered start at the diagonal: neighbouring work-groups stream the same K/V tiles at
     // nearly the same time, which keeps them in L2
@@ -726,7 +767,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RECAP_W
     if (MODE == kCaptureR && ((cptr_u8)p.flags)[tile] == 0) return;  // done in the dense pass
     ListSeq seq{lst, nlist, 0, p.M};
     attend_phase<D, NW, STAGES, false>(seq, kbuf, vbuf, kp, vp, p.st.n, p.N, p.block,
-                               p.scale_log2, qf, o, sm, wave, lane, lc, ka);
+                               p.scale_log2, qf, o, sm, wave, lane, lc, ka, nullptr,
+                               last_step);
   }
 
   const float lt = cross_half_sum(sm.l);
@@ -830,6 +872,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RECAP_W
 
   bf16_t* dst = p.out + orow;
   const float c = p.res_scale.v[h];
+  if (LATE_RES && has_res) wait_vmem<0>();  // this wavefront's residual rows are in LDS
+  const uint32_t res_lds = lds_base(kbuf) + wave * RES_WAVE_BYTES + n * (D * 2) + half * 8;
   float* dst32 = (MODE == kSparse && p.o32_out != nullptr)
                      ? p.o32_out + ((int64_t)bh * p.N + qrow) * D : nullptr;
 #pragma unroll
@@ -847,6 +891,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RECAP_W
       if (has_res) {
         bf16x4 r4;
         if constexpr (PREFETCH_RES) r4 = rpre[dt][g];
+        else if constexpr (LATE_RES)
+          r4 = *reinterpret_cast<const __attribute__((address_space(3))) bf16x4*>(
+              (size_t)(res_lds + (((dt * 4 + g) ^ (n & (D / 8 - 1))) << 4)));
         else r4 = *reinterpret_cast<const bf16x4*>(p.res + orow + d0);
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] += c * (float)r4[e];

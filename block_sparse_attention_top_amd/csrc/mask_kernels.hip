@@ -546,8 +546,14 @@ __device__ __forceinline__ double wave_sum(double x) {
   return x;
 }
 
+// Rows of 16 or 20 values per lane (up to 1280 blocks: the 720p and HunyuanVideo rows) run at
+// six wavefronts per SIMD instead of the four their default register allocation gives (one
+// register is held in scratch across the threshold search: one store and one load per row);
+// longer rows would spill inside the search, shorter ones reach that occupancy anyway.
+__host__ __device__ constexpr int topp_min_waves(int vpl) { return vpl == 16 || vpl == 20 ? 6 : 1; }
+
 template <int VPL>
-__global__ __launch_bounds__(256) void topp_wave_kernel(const float* __restrict__ probs, int H,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(topp_min_waves(VPL)))) void topp_wave_kernel(const float* __restrict__ probs, int H,
                                                         int M, int rows, HeadScalars top_p,
                                                         const int32_t* __restrict__ ccount,
                                                         const int32_t* __restrict__ cidx,
