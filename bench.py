@@ -414,10 +414,12 @@ def bench_fp8(bsa, cfg, desc, dev_inputs, counts, idxs, s, res, res_scale, avg, 
     }
 
 
-def probe_peaks(dev):
+def probe_peaks(dev, bsa):
     """Practical ceilings on this machine: a plain bf16 GEMM (8192^3, contiguous 2-D operands,
-    torch's library GEMM) and a 2 GiB device-to-device copy, each timed with HIP events over
-    several repetitions after a warm-up."""
+    torch's library GEMM), a 2 GiB device-to-device copy, and dense attention at 8 heads of the
+    720p shape (B=1, N=75,600, D=128, bf16) through this library's recap_dense_attn and through
+    torch's scaled_dot_product_attention restricted to its flash and memory-efficient backends
+    (no math fallback), each timed with HIP events over several repetitions after a warm-up."""
     import numpy as np
     import torch
 
@@ -446,9 +448,33 @@ def probe_peaks(dev):
     ms_copy = timed(lambda: dst.copy_(src), 20)
     gemm = 2.0 * n ** 3 / (ms_gemm * 1e-3) / 1e12
     copy = 2.0 * nbytes / (ms_copy * 1e-3) / 1e9  # read + write
+    del a, b, c, src, dst
+
+    # dense attention, this library against torch's fused attention backends
+    ah, an, ad = 8, 75600, 128
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    q, k, v = (torch.randn((1, ah, an, ad), generator=g, device=dev).to(torch.bfloat16)
+               for _ in range(3))
+    aflops = 4.0 * ah * an * an * ad
+    out = torch.empty_like(q)
+    desc = bsa.make_desc(q, 64)
+    attn = {"shape": {"batch": 1, "heads": ah, "seq": an, "head_dim": ad}}
+    ms = timed(lambda: bsa.recap_dense_attn(desc, q, k, v, None, None, None, out), 3)
+    attn["recap_dense_attn_tflops"] = aflops / (ms * 1e-3) / 1e12
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    for name, backend in (("flash", SDPBackend.FLASH_ATTENTION),
+                          ("efficient", SDPBackend.EFFICIENT_ATTENTION)):
+        try:
+            with sdpa_kernel([backend]):
+                ms = timed(lambda: torch.nn.functional.scaled_dot_product_attention(q, k, v), 3)
+            attn[f"torch_sdpa_{name}_tflops"] = aflops / (ms * 1e-3) / 1e12
+        except RuntimeError as e:  # backend not built for this device: no fallback is timed
+            attn[f"torch_sdpa_{name}_tflops"] = None
+            log(f"torch SDPA {name} backend unavailable: {str(e)[:120]}")
     return {"gemm_bf16_tflops": gemm, "gemm_frac_bf16_peak": gemm / PEAK_BF16_TFLOPS,
             "gemm_shape": [n, n, n], "copy_gbs": copy, "copy_frac_hbm_peak": copy / PEAK_HBM_GBS,
-            "copy_bytes": nbytes}
+            "copy_bytes": nbytes, "dense_attention": attn}
 
 
 def cpu_model():
@@ -681,8 +707,8 @@ def main():
         "roofline_mask": mask_roof,
     }
     if args.probe_peaks:
-        log("probe: bf16 GEMM and device copy")
-        result["probe"] = probe_peaks(dev)
+        log("probe: bf16 GEMM, device copy, dense attention against torch SDPA")
+        result["probe"] = probe_peaks(dev, bsa)
     if args.fp8:
         res = rcap if cfg.refresh_then_sparse else r_dev
         result["fp8"] = bench_fp8(bsa, cfg, desc, dev_inputs, counts, idxs, s, res, res_scale,
