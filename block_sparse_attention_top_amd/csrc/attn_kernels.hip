@@ -844,6 +844,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RECAP_W
     return;
   }
 
+  // this wavefront's residual rows are in LDS (waited for before any lane leaves: a wavefront
+  // whose rows all lie past N ends here, with no load of its own still in flight)
+  if (LATE_RES && has_res) wait_vmem<0>();
   if (qrow >= p.N) return;
   const int64_t orow = base + (int64_t)qrow * p.st.n;
   if (MODE != kCaptureR && p.lse_out != nullptr && half == 0)
@@ -872,7 +875,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RECAP_W
 
   bf16_t* dst = p.out + orow;
   const float c = p.res_scale.v[h];
-  if (LATE_RES && has_res) wait_vmem<0>();  // this wavefront's residual rows are in LDS
   const uint32_t res_lds = lds_base(kbuf) + wave * RES_WAVE_BYTES + n * (D * 2) + half * 8;
   float* dst32 = (MODE == kSparse && p.o32_out != nullptr)
                      ? p.o32_out + ((int64_t)bh * p.N + qrow) * D : nullptr;
